@@ -1,0 +1,147 @@
+"""fp64 CPU oracle for the Kimi Delta Attention (KDA) forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the HIP product path never does, and
+this package never imports the HIP path.
+
+What it computes (definitions cited by page title and section):
+
+* Recurrence (Eq. 1), "Kimi K3: the paper and proofs side by side", section
+  2.1.1 (Equation 1) and its factorised ``update``: per (batch, head), token
+  by token, decay the key rows of S by alpha_t, read the decayed state with
+  k_t, subtract beta_t k_t (x) read, add beta_t k_t (x) v_t; then the query
+  reads the updated state, o_t = S_t^T q_t.  Implemented in C
+  (kda_oracle.c), fp64 throughout.
+* Gate (Eq. 5), "Kimi K3 reading notes", section 2: g = g_min *
+  sigmoid(exp(A^h) z), alpha = exp(g), g_min = -5.
+* Decode: one step of the same recurrence per sequence, state carried.
+
+Every entry point takes fp64 numpy arrays in the layouts of kda_oracle.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+
+from . import build as _build
+
+G_MIN = -5.0
+
+_DP = ctypes.POINTER(ctypes.c_double)
+
+
+def _p(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    assert a.dtype == np.float64 and a.flags.c_contiguous
+    return a.ctypes.data_as(_DP)
+
+
+def _f64(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
+
+
+class Oracle:
+    """ctypes view of one build of kda_oracle.c (the default build, or a
+    variant library built by a test from a modified copy of the source)."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        L = ctypes.c_long
+        lib.kda_oracle_gate.argtypes = [_DP, _DP, ctypes.c_double, L, L, L, L, L, _DP]
+        lib.kda_oracle_gate.restype = ctypes.c_int
+        lib.kda_oracle_recurrence.argtypes = [_DP, _DP, _DP, _DP, _DP, _DP, _DP, _DP, L, L, L, L, L,
+                                              ctypes.c_double, ctypes.c_int]
+        lib.kda_oracle_recurrence.restype = ctypes.c_int
+        lib.kda_oracle_forward_z.argtypes = [_DP, _DP, _DP, _DP, _DP, _DP, ctypes.c_double, _DP, _DP, _DP,
+                                             L, L, L, L, L, ctypes.c_double, ctypes.c_int]
+        lib.kda_oracle_forward_z.restype = ctypes.c_int
+        self.lib = lib
+        self.path = path
+
+    def gate(self, z: np.ndarray, A: np.ndarray, g_min: float = G_MIN, chunk: int = 1) -> np.ndarray:
+        """G [B,T,H,dk]: chunk-local inclusive sums of g = g_min*sigmoid(exp(A) z)
+        over chunks of ``chunk`` tokens (chunk=1 gives g itself)."""
+        z = _f64(z)
+        A = _f64(A)
+        B, T, H, dk = z.shape
+        G = np.empty_like(z)
+        rc = self.lib.kda_oracle_gate(_p(z), _p(A), float(g_min), B, T, H, dk, int(chunk), _p(G))
+        if rc != 0:
+            raise ValueError("kda_oracle_gate: bad arguments")
+        return G
+
+    def recurrence(self, q, k, v, beta, g, S0=None, scale: float = 1.0,
+                   nthreads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+        """Eq. 1 token by token with per-token log-decay g (alpha = exp(g)).
+        Returns (o [B,T,H,dv], S_T [B,H,dk,dv])."""
+        q, k, v, beta, g, S0 = map(_f64, (q, k, v, beta, g, S0))
+        B, T, H, dk = k.shape
+        dv = v.shape[-1]
+        o = np.zeros((B, T, H, dv))
+        S = np.zeros((B, H, dk, dv))
+        rc = self.lib.kda_oracle_recurrence(_p(q), _p(k), _p(v), _p(beta), _p(g), _p(S0), _p(o), _p(S),
+                                            B, T, H, dk, dv, float(scale), int(nthreads))
+        if rc != 0:
+            raise ValueError("kda_oracle_recurrence: bad arguments")
+        return o, S
+
+    def forward_z(self, q, k, v, beta, z, A, g_min: float = G_MIN, S0=None, scale: float = 1.0,
+                  nthreads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+        """Gate from decay logits z, then Eq. 1.  Returns (o, S_T)."""
+        q, k, v, beta, z, A, S0 = map(_f64, (q, k, v, beta, z, A, S0))
+        B, T, H, dk = k.shape
+        dv = v.shape[-1]
+        o = np.zeros((B, T, H, dv))
+        S = np.zeros((B, H, dk, dv))
+        rc = self.lib.kda_oracle_forward_z(_p(q), _p(k), _p(v), _p(beta), _p(z), _p(A), float(g_min),
+                                           _p(S0), _p(o), _p(S), B, T, H, dk, dv, float(scale), int(nthreads))
+        if rc != 0:
+            raise ValueError("kda_oracle_forward_z: bad arguments")
+        return o, S
+
+
+_default: Optional[Oracle] = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        if not os.path.exists(_build.LIB) or os.path.getmtime(_build.LIB) < os.path.getmtime(_build.SRC):
+            _build.build()
+        _default = Oracle(_build.LIB)
+    return _default
+
+
+def gate(z, A, g_min: float = G_MIN, chunk: int = 1):
+    return default().gate(z, A, g_min, chunk)
+
+
+def recurrence(q, k, v, beta, g, S0=None, scale: float = 1.0, nthreads: int = 0):
+    return default().recurrence(q, k, v, beta, g, S0, scale, nthreads)
+
+
+def forward_z(q, k, v, beta, z, A, g_min: float = G_MIN, S0=None, scale: float = 1.0, nthreads: int = 0):
+    return default().forward_z(q, k, v, beta, z, A, g_min, S0, scale, nthreads)
+
+
+def decode(q, k, v, z, beta, A, S0, g_min: float = G_MIN, scale: float = 1.0,
+           nthreads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """Decode protocol: ``steps`` consecutive single-token updates.
+
+    q, k, z: [steps, N, H, dk]; v: [steps, N, H, dv]; beta: [steps, N, H];
+    S0: [N, H, dk, dv].  Each step advances every sequence's state by one
+    token (the same recurrence with T = 1) and reads it.
+    Returns (o [steps, N, H, dv], S after the last step)."""
+    q, k, v, z, beta, A, S = map(_f64, (q, k, v, z, beta, A, S0))
+    steps = q.shape[0]
+    outs = []
+    for s in range(steps):
+        # [N, H, d] -> [B=N, T=1, H, d]
+        o, S = forward_z(q[s][:, None], k[s][:, None], v[s][:, None], beta[s][:, None], z[s][:, None], A,
+                         g_min, S, scale, nthreads)
+        outs.append(o[:, 0])
+    return np.stack(outs) if outs else np.zeros((0,) + S.shape[:2] + (S.shape[-1],)), S

@@ -1,0 +1,68 @@
+"""Plant plausible mistakes in a copy of the oracle's C source (on the CPU)
+and require each broken build to fail at least one pin.  This is what makes
+the pins a check of the oracle rather than a restatement of it."""
+import os
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+from oracle import build as obuild
+from tests import _pins
+
+SRC = open(obuild.SRC).read()
+READ_CALL = "    read_output(J, S, qt, row, j0, nc);\n"
+
+MUTATIONS = {
+    "correction_sign": [("S[c * nc + j] - bt * kt[c] * read[j]", "S[c * nc + j] + bt * kt[c] * read[j]")],
+    "write_without_beta": [("+ bt * kt[c] * vt[j0 + j]", "+ kt[c] * vt[j0 + j]")],
+    "read_with_query": [("acc += kt[c] * S[c * nc + j]", "acc += qt[c] * S[c * nc + j]")],
+    "no_decay": [("S[c * nc + j] *= alpha[c];", "S[c * nc + j] *= 1.0;")],
+    "decay_after_erase": [
+        ("S[c * nc + j] *= alpha[c];", "S[c * nc + j] *= 1.0;"),
+        ("S[c * nc + j] = S[c * nc + j] - bt * kt[c] * read[j] + bt * kt[c] * vt[j0 + j];",
+         "S[c * nc + j] = alpha[c] * (S[c * nc + j] - bt * kt[c] * read[j]) + bt * kt[c] * vt[j0 + j];"),
+    ],
+    "read_before_update": [
+        (READ_CALL, ""),
+        ("    /* 1. decay:", READ_CALL + "    /* 1. decay:"),
+    ],
+    "sigmoid_sign": [("double s = 1.0 / (1.0 + exp(-x));", "double s = 1.0 / (1.0 + exp(x));")],
+    "gate_without_exp_A": [("double x = exp(A) * z;", "double x = A * z;")],
+    "chunk_reset_off_by_one": [("if (t % chunk == 0) run = 0.0;", "if (t % chunk == 1) run = 0.0;")],
+    "state_in_ignored": [("if (J->S_in) {", "if (0) {")],
+    "state_in_transposed": [("S[c * nc + (j - j0)] = Si[c * dv + j];", "S[c * nc + (j - j0)] = Si[j * dk + c];")],
+    "scale_ignored": [("ot[j0 + j] = J->scale * acc;", "ot[j0 + j] = acc;")],
+    "alpha_not_exponentiated": [("alpha[c] = exp(g);", "alpha[c] = 1.0 + g;")],
+}
+
+
+@pytest.fixture(scope="module")
+def workdir():
+    d = tempfile.mkdtemp(prefix="kda_oracle_mut_")
+    shutil.copy(os.path.join(os.path.dirname(obuild.SRC), "kda_oracle.h"), d)
+    yield d
+    shutil.rmtree(d, ignore_errors=True)
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, workdir):
+    src = SRC
+    for old, new in MUTATIONS[name]:
+        assert src.count(old) == 1, f"mutation anchor not unique/found: {old!r}"
+        src = src.replace(old, new)
+    c = os.path.join(workdir, f"{name}.c")
+    so = os.path.join(workdir, f"{name}.so")
+    with open(c, "w") as f:
+        f.write(src)
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-o", so, c, "-lm"], check=True)
+    orc = oracle.Oracle(so)
+    failed = []
+    for pin in _pins.ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches the planted mistake {name}"
