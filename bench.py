@@ -1,0 +1,215 @@
+#!/usr/bin/env python
+"""Benchmark of the KDA forward hot path on one MI355X.
+
+One step = one pass of the whole path over synthetic inputs:
+  * chunked prefill with the fused gate (kda_chunk_fwd_z) over
+    B=4, H=32, T=32768, d_k=d_v=128, chunk 64, bf16 q/k/v/z/beta, fp32 state in
+    and out, bf16 outputs -- one kernel launch;
+  * 64 consecutive decode steps (kda_decode_step) over N=256 sequences x
+    H=32 heads, d=128, fp32 state updated in place in HBM, bf16 outputs.
+
+value = prefill tokens/s (B*T per prefill launch / launch time); the decode
+rate is reported beside it.  Inputs are generated on the host, copied to the
+GPU before the timed region, and stay resident.  Kernel durations are taken
+with HIP events recorded on the stream the kernels are launched on.
+
+The CPU baseline times the fp64 oracle (test infrastructure) on a bounded
+sample of the same prefill workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KDA chunked-prefill tokens/sec/GPU (H=32,d=128,T=32K); decode tokens/sec"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+# Algorithmic work per token-head of the chunked prefill at d = 128, chunk 64:
+# 2 * [3 * d_k * d_v + C * (1.5 d_k + d_v)] flops (W S, Q S, K^T U; L, P, T K;
+# T V and P U), and bytes: q, k, v, z (bf16) + beta (bf16) + o (bf16).
+PREFILL_FLOP_PER_TOKEN_HEAD = 2 * (3 * 128 * 128 + 64 * (1.5 * 128 + 128))
+PREFILL_BYTES_PER_TOKEN_HEAD = 4 * 128 * 2 + 2 + 128 * 2
+# Decode per (sequence, head) per step: state read + write (fp32), q, k, v, z
+# (bf16), beta (bf16), o (bf16).
+DECODE_BYTES_PER_SEQ_HEAD = 2 * 128 * 128 * 4 + 4 * 128 * 2 + 2 + 128 * 2
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-heads", type=int, default=32,
+                    help="heads of batch entry 0 the oracle runs for the CPU baseline")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} (WORLD_SIZE={world}) is not supported; "
+              "the KDA path here has no multi-GPU mode (batch/head sharding needs no communication).",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import gated_delta_rule_11_amd as kda
+    import kda_inputs as ki
+
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(a, dtype):
+        if a is None:
+            return None
+        if dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    # ---------------- inputs ----------------
+    ps = ki.PREFILL_32K
+    t0 = time.time()
+    pd = ki.prefill_inputs(ps)
+    log(f"prefill inputs generated in {time.time() - t0:.1f}s")
+    P = {k: to_dev(pd[k], ps.dtype) for k in ("q", "k", "v", "z", "beta")}
+    P["A"] = to_dev(pd["A"], "f32")
+    P["S0"] = to_dev(pd["S0"], "f32")
+    o_pre = torch.empty((ps.B, ps.T, ps.H, ps.dv), dtype=torch.bfloat16, device=dev)
+    S_pre = torch.empty((ps.B, ps.H, ps.dk, ps.dv), dtype=torch.float32, device=dev)
+
+    ds = ki.DECODE_256
+    t0 = time.time()
+    dd = ki.decode_inputs(ds)
+    log(f"decode inputs generated in {time.time() - t0:.1f}s")
+    D = {k: to_dev(dd[k], ds.dtype) for k in ("q", "k", "v", "z", "beta")}
+    D["A"] = to_dev(dd["A"], "f32")
+    S_dec = to_dev(dd["S0"], "f32")
+    o_dec = torch.empty((ds.steps, ds.N, ds.H, ds.dv), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def prefill():
+        kda.chunk_fwd_z(P["q"], P["k"], P["v"], P["beta"], P["z"], P["A"], -5.0, ps.chunk, S_in=P["S0"],
+                        o=o_pre, S_out=S_pre, stream=stream)
+
+    def decode_pass():
+        for s in range(ds.steps):
+            kda.decode_step(D["q"][s], D["k"][s], D["v"][s], D["z"][s], D["beta"][s], D["A"], S_dec, -5.0,
+                            o=o_dec[s], stream=stream)
+
+    # ---------------- warmup ----------------
+    for _ in range(args.warmup):
+        prefill()
+        decode_pass()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    # ---------------- timed ----------------
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        e0, e1, e2 = ev[i]
+        e0.record(stream)
+        prefill()
+        e1.record(stream)
+        decode_pass()
+        e2.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    pre_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
+    dec_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)]
+    log(f"timed {args.steps} steps: wall {wall * 1e3:.2f} ms; prefill ms {['%.3f' % x for x in pre_ms]}; "
+        f"decode(64 steps) ms {['%.3f' % x for x in dec_ms]}")
+
+    pre_avg_s = float(np.mean(pre_ms)) / 1e3
+    dec_avg_s = float(np.mean(dec_ms)) / 1e3
+    tokens = ps.B * ps.T
+    token_heads = tokens * ps.H
+    prefill_tps = tokens / pre_avg_s
+    pre_bytes = token_heads * PREFILL_BYTES_PER_TOKEN_HEAD + 2 * ps.B * ps.H * ps.dk * ps.dv * 4
+    pre_flops = token_heads * PREFILL_FLOP_PER_TOKEN_HEAD
+    pre_gbs = pre_bytes / pre_avg_s / 1e9
+    dec_step_s = dec_avg_s / ds.steps
+    dec_bytes = ds.N * ds.H * DECODE_BYTES_PER_SEQ_HEAD
+    dec_gbs = dec_bytes / dec_step_s / 1e9
+    decode_tps = ds.N * ds.steps / dec_avg_s
+    mfma = kda.chunk_uses_mfma(torch.bfloat16, ps.dk, ps.dv, ps.chunk)
+
+    # ---------------- CPU baseline (oracle on a bounded sample) ----------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        nh = max(1, min(ps.H, args.cpu_sample_heads))
+        cores = max(1, min(16, os.cpu_count() or 1))
+        f = {k: ki.to_f64(pd[k][0:1, :, 0:nh], ps.dtype) for k in ("q", "k", "v", "z", "beta")}
+        A64 = pd["A"][0:nh].astype(np.float64)
+        S064 = pd["S0"][0:1, 0:nh].astype(np.float64)
+        log(f"cpu baseline: oracle on b=0, heads 0..{nh - 1}, T={ps.T}, {cores} threads")
+        c0 = time.perf_counter()
+        o_ref, S_ref = oracle.forward_z(f["q"], f["k"], f["v"], f["beta"], f["z"], A64, -5.0, S064,
+                                        nthreads=cores)
+        cdt = time.perf_counter() - c0
+        # tokens/s of the whole workload (all H heads) at the sample's rate
+        cpu_tps = ps.T * (nh / ps.H) / cdt
+        o_gpu = o_pre[0:1, :, 0:nh].float().cpu().numpy().astype(np.float64)
+        S_gpu = S_pre[0:1, 0:nh].cpu().numpy().astype(np.float64)
+        rel_o = float(np.linalg.norm(o_gpu - o_ref) / np.linalg.norm(o_ref))
+        rel_S = float(np.linalg.norm(S_gpu - S_ref) / np.linalg.norm(S_ref))
+        log(f"cpu baseline {cdt:.1f}s -> {cpu_tps:.1f} tokens/s; sample parity rel-L2 o={rel_o:.2e} S={rel_S:.2e}")
+        cpu = {"value": round(cpu_tps, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+               "sample": f"prefill b=0, heads 0-{nh - 1} of {ps.H}, all {ps.T} tokens (fp64 token loop, "
+                         f"{cdt:.1f}s); throughput scaled to all heads",
+               "sample_parity_rel_l2": {"o": rel_o, "S": rel_S}}
+
+    out = {
+        "metric": METRIC,
+        "value": round(prefill_tps, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if mfma else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{ps.name} (prefill, fused gate) + {ds.name}", "global_batch": ps.B,
+                   "seq_len": ps.T, "heads": ps.H, "d_k": ps.dk, "d_v": ps.dv, "chunk": ps.chunk,
+                   "parallelism": "single GPU"},
+        "prefill_ms": round(pre_avg_s * 1e3, 4),
+        "roofline": {"bound": "hbm", "achieved": round(pre_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(pre_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "chunk prefill (kda_chunk_fwd_z)",
+                     "algorithmic_bytes_per_launch": pre_bytes,
+                     "mfma_tflops_algorithmic": round(pre_flops / pre_avg_s / 1e12, 2),
+                     "mfma_frac_algorithmic": round(pre_flops / pre_avg_s / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        "decode": {"value": round(decode_tps, 1), "unit": "tokens/s", "ms_per_64_steps": round(dec_avg_s * 1e3, 4),
+                   "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                                "algorithmic_bytes_per_launch": dec_bytes}},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

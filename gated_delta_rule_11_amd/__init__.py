@@ -1,0 +1,165 @@
+"""Python binding of libkda.so -- the MI355X (gfx950) Kimi Delta Attention
+forward library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI (include/kda.h).  PyTorch supplies device memory and
+the current stream.  There is no CPU fallback: the functions raise when the
+library is not built or when a tensor is not on a GPU.
+
+Entry points (same names as the C ABI):
+  gate(z, A, g_min, chunk)                        -> G           (kda_gate)
+  chunk_fwd(q, k, v, beta, G, chunk, ...)         -> (o, S_out)  (kda_chunk_fwd)
+  chunk_fwd_z(q, k, v, beta, z, A, g_min, chunk)  -> (o, S_out)  (kda_chunk_fwd_z)
+  decode_step(q, k, v, z, beta, A, S, g_min)      -> o           (kda_decode_step; S updated in place)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["gate", "chunk_fwd", "chunk_fwd_z", "decode_step", "chunk_uses_mfma", "lib", "KDAError", "LIB_PATH", "G_MIN"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
+G_MIN = -5.0
+KDA_F32, KDA_BF16 = 0, 1
+
+_lib = None
+
+
+class KDAError(RuntimeError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkda.so (raises when it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise KDAError(f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    L.kda_status_string.argtypes = [I]
+    L.kda_status_string.restype = ctypes.c_char_p
+    L.kda_version.argtypes = []
+    L.kda_version.restype = I
+    L.kda_chunk_uses_mfma.argtypes = [I, I, I, I]
+    L.kda_chunk_uses_mfma.restype = I
+    L.kda_gate.argtypes = [P, I, P, F, I, I, I, I, I, P, P]
+    L.kda_gate.restype = I
+    L.kda_chunk_fwd.argtypes = [P, P, P, P, I, P, P, P, I, P, I, I, I, I, I, I, F, P]
+    L.kda_chunk_fwd.restype = I
+    L.kda_chunk_fwd_z.argtypes = [P, P, P, P, P, I, P, F, P, P, I, P, I, I, I, I, I, I, F, P]
+    L.kda_chunk_fwd_z.restype = I
+    L.kda_decode_step.argtypes = [P, P, P, P, P, I, P, F, P, P, I, I, I, I, I, F, P]
+    L.kda_decode_step.restype = I
+    _lib = L
+    return L
+
+
+def chunk_uses_mfma(dtype: torch.dtype, dk: int, dv: int, chunk: int) -> bool:
+    """True when the chunked prefill runs the MFMA kernel for these arguments."""
+    code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
+    return bool(lib().kda_chunk_uses_mfma(code, dk, dv, chunk))
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = lib().kda_status_string(status).decode()
+        raise KDAError(f"{what}: {msg}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return KDA_F32
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise KDAError("libkda runs on the GPU only: tensor is on the CPU")
+        if not t.is_contiguous():
+            raise KDAError("tensors must be contiguous")
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def gate(z: torch.Tensor, A: torch.Tensor, g_min: float = G_MIN, chunk: int = 1,
+         out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """G [B,T,H,dk] fp32: chunk-local sums of g = g_min*sigmoid(exp(A) z)."""
+    B, T, H, dk = z.shape
+    if out is None:
+        out = torch.empty((B, T, H, dk), dtype=torch.float32, device=z.device)
+    _dev(z, A, out)
+    _check(lib().kda_gate(_p(z), _dtype_code(z), _p(A), float(g_min), B, T, H, dk, int(chunk), _p(out),
+                          _stream(stream)), "kda_gate")
+    return out
+
+
+def _outs(q, v, o, S_out, o_dtype, want_state):
+    B, T, H, _ = q.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=o_dtype or torch.float32, device=q.device)
+    if S_out is None and want_state:
+        S_out = torch.empty((B, H, q.shape[-1], dv), dtype=torch.float32, device=q.device)
+    return o, S_out
+
+
+def chunk_fwd(q, k, v, beta, G, chunk: int = 64, S_in=None, o=None, S_out=None, o_dtype=None,
+              scale: float = 1.0, want_state: bool = True, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked prefill from the chunk-local sums G of kda_gate (same chunk).
+    Returns (o [B,T,H,dv], S_out [B,H,dk,dv] or None)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    o, S_out = _outs(q, v, o, S_out, o_dtype, want_state)
+    _dev(q, k, v, beta, G, S_in, o, S_out)
+    _check(lib().kda_chunk_fwd(_p(q), _p(k), _p(v), _p(beta), _dtype_code(q), _p(G), _p(S_in), _p(o),
+                               _dtype_code(o), _p(S_out), B, T, H, dk, dv, int(chunk), float(scale),
+                               _stream(stream)), "kda_chunk_fwd")
+    return o, S_out
+
+
+def chunk_fwd_z(q, k, v, beta, z, A, g_min: float = G_MIN, chunk: int = 64, S_in=None, o=None, S_out=None,
+                o_dtype=None, scale: float = 1.0, want_state: bool = True,
+                stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked prefill with the gate fused (decay logits z, A, g_min).
+    Returns (o [B,T,H,dv], S_out [B,H,dk,dv] or None)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    o, S_out = _outs(q, v, o, S_out, o_dtype, want_state)
+    _dev(q, k, v, beta, z, A, S_in, o, S_out)
+    _check(lib().kda_chunk_fwd_z(_p(q), _p(k), _p(v), _p(beta), _p(z), _dtype_code(q), _p(A), float(g_min),
+                                 _p(S_in), _p(o), _dtype_code(o), _p(S_out), B, T, H, dk, dv, int(chunk),
+                                 float(scale), _stream(stream)), "kda_chunk_fwd_z")
+    return o, S_out
+
+
+def decode_step(q, k, v, z, beta, A, S, g_min: float = G_MIN, o=None, o_dtype=None, scale: float = 1.0,
+                stream=None) -> torch.Tensor:
+    """One token per sequence; S [N,H,dk,dv] fp32 is updated in place.
+    Returns o [N,H,dv]."""
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=o_dtype or torch.float32, device=q.device)
+    _dev(q, k, v, z, beta, A, S, o)
+    _check(lib().kda_decode_step(_p(q), _p(k), _p(v), _p(z), _p(beta), _dtype_code(q), _p(A), float(g_min),
+                                 _p(S), _p(o), _dtype_code(o), N, H, dk, dv, float(scale), _stream(stream)),
+           "kda_decode_step")
+    return o

@@ -1,0 +1,177 @@
+// kda_api.cpp -- the C ABI of libkda.so (declared in include/kda.h).
+//
+// Every entry point validates its arguments on the host first; on any error
+// it returns a status and launches nothing.  Launches are asynchronous on the
+// caller's stream.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <initializer_list>
+
+#include "../../include/kda.h"
+#include "kda_launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 62;
+
+bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool dtype_ok(int t) { return t == KDA_F32 || t == KDA_BF16; }
+size_t esize(int t) { return t == KDA_BF16 ? 2 : 4; }
+
+struct Range {
+  const void* p;
+  int64_t bytes;
+};
+
+// True when two non-empty byte ranges overlap.
+bool overlap(Range a, Range b) {
+  if (!a.p || !b.p || a.bytes <= 0 || b.bytes <= 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + static_cast<uintptr_t>(b.bytes) && b0 < a0 + static_cast<uintptr_t>(a.bytes);
+}
+
+// Checks B, T, H, dk, dv and returns false when any product overflows the
+// supported index range.
+bool sizes_ok(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv) {
+  if (B < 0 || T < 0 || H < 1) return false;
+  if (B * H > 0x7fffffffLL) return false;
+  if (H * dk > 0x7fffffffLL || H * dv > 0x7fffffffLL) return false;
+  if (B > 0 && T > 0 && B * T > kMaxElems / (H * (dk > dv ? dk : dv))) return false;
+  if (B * H > kMaxElems / (dk * dv)) return false;
+  return true;
+}
+
+kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Tensor bases 16-byte aligned, beta to its element size (NULL passes).
+bool all_aligned(std::initializer_list<const void*> vec16, const void* beta, size_t beta_size) {
+  for (const void* p : vec16)
+    if (!aligned(p, 16)) return false;
+  return aligned(beta, beta_size);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(int s) {
+  switch (s) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_NULL: return "KDA_ERR_NULL: a required pointer is NULL";
+    case KDA_ERR_SHAPE: return "KDA_ERR_SHAPE: a size is negative or too large";
+    case KDA_ERR_DTYPE: return "KDA_ERR_DTYPE: unknown dtype";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: head dim, chunk or parameter outside the supported set";
+    case KDA_ERR_ALIAS: return "KDA_ERR_ALIAS: an output overlaps an input";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP: the HIP runtime reported a launch error";
+    case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN: a tensor pointer is not 16-byte aligned";
+  }
+  return "unknown kda_status";
+}
+
+int kda_version(void) { return 100; }
+
+int kda_chunk_uses_mfma(kda_dtype in_dtype, int dk, int dv, int chunk) {
+  kda::ChunkArgs a{};
+  a.dk = dk; a.dv = dv; a.chunk = chunk; a.in_bf16 = in_dtype == KDA_BF16;
+  return dtype_ok(in_dtype) && kda::chunk_mfma_supports(a) ? 1 : 0;
+}
+
+kda_status kda_gate(const void* z, kda_dtype z_dtype, const float* A, float g_min, int B, int T, int H, int dk,
+                    int chunk, float* G, void* stream) {
+  if (!dtype_ok(z_dtype)) return KDA_ERR_DTYPE;
+  if (!sizes_ok(B, T, H, dk, dk)) return KDA_ERR_SHAPE;
+  if (!dim_ok(dk) || !(chunk == 1 || chunk == 16 || chunk == 64)) return KDA_ERR_UNSUPPORTED;
+  if (!isfinite(g_min) || g_min > 0.f) return KDA_ERR_UNSUPPORTED;
+  const int64_t n = int64_t(B) * T * H * dk;
+  if (n == 0) return KDA_OK;
+  if (!z || !A || !G) return KDA_ERR_NULL;
+  if (!all_aligned({z, A, G}, nullptr, 1)) return KDA_ERR_ALIGN;
+  const Range rG{G, n * 4};
+  if (overlap(rG, Range{z, n * int64_t(esize(z_dtype))}) || overlap(rG, Range{A, int64_t(H) * dk * 4}))
+    return KDA_ERR_ALIAS;
+  kda::GateArgs a{z, A, g_min, G, B, T, H, dk, chunk, z_dtype == KDA_BF16};
+  return from_hip(kda::launch_gate(a, static_cast<hipStream_t>(stream)));
+}
+
+static kda_status chunk_common(const void* q, const void* k, const void* v, const void* beta, const void* z,
+                               kda_dtype in_dtype, const float* G, const float* A, float g_min,
+                               const float* S_in, void* o, kda_dtype o_dtype, float* S_out, int B, int T, int H,
+                               int dk, int dv, int chunk, float scale, bool from_z, void* stream) {
+  if (!dtype_ok(in_dtype) || !dtype_ok(o_dtype)) return KDA_ERR_DTYPE;
+  if (!sizes_ok(B, T, H, dk, dv)) return KDA_ERR_SHAPE;
+  if (!dim_ok(dk) || !dim_ok(dv) || !(chunk == 16 || chunk == 64)) return KDA_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return KDA_ERR_UNSUPPORTED;
+  if (from_z && (!isfinite(g_min) || g_min > 0.f || g_min < -5.5f)) return KDA_ERR_UNSUPPORTED;
+  const int64_t ntok = int64_t(B) * T * H;
+  const int64_t nstate = int64_t(B) * H * dk * dv;
+  if (int64_t(B) * H == 0) return KDA_OK;
+  if (ntok > 0) {
+    if (!q || !k || !v || !beta || !o) return KDA_ERR_NULL;
+    if (from_z ? (!z || !A) : !G) return KDA_ERR_NULL;
+  }
+  if (!all_aligned({q, k, v, z, G, A, o, S_in, S_out}, beta, esize(in_dtype))) return KDA_ERR_ALIGN;
+  const int64_t ein = esize(in_dtype);
+  const Range rq{q, ntok * dk * ein}, rk{k, ntok * dk * ein}, rv{v, ntok * dv * ein}, rb{beta, ntok * ein};
+  const Range rz{from_z ? z : nullptr, ntok * dk * ein}, rG{from_z ? nullptr : G, ntok * dk * 4};
+  const Range rA{from_z ? A : nullptr, int64_t(H) * dk * 4};
+  const Range ro{o, ntok * dv * int64_t(esize(o_dtype))};
+  const Range rSi{S_in, nstate * 4}, rSo{S_out, nstate * 4};
+  for (Range in : {rq, rk, rv, rb, rz, rG, rA, rSi})
+    if (overlap(ro, in)) return KDA_ERR_ALIAS;
+  for (Range in : {rq, rk, rv, rb, rz, rG, rA, ro})
+    if (overlap(rSo, in)) return KDA_ERR_ALIAS;
+  if (overlap(rSo, rSi) && S_out != S_in) return KDA_ERR_ALIAS;
+
+  kda::ChunkArgs a{};
+  a.q = q; a.k = k; a.v = v; a.beta = beta; a.G = from_z ? nullptr : G; a.z = from_z ? z : nullptr;
+  a.A = from_z ? A : nullptr; a.g_min = g_min; a.S_in = S_in; a.o = o; a.S_out = S_out;
+  a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv; a.chunk = chunk; a.scale = scale;
+  a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = o_dtype == KDA_BF16; a.from_z = from_z;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (kda::chunk_mfma_supports(a)) return from_hip(kda::launch_chunk_mfma(a, st));
+  return from_hip(kda::launch_chunk_generic(a, st));
+}
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* beta, kda_dtype in_dtype,
+                         const float* G, const float* S_in, void* o, kda_dtype o_dtype, float* S_out, int B, int T,
+                         int H, int dk, int dv, int chunk, float scale, void* stream) {
+  return chunk_common(q, k, v, beta, nullptr, in_dtype, G, nullptr, -5.0f, S_in, o, o_dtype, S_out, B, T, H, dk, dv,
+                      chunk, scale, false, stream);
+}
+
+kda_status kda_chunk_fwd_z(const void* q, const void* k, const void* v, const void* beta, const void* z,
+                           kda_dtype in_dtype, const float* A, float g_min, const float* S_in, void* o,
+                           kda_dtype o_dtype, float* S_out, int B, int T, int H, int dk, int dv, int chunk,
+                           float scale, void* stream) {
+  return chunk_common(q, k, v, beta, z, in_dtype, nullptr, A, g_min, S_in, o, o_dtype, S_out, B, T, H, dk, dv, chunk,
+                      scale, true, stream);
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* z, const void* beta,
+                           kda_dtype in_dtype, const float* A, float g_min, float* S, void* o, kda_dtype o_dtype,
+                           int N, int H, int dk, int dv, float scale, void* stream) {
+  if (!dtype_ok(in_dtype) || !dtype_ok(o_dtype)) return KDA_ERR_DTYPE;
+  if (!sizes_ok(N, 1, H, dk, dv)) return KDA_ERR_SHAPE;
+  if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
+  if (!isfinite(g_min) || g_min > 0.f || !isfinite(scale)) return KDA_ERR_UNSUPPORTED;
+  const int64_t nh = int64_t(N) * H;
+  if (nh == 0) return KDA_OK;
+  if (!q || !k || !v || !z || !beta || !A || !S || !o) return KDA_ERR_NULL;
+  if (!all_aligned({q, k, v, z, A, S, o}, beta, esize(in_dtype))) return KDA_ERR_ALIGN;
+  const int64_t ein = esize(in_dtype);
+  const Range rS{S, nh * dk * dv * 4}, ro{o, nh * dv * int64_t(esize(o_dtype))};
+  const Range ins[] = {{q, nh * dk * ein}, {k, nh * dk * ein}, {v, nh * dv * ein}, {z, nh * dk * ein},
+                       {beta, nh * ein}, {A, int64_t(H) * dk * 4}};
+  for (const Range& in : ins)
+    if (overlap(rS, in) || overlap(ro, in)) return KDA_ERR_ALIAS;
+  if (overlap(rS, ro)) return KDA_ERR_ALIAS;
+  kda::DecodeArgs a{q, k, v, z, beta, A, g_min, S, o, N, H, dk, dv, scale, in_dtype == KDA_BF16,
+                    o_dtype == KDA_BF16};
+  return from_hip(kda::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

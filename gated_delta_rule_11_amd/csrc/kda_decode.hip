@@ -1,0 +1,158 @@
+// kda_decode.hip -- single-token KDA state update, in place, HBM-streaming.
+//
+// One workgroup per (sequence n, head h).  The fp32 state S[n,h] (dk x dv,
+// rows = key channels) is read from HBM once, held in registers, updated and
+// written back once:
+//   alpha = exp(g_min * sigmoid(exp(A) z))                 (gate, inline)
+//   D     = Diag(alpha) S                                  (decay rows)
+//   r     = D^T k,  y = D^T q                              (one pass, two reductions over rows)
+//   S'    = D + beta k (x) (v - r)                          (erase + write, Eq. 1)
+//   o     = scale * S'^T q = scale * (y + beta (v - r) (k . q))
+// Sources: Eq. 1 and its factorised update -- "Kimi K3: the paper and proofs
+// side by side", section 2.1.1; the gate -- "Kimi K3 reading notes", section 2.
+//
+// Thread layout: thread (rg, j4) owns 4 consecutive value columns 4*j4..+3
+// (one 16-byte access per row) of the rows rg + NR*i, i < RPT.  A wavefront
+// therefore reads 64/NJ whole rows per access: contiguous 512-byte runs at
+// dv = 128.  Column partial sums are reduced through LDS.
+#include "kda_common.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+
+constexpr int decode_threads(int dk, int dv) { return (dk * dv / 4) < 256 ? (dk * dv / 4) : 256; }
+
+template <int DK, int DV>
+struct DecodeShape {
+  static constexpr int NJ = DV / 4;                                  // column groups
+  static constexpr int NTHREADS = decode_threads(DK, DV);
+  static constexpr int NR = NTHREADS / NJ;                           // row groups
+  static constexpr int RPT = DK / NR;                                // rows per thread
+  static_assert(NR * RPT == DK, "rows must split evenly");
+  static_assert(NJ * NR == NTHREADS, "threads must split evenly");
+};
+
+template <int DK, int DV, typename Tin, typename Tout>
+__global__ __launch_bounds__(decode_threads(DK, DV)) void decode_step_kernel(
+    const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
+    const Tin* __restrict__ z, const Tin* __restrict__ beta, const float* __restrict__ A,
+    float gmin_l2e, float* __restrict__ S, Tout* __restrict__ o, int H, float scale) {
+  using Sh = DecodeShape<DK, DV>;
+  const int nh = blockIdx.x;  // n * H + h
+  const int h = nh % H;
+  const int tid = threadIdx.x;
+  const int j4 = tid % Sh::NJ;
+  const int rg = tid / Sh::NJ;
+
+  __shared__ float red_r[Sh::NR][DV];
+  __shared__ float red_y[Sh::NR][DV];
+  __shared__ float red_kq[Sh::NR];
+
+  const int64_t tok = static_cast<int64_t>(nh);
+  f32x4* Sp = reinterpret_cast<f32x4*>(S + tok * DK * DV);
+
+  // Issue all state loads first (the HBM stream), then the small vectors.
+  f32x4 s[Sh::RPT];
+#pragma unroll
+  for (int i = 0; i < Sh::RPT; ++i) {
+    const int c = rg + Sh::NR * i;
+    s[i] = __builtin_nontemporal_load(&Sp[c * Sh::NJ + j4]);
+  }
+
+  float kc[Sh::RPT], qc[Sh::RPT], ac[Sh::RPT];
+#pragma unroll
+  for (int i = 0; i < Sh::RPT; ++i) {
+    const int c = rg + Sh::NR * i;
+    kc[i] = io<Tin>::load(k, tok * DK + c);
+    qc[i] = io<Tin>::load(q, tok * DK + c);
+    const float ea = __expf(A[h * DK + c]) * kLog2e;
+    ac[i] = fast_exp2(gate_log2(io<Tin>::load(z, tok * DK + c), ea, gmin_l2e));
+  }
+  const float bt = io<Tin>::load(beta, tok);
+
+  // Decay rows, then partial column sums r = D^T k and y = D^T q.
+  float r[4] = {0.f, 0.f, 0.f, 0.f}, y[4] = {0.f, 0.f, 0.f, 0.f};
+  float kq = 0.f;
+#pragma unroll
+  for (int i = 0; i < Sh::RPT; ++i) {
+    s[i].x *= ac[i]; s[i].y *= ac[i]; s[i].z *= ac[i]; s[i].w *= ac[i];
+    r[0] += kc[i] * s[i].x; r[1] += kc[i] * s[i].y; r[2] += kc[i] * s[i].z; r[3] += kc[i] * s[i].w;
+    y[0] += qc[i] * s[i].x; y[1] += qc[i] * s[i].y; y[2] += qc[i] * s[i].z; y[3] += qc[i] * s[i].w;
+    kq += kc[i] * qc[i];
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    red_r[rg][4 * j4 + e] = r[e];
+    red_y[rg][4 * j4 + e] = y[e];
+  }
+  if (j4 == 0) red_kq[rg] = kq;
+  __syncthreads();
+  float rt[4] = {0.f, 0.f, 0.f, 0.f}, yt[4] = {0.f, 0.f, 0.f, 0.f};
+  float kqt = 0.f;
+#pragma unroll
+  for (int g = 0; g < Sh::NR; ++g) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      rt[e] += red_r[g][4 * j4 + e];
+      yt[e] += red_y[g][4 * j4 + e];
+    }
+    kqt += red_kq[g];
+  }
+
+  // Correction e_j = beta (v_j - r_j); S' = D + k (x) e.
+  float ev[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ev[e] = bt * (io<Tin>::load(v, tok * DV + 4 * j4 + e) - rt[e]);
+#pragma unroll
+  for (int i = 0; i < Sh::RPT; ++i) {
+    const int c = rg + Sh::NR * i;
+    f32x4 t = s[i];
+    t.x += kc[i] * ev[0]; t.y += kc[i] * ev[1]; t.z += kc[i] * ev[2]; t.w += kc[i] * ev[3];
+    __builtin_nontemporal_store(t, &Sp[c * Sh::NJ + j4]);
+  }
+  if (rg == 0) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) io<Tout>::store(o, tok * DV + 4 * j4 + e, scale * (yt[e] + ev[e] * kqt));
+  }
+}
+
+template <int DK, int DV, typename Tin, typename Tout>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
+  using Sh = DecodeShape<DK, DV>;
+  hipLaunchKernelGGL((decode_step_kernel<DK, DV, Tin, Tout>), dim3(a.N * a.H), dim3(Sh::NTHREADS), 0, st,
+                     static_cast<const Tin*>(a.q), static_cast<const Tin*>(a.k), static_cast<const Tin*>(a.v),
+                     static_cast<const Tin*>(a.z), static_cast<const Tin*>(a.beta), a.A, a.g_min * kLog2e, a.S,
+                     static_cast<Tout*>(a.o), a.H, a.scale);
+  return hipGetLastError();
+}
+
+template <int DK, int DV>
+static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t st) {
+  if (a.in_bf16) {
+    return a.out_bf16 ? launch_decode_t<DK, DV, bf16_t, bf16_t>(a, st) : launch_decode_t<DK, DV, bf16_t, float>(a, st);
+  }
+  return a.out_bf16 ? launch_decode_t<DK, DV, float, bf16_t>(a, st) : launch_decode_t<DK, DV, float, float>(a, st);
+}
+
+template <int DK>
+static hipError_t launch_decode_k(const DecodeArgs& a, hipStream_t st) {
+  switch (a.dv) {
+    case 16: return launch_decode_d<DK, 16>(a, st);
+    case 32: return launch_decode_d<DK, 32>(a, st);
+    case 64: return launch_decode_d<DK, 64>(a, st);
+    case 128: return launch_decode_d<DK, 128>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
+  switch (a.dk) {
+    case 16: return launch_decode_k<16>(a, st);
+    case 32: return launch_decode_k<32>(a, st);
+    case 64: return launch_decode_k<64>(a, st);
+    case 128: return launch_decode_k<128>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kda

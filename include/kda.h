@@ -1,0 +1,157 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention forward library
+ * (libkda.so).
+ *
+ * What is computed.  For every batch entry b and head h independently, with
+ * state S in R^{dk x dv} (rows = key channels, columns = value channels):
+ *
+ *   g_t     = g_min * sigmoid(exp(A[h]) * z_t)     per key channel   (Eq. 5)
+ *   alpha_t = exp(g_t)
+ *   S_t     = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T   (Eq. 1)
+ *   o_t     = scale * S_t^T q_t                    (read AFTER the update)
+ *
+ * Sources: Eq. 1 and the read-after-update order -- "Kimi K3: the paper and
+ * proofs side by side", section 2.1.1 (Equation 1) and its Lean `step`; the
+ * bounded gate with g_min = -5 -- "Kimi K3 reading notes", section 2 (Hybrid
+ * Attention); carrying the state across a split of the sequence -- the
+ * paper-and-proofs page, "Streaming, full sequences, and chunk boundaries"
+ * (run_append); heads packed and independent -- the same page, updateTerm.
+ * Eq. 1 has no output scale; pass scale = 1 for the equation as written.
+ *
+ * Conventions shared by every entry point.
+ *  - All tensor pointers are DEVICE pointers (hipMalloc'd or equivalent),
+ *    owned by the caller.  The library never allocates, frees or retains them.
+ *  - Layouts are contiguous row-major, token-major:
+ *      q, k, z, G : [B, T, H, dk]     v, o : [B, T, H, dv]     beta : [B, T, H]
+ *      A          : [H, dk] fp32      state: [B, H, dk, dv] fp32
+ *    (decode uses N sequences in place of B and no T axis).
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *    asynchronously; the call returns after enqueue without synchronising.
+ *  - Arguments are validated on the host before anything is launched.  On any
+ *    error the call launches nothing and writes no output or state.  A launch
+ *    failure reported by the runtime returns KDA_ERR_HIP.  Nothing throws.
+ *  - Supported: dk, dv in {16, 32, 64, 128}; chunk in {16, 64}; any T >= 0
+ *    (the last chunk may be partial); input dtype KDA_F32 or KDA_BF16 (q, k,
+ *    v, z, beta share it); output dtype KDA_F32 or KDA_BF16.  Anything else
+ *    returns KDA_ERR_UNSUPPORTED.  Sizes are limited so that every element
+ *    index fits in 63 bits and B*H, N*H fit in 31 bits.
+ *  - Alignment: tensor base pointers 16-byte aligned (beta: its element
+ *    size).  Allocator pointers and token slices of contiguous tensors with
+ *    d >= 16 satisfy this.  Otherwise KDA_ERR_ALIGN.
+ *  - Calls on one stream run in order; concurrent calls on different streams
+ *    must not write the same state or output buffers.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kda_status {
+  KDA_OK = 0,
+  KDA_ERR_NULL = 1,        /* a required pointer is NULL                     */
+  KDA_ERR_SHAPE = 2,       /* a size is negative or too large                */
+  KDA_ERR_DTYPE = 3,       /* dtype enum out of range                        */
+  KDA_ERR_UNSUPPORTED = 4, /* valid but not provided (dk, dv, chunk, ...)    */
+  KDA_ERR_ALIAS = 5,       /* outputs overlap inputs in a forbidden way      */
+  KDA_ERR_HIP = 6,         /* the HIP runtime reported an error at launch    */
+  KDA_ERR_ALIGN = 7        /* a pointer is not aligned as required           */
+} kda_status;
+
+typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* kda_status_string(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int kda_version(void);
+
+/* 1 when kda_chunk_fwd / kda_chunk_fwd_z run the MFMA kernel (bf16 matrix
+ * products with fp32 accumulation) for these arguments, 0 when they run the
+ * fp32 vector-ALU kernel.  Pure query: touches no device. */
+int kda_chunk_uses_mfma(kda_dtype in_dtype, int dk, int dv, int chunk);
+
+/*
+ * kda_gate -- bounded decay gate and chunk-local log-decay sums.
+ *
+ * G[b,t,h,c] = sum over u from the start of t's chunk up to t of
+ *              g_min * sigmoid(exp(A[h,c]) * z[b,u,h,c]),
+ * chunks being consecutive runs of `chunk` tokens starting at t = 0
+ * (chunk = 1 returns g itself).  Natural-log units, fp32 output.
+ * Source: "Kimi K3 reading notes", section 2 (g and alpha = exp(g)); the
+ * chunk-local sums are the cumulative log-decay whose 16-token range
+ * (-80, 0) the same section states.
+ *
+ *   z      [B,T,H,dk] in z_dtype (device)     A [H,dk] fp32 (device)
+ *   g_min  lower bound of g (the pages fix -5); must be finite and < 0
+ *   chunk  1, 16 or 64
+ *   G      [B,T,H,dk] fp32 (device, written); must not overlap z or A
+ */
+kda_status kda_gate(const void* z, kda_dtype z_dtype, const float* A,
+                    float g_min, int B, int T, int H, int dk, int chunk,
+                    float* G, void* stream);
+
+/*
+ * kda_chunk_fwd -- chunked prefill with state in and out, from precomputed
+ * chunk-local log-decay sums G (the output of kda_gate with the same chunk).
+ *
+ * Computes, for t = 0..T-1 of every (b, h), o_t and the final state S_T of
+ * the recurrence above, starting from S_in (or zero).  The chunked algorithm
+ * regroups the token updates inside each chunk of `chunk` tokens (the
+ * chunkwise form named on "Kimi K3: architecture, derivations and a
+ * pinned-source audit", section 4.5) and carries the state between chunks;
+ * results equal the token recurrence up to rounding.
+ *
+ *   q, k   [B,T,H,dk] in_dtype     v [B,T,H,dv] in_dtype     beta [B,T,H] in_dtype
+ *   G      [B,T,H,dk] fp32 chunk-local sums (chunk must match kda_gate's)
+ *   S_in   [B,H,dk,dv] fp32 or NULL (zero state)
+ *   o      [B,T,H,dv] in o_dtype (written)
+ *   S_out  [B,H,dk,dv] fp32 or NULL (not written); may equal S_in exactly
+ *          (in-place state update) but must not partially overlap it
+ *   scale  output scale (1 for Eq. 1 as written)
+ */
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
+                         const void* beta, kda_dtype in_dtype, const float* G,
+                         const float* S_in, void* o, kda_dtype o_dtype,
+                         float* S_out, int B, int T, int H, int dk, int dv,
+                         int chunk, float scale, void* stream);
+
+/*
+ * kda_chunk_fwd_z -- the same chunked prefill with the gate fused: takes the
+ * decay logits z [B,T,H,dk] (in_dtype), A [H,dk] fp32 and g_min instead of G.
+ * Equal to kda_gate followed by kda_chunk_fwd up to rounding; this is the
+ * path that avoids the fp32 round trip of G through memory.
+ */
+kda_status kda_chunk_fwd_z(const void* q, const void* k, const void* v,
+                           const void* beta, const void* z, kda_dtype in_dtype,
+                           const float* A, float g_min, const float* S_in,
+                           void* o, kda_dtype o_dtype, float* S_out, int B,
+                           int T, int H, int dk, int dv, int chunk, float scale,
+                           void* stream);
+
+/*
+ * kda_decode_step -- one token per sequence, state updated IN PLACE.
+ *
+ * For n < N, h < H: gate from z and A, S[n,h] <- (I - beta k k^T)
+ * Diag(alpha) S[n,h] + beta k v^T, o[n,h] = scale * S[n,h]^T q.
+ * The state is fixed-size per sequence; a caller that must keep the old
+ * state (a cached prefix) copies it before calling ("Kimi K3: architecture,
+ * derivations and a pinned-source audit", section 9.3: copy before mutation).
+ *
+ *   q, k, z [N,H,dk] in_dtype    v [N,H,dv] in_dtype    beta [N,H] in_dtype
+ *   A       [H,dk] fp32          S [N,H,dk,dv] fp32 (read and written)
+ *   o       [N,H,dv] in o_dtype (written; must not overlap S)
+ */
+kda_status kda_decode_step(const void* q, const void* k, const void* v,
+                           const void* z, const void* beta, kda_dtype in_dtype,
+                           const float* A, float g_min, float* S, void* o,
+                           kda_dtype o_dtype, int N, int H, int dk, int dv,
+                           float scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H */

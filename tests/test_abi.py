@@ -1,0 +1,146 @@
+"""The C ABI on the CPU: libkda.so loads, exports every symbol include/kda.h
+declares, and rejects bad arguments on the host without launching anything
+(no compute call is made here: every call below fails validation or has
+nothing to do)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_11_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_UNSUPPORTED, ERR_ALIAS, ERR_HIP, ERR_ALIGN = range(8)
+F32, BF16 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def L():
+    from gated_delta_rule_11_amd import _build
+    if _build.is_stale():
+        _build.build()
+    return kda.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_z", "kda_decode_step", "kda_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for s in range(8):
+        assert L.kda_status_string(s).decode().startswith("KDA_")
+    assert b"unknown" in L.kda_status_string(99)
+    assert L.kda_version() >= 100
+
+
+# Fake device addresses: validation must reject before any of them is used.
+def P(i):
+    return ctypes.c_void_p(0x10000000 * (i + 1))
+
+
+N = None
+
+
+def gate(L, z=P(0), zt=BF16, A=P(1), gmin=-5.0, B=1, T=64, H=2, dk=128, chunk=64, G=P(2)):
+    return L.kda_gate(z, zt, A, gmin, B, T, H, dk, chunk, G, N)
+
+
+def chunk(L, q=P(0), k=P(1), v=P(2), beta=P(3), it=BF16, G=P(4), S_in=P(5), o=P(6), ot=BF16, S_out=P(7),
+          B=1, T=64, H=2, dk=128, dv=128, c=64, scale=1.0):
+    return L.kda_chunk_fwd(q, k, v, beta, it, G, S_in, o, ot, S_out, B, T, H, dk, dv, c, scale, N)
+
+
+def chunk_z(L, q=P(0), k=P(1), v=P(2), beta=P(3), z=P(4), it=BF16, A=P(8), gmin=-5.0, S_in=P(5), o=P(6), ot=BF16,
+            S_out=P(7), B=1, T=64, H=2, dk=128, dv=128, c=64, scale=1.0):
+    return L.kda_chunk_fwd_z(q, k, v, beta, z, it, A, gmin, S_in, o, ot, S_out, B, T, H, dk, dv, c, scale, N)
+
+
+def decode(L, q=P(0), k=P(1), v=P(2), z=P(3), beta=P(4), it=BF16, A=P(5), gmin=-5.0, S=P(6), o=P(7), ot=BF16,
+           Nn=4, H=2, dk=128, dv=128, scale=1.0):
+    return L.kda_decode_step(q, k, v, z, beta, it, A, gmin, S, o, ot, Nn, H, dk, dv, scale, N)
+
+
+def test_gate_validation(L):
+    assert gate(L, zt=7) == ERR_DTYPE
+    assert gate(L, B=-1) == ERR_SHAPE
+    assert gate(L, T=-5) == ERR_SHAPE
+    assert gate(L, H=0) == ERR_SHAPE
+    assert gate(L, dk=48) == ERR_UNSUPPORTED
+    assert gate(L, chunk=32) == ERR_UNSUPPORTED
+    assert gate(L, gmin=1.0) == ERR_UNSUPPORTED
+    assert gate(L, gmin=float("nan")) == ERR_UNSUPPORTED
+    assert gate(L, z=None) == ERR_NULL
+    assert gate(L, G=None) == ERR_NULL
+    assert gate(L, A=None) == ERR_NULL
+    assert gate(L, G=P(0)) == ERR_ALIAS          # G overlaps z
+    assert gate(L, G=ctypes.c_void_p(0x30000008)) == ERR_ALIGN
+    assert gate(L, B=0) == OK                    # nothing to do, nothing launched
+    assert gate(L, T=0, z=None, G=None) == OK
+
+
+def test_chunk_validation(L):
+    assert chunk(L, it=3) == ERR_DTYPE
+    assert chunk(L, ot=-1) == ERR_DTYPE
+    assert chunk(L, B=-1) == ERR_SHAPE
+    assert chunk(L, T=-1) == ERR_SHAPE
+    assert chunk(L, H=0) == ERR_SHAPE
+    assert chunk(L, B=1 << 20, H=1 << 12) == ERR_SHAPE
+    assert chunk(L, dk=96) == ERR_UNSUPPORTED
+    assert chunk(L, dv=256) == ERR_UNSUPPORTED
+    assert chunk(L, c=32) == ERR_UNSUPPORTED
+    assert chunk(L, c=1) == ERR_UNSUPPORTED
+    assert chunk(L, scale=float("inf")) == ERR_UNSUPPORTED
+    for name in ("q", "k", "v", "beta", "G", "o"):
+        assert chunk(L, **{name: None}) == ERR_NULL, name
+    assert chunk(L, o=P(0)) == ERR_ALIAS                 # o overlaps q
+    assert chunk(L, S_out=P(4)) == ERR_ALIAS             # S_out overlaps G
+    assert chunk(L, S_out=ctypes.c_void_p(0x60000000 + 256)) == ERR_ALIAS  # partial overlap with S_in
+    assert chunk(L, S_in=ctypes.c_void_p(0x60000004)) == ERR_ALIGN
+    assert chunk(L, q=ctypes.c_void_p(0x10000002)) == ERR_ALIGN
+    assert chunk(L, beta=ctypes.c_void_p(0x40000001)) == ERR_ALIGN
+    # a 2-byte-aligned bf16 beta passes the alignment check (and then fails on the overlap)
+    assert chunk(L, beta=ctypes.c_void_p(0x40000002), o=P(0)) == ERR_ALIAS
+    assert chunk(L, B=0) == OK
+    assert chunk_z(L, gmin=-6.0) == ERR_UNSUPPORTED
+    assert chunk_z(L, gmin=0.5) == ERR_UNSUPPORTED
+    assert chunk_z(L, z=None) == ERR_NULL
+    assert chunk_z(L, A=None) == ERR_NULL
+    assert chunk_z(L, o=P(4)) == ERR_ALIAS               # o overlaps z
+    assert chunk_z(L, B=0) == OK
+
+
+def test_decode_validation(L):
+    assert decode(L, it=2) == ERR_DTYPE
+    assert decode(L, Nn=-1) == ERR_SHAPE
+    assert decode(L, dk=8) == ERR_UNSUPPORTED
+    assert decode(L, gmin=3.0) == ERR_UNSUPPORTED
+    for name in ("q", "k", "v", "z", "beta", "A", "S", "o"):
+        assert decode(L, **{name: None}) == ERR_NULL, name
+    assert decode(L, o=P(6)) == ERR_ALIAS                # o overlaps S
+    assert decode(L, S=P(2)) == ERR_ALIAS                # S overlaps v
+    assert decode(L, S=ctypes.c_void_p(0x70000008)) == ERR_ALIGN
+    assert decode(L, Nn=0) == OK
+
+
+def test_binding_refuses_cpu_tensors(L):
+    import torch
+    z = torch.zeros(1, 4, 1, 16)
+    A = torch.zeros(1, 16)
+    with pytest.raises(kda.KDAError):
+        kda.gate(z, A, chunk=1, out=torch.zeros(1, 4, 1, 16))
