@@ -53,6 +53,8 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
+                    help="profiling runs: time one path only (the JSON line then reports that path)")
     ap.add_argument("--cpu-sample-heads", type=int, default=32,
                     help="heads of batch entry 0 the oracle runs for the CPU baseline")
     args = ap.parse_args()
@@ -81,8 +83,17 @@ def main():
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
 
+    run_pre = args.only in ("all", "prefill")
+    run_dec = args.only in ("all", "decode")
+
     # ---------------- inputs ----------------
     ps = ki.PREFILL_32K
+    ds = ki.DECODE_256
+    if not run_pre:  # a one-token stand-in keeps the code below uniform; it is never launched
+        ps = ki.small_spec(ps.B, ps.H, 1, ps.dk, ps.dv, ps.chunk, ps.dtype, ps.seed, s0_std=ps.s0_std,
+                           name=ps.name)
+    if not run_dec:
+        ds = ki.DecodeSpec(ds.name, N=1, H=ds.H, dk=ds.dk, dv=ds.dv, steps=ds.steps, dtype=ds.dtype, seed=ds.seed)
     t0 = time.time()
     pd = ki.prefill_inputs(ps)
     log(f"prefill inputs generated in {time.time() - t0:.1f}s")
@@ -92,7 +103,6 @@ def main():
     o_pre = torch.empty((ps.B, ps.T, ps.H, ps.dv), dtype=torch.bfloat16, device=dev)
     S_pre = torch.empty((ps.B, ps.H, ps.dk, ps.dv), dtype=torch.float32, device=dev)
 
-    ds = ki.DECODE_256
     t0 = time.time()
     dd = ki.decode_inputs(ds)
     log(f"decode inputs generated in {time.time() - t0:.1f}s")
@@ -105,10 +115,14 @@ def main():
     stream = torch.cuda.current_stream()
 
     def prefill():
+        if not run_pre:
+            return
         kda.chunk_fwd_z(P["q"], P["k"], P["v"], P["beta"], P["z"], P["A"], -5.0, ps.chunk, S_in=P["S0"],
                         o=o_pre, S_out=S_pre, stream=stream)
 
     def decode_pass():
+        if not run_dec:
+            return
         for s in range(ds.steps):
             kda.decode_step(D["q"][s], D["k"][s], D["v"][s], D["z"][s], D["beta"][s], D["A"], S_dec, -5.0,
                             o=o_dec[s], stream=stream)
@@ -139,8 +153,8 @@ def main():
     log(f"timed {args.steps} steps: wall {wall * 1e3:.2f} ms; prefill ms {['%.3f' % x for x in pre_ms]}; "
         f"decode(64 steps) ms {['%.3f' % x for x in dec_ms]}")
 
-    pre_avg_s = float(np.mean(pre_ms)) / 1e3
-    dec_avg_s = float(np.mean(dec_ms)) / 1e3
+    pre_avg_s = max(float(np.mean(pre_ms)) / 1e3, 1e-9)
+    dec_avg_s = max(float(np.mean(dec_ms)) / 1e3, 1e-9)
     tokens = ps.B * ps.T
     token_heads = tokens * ps.H
     prefill_tps = tokens / pre_avg_s
@@ -155,7 +169,7 @@ def main():
 
     # ---------------- CPU baseline (oracle on a bounded sample) ----------------
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and run_pre:
         import oracle
         nh = max(1, min(ps.H, args.cpu_sample_heads))
         cores = max(1, min(16, os.cpu_count() or 1))
