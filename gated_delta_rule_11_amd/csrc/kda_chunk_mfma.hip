@@ -42,27 +42,34 @@ constexpr int NTH = 256;       // 4 wavefronts
 constexpr int RS = DK + 8;     // row stride (bf16 elements) of [token][channel] tiles
 constexpr int TS = C + 8;      // row stride of [channel][token] tiles
 constexpr int XS = 24;         // row stride of the 16x16 diagonal inverses
-constexpr int LDS_ = 20;       // row stride (floats) of the fp32 diagonal L blocks
+constexpr int LTS = 20;        // row stride (floats) of the transposed fp32 diagonal L blocks
+
+// pair (i, j <= i) of 16-token tiles -> slot of its anchored key tile
+__host__ __device__ constexpr int slot(int i, int j) { return i * (i + 1) / 2 + j; }
 
 template <int DVS>
 struct Layout {
   static constexpr int KR = 0;                          // [64][RS]  k r       (later: -W)
   static constexpr int QR = KR + C * RS * 2;            // [64][RS]  q r
-  static constexpr int KC = QR + C * RS * 2;            // [64][RS]  k sf
-  static constexpr int QT = KC + C * RS * 2;            // [64][RS]  q Gamma
-  static constexpr int KTT = QT + C * RS * 2;           // [128][TS] (k Gamma)^T
-  static constexpr int KHT = KTT + DK * TS * 2;         // [128][TS] (k Gamma_C/Gamma)^T
+  static constexpr int KA = QR + C * RS * 2;            // [10][16][RS] anchored keys k e^(B_i - G)
+  static constexpr int QT = KA + 10 * 16 * RS * 2;      // [64][RS]  q Gamma
+  static constexpr int KHT = QT + C * RS * 2;           // [128][TS] (k Gamma_C/Gamma)^T
   static constexpr int VT = KHT + DK * TS * 2;          // [DVS][TS] v^T
   static constexpr int LM = VT + DVS * TS * 2;          // [64][TS]  -L (off-diagonal tiles)
   static constexpr int PM = LM + C * TS * 2;            // [64][TS]  P
-  static constexpr int XM = PM + C * TS * 2;            // [4][16][XS] diagonal inverses
-  static constexpr int LD = XM + 4 * 16 * XS * 2;       // [4][16][LDS_] fp32 diagonal L
-  static constexpr int DT = LD + 4 * 16 * LDS_ * 4;     // [4][128] fp32 tile decays
-  static constexpr int GC = DT + 4 * DK * 4;            // [128] fp32 chunk decay
+  static constexpr int XM = PM + C * TS * 2;            // [4][16][XS] diagonal inverses (bf16)
+  static constexpr int LT = XM + 4 * 16 * XS * 2;       // [4][16][LTS] fp32 diagonal L, transposed
+  static constexpr int DT = LT + 4 * 16 * LTS * 4;      // [4][128] fp32 tile decays D_i
+  static constexpr int EB = DT + 4 * DK * 4;            // [4][128] fp32 decay before tile i
+  static constexpr int GC = EB + 4 * DK * 4;            // [128] fp32 chunk decay
   static constexpr int BT = GC + DK * 4;                // [64] fp32 beta
   static constexpr int BYTES = BT + C * 4;
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
+
+// Raw buffer resource: base, byte range; loads outside the range read 0 and
+// stores outside it are dropped by the hardware.
+constexpr int kRsrcFlags = 0x00020000;
 }  // namespace mf
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -86,19 +93,30 @@ __device__ __forceinline__ s16x4 lds64(const uint16_t* p) {
   return __builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(p));
 }
 __device__ __forceinline__ u32x4 lds128(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ u32x4 cat(s16x4 lo, s16x4 hi) {
+  const u32x2 l = __builtin_bit_cast(u32x2, lo), h = __builtin_bit_cast(u32x2, hi);
+  return u32x4{l[0], l[1], h[0], h[1]};
+}
 __device__ __forceinline__ f32x4 mma16(s16x4 a, s16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
+// 16x16x32: lane group g holds k = 8g..8g+7 of both operands, so any
+// consistent assignment of channels to those slots gives the same product.
 __device__ __forceinline__ f32x4 mma32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                  0, 0, 0);
 }
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+  const int nrec = bytes > 0x7fffffffLL ? 0x7fffffff : static_cast<int>(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), nrec, mf::kRsrcFlags);
+}
+__device__ __forceinline__ uint32_t bload32(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
 
-// Tile pairs (i, j <= i) of the L / P products, per wavefront.
-__constant__ int8_t kPairs[4][3][2] = {{{0, 0}, {3, 0}, {3, 1}},
-                                       {{1, 0}, {1, 1}, {3, 2}},
-                                       {{2, 0}, {2, 1}, {-1, -1}},
-                                       {{2, 2}, {3, 3}, {-1, -1}}};
+// Tile pairs (i, j < i) of the L / P products per wavefront; each wavefront's
+// diagonal pair (wv, wv) is handled first and separately.
+__constant__ int8_t kOffPairs[4][2][2] = {{{3, 0}, {3, 1}}, {{1, 0}, {3, 2}}, {{2, 0}, {-1, -1}}, {{2, 1}, {-1, -1}}};
 
 template <int DVS, bool FROM_Z, typename Tout>
 __global__ __launch_bounds__(mf::NTH) void chunk_mfma_kernel(const ChunkArgs a, int ns, int xcd_map) {
@@ -106,21 +124,22 @@ __global__ __launch_bounds__(mf::NTH) void chunk_mfma_kernel(const ChunkArgs a, 
   using Ly = Layout<DVS>;
   constexpr int NJT = DVS / 16;              // value-column tiles in the slice
   constexpr int JPW = (NJT + 3) / 4;         // value-column tiles per wavefront (max)
+  constexpr int ES = sizeof(Tout);
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint16_t* sKR = reinterpret_cast<uint16_t*>(smem + Ly::KR);
-  uint16_t* sW = sKR;  // -W overwrites k r once L and P are done
+  uint16_t* sW = sKR;  // -W overwrites k r column by column (each wavefront its own columns)
   uint16_t* sQR = reinterpret_cast<uint16_t*>(smem + Ly::QR);
-  uint16_t* sKC = reinterpret_cast<uint16_t*>(smem + Ly::KC);
+  uint16_t* sKA = reinterpret_cast<uint16_t*>(smem + Ly::KA);
   uint16_t* sQt = reinterpret_cast<uint16_t*>(smem + Ly::QT);
-  uint16_t* sKtT = reinterpret_cast<uint16_t*>(smem + Ly::KTT);
   uint16_t* sKhT = reinterpret_cast<uint16_t*>(smem + Ly::KHT);
   uint16_t* sVT = reinterpret_cast<uint16_t*>(smem + Ly::VT);
   uint16_t* sLm = reinterpret_cast<uint16_t*>(smem + Ly::LM);
   uint16_t* sP = reinterpret_cast<uint16_t*>(smem + Ly::PM);
   uint16_t* sX = reinterpret_cast<uint16_t*>(smem + Ly::XM);
-  float* sLd = reinterpret_cast<float*>(smem + Ly::LD);
+  float* sLT = reinterpret_cast<float*>(smem + Ly::LT);
   float* sD = reinterpret_cast<float*>(smem + Ly::DT);
+  float* sEB = reinterpret_cast<float*>(smem + Ly::EB);
   float* sGC = reinterpret_cast<float*>(smem + Ly::GC);
   float* sBeta = reinterpret_cast<float*>(smem + Ly::BT);
 
@@ -142,18 +161,12 @@ __global__ __launch_bounds__(mf::NTH) void chunk_mfma_kernel(const ChunkArgs a, 
   const int j0 = sl * DVS;
   const int T = a.T;
   const int H = a.H;
-  const int wv = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ln = threadIdx.x & 63;
   const int g4 = ln >> 4;   // MFMA lane group
   const int r16 = ln & 15;  // MFMA lane row/column
   const int c0 = 2 * ln;    // gate layout: channels c0, c0+1
-
-  const uint32_t* kq32 = static_cast<const uint32_t*>(a.q);
-  const uint32_t* kk32 = static_cast<const uint32_t*>(a.k);
-  const uint32_t* kz32 = static_cast<const uint32_t*>(a.z);
-  const uint16_t* vv = static_cast<const uint16_t*>(a.v);
-  const uint16_t* bb = static_cast<const uint16_t*>(a.beta);
-  Tout* o = static_cast<Tout*>(a.o);
+  const int rowb = H * DK * 2;  // bytes between consecutive tokens of one head (bf16 rows)
 
   // gate constants for the lane's two channels (log2 units)
   float ea0 = 0.f, ea1 = 0.f;
@@ -183,31 +196,38 @@ __global__ __launch_bounds__(mf::NTH) void chunk_mfma_kernel(const ChunkArgs a, 
   for (int t0 = 0; t0 < T; t0 += C) {
     const int n = min(C, T - t0);
     const int64_t row0 = (static_cast<int64_t>(b) * T + t0) * H + h;  // token t0's row index
+    const int64_t span = static_cast<int64_t>(n - 1) * H + 1;         // rows this chunk may touch
+    const auto rq = rsrc(static_cast<const uint16_t*>(a.q) + row0 * DK, span * DK * 2);
+    const auto rk = rsrc(static_cast<const uint16_t*>(a.k) + row0 * DK, span * DK * 2);
+    const auto rv = rsrc(static_cast<const uint16_t*>(a.v) + row0 * DK + j0, span * DK * 2);
+    const auto rb = rsrc(static_cast<const uint16_t*>(a.beta) + row0, span * 2);
 
     // ---------------- phase 1: gate, decays, operand tiles ----------------
+    const int i1 = wv;  // this wavefront's tile
+    uint32_t kp[16], qp[16];
+    float r0[16], r1[16], f0[16], f1[16];
+    float D0 = 1.f, D1 = 1.f;
     {
-      const int i = wv;  // this wavefront's tile
-      uint32_t kp[16], qp[16];
-      float r0[16], r1[16], f0[16], f1[16];
-      float D0 = 1.f, D1 = 1.f;
+      const int i = i1;
       if (FROM_Z) {
+        const auto rz = rsrc(static_cast<const uint16_t*>(a.z) + row0 * DK, span * DK * 2);
         float al0[16], al1[16];
+        uint32_t zp[16];
+        // all loads first (padded tokens read the last valid token and are masked below)
 #pragma unroll
         for (int tt = 0; tt < 16; ++tt) {
-          const int t = 16 * i + tt;
-          if (t < n) {
-            const int64_t e = ((row0 + static_cast<int64_t>(t) * H) * DK + c0) >> 1;
-            kp[tt] = kk32[e];
-            qp[tt] = kq32[e];
-            const uint32_t zp = kz32[e];
-            al0[tt] = fast_exp2(gate_log2(bflo(zp), ea0, gmin_l2e));
-            al1[tt] = fast_exp2(gate_log2(bfhi(zp), ea1, gmin_l2e));
-          } else {
-            kp[tt] = 0u;
-            qp[tt] = 0u;
-            al0[tt] = 1.f;
-            al1[tt] = 1.f;
-          }
+          const int so = min(16 * i + tt, n - 1) * rowb;
+          kp[tt] = bload32(rk, c0 * 2, so);
+          qp[tt] = bload32(rq, c0 * 2, so);
+          zp[tt] = bload32(rz, c0 * 2, so);
+        }
+#pragma unroll
+        for (int tt = 0; tt < 16; ++tt) {
+          const bool valid = 16 * i + tt < n;
+          al0[tt] = valid ? fast_exp2(gate_log2(bflo(zp[tt]), ea0, gmin_l2e)) : 1.f;
+          al1[tt] = valid ? fast_exp2(gate_log2(bfhi(zp[tt]), ea1, gmin_l2e)) : 1.f;
+          kp[tt] = valid ? kp[tt] : 0u;
+          qp[tt] = valid ? qp[tt] : 0u;
         }
 #pragma unroll
         for (int tt = 0; tt < 16; ++tt) {
@@ -225,26 +245,30 @@ __global__ __launch_bounds__(mf::NTH) void chunk_mfma_kernel(const ChunkArgs a, 
           s1 *= al1[tt];
         }
       } else {
-        // chunk-local sums G (natural log) -> log2 within this tile
+        // chunk-local sums G (natural log, fp32) -> log2 within this tile
+        const auto rg = rsrc(a.G + row0 * DK, span * DK * 4);
         float G0[16], G1[16];
-        const float2* G2 = reinterpret_cast<const float2*>(a.G);
+        u32x2 gg[16];
+#pragma unroll
+        for (int tt = 0; tt < 16; ++tt) {
+          const int so = min(16 * i + tt, n - 1) * rowb * 2;
+          kp[tt] = bload32(rk, c0 * 2, min(16 * i + tt, n - 1) * rowb);
+          qp[tt] = bload32(rq, c0 * 2, min(16 * i + tt, n - 1) * rowb);
+          gg[tt] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, c0 * 4, so, 0));
+        }
         float base0 = 0.f, base1 = 0.f;
         if (i > 0 && 16 * i < n) {
-          const float2 gb = G2[((row0 + static_cast<int64_t>(16 * i - 1) * H) * DK + c0) >> 1];
-          base0 = gb.x * kLog2e;
-          base1 = gb.y * kLog2e;
+          const u32x2 gb = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, c0 * 4, (16 * i - 1) * rowb * 2, 0));
+          base0 = __uint_as_float(gb[0]) * kLog2e;
+          base1 = __uint_as_float(gb[1]) * kLog2e;
         }
         float last0 = base0, last1 = base1;
 #pragma unroll
         for (int tt = 0; tt < 16; ++tt) {
-          const int t = 16 * i + tt;
-          if (t < n) {
-            const int64_t e = ((row0 + static_cast<int64_t>(t) * H) * DK + c0) >> 1;
-            kp[tt] = kk32[e];
-            qp[tt] = kq32[e];
-            const float2 gg = G2[e];
-            G0[tt] = gg.x * kLog2e;
-            G1[tt] = gg.y * kLog2e;
+          if (16 * i + tt < n) {
+            G0[tt] = __uint_as_float(gg[tt][0]) * kLog2e;
+            G1[tt] = __uint_as_float(gg[tt][1]) * kLog2e;
             last0 = G0[tt];
             last1 = G1[tt];
           } else {
@@ -268,16 +292,14 @@ __global__ __launch_bounds__(mf::NTH) void chunk_mfma_kernel(const ChunkArgs a, 
       sD[i * DK + c0 + 1] = D1;
       if (ln < 16) {
         const int t = 16 * i + ln;
-        sBeta[t] = t < n ? bf16_to_f32(bb[row0 + static_cast<int64_t>(t) * H]) : 0.f;
+        const uint32_t bv = __builtin_amdgcn_raw_buffer_load_b16(rb, min(t, n - 1) * H * 2, 0, 0);
+        sBeta[t] = t < n ? bf16_to_f32(static_cast<uint16_t>(bv)) : 0.f;
       }
 #pragma unroll
       for (int tt = 0; tt < 16; ++tt) {
         const int t = 16 * i + tt;
-        const float k0 = bflo(kp[tt]), k1 = bfhi(kp[tt]);
-        const float q0 = bflo(qp[tt]), q1 = bfhi(qp[tt]);
-        *reinterpret_cast<uint32_t*>(&sKR[t * RS + c0]) = pack2(k0 * r0[tt], k1 * r1[tt]);
-        *reinterpret_cast<uint32_t*>(&sQR[t * RS + c0]) = pack2(q0 * r0[tt], q1 * r1[tt]);
-        *reinterpret_cast<uint32_t*>(&sKC[t * RS + c0]) = pack2(k0 * f0[tt], k1 * f1[tt]);
+        *reinterpret_cast<uint32_t*>(&sKR[t * RS + c0]) = pack2(bflo(kp[tt]) * r0[tt], bfhi(kp[tt]) * r1[tt]);
+        *reinterpret_cast<uint32_t*>(&sQR[t * RS + c0]) = pack2(bflo(qp[tt]) * r0[tt], bfhi(qp[tt]) * r1[tt]);
       }
       // v^T for the slice's columns: lane -> columns ln*(DVS/64).. (DVS >= 64) or ln (< DVS)
       constexpr int VPL = DVS >= 64 ? DVS / 64 : 1;
@@ -285,13 +307,15 @@ __global__ __launch_bounds__(mf::NTH) void chunk_mfma_kernel(const ChunkArgs a, 
 #pragma unroll
         for (int cc = 0; cc < VPL; ++cc) {
           const int jc = ln * VPL + cc;
-          uint32_t w[8];
+          uint32_t vl[16], w[8];
+#pragma unroll
+          for (int tt = 0; tt < 16; ++tt)
+            vl[tt] = __builtin_amdgcn_raw_buffer_load_b16(rv, jc * 2, min(16 * i + tt, n - 1) * rowb, 0);
 #pragma unroll
           for (int tp = 0; tp < 8; ++tp) {
-            uint32_t lo = 0u, hi = 0u;
             const int t = 16 * i + 2 * tp;
-            if (t < n) lo = vv[(row0 + static_cast<int64_t>(t) * H) * DK + j0 + jc];
-            if (t + 1 < n) hi = vv[(row0 + static_cast<int64_t>(t + 1) * H) * DK + j0 + jc];
+            const uint32_t lo = t < n ? (vl[2 * tp] & 0xffffu) : 0u;
+            const uint32_t hi = t + 1 < n ? (vl[2 * tp + 1] & 0xffffu) : 0u;
             w[tp] = lo | (hi << 16);
           }
           u32x4* dst = reinterpret_cast<u32x4*>(&sVT[jc * TS + 16 * i]);
@@ -299,158 +323,187 @@ __global__ __launch_bounds__(mf::NTH) void chunk_mfma_kernel(const ChunkArgs a, 
           dst[1] = u32x4{w[4], w[5], w[6], w[7]};
         }
       }
-      __syncthreads();
-      float eB0 = 1.f, eB1 = 1.f, af0 = 1.f, af1 = 1.f, gc0 = 1.f, gc1 = 1.f;
+    }
+    __syncthreads();
+    {
+      const int i = i1;
+      float d0[4], d1[4];
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
-        const float d0 = sD[ii * DK + c0], d1 = sD[ii * DK + c0 + 1];
-        if (ii < i) { eB0 *= d0; eB1 *= d1; }
-        if (ii > i) { af0 *= d0; af1 *= d1; }
-        gc0 *= d0;
-        gc1 *= d1;
+        d0[ii] = sD[ii * DK + c0];
+        d1[ii] = sD[ii * DK + c0 + 1];
       }
-      if (wv == 0) {
-        sGC[c0] = gc0;
-        sGC[c0 + 1] = gc1;
+      float eB0 = 1.f, eB1 = 1.f, af0 = 1.f, af1 = 1.f;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        if (ii < i) { eB0 *= d0[ii]; eB1 *= d1[ii]; }
+        if (ii > i) { af0 *= d0[ii]; af1 *= d1[ii]; }
       }
-      uint32_t kt0[8], kt1[8], kh0[8], kh1[8];
+      sEB[i * DK + c0] = eB0;
+      sEB[i * DK + c0 + 1] = eB1;
+      if (i == 0) {
+        sGC[c0] = af0 * D0;
+        sGC[c0 + 1] = af1 * D1;
+      }
+      // q Gamma (token-major) and (k Gamma_C / Gamma)^T (channel-major)
+      uint32_t kh0[8], kh1[8];
 #pragma unroll
       for (int tt = 0; tt < 16; ++tt) {
         const int t = 16 * i + tt;
-        const float k0 = bflo(kp[tt]), k1 = bfhi(kp[tt]);
-        const float q0 = bflo(qp[tt]), q1 = bfhi(qp[tt]);
-        *reinterpret_cast<uint32_t*>(&sQt[t * RS + c0]) = pack2(q0 * r0[tt] * eB0, q1 * r1[tt] * eB1);
-        const uint32_t a0 = f2bf(k0 * r0[tt] * eB0), a1 = f2bf(k1 * r1[tt] * eB1);
-        const uint32_t b0 = f2bf(k0 * f0[tt] * af0), b1 = f2bf(k1 * f1[tt] * af1);
+        *reinterpret_cast<uint32_t*>(&sQt[t * RS + c0]) =
+            pack2(bflo(qp[tt]) * r0[tt] * eB0, bfhi(qp[tt]) * r1[tt] * eB1);
+        const uint32_t b0 = f2bf(bflo(kp[tt]) * f0[tt] * af0), b1 = f2bf(bfhi(kp[tt]) * f1[tt] * af1);
         if (tt & 1) {
-          kt0[tt >> 1] |= a0 << 16; kt1[tt >> 1] |= a1 << 16;
           kh0[tt >> 1] |= b0 << 16; kh1[tt >> 1] |= b1 << 16;
         } else {
-          kt0[tt >> 1] = a0; kt1[tt >> 1] = a1;
           kh0[tt >> 1] = b0; kh1[tt >> 1] = b1;
         }
       }
-      u32x4* d;
-      d = reinterpret_cast<u32x4*>(&sKtT[c0 * TS + 16 * i]);
-      d[0] = u32x4{kt0[0], kt0[1], kt0[2], kt0[3]}; d[1] = u32x4{kt0[4], kt0[5], kt0[6], kt0[7]};
-      d = reinterpret_cast<u32x4*>(&sKtT[(c0 + 1) * TS + 16 * i]);
-      d[0] = u32x4{kt1[0], kt1[1], kt1[2], kt1[3]}; d[1] = u32x4{kt1[4], kt1[5], kt1[6], kt1[7]};
-      d = reinterpret_cast<u32x4*>(&sKhT[c0 * TS + 16 * i]);
+      u32x4* d = reinterpret_cast<u32x4*>(&sKhT[c0 * TS + 16 * i]);
       d[0] = u32x4{kh0[0], kh0[1], kh0[2], kh0[3]}; d[1] = u32x4{kh0[4], kh0[5], kh0[6], kh0[7]};
       d = reinterpret_cast<u32x4*>(&sKhT[(c0 + 1) * TS + 16 * i]);
       d[0] = u32x4{kh1[0], kh1[1], kh1[2], kh1[3]}; d[1] = u32x4{kh1[4], kh1[5], kh1[6], kh1[7]};
+      // anchored keys of this tile (j = i) for every tile m >= i:
+      //   k_s e^(B_m - G_s) = (k_s sf_s) * (m == i ? 1 / D_i : prod_{i < ii < m} D_ii)
+      for (int m = i; m < 4; ++m) {
+        float fa0, fa1;
+        if (m == i) {
+          fa0 = fast_rcp(D0);
+          fa1 = fast_rcp(D1);
+        } else {
+          fa0 = 1.f;
+          fa1 = 1.f;
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii)
+            if (ii > i && ii < m) { fa0 *= d0[ii]; fa1 *= d1[ii]; }
+        }
+        uint16_t* dst = sKA + slot(m, i) * 16 * RS + c0;
+#pragma unroll
+        for (int tt = 0; tt < 16; ++tt)
+          *reinterpret_cast<uint32_t*>(dst + tt * RS) =
+              pack2(bflo(kp[tt]) * f0[tt] * fa0, bfhi(kp[tt]) * f1[tt] * fa1);
+      }
     }
     __syncthreads();
 
-    // ---------------- phase 2: L and P tiles ----------------
+    // ---------------- phase 2: L and P tiles, diagonal inverses ----------------
+    {
+      // L^T / P^T tile for pair (i, j): rows s of tile j, columns t of tile i
+      auto lp_tile = [&](int i, int j, f32x4& accL, f32x4& accP) {
+        accL = f32x4{0.f, 0.f, 0.f, 0.f};
+        accP = f32x4{0.f, 0.f, 0.f, 0.f};
+        const uint16_t* Ar = sKA + (slot(i, j) * 16 + r16) * RS;
 #pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      const int i = kPairs[wv][p][0];
-      const int j = kPairs[wv][p][1];
-      if (i < 0) continue;
-      f32x4 accL = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const int cb = 32 * kb + 8 * g4;
-        float f[8];
-        if (i == j) {
-#pragma unroll
-          for (int v = 0; v < 8; ++v) f[v] = fast_rcp(sD[i * DK + cb + v]);
-        } else {
-#pragma unroll
-          for (int v = 0; v < 8; ++v) f[v] = 1.f;
-          for (int ii = j + 1; ii < i; ++ii) {
-#pragma unroll
-            for (int v = 0; v < 8; ++v) f[v] *= sD[ii * DK + cb + v];
-          }
+        for (int kb = 0; kb < 4; ++kb) {
+          const int cb = 32 * kb + 8 * g4;
+          const u32x4 A = lds128(Ar + cb);
+          accL = mma32(A, lds128(&sKR[(16 * i + r16) * RS + cb]), accL);
+          accP = mma32(A, lds128(&sQR[(16 * i + r16) * RS + cb]), accP);
         }
-        const u32x4 kc = lds128(&sKC[(16 * j + r16) * RS + cb]);
-        u32x4 A;
-#pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2)
-          A[w2] = pack2(bflo(kc[w2]) * f[2 * w2], bfhi(kc[w2]) * f[2 * w2 + 1]);
-        const u32x4 Bk = lds128(&sKR[(16 * i + r16) * RS + cb]);
-        const u32x4 Bq = lds128(&sQR[(16 * i + r16) * RS + cb]);
-        accL = mma32(A, Bk, accL);
-        accP = mma32(A, Bq, accP);
-      }
-      // lane holds L^T / P^T at rows s = 16j + 4 g4 + v, column t = 16i + r16
-      const int t = 16 * i + r16;
-      const float bt = sBeta[t];
-      f32x4 pv;
-      if (i == j) {
+      };
+      const int i = wv;
+      f32x4 dL, dP;
+      lp_tile(i, i, dL, dP);
+      // lane holds L^T / P^T at rows s = 4 g4 + v, column t = r16 (both in tile i)
+      {
+        const float bt = sBeta[16 * i + r16];
+        f32x4 pv;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int s = 4 * g4 + v;
-          sLd[(i * 16 + r16) * LDS_ + s] = s < r16 ? bt * accL[v] : 0.f;
-          pv[v] = s <= r16 ? accP[v] : 0.f;
+          sLT[(i * 16 + s) * LTS + r16] = s < r16 ? bt * dL[v] : 0.f;  // L[t][s] stored at [s][t]
+          pv[v] = s <= r16 ? dP[v] : 0.f;
         }
-      } else {
+        *reinterpret_cast<s16x4*>(&sP[(16 * i + r16) * TS + 16 * i + 4 * g4]) = cvt4(pv);
+      }
+      // off-diagonal pairs of this wavefront (issued before the inverse so they overlap it)
+      f32x4 oL[2], oP[2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int pi = kOffPairs[wv][p][0], pj = kOffPairs[wv][p][1];
+        if (pi >= 0) lp_tile(pi, pj, oL[p], oP[p]);
+      }
+      // X_ii = (I + L_ii)^-1, one column per lane (lanes 0..15), right-looking
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (ln < 16) {
+        const float* Lt = sLT + i * 16 * LTS;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = (r == ln) ? 1.f : 0.f;
+#pragma unroll
+        for (int m = 0; m < 15; ++m) {
+#pragma unroll
+          for (int r = m + 1; r < 16; ++r) x[r] -= Lt[m * LTS + r] * x[m];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sX[(16 * i + r) * XS + ln] = f2bf(x[r]);
+      }
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int pi = kOffPairs[wv][p][0], pj = kOffPairs[wv][p][1];
+        if (pi < 0) continue;
+        const int t = 16 * pi + r16;
+        const float bt = sBeta[t];
         f32x4 nl;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) nl[v] = -bt * accL[v];
-        *reinterpret_cast<s16x4*>(&sLm[t * TS + 16 * j + 4 * g4]) = cvt4(nl);
-        pv = accP;
+        for (int v = 0; v < 4; ++v) nl[v] = -bt * oL[p][v];
+        *reinterpret_cast<s16x4*>(&sLm[t * TS + 16 * pj + 4 * g4]) = cvt4(nl);
+        *reinterpret_cast<s16x4*>(&sP[t * TS + 16 * pj + 4 * g4]) = cvt4(oP[p]);
       }
-      *reinterpret_cast<s16x4*>(&sP[t * TS + 16 * j + 4 * g4]) = cvt4(pv);
     }
     __syncthreads();
 
-    // ---------------- phase 3: diagonal inverses X_ii = (I + L_ii)^-1 ----------------
-    if (ln < 16) {
-      const int i = wv, jj = ln;
-      const float* Ld = sLd + i * 16 * LDS_;
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float acc = (r == jj) ? 1.f : 0.f;
-#pragma unroll
-        for (int m = 0; m < r; ++m) acc -= Ld[r * LDS_ + m] * x[m];
-        x[r] = acc;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sX[(i * 16 + r) * XS + jj] = f2bf(x[r]);
-    }
-    __syncthreads();
-
-    // ---------------- phase 4: (I + L) [W | Ut] = Diag(beta) [K Gamma | V] ----------------
-    f32x4 Ut[JPW][4];
-#pragma unroll
-    for (int col = 0; col < 2 + JPW; ++col) {
-      // columns 0,1: key-channel tiles 2wv, 2wv+1 of W; then value tiles wv + 4u of Ut
-      const bool is_w = col < 2;
-      const int u = col - 2;
-      const int ct = is_w ? 2 * wv + col : wv + 4 * u;
-      if (!is_w && ct >= NJT) continue;
-      const uint16_t* Y = is_w ? sKtT : sVT;
-      f32x4 Z[4];
-      s16x4 Zb[4];
+    // ---------------- phase 3: (I + L) [W | Ut] = Diag(beta) [K Gamma | V] ----------------
+    // columns: 0, 1 -> key-channel tiles 2wv, 2wv+1 of W; 2.. -> value tiles wv + 4u of Ut
+    constexpr int NCOL = 2 + JPW;
+    f32x4 Z[NCOL][4];
+    {
+      s16x4 Zb[NCOL][4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const s16x4 yv = lds64(&Y[(16 * ct + r16) * TS + 16 * i + 4 * g4]);
-        f32x4 acc;
+        float bt[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          acc[v] = sBeta[16 * i + 4 * g4 + v] * bf16_to_f32(static_cast<uint16_t>(yv[v]));
+        for (int v = 0; v < 4; ++v) bt[v] = sBeta[16 * i + 4 * g4 + v];
 #pragma unroll
-        for (int j = 0; j < i; ++j) acc = mma16(lds64(&sLm[(16 * i + r16) * TS + 16 * j + 4 * g4]), Zb[j], acc);
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        Z[i] = mma16(lds64(&sX[(16 * i + r16) * XS + 4 * g4]), cvt4(acc), zero);
-        Zb[i] = cvt4(Z[i]);
+        for (int col = 0; col < NCOL; ++col) {
+          const bool is_w = col < 2;
+          const int ct = is_w ? 2 * wv + col : wv + 4 * (col - 2);
+          if (!is_w && ct >= NJT) continue;
+          f32x4 acc;
+          if (is_w) {  // K Gamma = (k r) * eB_i, rows t = 16i + 4 g4 + v, channel 16 ct + r16
+            const float e = sEB[i * DK + 16 * ct + r16];
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              acc[v] = bt[v] * e * bf16_to_f32(sKR[(16 * i + 4 * g4 + v) * RS + 16 * ct + r16]);
+          } else {
+            const s16x4 yv = lds64(&sVT[(16 * ct + r16) * TS + 16 * i + 4 * g4]);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[v] = bt[v] * bf16_to_f32(static_cast<uint16_t>(yv[v]));
+          }
+#pragma unroll
+          for (int j = 0; j < i; ++j)
+            acc = mma16(lds64(&sLm[(16 * i + r16) * TS + 16 * j + 4 * g4]), Zb[col][j], acc);
+          const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+          Z[col][i] = mma16(lds64(&sX[(16 * i + r16) * XS + 4 * g4]), cvt4(acc), zero);
+          Zb[col][i] = cvt4(Z[col][i]);
+        }
       }
-      if (is_w) {
+      // -W into the k r storage (this wavefront's own channel columns; all their reads are done)
+#pragma unroll
+      for (int col = 0; col < 2; ++col) {
+        const int ct = 2 * wv + col;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) sW[(16 * i + 4 * g4 + v) * RS + 16 * ct + r16] = f2bf(-Z[i][v]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Ut[u][i] = Z[i];
+          for (int v = 0; v < 4; ++v) sW[(16 * i + 4 * g4 + v) * RS + 16 * ct + r16] = f2bf(-Z[col][i][v]);
       }
     }
     __syncthreads();
 
-    // ---------------- phases 5-7: U, outputs, state update (per owned value tile) ----------------
+    // ---------------- phase 4: U, outputs, state update (per owned value tile) ----------------
+    const auto ro = rsrc(static_cast<Tout*>(a.o) + row0 * DK + j0, (span - 1) * DK * ES + DVS * ES);
 #pragma unroll
     for (int u = 0; u < JPW; ++u) {
       const int jt = wv + 4 * u;
@@ -462,24 +515,38 @@ __global__ __launch_bounds__(mf::NTH) void chunk_mfma_kernel(const ChunkArgs a, 
       s16x4 Ub[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        f32x4 acc = Ut[u][i];
+        f32x4 acc = Z[2 + u][i];
+        const uint16_t* Wr = &sW[(16 * i + r16) * RS + 4 * g4];
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) acc = mma16(lds64(&sW[(16 * i + r16) * RS + 16 * ct + 4 * g4]), Sb[ct], acc);
+        for (int cp = 0; cp < 4; ++cp)
+          acc = mma32(cat(lds64(Wr + 32 * cp), lds64(Wr + 32 * cp + 16)), cat(Sb[2 * cp], Sb[2 * cp + 1]), acc);
         Ub[i] = cvt4(acc);
       }
       // O = (Q Gamma) S + P U
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const uint16_t* Qr = &sQt[(16 * i + r16) * RS + 4 * g4];
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) acc = mma16(lds64(&sQt[(16 * i + r16) * RS + 16 * ct + 4 * g4]), Sb[ct], acc);
+        for (int cp = 0; cp < 4; ++cp)
+          acc = mma32(cat(lds64(Qr + 32 * cp), lds64(Qr + 32 * cp + 16)), cat(Sb[2 * cp], Sb[2 * cp + 1]), acc);
+        const uint16_t* Pr = &sP[(16 * i + r16) * TS + 4 * g4];
 #pragma unroll
-        for (int m = 0; m <= i; ++m) acc = mma16(lds64(&sP[(16 * i + r16) * TS + 16 * m + 4 * g4]), Ub[m], acc);
+        for (int m = 0; m + 1 <= i; m += 2)
+          acc = mma32(cat(lds64(Pr + 16 * m), lds64(Pr + 16 * m + 16)), cat(Ub[m], Ub[m + 1]), acc);
+        // the unpaired last tile runs on the same 16x16x32 shape, zero-padded: an
+        // accumulator produced by one MFMA shape is never fed to the other shape
+        if ((i & 1) == 0) acc = mma32(cat(lds64(Pr + 16 * i), s16x4{0, 0, 0, 0}), cat(Ub[i], s16x4{0, 0, 0, 0}), acc);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int t = 16 * i + 4 * g4 + v;
-          if (t < n)
-            io<Tout>::store(o, (row0 + static_cast<int64_t>(t) * H) * DK + j0 + 16 * jt + r16, a.scale * acc[v]);
+          if (t < n) {
+            const int voff = (t * H * DK + 16 * jt + r16) * ES;
+            if (ES == 2)
+              __builtin_amdgcn_raw_buffer_store_b16(f2bf(a.scale * acc[v]), ro, voff, 0, 0);
+            else
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a.scale * acc[v]), ro, voff, 0, 0);
+          }
         }
       }
       // S <- Diag(Gamma_C) S + (K Gamma_C / Gamma)^T U
@@ -488,8 +555,9 @@ __global__ __launch_bounds__(mf::NTH) void chunk_mfma_kernel(const ChunkArgs a, 
         f32x4 acc;
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[v] = S[u][ct][v] * sGC[16 * ct + 4 * g4 + v];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) acc = mma16(lds64(&sKhT[(16 * ct + r16) * TS + 16 * m + 4 * g4]), Ub[m], acc);
+        const uint16_t* Kr = &sKhT[(16 * ct + r16) * TS + 4 * g4];
+        acc = mma32(cat(lds64(Kr), lds64(Kr + 16)), cat(Ub[0], Ub[1]), acc);
+        acc = mma32(cat(lds64(Kr + 32), lds64(Kr + 48)), cat(Ub[2], Ub[3]), acc);
         S[u][ct] = acc;
       }
     }
@@ -511,7 +579,8 @@ __global__ __launch_bounds__(mf::NTH) void chunk_mfma_kernel(const ChunkArgs a, 
 }
 
 bool chunk_mfma_supports(const ChunkArgs& a) {
-  return a.in_bf16 && a.dk == 128 && a.dv == 128 && a.chunk == 64;
+  // H bound: one chunk's byte span must fit the 32-bit buffer offsets
+  return a.in_bf16 && a.dk == 128 && a.dv == 128 && a.chunk == 64 && a.H <= 65536;
 }
 
 template <int DVS, bool FROM_Z, typename Tout>
