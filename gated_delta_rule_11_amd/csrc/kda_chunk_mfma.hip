@@ -67,8 +67,9 @@ struct Layout {
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
-// Raw buffer resource: base, byte range; loads outside the range read 0 and
-// stores outside it are dropped by the hardware.
+// Raw buffer resource: base, byte range.  The hardware range check covers the
+// per-lane offset only, not the scalar (token) offset, so every token offset
+// used below is clamped to the chunk's last valid token by construction.
 constexpr int kRsrcFlags = 0x00020000;
 }  // namespace mf
 
@@ -112,6 +113,67 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
 }
 __device__ __forceinline__ uint32_t bload32(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
+// One wavefront's raw inputs for its 16-token tile of a chunk (gate layout:
+// lane -> channels 2*lane, 2*lane+1), loaded ahead of use.
+template <int DVS>
+struct RawTile {
+  static constexpr int VPL = DVS >= 64 ? DVS / 64 : 1;  // value columns per lane
+  uint32_t k[16], q[16], zg[16], zg2[16];  // bf16 pairs; z (bf16 pairs) or G (fp32 x, fp32 y)
+  uint32_t gb0, gb1;                       // G at the token before the tile (G input only)
+  uint32_t v[VPL][16];
+  uint32_t beta;
+};
+
+template <int DVS, bool FROM_Z>
+__device__ __forceinline__ void load_tile(RawTile<DVS>& R, const ChunkArgs& a, int b, int h, int t0, int i, int ln,
+                                          int j0) {
+  using namespace mf;
+  const int T = a.T, H = a.H;
+  const int n = min(C, T - t0);
+  const int64_t row0 = (static_cast<int64_t>(b) * T + t0) * H + h;
+  const int64_t span = static_cast<int64_t>(n - 1) * H + 1;
+  const int rowb = H * DK * 2;
+  const int c0 = 2 * ln;
+  const auto rq = rsrc(static_cast<const uint16_t*>(a.q) + row0 * DK, span * DK * 2);
+  const auto rk = rsrc(static_cast<const uint16_t*>(a.k) + row0 * DK, span * DK * 2);
+  const auto rv = rsrc(static_cast<const uint16_t*>(a.v) + row0 * DK + j0, span * DK * 2);
+  const auto rb = rsrc(static_cast<const uint16_t*>(a.beta) + row0, span * 2);
+  // padded tokens read the last valid token and are masked by the consumer
+#pragma unroll
+  for (int tt = 0; tt < 16; ++tt) {
+    const int so = min(16 * i + tt, n - 1) * rowb;
+    R.k[tt] = bload32(rk, c0 * 2, so);
+    R.q[tt] = bload32(rq, c0 * 2, so);
+  }
+  if (FROM_Z) {
+    const auto rz = rsrc(static_cast<const uint16_t*>(a.z) + row0 * DK, span * DK * 2);
+#pragma unroll
+    for (int tt = 0; tt < 16; ++tt) R.zg[tt] = bload32(rz, c0 * 2, min(16 * i + tt, n - 1) * rowb);
+  } else {
+    const auto rg = rsrc(a.G + row0 * DK, span * DK * 4);
+#pragma unroll
+    for (int tt = 0; tt < 16; ++tt) {
+      const u32x2 g = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, c0 * 4, min(16 * i + tt, n - 1) * rowb * 2, 0));
+      R.zg[tt] = g[0];
+      R.zg2[tt] = g[1];
+    }
+    const u32x2 gb = __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, c0 * 4, min(max(16 * i - 1, 0), n - 1) * rowb * 2, 0));
+    R.gb0 = gb[0];
+    R.gb1 = gb[1];
+  }
+  constexpr int VPL = RawTile<DVS>::VPL;
+  if (ln * VPL < DVS) {
+#pragma unroll
+    for (int cc = 0; cc < VPL; ++cc)
+#pragma unroll
+      for (int tt = 0; tt < 16; ++tt)
+        R.v[cc][tt] = __builtin_amdgcn_raw_buffer_load_b16(rv, (ln * VPL + cc) * 2, min(16 * i + tt, n - 1) * rowb, 0);
+  }
+  if (ln < 16) R.beta = __builtin_amdgcn_raw_buffer_load_b16(rb, min(16 * i + ln, n - 1) * H * 2, 0, 0);
 }
 
 // Tile pairs (i, j < i) of the L / P products per wavefront; each wavefront's
@@ -166,7 +228,6 @@ __global__ __launch_bounds__(mf::NTH) void chunk_mfma_kernel(const ChunkArgs a, 
   const int g4 = ln >> 4;   // MFMA lane group
   const int r16 = ln & 15;  // MFMA lane row/column
   const int c0 = 2 * ln;    // gate layout: channels c0, c0+1
-  const int rowb = H * DK * 2;  // bytes between consecutive tokens of one head (bf16 rows)
 
   // gate constants for the lane's two channels (log2 units)
   float ea0 = 0.f, ea1 = 0.f;
@@ -193,14 +254,13 @@ __global__ __launch_bounds__(mf::NTH) void chunk_mfma_kernel(const ChunkArgs a, 
     }
   }
 
+  RawTile<DVS> raw;
+  if (T > 0) load_tile<DVS, FROM_Z>(raw, a, b, h, 0, wv, ln, j0);
+
   for (int t0 = 0; t0 < T; t0 += C) {
     const int n = min(C, T - t0);
     const int64_t row0 = (static_cast<int64_t>(b) * T + t0) * H + h;  // token t0's row index
     const int64_t span = static_cast<int64_t>(n - 1) * H + 1;         // rows this chunk may touch
-    const auto rq = rsrc(static_cast<const uint16_t*>(a.q) + row0 * DK, span * DK * 2);
-    const auto rk = rsrc(static_cast<const uint16_t*>(a.k) + row0 * DK, span * DK * 2);
-    const auto rv = rsrc(static_cast<const uint16_t*>(a.v) + row0 * DK + j0, span * DK * 2);
-    const auto rb = rsrc(static_cast<const uint16_t*>(a.beta) + row0, span * 2);
 
     // ---------------- phase 1: gate, decays, operand tiles ----------------
     const int i1 = wv;  // this wavefront's tile
@@ -209,25 +269,19 @@ __global__ __launch_bounds__(mf::NTH) void chunk_mfma_kernel(const ChunkArgs a, 
     float D0 = 1.f, D1 = 1.f;
     {
       const int i = i1;
-      if (FROM_Z) {
-        const auto rz = rsrc(static_cast<const uint16_t*>(a.z) + row0 * DK, span * DK * 2);
-        float al0[16], al1[16];
-        uint32_t zp[16];
-        // all loads first (padded tokens read the last valid token and are masked below)
 #pragma unroll
-        for (int tt = 0; tt < 16; ++tt) {
-          const int so = min(16 * i + tt, n - 1) * rowb;
-          kp[tt] = bload32(rk, c0 * 2, so);
-          qp[tt] = bload32(rq, c0 * 2, so);
-          zp[tt] = bload32(rz, c0 * 2, so);
-        }
+      for (int tt = 0; tt < 16; ++tt) {
+        const bool valid = 16 * i + tt < n;
+        kp[tt] = valid ? raw.k[tt] : 0u;
+        qp[tt] = valid ? raw.q[tt] : 0u;
+      }
+      if (FROM_Z) {
+        float al0[16], al1[16];
 #pragma unroll
         for (int tt = 0; tt < 16; ++tt) {
           const bool valid = 16 * i + tt < n;
-          al0[tt] = valid ? fast_exp2(gate_log2(bflo(zp[tt]), ea0, gmin_l2e)) : 1.f;
-          al1[tt] = valid ? fast_exp2(gate_log2(bfhi(zp[tt]), ea1, gmin_l2e)) : 1.f;
-          kp[tt] = valid ? kp[tt] : 0u;
-          qp[tt] = valid ? qp[tt] : 0u;
+          al0[tt] = valid ? fast_exp2(gate_log2(bflo(raw.zg[tt]), ea0, gmin_l2e)) : 1.f;
+          al1[tt] = valid ? fast_exp2(gate_log2(bfhi(raw.zg[tt]), ea1, gmin_l2e)) : 1.f;
         }
 #pragma unroll
         for (int tt = 0; tt < 16; ++tt) {
@@ -246,34 +300,21 @@ __global__ __launch_bounds__(mf::NTH) void chunk_mfma_kernel(const ChunkArgs a, 
         }
       } else {
         // chunk-local sums G (natural log, fp32) -> log2 within this tile
-        const auto rg = rsrc(a.G + row0 * DK, span * DK * 4);
         float G0[16], G1[16];
-        u32x2 gg[16];
-#pragma unroll
-        for (int tt = 0; tt < 16; ++tt) {
-          const int so = min(16 * i + tt, n - 1) * rowb * 2;
-          kp[tt] = bload32(rk, c0 * 2, min(16 * i + tt, n - 1) * rowb);
-          qp[tt] = bload32(rq, c0 * 2, min(16 * i + tt, n - 1) * rowb);
-          gg[tt] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, c0 * 4, so, 0));
-        }
         float base0 = 0.f, base1 = 0.f;
         if (i > 0 && 16 * i < n) {
-          const u32x2 gb = __builtin_bit_cast(
-              u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, c0 * 4, (16 * i - 1) * rowb * 2, 0));
-          base0 = __uint_as_float(gb[0]) * kLog2e;
-          base1 = __uint_as_float(gb[1]) * kLog2e;
+          base0 = __uint_as_float(raw.gb0) * kLog2e;
+          base1 = __uint_as_float(raw.gb1) * kLog2e;
         }
         float last0 = base0, last1 = base1;
 #pragma unroll
         for (int tt = 0; tt < 16; ++tt) {
           if (16 * i + tt < n) {
-            G0[tt] = __uint_as_float(gg[tt][0]) * kLog2e;
-            G1[tt] = __uint_as_float(gg[tt][1]) * kLog2e;
+            G0[tt] = __uint_as_float(raw.zg[tt]) * kLog2e;
+            G1[tt] = __uint_as_float(raw.zg2[tt]) * kLog2e;
             last0 = G0[tt];
             last1 = G1[tt];
           } else {
-            kp[tt] = 0u;
-            qp[tt] = 0u;
             G0[tt] = last0;
             G1[tt] = last1;
           }
@@ -292,8 +333,7 @@ __global__ __launch_bounds__(mf::NTH) void chunk_mfma_kernel(const ChunkArgs a, 
       sD[i * DK + c0 + 1] = D1;
       if (ln < 16) {
         const int t = 16 * i + ln;
-        const uint32_t bv = __builtin_amdgcn_raw_buffer_load_b16(rb, min(t, n - 1) * H * 2, 0, 0);
-        sBeta[t] = t < n ? bf16_to_f32(static_cast<uint16_t>(bv)) : 0.f;
+        sBeta[t] = t < n ? bf16_to_f32(static_cast<uint16_t>(raw.beta)) : 0.f;
       }
 #pragma unroll
       for (int tt = 0; tt < 16; ++tt) {
@@ -307,15 +347,12 @@ __global__ __launch_bounds__(mf::NTH) void chunk_mfma_kernel(const ChunkArgs a, 
 #pragma unroll
         for (int cc = 0; cc < VPL; ++cc) {
           const int jc = ln * VPL + cc;
-          uint32_t vl[16], w[8];
-#pragma unroll
-          for (int tt = 0; tt < 16; ++tt)
-            vl[tt] = __builtin_amdgcn_raw_buffer_load_b16(rv, jc * 2, min(16 * i + tt, n - 1) * rowb, 0);
+          uint32_t w[8];
 #pragma unroll
           for (int tp = 0; tp < 8; ++tp) {
             const int t = 16 * i + 2 * tp;
-            const uint32_t lo = t < n ? (vl[2 * tp] & 0xffffu) : 0u;
-            const uint32_t hi = t + 1 < n ? (vl[2 * tp + 1] & 0xffffu) : 0u;
+            const uint32_t lo = t < n ? (raw.v[cc][2 * tp] & 0xffffu) : 0u;
+            const uint32_t hi = t + 1 < n ? (raw.v[cc][2 * tp + 1] & 0xffffu) : 0u;
             w[tp] = lo | (hi << 16);
           }
           u32x4* dst = reinterpret_cast<u32x4*>(&sVT[jc * TS + 16 * i]);
@@ -384,6 +421,8 @@ __global__ __launch_bounds__(mf::NTH) void chunk_mfma_kernel(const ChunkArgs a, 
               pack2(bflo(kp[tt]) * f0[tt] * fa0, bfhi(kp[tt]) * f1[tt] * fa1);
       }
     }
+    // the next chunk's raw tile is fetched now and lands during phases 2-4
+    if (t0 + C < T) load_tile<DVS, FROM_Z>(raw, a, b, h, t0 + C, wv, ln, j0);
     __syncthreads();
 
     // ---------------- phase 2: L and P tiles, diagonal inverses ----------------
