@@ -43,6 +43,28 @@ PREFILL_BYTES_PER_TOKEN_HEAD = 4 * 128 * 2 + 2 + 128 * 2
 DECODE_BYTES_PER_SEQ_HEAD = 2 * 128 * 128 * 4 + 4 * 128 * 2 + 2 + 128 * 2
 
 
+# HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE passes, each scaled
+# by what the same counter reads for a plain device copy of known size (read factor 2.0,
+# write factor 1.0; summaries in profiles/).  A figure is reported only while the kernel
+# sources it was taken on are unchanged (sha256 of the listed files), else null.
+MEASURED_TRAFFIC = {
+    "prefill": {"files": ["gated_delta_rule_11_amd/csrc/kda_chunk_mfma.hip", "gated_delta_rule_11_amd/csrc/kda_common.hpp"],
+                "sha256": "221cbdc411fb3c17", "bytes": 5.454e9},
+    "decode": {"files": ["gated_delta_rule_11_amd/csrc/kda_decode.hip", "gated_delta_rule_11_amd/csrc/kda_common.hpp"],
+               "sha256": "03354a1f412561c7", "bytes": 1.0849e9},
+}
+
+
+def measured_traffic(key):
+    import hashlib
+    rec = MEASURED_TRAFFIC[key]
+    h = hashlib.sha256()
+    for f in rec["files"]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return rec["bytes"] if h.hexdigest()[:16] == rec["sha256"] else None
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -55,6 +77,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
                     help="profiling runs: time one path only (the JSON line then reports that path)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the timed region, run one plain device-to-device copy of this many MiB "
+                         "(outside the timed region) so a counter pass can scale FETCH_SIZE/WRITE_SIZE")
     ap.add_argument("--cpu-sample-heads", type=int, default=32,
                     help="heads of batch entry 0 the oracle runs for the CPU baseline")
     args = ap.parse_args()
@@ -153,6 +178,16 @@ def main():
     log(f"timed {args.steps} steps: wall {wall * 1e3:.2f} ms; prefill ms {['%.3f' % x for x in pre_ms]}; "
         f"decode(64 steps) ms {['%.3f' % x for x in dec_ms]}")
 
+    if args.copy_calibration_mib > 0:
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {nbytes} bytes device-to-device")
+        del src, dst
+
     pre_avg_s = max(float(np.mean(pre_ms)) / 1e3, 1e-9)
     dec_avg_s = max(float(np.mean(dec_ms)) / 1e3, 1e-9)
     tokens = ps.B * ps.T
@@ -211,14 +246,14 @@ def main():
                    "parallelism": "single GPU"},
         "prefill_ms": round(pre_avg_s * 1e3, 4),
         "roofline": {"bound": "hbm", "achieved": round(pre_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(pre_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(pre_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("prefill"),
                      "kernel": "chunk prefill (kda_chunk_fwd_z)",
                      "algorithmic_bytes_per_launch": pre_bytes,
                      "mfma_tflops_algorithmic": round(pre_flops / pre_avg_s / 1e12, 2),
                      "mfma_frac_algorithmic": round(pre_flops / pre_avg_s / 1e12 / BF16_PEAK_TFLOPS, 4)},
         "decode": {"value": round(decode_tps, 1), "unit": "tokens/s", "ms_per_64_steps": round(dec_avg_s * 1e3, 4),
                    "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                                "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("decode"),
                                 "algorithmic_bytes_per_launch": dec_bytes}},
         "cpu_baseline": cpu,
     }
