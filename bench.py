@@ -80,8 +80,8 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed region, run one plain device-to-device copy of this many MiB "
                          "(outside the timed region) so a counter pass can scale FETCH_SIZE/WRITE_SIZE")
-    ap.add_argument("--cpu-sample-heads", type=int, default=32,
-                    help="heads of batch entry 0 the oracle runs for the CPU baseline")
+    ap.add_argument("--cpu-sample-batches", type=int, default=4,
+                    help="batch entries (all heads, all tokens) the oracle runs for the CPU baseline")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -206,26 +206,26 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and run_pre:
         import oracle
-        nh = max(1, min(ps.H, args.cpu_sample_heads))
+        nb = max(1, min(ps.B, args.cpu_sample_batches))
         cores = max(1, min(16, os.cpu_count() or 1))
-        f = {k: ki.to_f64(pd[k][0:1, :, 0:nh], ps.dtype) for k in ("q", "k", "v", "z", "beta")}
-        A64 = pd["A"][0:nh].astype(np.float64)
-        S064 = pd["S0"][0:1, 0:nh].astype(np.float64)
-        log(f"cpu baseline: oracle on b=0, heads 0..{nh - 1}, T={ps.T}, {cores} threads")
+        f = {k: ki.to_f64(pd[k][0:nb], ps.dtype) for k in ("q", "k", "v", "z", "beta")}
+        A64 = pd["A"].astype(np.float64)
+        S064 = pd["S0"][0:nb].astype(np.float64)
+        log(f"cpu baseline: oracle on batch entries 0..{nb - 1}, all {ps.H} heads, T={ps.T}, {cores} threads")
         c0 = time.perf_counter()
         o_ref, S_ref = oracle.forward_z(f["q"], f["k"], f["v"], f["beta"], f["z"], A64, -5.0, S064,
                                         nthreads=cores)
         cdt = time.perf_counter() - c0
-        # tokens/s of the whole workload (all H heads) at the sample's rate
-        cpu_tps = ps.T * (nh / ps.H) / cdt
-        o_gpu = o_pre[0:1, :, 0:nh].float().cpu().numpy().astype(np.float64)
-        S_gpu = S_pre[0:1, 0:nh].cpu().numpy().astype(np.float64)
+        cpu_tps = nb * ps.T / cdt
+        o_gpu = o_pre[0:nb].float().cpu().numpy().astype(np.float64)
+        S_gpu = S_pre[0:nb].cpu().numpy().astype(np.float64)
         rel_o = float(np.linalg.norm(o_gpu - o_ref) / np.linalg.norm(o_ref))
         rel_S = float(np.linalg.norm(S_gpu - S_ref) / np.linalg.norm(S_ref))
         log(f"cpu baseline {cdt:.1f}s -> {cpu_tps:.1f} tokens/s; sample parity rel-L2 o={rel_o:.2e} S={rel_S:.2e}")
+        whole = "the whole workload" if nb == ps.B else f"batch entries 0-{nb - 1} of {ps.B}"
         cpu = {"value": round(cpu_tps, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-               "sample": f"prefill b=0, heads 0-{nh - 1} of {ps.H}, all {ps.T} tokens (fp64 token loop, "
-                         f"{cdt:.1f}s); throughput scaled to all heads",
+               "sample": f"prefill {whole}: all {ps.H} heads, all {ps.T} tokens (fp64 token loop, "
+                         f"{cdt:.1f}s)",
                "sample_parity_rel_l2": {"o": rel_o, "S": rel_S}}
 
     out = {
@@ -257,6 +257,13 @@ def main():
                                 "algorithmic_bytes_per_launch": dec_bytes}},
         "cpu_baseline": cpu,
     }
+    # a profiling run that timed one path reports nothing for the other
+    if not run_dec:
+        out["decode"] = None
+    if not run_pre:
+        out["value"] = None
+        out["prefill_ms"] = None
+        out["roofline"] = None
     print(json.dumps(out), flush=True)
 
 
