@@ -138,9 +138,11 @@ template <bool FROM_Z> struct RawTile {
   uint32_t beta;               // beta of token ln of the tile (lanes 0..15)
 };
 
-// Raw inputs of one wavefront's 16-token tile, token offsets clamped to the chunk.
-template <int DVS, bool FROM_Z>
-__device__ __forceinline__ void load_tile(RawTile<FROM_Z>& R, const ChunkArgs& a, int b, int h, int t0, int i,
+// Raw inputs of one wavefront's 16-token tile, token offsets clamped to the chunk,
+// in four parts (keys; queries; gate inputs; values and beta) so that the loads
+// of a tile can go out in different phases.
+template <int DVS, bool FROM_Z, int PART>
+__device__ __forceinline__ void load_part(RawTile<FROM_Z>& R, const ChunkArgs& a, int b, int h, int t0, int i,
                                           int ln, int j0) {
   using namespace mf;
   static_assert(DVS <= 64, "one value column per lane");
@@ -150,40 +152,54 @@ __device__ __forceinline__ void load_tile(RawTile<FROM_Z>& R, const ChunkArgs& a
   const int64_t span = static_cast<int64_t>(n - 1) * H + 1;
   const int rowb = H * DK * 2;
   const int c0 = 2 * ln;
-  const auto rq = rsrc(static_cast<const uint16_t*>(a.q) + row0 * DK, span * DK * 2);
-  const auto rk = rsrc(static_cast<const uint16_t*>(a.k) + row0 * DK, span * DK * 2);
-  const auto rv = rsrc(static_cast<const uint16_t*>(a.v) + row0 * DK + j0, span * DK * 2);
-  const auto rb = rsrc(static_cast<const uint16_t*>(a.beta) + row0, span * 2);
-#pragma unroll
-  for (int tt = 0; tt < 16; ++tt) {
-    const int so = min(16 * i + tt, n - 1) * rowb;
-    R.k[tt] = bload32(rk, c0 * 2, so);
-    R.q[tt] = bload32(rq, c0 * 2, so);
-  }
-  if constexpr (FROM_Z) {
-    const auto rz = rsrc(static_cast<const uint16_t*>(a.z) + row0 * DK, span * DK * 2);
-#pragma unroll
-    for (int tt = 0; tt < 16; ++tt) R.g0[tt] = bload32(rz, c0 * 2, min(16 * i + tt, n - 1) * rowb);
-  } else {
-    const auto rg = rsrc(a.G + row0 * DK, span * DK * 4);
+  if constexpr (PART == 0 || PART == 1) {
+    const auto r = rsrc(static_cast<const uint16_t*>(PART == 0 ? a.k : a.q) + row0 * DK, span * DK * 2);
 #pragma unroll
     for (int tt = 0; tt < 16; ++tt) {
-      const u32x2 g = __builtin_bit_cast(
-          u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, c0 * 4, min(16 * i + tt, n - 1) * rowb * 2, 0));
-      R.g0[tt] = g[0];
-      R.g1[tt] = g[1];
+      const uint32_t x = bload32(r, c0 * 2, min(16 * i + tt, n - 1) * rowb);
+      if constexpr (PART == 0)
+        R.k[tt] = x;
+      else
+        R.q[tt] = x;
     }
-    const u32x2 gb = __builtin_bit_cast(
-        u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, c0 * 4, min(max(16 * i - 1, 0), n - 1) * rowb * 2, 0));
-    R.gb[0] = gb[0];
-    R.gb[1] = gb[1];
-  }
-  if (ln < DVS) {
+  } else if constexpr (PART == 2) {
+    if constexpr (FROM_Z) {
+      const auto rz = rsrc(static_cast<const uint16_t*>(a.z) + row0 * DK, span * DK * 2);
 #pragma unroll
-    for (int tt = 0; tt < 16; ++tt)
-      R.v[tt] = __builtin_amdgcn_raw_buffer_load_b16(rv, ln * 2, min(16 * i + tt, n - 1) * rowb, 0);
+      for (int tt = 0; tt < 16; ++tt) R.g0[tt] = bload32(rz, c0 * 2, min(16 * i + tt, n - 1) * rowb);
+    } else {
+      const auto rg = rsrc(a.G + row0 * DK, span * DK * 4);
+#pragma unroll
+      for (int tt = 0; tt < 16; ++tt) {
+        const u32x2 g = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, c0 * 4, min(16 * i + tt, n - 1) * rowb * 2, 0));
+        R.g0[tt] = g[0];
+        R.g1[tt] = g[1];
+      }
+      const u32x2 gb = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, c0 * 4, min(max(16 * i - 1, 0), n - 1) * rowb * 2, 0));
+      R.gb[0] = gb[0];
+      R.gb[1] = gb[1];
+    }
+  } else {
+    const auto rv = rsrc(static_cast<const uint16_t*>(a.v) + row0 * DK + j0, span * DK * 2);
+    const auto rb = rsrc(static_cast<const uint16_t*>(a.beta) + row0, span * 2);
+    if (ln < DVS) {
+#pragma unroll
+      for (int tt = 0; tt < 16; ++tt)
+        R.v[tt] = __builtin_amdgcn_raw_buffer_load_b16(rv, ln * 2, min(16 * i + tt, n - 1) * rowb, 0);
+    }
+    if (ln < 16) R.beta = __builtin_amdgcn_raw_buffer_load_b16(rb, min(16 * i + ln, n - 1) * H * 2, 0, 0);
   }
-  if (ln < 16) R.beta = __builtin_amdgcn_raw_buffer_load_b16(rb, min(16 * i + ln, n - 1) * H * 2, 0, 0);
+}
+
+template <int DVS, bool FROM_Z>
+__device__ __forceinline__ void load_tile(RawTile<FROM_Z>& R, const ChunkArgs& a, int b, int h, int t0, int i,
+                                          int ln, int j0) {
+  load_part<DVS, FROM_Z, 0>(R, a, b, h, t0, i, ln, j0);
+  load_part<DVS, FROM_Z, 1>(R, a, b, h, t0, i, ln, j0);
+  load_part<DVS, FROM_Z, 2>(R, a, b, h, t0, i, ln, j0);
+  load_part<DVS, FROM_Z, 3>(R, a, b, h, t0, i, ln, j0);
 }
 
 // Off-diagonal tile pairs (i, j < i) of the L / P products, per gate wavefront.
@@ -667,8 +683,15 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
       lds_barrier();
       relane();
 
-      // ---- 2: prefetch the next chunk's raw tile (lands by A1); off-diagonal L, P tiles
-      if (more) load_tile<DVS, FROM_Z>(R, a, b, h, t0 + C, i, ln, j0);
+      // ---- 2: off-diagonal L, P tiles; keys, queries and gate inputs of the next chunk,
+      // in flight until A1.  All workgroups load at once here and the loads issue only
+      // as fast as memory takes them, so this phase (which waits for the state chain)
+      // carries most of them; values and beta follow in phase 3.
+      if (more) {
+        load_part<DVS, FROM_Z, 0>(R, a, b, h, t0 + C, i, ln, j0);
+        load_part<DVS, FROM_Z, 1>(R, a, b, h, t0 + C, i, ln, j0);
+        load_part<DVS, FROM_Z, 2>(R, a, b, h, t0 + C, i, ln, j0);
+      }
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
         const int pi = kOffPairs8[i][p][0], pj = kOffPairs8[i][p][1];
@@ -687,6 +710,7 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
       relane();
 
       // ---- 3: W column tile wv
+      if (more) load_part<DVS, FROM_Z, 3>(R, a, b, h, t0 + C, i, ln, j0);
       {
         f32x4 unused[4];
         solve(std::integral_constant<int, 1>{}, unused);
