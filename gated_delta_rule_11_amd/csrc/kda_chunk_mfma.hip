@@ -43,7 +43,6 @@ constexpr int DK = 128;        // key / value head dim
 constexpr int RS = DK + 8;     // row stride (bf16 elements) of [token][channel] tiles
 constexpr int TS = C + 8;      // row stride of [channel][token] tiles
 constexpr int XS = 24;         // row stride of the 16x16 diagonal inverses
-constexpr int LTS = 20;        // row stride (floats) of the transposed fp32 diagonal L blocks
 
 // pair (i, j <= i) of 16-token tiles -> slot of its anchored key tile
 __host__ __device__ constexpr int slot(int i, int j) { return i * (i + 1) / 2 + j; }
@@ -59,8 +58,7 @@ struct Layout {
   static constexpr int LM = VT + DVS * TS * 2;          // [64][TS]  -L (off-diagonal tiles)
   static constexpr int PM = LM + C * TS * 2;            // [64][TS]  P
   static constexpr int XM = PM + C * TS * 2;            // [4][16][XS] diagonal inverses (bf16)
-  static constexpr int LT = XM + 4 * 16 * XS * 2;       // [4][16][LTS] fp32 diagonal L, transposed
-  static constexpr int DT = LT + 4 * 16 * LTS * 4;      // [4][128] fp32 tile decays D_i
+  static constexpr int DT = XM + 4 * 16 * XS * 2;       // [4][128] fp32 tile decays D_i
   static constexpr int EB = DT + 4 * DK * 4;            // [4][128] fp32 decay before tile i
   static constexpr int GC = EB + 4 * DK * 4;            // [128] fp32 chunk decay
   static constexpr int BT = GC + DK * 4;                // [64] fp32 beta
@@ -235,7 +233,6 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
   uint16_t* sLm = reinterpret_cast<uint16_t*>(smem + Ly::LM);
   uint16_t* sP = reinterpret_cast<uint16_t*>(smem + Ly::PM);
   uint16_t* sX = reinterpret_cast<uint16_t*>(smem + Ly::XM);
-  float* sLT = reinterpret_cast<float*>(smem + Ly::LT);
   float* sD = reinterpret_cast<float*>(smem + Ly::DT);
   float* sEB = reinterpret_cast<float*>(smem + Ly::EB);
   float* sGC = reinterpret_cast<float*>(smem + Ly::GC);
@@ -363,28 +360,31 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
         f32x4 dL, dP;
         lp_tile(i, i, dL, dP);
         const float bt = sBeta[16 * i + r16];
+        // lane (t = r16, g4): P[t][s] and beta_t L[t][s] for s = 4 g4 + v (masked); the L
+        // values sit in a plain array, whose elements are scalars for the broadcasts below
         f32x4 pv;
+        float lv[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int s = 4 * g4 + v;
-          sLT[(i * 16 + s) * LTS + r16] = s < r16 ? bt * dL[v] : 0.f;  // L[t][s] stored at [s][t]
+          lv[v] = s < r16 ? bt * dL[v] : 0.f;
           pv[v] = s <= r16 ? dP[v] : 0.f;
         }
         *reinterpret_cast<s16x4*>(&sP[(16 * i + r16) * TS + 16 * i + 4 * g4]) = cvt4(pv);
-        // X_ii = (I + L_ii)^-1, one column per lane (lanes 0..15), right-looking
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (ln < 16) {
-          const float* Lt = sLT + i * 16 * LTS;
-          float x[16];
+        // X_ii = (I + L_ii)^-1, one column per lane (lanes 0..15), right-looking; L[r][m]
+        // is broadcast from the accumulator lane that holds it (lane r + 16 (m / 4), slot m % 4)
+        float x[16];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) x[r] = (r == ln) ? 1.f : 0.f;
+        for (int r = 0; r < 16; ++r) x[r] = (r == ln) ? 1.f : 0.f;
 #pragma unroll
-          for (int m = 0; m < 15; ++m) {
+        for (int m = 0; m < 15; ++m) {
 #pragma unroll
-            for (int r = m + 1; r < 16; ++r) x[r] -= Lt[m * LTS + r] * x[m];
+          for (int r = m + 1; r < 16; ++r) {
+            const float l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv[m % 4]), r + 16 * (m / 4)));
+            x[r] -= l * x[m];
           }
+        }
+        if (ln < 16) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) sX[(16 * i + r) * XS + ln] = f2bf(x[r]);
         }
