@@ -178,6 +178,33 @@ def main():
     log(f"timed {args.steps} steps: wall {wall * 1e3:.2f} ms; prefill ms {['%.3f' % x for x in pre_ms]}; "
         f"decode(64 steps) ms {['%.3f' % x for x in dec_ms]}")
 
+    # ---------------- draft replay (reported beside the step, not part of it) ----------------
+    # The first 8 decode tokens of every sequence as drafts, from a snapshot of the decode
+    # state, with seeded accepted-prefix lengths: one kda_decode_replay launch against the
+    # 8 kda_decode_step launches that would advance (and then need rolling back) the state.
+    replay = None
+    if run_dec:
+        nd = 8
+        snap = S_dec.clone()
+        acc = torch.from_numpy(np.random.default_rng(ds.seed).integers(0, nd + 1, ds.N).astype(np.int32)).to(dev)
+        o_rep = torch.empty((nd, ds.N, ds.H, ds.dv), dtype=torch.bfloat16, device=dev)
+        S_rep = torch.empty_like(snap)
+        rep_args = (D["q"][:nd], D["k"][:nd], D["v"][:nd], D["z"][:nd], D["beta"][:nd], D["A"], snap, acc)
+        kda.decode_replay(*rep_args, o=o_rep, S_commit=S_rep, stream=stream)
+        rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+        for r0, r1 in rev:
+            r0.record(stream)
+            kda.decode_replay(*rep_args, o=o_rep, S_commit=S_rep, stream=stream)
+            r1.record(stream)
+        torch.cuda.synchronize()
+        rep_ms = float(np.mean([r0.elapsed_time(r1) for r0, r1 in rev]))
+        rep_bytes = ds.N * ds.H * (2 * ds.dk * ds.dv * 4 + nd * (3 * ds.dk * 2 + ds.dv * 2 + 2 + ds.dv * 2))
+        replay = {"n_draft": nd, "ms": round(rep_ms, 4), "tokens_per_s": round(ds.N * nd / (rep_ms / 1e3), 1),
+                  "algorithmic_bytes": rep_bytes, "achieved_GBps": round(rep_bytes / (rep_ms / 1e3) / 1e9, 1),
+                  "same_tokens_as_decode_steps_ms": round(float(np.mean(dec_ms)) * nd / ds.steps, 4)}
+        log(f"replay of {nd} drafts: {rep_ms:.3f} ms (vs {replay['same_tokens_as_decode_steps_ms']:.3f} ms "
+            f"for {nd} decode steps)")
+
     if args.copy_calibration_mib > 0:
         nbytes = args.copy_calibration_mib << 20
         src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
@@ -256,6 +283,7 @@ def main():
                                 "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("decode"),
                                 "algorithmic_bytes_per_launch": dec_bytes}},
         "cpu_baseline": cpu,
+        "replay": replay,
     }
     # a profiling run that timed one path reports nothing for the other
     if not run_dec:

@@ -56,6 +56,8 @@ def lib() -> ctypes.CDLL:
     L.kda_chunk_fwd_z.restype = I
     L.kda_decode_step.argtypes = [P, P, P, P, P, I, P, F, P, P, I, I, I, I, I, F, P]
     L.kda_decode_step.restype = I
+    L.kda_decode_replay.argtypes = [P, P, P, P, P, I, P, F, P, P, P, I, P, I, I, I, I, I, F, P]
+    L.kda_decode_replay.restype = I
     _lib = L
     return L
 
@@ -163,3 +165,26 @@ def decode_step(q, k, v, z, beta, A, S, g_min: float = G_MIN, o=None, o_dtype=No
                                  _p(S), _p(o), _dtype_code(o), N, H, dk, dv, float(scale), _stream(stream)),
            "kda_decode_step")
     return o
+
+
+def decode_replay(q, k, v, z, beta, A, S_snapshot, accepted, g_min: float = G_MIN, o=None, o_dtype=None,
+                  S_commit=None, scale: float = 1.0, stream=None):
+    """Speculative-decoding replay: the drafted tokens q, k, z [n_draft,N,H,dk],
+    v [n_draft,N,H,dv], beta [n_draft,N,H] run from S_snapshot [N,H,dk,dv] fp32
+    (left unchanged); accepted [N] int32 holds each sequence's accepted prefix
+    length.  Returns (o [n_draft,N,H,dv] for every drafted token, S_commit
+    [N,H,dk,dv], the state after the accepted prefix)."""
+    n_draft, N, H, dk = q.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((n_draft, N, H, dv), dtype=o_dtype or torch.float32, device=q.device)
+    if S_commit is None:
+        S_commit = torch.empty_like(S_snapshot)
+    if accepted.dtype != torch.int32:
+        raise KDAError("decode_replay: accepted must be int32")
+    _dev(q, k, v, z, beta, A, S_snapshot, accepted, o, S_commit)
+    _check(lib().kda_decode_replay(_p(q), _p(k), _p(v), _p(z), _p(beta), _dtype_code(q), _p(A), float(g_min),
+                                   _p(S_snapshot), _p(accepted), _p(o), _dtype_code(o), _p(S_commit), n_draft, N,
+                                   H, dk, dv, float(scale), _stream(stream)),
+           "kda_decode_replay")
+    return o, S_commit

@@ -174,4 +174,32 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
   return from_hip(kda::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
+kda_status kda_decode_replay(const void* q, const void* k, const void* v, const void* z, const void* beta,
+                             kda_dtype in_dtype, const float* A, float g_min, const float* S_snapshot,
+                             const int* accepted, void* o, kda_dtype o_dtype, float* S_commit, int n_draft, int N,
+                             int H, int dk, int dv, float scale, void* stream) {
+  if (!dtype_ok(in_dtype) || !dtype_ok(o_dtype)) return KDA_ERR_DTYPE;
+  if (!sizes_ok(N, n_draft, H, dk, dv)) return KDA_ERR_SHAPE;
+  if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
+  if (!isfinite(g_min) || g_min > 0.f || !isfinite(scale)) return KDA_ERR_UNSUPPORTED;
+  const int64_t nh = int64_t(N) * H;
+  if (nh == 0) return KDA_OK;
+  if (!A || !S_snapshot || !accepted || !S_commit) return KDA_ERR_NULL;
+  if (n_draft > 0 && (!q || !k || !v || !z || !beta || !o)) return KDA_ERR_NULL;
+  if (!all_aligned({A, S_snapshot, S_commit}, nullptr, 1) || reinterpret_cast<uintptr_t>(accepted) % 4)
+    return KDA_ERR_ALIGN;
+  if (n_draft > 0 && !all_aligned({q, k, v, z, o}, beta, esize(in_dtype))) return KDA_ERR_ALIGN;
+  const int64_t ein = esize(in_dtype), nt = nh * n_draft;
+  const Range rC{S_commit, nh * dk * dv * 4}, ro{o, nt * dv * int64_t(esize(o_dtype))};
+  const Range ins[] = {{q, nt * dk * ein}, {k, nt * dk * ein}, {v, nt * dv * ein}, {z, nt * dk * ein},
+                       {beta, nt * ein}, {A, int64_t(H) * dk * 4}, {S_snapshot, nh * dk * dv * 4},
+                       {accepted, int64_t(N) * 4}};
+  for (const Range& in : ins)
+    if (overlap(rC, in) || overlap(ro, in)) return KDA_ERR_ALIAS;
+  if (overlap(rC, ro)) return KDA_ERR_ALIAS;
+  kda::ReplayArgs a{q,        k,          v,     z, beta, A, g_min, S_snapshot, o, S_commit, accepted, n_draft, N, H,
+                    dk,       dv,         scale, in_dtype == KDA_BF16, o_dtype == KDA_BF16};
+  return from_hip(kda::launch_replay(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

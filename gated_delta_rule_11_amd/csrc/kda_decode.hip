@@ -20,18 +20,6 @@
 
 namespace kda {
 
-constexpr int decode_threads(int dk, int dv) { return (dk * dv / 4) < 256 ? (dk * dv / 4) : 256; }
-
-template <int DK, int DV>
-struct DecodeShape {
-  static constexpr int NJ = DV / 4;                                  // column groups
-  static constexpr int NTHREADS = decode_threads(DK, DV);
-  static constexpr int NR = NTHREADS / NJ;                           // row groups
-  static constexpr int RPT = DK / NR;                                // rows per thread
-  static_assert(NR * RPT == DK, "rows must split evenly");
-  static_assert(NJ * NR == NTHREADS, "threads must split evenly");
-};
-
 template <int DK, int DV, typename Tin, typename Tout>
 __global__ __launch_bounds__(decode_threads(DK, DV)) void decode_step_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,

@@ -42,7 +42,35 @@ struct DecodeArgs {
   bool in_bf16, out_bf16;
 };
 
+struct ReplayArgs {
+  const void *q, *k, *v, *z, *beta;  // [n_draft, N, H, d], beta [n_draft, N, H]
+  const float* A;
+  float g_min;
+  const float* S_snap;  // [N, H, dk, dv], read only
+  void* o;              // [n_draft, N, H, dv]
+  float* S_commit;      // [N, H, dk, dv]
+  const int* accepted;  // [N]
+  int n_draft, N, H, dk, dv;
+  float scale;
+  bool in_bf16, out_bf16;
+};
+
+// Thread layout shared by the single-token kernels (decode, replay): thread
+// (rg, j4) owns value columns 4 j4 .. 4 j4 + 3 of rows rg + NR i, i < RPT.
+constexpr int decode_threads(int dk, int dv) { return (dk * dv / 4) < 256 ? (dk * dv / 4) : 256; }
+
+template <int DK, int DV>
+struct DecodeShape {
+  static constexpr int NJ = DV / 4;                                  // column groups
+  static constexpr int NTHREADS = decode_threads(DK, DV);
+  static constexpr int NR = NTHREADS / NJ;                           // row groups
+  static constexpr int RPT = DK / NR;                                // rows per thread
+  static_assert(NR * RPT == DK, "rows must split evenly");
+  static_assert(NJ * NR == NTHREADS, "threads must split evenly");
+};
+
 hipError_t launch_gate(const GateArgs& a, hipStream_t st);
+hipError_t launch_replay(const ReplayArgs& a, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_chunk_generic(const ChunkArgs& a, hipStream_t st);
 // The MFMA path for bf16 inputs, dk = dv = 128, chunk = 64.  Returns

@@ -151,6 +151,36 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v,
                            kda_dtype o_dtype, int N, int H, int dk, int dv,
                            float scale, void* stream);
 
+/*
+ * kda_decode_replay -- speculative-decoding state replay in one launch
+ * ("Kimi K3: architecture, derivations and a pinned-source audit", section
+ * 10.3: the drafted tokens' inputs are cached and the accepted prefix is
+ * replayed on chip instead of rolling the state back).
+ *
+ * For n < N, h < H the drafted tokens t = 0 .. n_draft-1 run one at a time
+ * from S_snapshot[n,h], each step the update of kda_decode_step; o[t,n,h]
+ * is written for every drafted token, and S_commit[n,h] receives the state
+ * after the first accepted[n] of them (a copy of S_snapshot[n,h] when
+ * accepted[n] == 0).  S_snapshot is only read.
+ *
+ *   q, k, z  [n_draft,N,H,dk] in_dtype     v [n_draft,N,H,dv] in_dtype
+ *   beta     [n_draft,N,H] in_dtype        A [H,dk] fp32
+ *   S_snapshot [N,H,dk,dv] fp32 (read)     accepted [N] int32, device memory,
+ *                                          values clamped to [0, n_draft]
+ *   o        [n_draft,N,H,dv] o_dtype (written)
+ *   S_commit [N,H,dk,dv] fp32 (written)
+ * n_draft >= 0 (0: the snapshot is copied to S_commit).  o and S_commit must
+ * not overlap any input or each other (KDA_ERR_ALIAS).  Alignment: 16 bytes
+ * for q, k, v, z, A, S_snapshot, o, S_commit; 4 bytes for accepted; beta
+ * element-aligned.
+ */
+kda_status kda_decode_replay(const void* q, const void* k, const void* v,
+                             const void* z, const void* beta, kda_dtype in_dtype,
+                             const float* A, float g_min, const float* S_snapshot,
+                             const int* accepted, void* o, kda_dtype o_dtype,
+                             float* S_commit, int n_draft, int N, int H, int dk,
+                             int dv, float scale, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

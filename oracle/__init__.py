@@ -15,6 +15,11 @@ What it computes (definitions cited by page title and section):
 * Gate (Eq. 5), "Kimi K3 reading notes", section 2: g = g_min *
   sigmoid(exp(A^h) z), alpha = exp(g), g_min = -5.
 * Decode: one step of the same recurrence per sequence, state carried.
+* Draft replay, "Kimi K3: architecture, derivations and a pinned-source
+  audit", section 10.3 (KDA state replay for speculative decoding): the
+  drafted tokens of each sequence run from a cached state that is itself
+  left unchanged; every drafted token's output is produced, and the state
+  committed is the one after the accepted prefix.
 
 Every entry point takes fp64 numpy arrays in the layouts of kda_oracle.h.
 """
@@ -103,6 +108,34 @@ class Oracle:
             raise ValueError("kda_oracle_forward_z: bad arguments")
         return o, S
 
+    def replay(self, q, k, v, z, beta, A, S_snapshot, accepted, g_min: float = G_MIN, scale: float = 1.0,
+               nthreads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+        """Speculative-decoding replay of ``n_draft`` drafted tokens per sequence.
+
+        q, k, z: [n_draft, N, H, dk]; v: [n_draft, N, H, dv]; beta: [n_draft, N, H];
+        S_snapshot: [N, H, dk, dv], the state before the drafts (not modified);
+        accepted: [N] integers in [0, n_draft], the accepted prefix length of
+        each sequence.  The drafts run one token at a time from the snapshot
+        exactly as in ``decode``.  Returns (o [n_draft, N, H, dv] for every
+        drafted token, the state of each sequence after its first accepted[n]
+        tokens: the snapshot itself where accepted[n] == 0)."""
+        q, k, v, z, beta, A = map(_f64, (q, k, v, z, beta, A))
+        S = _f64(S_snapshot).copy()
+        acc = np.asarray(accepted, dtype=np.int64)
+        n_draft, N = q.shape[0], S.shape[0]
+        if acc.shape != (N,) or np.any(acc < 0) or np.any(acc > n_draft):
+            raise ValueError("accepted must hold N values in [0, n_draft]")
+        committed = S.copy()
+        outs = []
+        for s in range(n_draft):
+            o, S = self.forward_z(q[s][:, None], k[s][:, None], v[s][:, None], beta[s][:, None], z[s][:, None],
+                                  A, g_min, S, scale, nthreads)
+            outs.append(o[:, 0])
+            done = acc == s + 1
+            committed[done] = S[done]
+        o = np.stack(outs) if outs else np.zeros((0,) + S.shape[:2] + (S.shape[-1],))
+        return o, committed
+
 
 _default: Optional[Oracle] = None
 
@@ -145,3 +178,10 @@ def decode(q, k, v, z, beta, A, S0, g_min: float = G_MIN, scale: float = 1.0,
                          g_min, S, scale, nthreads)
         outs.append(o[:, 0])
     return np.stack(outs) if outs else np.zeros((0,) + S.shape[:2] + (S.shape[-1],)), S
+
+
+
+def replay(q, k, v, z, beta, A, S_snapshot, accepted, g_min: float = G_MIN, scale: float = 1.0,
+           nthreads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """Speculative-decoding replay (see ``Oracle.replay``) on the default build."""
+    return default().replay(q, k, v, z, beta, A, S_snapshot, accepted, g_min, scale, nthreads)

@@ -385,4 +385,37 @@ def pin_forward_z_matches_gate_then_recurrence(orc):
     assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
 
 
+def pin_replay(orc):
+    """Draft replay ("architecture, derivations and a pinned-source audit" page,
+    section 10.3, and its CPU laboratory): from a snapshot, the committed state is
+    the state after the accepted prefix, the same as running those tokens from the
+    start; rejecting drafts changes it; the snapshot is left as it was; every
+    drafted token gets its output.  Checked against the pure-Python token loop."""
+    rng = np.random.default_rng(23)
+    n_draft, N, H, dk, dv = 6, 4, 2, 5, 4
+    q = rng.standard_normal((n_draft, N, H, dk)) * 0.4
+    k = rng.standard_normal((n_draft, N, H, dk)) * 0.4
+    v = rng.standard_normal((n_draft, N, H, dv))
+    z = rng.standard_normal((n_draft, N, H, dk))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((n_draft, N, H))))
+    A = rng.standard_normal((H, dk)) * 0.5
+    snap = rng.standard_normal((N, H, dk, dv)) * 0.3
+    snap_copy = snap.copy()
+    accepted = np.array([0, 2, 5, 6])
+    o, S = orc.replay(q, k, v, z, beta, A, snap, accepted)
+    assert np.array_equal(snap, snap_copy)              # snapshot untouched
+    assert np.array_equal(S[0], snap[0])                # nothing accepted: the snapshot itself
+    for n in range(N):
+        for h in range(H):
+            alpha = [brute.gate_alpha(z[t, n, h], A[h]) for t in range(n_draft)]
+            ob, _ = brute.forward(q[:, n, h], k[:, n, h], v[:, n, h], beta[:, n, h], alpha, snap[n, h])
+            np.testing.assert_allclose(o[:, n, h], np.array(ob), rtol=0, atol=1e-12)
+            m = accepted[n]
+            _, Sm = brute.forward(q[:m, n, h], k[:m, n, h], v[:m, n, h], beta[:m, n, h], alpha[:m], snap[n, h])
+            np.testing.assert_allclose(S[n, h], np.array(Sm), rtol=0, atol=1e-12)
+            if m < n_draft:                              # the rejected drafts would have moved the state
+                _, Sall = brute.forward(q[:, n, h], k[:, n, h], v[:, n, h], beta[:, n, h], alpha, snap[n, h])
+                assert not np.allclose(np.array(Sall), S[n, h])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

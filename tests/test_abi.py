@@ -33,7 +33,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_z", "kda_decode_step", "kda_status_string"):
+    for n in ("kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_z", "kda_decode_step", "kda_decode_replay",
+              "kda_status_string"):
         assert n in names
 
 
@@ -144,3 +145,27 @@ def test_binding_refuses_cpu_tensors(L):
     A = torch.zeros(1, 16)
     with pytest.raises(kda.KDAError):
         kda.gate(z, A, chunk=1, out=torch.zeros(1, 4, 1, 16))
+
+
+def replay(L, q=P(0), k=P(1), v=P(2), z=P(3), beta=P(4), it=BF16, A=P(5), gmin=-5.0, S_snap=P(6),
+           acc=P(7), o=P(8), ot=BF16, S_commit=P(9), n_draft=4, Nn=4, H=2, dk=128, dv=128, scale=1.0):
+    return L.kda_decode_replay(q, k, v, z, beta, it, A, gmin, S_snap, acc, o, ot, S_commit, n_draft, Nn, H, dk, dv,
+                               scale, N)
+
+
+def test_replay_validation(L):
+    assert replay(L, it=5) == ERR_DTYPE
+    assert replay(L, n_draft=-1) == ERR_SHAPE
+    assert replay(L, Nn=-2) == ERR_SHAPE
+    assert replay(L, dv=48) == ERR_UNSUPPORTED
+    assert replay(L, gmin=0.5) == ERR_UNSUPPORTED
+    for name in ("A", "S_snap", "acc", "S_commit", "q", "k", "v", "z", "beta", "o"):
+        assert replay(L, **{name: None}) == ERR_NULL, name
+    # with nothing drafted only the state buffers and accepted are needed (still rejected on overlap)
+    assert replay(L, n_draft=0, q=None, k=None, v=None, z=None, beta=None, o=None, S_commit=P(6)) == ERR_ALIAS
+    assert replay(L, S_commit=P(6)) == ERR_ALIAS      # commit over the snapshot
+    assert replay(L, o=P(7)) == ERR_ALIAS             # output over accepted
+    assert replay(L, S_commit=P(8)) == ERR_ALIAS      # commit over the output
+    assert replay(L, acc=ctypes.c_void_p(0x80000002)) == ERR_ALIGN
+    assert replay(L, S_snap=ctypes.c_void_p(0x70000008)) == ERR_ALIGN
+    assert replay(L, Nn=0) == OK
