@@ -9,7 +9,8 @@ One step = one pass of the whole path over synthetic inputs:
     H=32 heads, d=128, fp32 state updated in place in HBM, bf16 outputs.
 
 value = prefill tokens/s (B*T per prefill launch / launch time); the decode
-rate is reported beside it.  Inputs are generated on the host, copied to the
+rate, a draft replay and the 1M-token single-sequence prefill (segment-parallel
+form against one pass) are reported beside it.  Inputs are generated on the host, copied to the
 GPU before the timed region, and stay resident.  Kernel durations are taken
 with HIP events recorded on the stream the kernels are launched on.
 
@@ -80,6 +81,8 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed region, run one plain device-to-device copy of this many MiB "
                          "(outside the timed region) so a counter pass can scale FETCH_SIZE/WRITE_SIZE")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the 1M-token single-sequence prefill reported beside the step")
     ap.add_argument("--cpu-sample-batches", type=int, default=4,
                     help="batch entries (all heads, all tokens) the oracle runs for the CPU baseline")
     args = ap.parse_args()
@@ -205,6 +208,44 @@ def main():
         log(f"replay of {nd} drafts: {rep_ms:.3f} ms (vs {replay['same_tokens_as_decode_steps_ms']:.3f} ms "
             f"for {nd} decode steps)")
 
+    # ---------------- 1M-token prefill (reported beside the step, not part of it) ----------------
+    # B=1, H=8, T=2^20: one pass of the chunk kernel has 8 sequences for 256 compute units;
+    # the segment-parallel form runs 16 segments per sequence side by side.
+    long_ctx = None
+    if run_pre and not args.no_long:
+        ls = ki.PREFILL_1M
+        t0 = time.time()
+        ld = ki.prefill_inputs(ls)
+        log(f"1M-token inputs generated in {time.time() - t0:.1f}s")
+        L = {k: to_dev(ld[k], ls.dtype) for k in ("q", "k", "v", "z", "beta")}
+        L["A"] = to_dev(ld["A"], "f32")
+        del ld
+        o_l = torch.empty((ls.B, ls.T, ls.H, ls.dv), dtype=torch.bfloat16, device=dev)
+        S_l = torch.empty((ls.B, ls.H, ls.dk, ls.dv), dtype=torch.float32, device=dev)
+        nseg = max(1, -(-128 // (ls.B * ls.H)))
+        ws = torch.empty(kda.chunk_fwd_z_segmented_workspace_bytes(ls.B, ls.H, ls.dk, ls.dv, nseg),
+                         dtype=torch.uint8, device=dev)
+        largs = (L["q"], L["k"], L["v"], L["beta"], L["z"], L["A"])
+
+        def timed(fn, reps):
+            fn()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            for r0, r1 in evs:
+                r0.record(stream)
+                fn()
+                r1.record(stream)
+            torch.cuda.synchronize()
+            return float(np.mean([r0.elapsed_time(r1) for r0, r1 in evs]))
+
+        seg_ms = timed(lambda: kda.chunk_fwd_z_segmented(*largs, nseg, -5.0, ls.chunk, o=o_l, S_out=S_l,
+                                                         workspace=ws, stream=stream), 5)
+        one_ms = timed(lambda: kda.chunk_fwd_z(*largs, -5.0, ls.chunk, o=o_l, S_out=S_l, stream=stream), 2)
+        long_ctx = {"workload": ls.name, "segments": nseg, "ms": round(seg_ms, 3),
+                    "tokens_per_s": round(ls.B * ls.T / (seg_ms / 1e3), 1), "one_pass_ms": round(one_ms, 3)}
+        log(f"1M-token prefill: {seg_ms:.2f} ms in {nseg} segments, {one_ms:.2f} ms in one pass")
+        del L, o_l, S_l, ws, largs
+        torch.cuda.empty_cache()
+
     if args.copy_calibration_mib > 0:
         nbytes = args.copy_calibration_mib << 20
         src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
@@ -284,6 +325,7 @@ def main():
                                 "algorithmic_bytes_per_launch": dec_bytes}},
         "cpu_baseline": cpu,
         "replay": replay,
+        "long_context": long_ctx,
     }
     # a profiling run that timed one path reports nothing for the other
     if not run_dec:

@@ -58,6 +58,11 @@ def lib() -> ctypes.CDLL:
     L.kda_decode_step.restype = I
     L.kda_decode_replay.argtypes = [P, P, P, P, P, I, P, F, P, P, P, I, P, I, I, I, I, I, F, P]
     L.kda_decode_replay.restype = I
+    L.kda_chunk_fwd_z_segmented_workspace_bytes.argtypes = [I, I, I, I, I]
+    L.kda_chunk_fwd_z_segmented_workspace_bytes.restype = ctypes.c_size_t
+    L.kda_chunk_fwd_z_segmented.argtypes = [P, P, P, P, P, I, P, F, P, P, I, P, I, I, I, I, I, I, F, I, P,
+                                            ctypes.c_size_t, P]
+    L.kda_chunk_fwd_z_segmented.restype = I
     _lib = L
     return L
 
@@ -149,6 +154,33 @@ def chunk_fwd_z(q, k, v, beta, z, A, g_min: float = G_MIN, chunk: int = 64, S_in
     _check(lib().kda_chunk_fwd_z(_p(q), _p(k), _p(v), _p(beta), _p(z), _dtype_code(q), _p(A), float(g_min),
                                  _p(S_in), _p(o), _dtype_code(o), _p(S_out), B, T, H, dk, dv, int(chunk),
                                  float(scale), _stream(stream)), "kda_chunk_fwd_z")
+    return o, S_out
+
+
+def chunk_fwd_z_segmented_workspace_bytes(B: int, H: int, dk: int, dv: int, segments: int) -> int:
+    """Device bytes the segment-parallel prefill needs for ``segments`` segments."""
+    return int(lib().kda_chunk_fwd_z_segmented_workspace_bytes(B, H, dk, dv, int(segments)))
+
+
+def chunk_fwd_z_segmented(q, k, v, beta, z, A, segments: int, g_min: float = G_MIN, chunk: int = 64, S_in=None,
+                          o=None, S_out=None, o_dtype=None, scale: float = 1.0, want_state: bool = True,
+                          workspace=None, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """``chunk_fwd_z`` with the sequence cut into ``segments`` chunk-aligned
+    segments run in parallel (for small B*H and long T).  ``workspace`` is a
+    device tensor of at least ``chunk_fwd_z_segmented_workspace_bytes`` bytes;
+    one is allocated when it is None.  Returns (o, S_out or None)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    o, S_out = _outs(q, v, o, S_out, o_dtype, want_state)
+    need = chunk_fwd_z_segmented_workspace_bytes(B, H, dk, dv, segments)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _dev(q, k, v, beta, z, A, S_in, o, S_out, workspace)
+    _check(lib().kda_chunk_fwd_z_segmented(_p(q), _p(k), _p(v), _p(beta), _p(z), _dtype_code(q), _p(A),
+                                           float(g_min), _p(S_in), _p(o), _dtype_code(o), _p(S_out), B, T, H, dk,
+                                           dv, int(chunk), float(scale), int(segments), _p(workspace),
+                                           workspace.numel() * workspace.element_size(), _stream(stream)),
+           "kda_chunk_fwd_z_segmented")
     return o, S_out
 
 

@@ -68,6 +68,7 @@ const char* kda_status_string(int s) {
     case KDA_ERR_ALIAS: return "KDA_ERR_ALIAS: an output overlaps an input";
     case KDA_ERR_HIP: return "KDA_ERR_HIP: the HIP runtime reported a launch error";
     case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN: a tensor pointer is not 16-byte aligned";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: the workspace is smaller than required";
   }
   return "unknown kda_status";
 }
@@ -100,7 +101,8 @@ kda_status kda_gate(const void* z, kda_dtype z_dtype, const float* A, float g_mi
 static kda_status chunk_common(const void* q, const void* k, const void* v, const void* beta, const void* z,
                                kda_dtype in_dtype, const float* G, const float* A, float g_min,
                                const float* S_in, void* o, kda_dtype o_dtype, float* S_out, int B, int T, int H,
-                               int dk, int dv, int chunk, float scale, bool from_z, void* stream) {
+                               int dk, int dv, int chunk, float scale, bool from_z, void* stream, int segments = 1,
+                               void* ws = nullptr, size_t ws_bytes = 0) {
   if (!dtype_ok(in_dtype) || !dtype_ok(o_dtype)) return KDA_ERR_DTYPE;
   if (!sizes_ok(B, T, H, dk, dv)) return KDA_ERR_SHAPE;
   if (!dim_ok(dk) || !dim_ok(dv) || !(chunk == 16 || chunk == 64)) return KDA_ERR_UNSUPPORTED;
@@ -125,6 +127,7 @@ static kda_status chunk_common(const void* q, const void* k, const void* v, cons
   for (Range in : {rq, rk, rv, rb, rz, rG, rA, ro})
     if (overlap(rSo, in)) return KDA_ERR_ALIAS;
   if (overlap(rSo, rSi) && S_out != S_in) return KDA_ERR_ALIAS;
+  if (segments < 1) return KDA_ERR_SHAPE;
 
   kda::ChunkArgs a{};
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.G = from_z ? nullptr : G; a.z = from_z ? z : nullptr;
@@ -132,8 +135,43 @@ static kda_status chunk_common(const void* q, const void* k, const void* v, cons
   a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv; a.chunk = chunk; a.scale = scale;
   a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = o_dtype == KDA_BF16; a.from_z = from_z;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (kda::chunk_mfma_supports(a)) return from_hip(kda::launch_chunk_mfma(a, st));
-  return from_hip(kda::launch_chunk_generic(a, st));
+  const int nch = (T + chunk - 1) / chunk;
+  const int seg_chunks = (nch + segments - 1) / (segments > 0 ? segments : 1);
+  const int nseg = seg_chunks > 0 ? (nch + seg_chunks - 1) / seg_chunks : 1;
+  if (!kda::chunk_mfma_supports(a)) {
+    if (segments > 1) return KDA_ERR_UNSUPPORTED;
+    return from_hip(kda::launch_chunk_generic(a, st));
+  }
+  if (nseg <= 1) return from_hip(kda::launch_chunk_mfma(a, st));
+
+  // Segment-parallel form ("Kimi K3 reading notes", section 7): each segment from the
+  // zero state (end states St), each segment's transition from the identity with zero
+  // values (M), the entry states by a scan, then each segment from its entry state.
+  const int64_t bh = int64_t(B) * H;
+  const int64_t nSt = bh * nseg * dk * dv, nM = bh * nseg * dk * dk;
+  if (!ws) return KDA_ERR_NULL;
+  if (!aligned(ws, 16)) return KDA_ERR_ALIGN;
+  if (ws_bytes < size_t(2 * nSt + nM) * 4) return KDA_ERR_WORKSPACE;
+  const Range rw{ws, int64_t(2 * nSt + nM) * 4};
+  for (Range in : {rq, rk, rv, rb, rz, rA, ro, rSi, rSo})
+    if (overlap(rw, in)) return KDA_ERR_ALIAS;
+  float* St = static_cast<float*>(ws);
+  float* M = St + nSt;
+  float* E = M + nM;
+  a.nseg = nseg;
+  a.seg_chunks = seg_chunks;
+  kda::ChunkArgs pa = a;  // pass A: end states from the zero state
+  pa.S_in = nullptr; pa.S_out = St; pa.S_out_mode = 1; pa.o_skip = true;
+  kda::ChunkArgs pb = a;  // pass B: transitions (identity entry state, zero values)
+  pb.S_in = nullptr; pb.S_identity = true; pb.v_zero = true; pb.S_out = M; pb.S_out_mode = 1; pb.o_skip = true;
+  kda::ChunkArgs pc = a;  // pass C: outputs and the final state from the true entry states
+  pc.S_in = E; pc.S_in_seg = true; pc.S_out_mode = 2;
+  const kda::SegScanArgs sa{S_in, St, M, E, int(bh), nseg, dk, dv};
+  hipError_t e = kda::launch_chunk_mfma(pa, st);
+  if (e == hipSuccess) e = kda::launch_chunk_mfma(pb, st);
+  if (e == hipSuccess) e = kda::launch_segscan(sa, st);
+  if (e == hipSuccess) e = kda::launch_chunk_mfma(pc, st);
+  return from_hip(e);
 }
 
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* beta, kda_dtype in_dtype,
@@ -141,6 +179,20 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
                          int H, int dk, int dv, int chunk, float scale, void* stream) {
   return chunk_common(q, k, v, beta, nullptr, in_dtype, G, nullptr, -5.0f, S_in, o, o_dtype, S_out, B, T, H, dk, dv,
                       chunk, scale, false, stream);
+}
+
+size_t kda_chunk_fwd_z_segmented_workspace_bytes(int B, int H, int dk, int dv, int segments) {
+  if (B < 0 || H < 0 || dk < 0 || dv < 0 || segments < 1) return 0;
+  return size_t(B) * size_t(H) * size_t(segments) * (2 * size_t(dk) * dv + size_t(dk) * dk) * 4;
+}
+
+kda_status kda_chunk_fwd_z_segmented(const void* q, const void* k, const void* v, const void* beta, const void* z,
+                                     kda_dtype in_dtype, const float* A, float g_min, const float* S_in, void* o,
+                                     kda_dtype o_dtype, float* S_out, int B, int T, int H, int dk, int dv, int chunk,
+                                     float scale, int segments, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  return chunk_common(q, k, v, beta, z, in_dtype, nullptr, A, g_min, S_in, o, o_dtype, S_out, B, T, H, dk, dv, chunk,
+                      scale, true, stream, segments, workspace, workspace_bytes);
 }
 
 kda_status kda_chunk_fwd_z(const void* q, const void* k, const void* v, const void* beta, const void* z,

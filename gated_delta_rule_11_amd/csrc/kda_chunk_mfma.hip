@@ -139,7 +139,7 @@ template <bool FROM_Z> struct RawTile {
 // Raw inputs of one wavefront's 16-token tile, token offsets clamped to the chunk,
 // in four parts (keys; queries; gate inputs; values and beta) so that the loads
 // of a tile can go out in different phases.
-template <int DVS, bool FROM_Z, int PART>
+template <int DVS, bool FROM_Z, int PART, bool SEG>
 __device__ __forceinline__ void load_part(RawTile<FROM_Z>& R, const ChunkArgs& a, int b, int h, int t0, int i,
                                           int ln, int j0) {
   using namespace mf;
@@ -185,19 +185,20 @@ __device__ __forceinline__ void load_part(RawTile<FROM_Z>& R, const ChunkArgs& a
     if (ln < DVS) {
 #pragma unroll
       for (int tt = 0; tt < 16; ++tt)
-        R.v[tt] = __builtin_amdgcn_raw_buffer_load_b16(rv, ln * 2, min(16 * i + tt, n - 1) * rowb, 0);
+        R.v[tt] = (SEG && a.v_zero) ? 0u
+                                    : __builtin_amdgcn_raw_buffer_load_b16(rv, ln * 2, min(16 * i + tt, n - 1) * rowb, 0);
     }
     if (ln < 16) R.beta = __builtin_amdgcn_raw_buffer_load_b16(rb, min(16 * i + ln, n - 1) * H * 2, 0, 0);
   }
 }
 
-template <int DVS, bool FROM_Z>
+template <int DVS, bool FROM_Z, bool SEG>
 __device__ __forceinline__ void load_tile(RawTile<FROM_Z>& R, const ChunkArgs& a, int b, int h, int t0, int i,
                                           int ln, int j0) {
-  load_part<DVS, FROM_Z, 0>(R, a, b, h, t0, i, ln, j0);
-  load_part<DVS, FROM_Z, 1>(R, a, b, h, t0, i, ln, j0);
-  load_part<DVS, FROM_Z, 2>(R, a, b, h, t0, i, ln, j0);
-  load_part<DVS, FROM_Z, 3>(R, a, b, h, t0, i, ln, j0);
+  load_part<DVS, FROM_Z, 0, SEG>(R, a, b, h, t0, i, ln, j0);
+  load_part<DVS, FROM_Z, 1, SEG>(R, a, b, h, t0, i, ln, j0);
+  load_part<DVS, FROM_Z, 2, SEG>(R, a, b, h, t0, i, ln, j0);
+  load_part<DVS, FROM_Z, 3, SEG>(R, a, b, h, t0, i, ln, j0);
 }
 
 // Off-diagonal tile pairs (i, j < i) of the L / P products, per gate wavefront.
@@ -215,7 +216,11 @@ __constant__ int8_t kOffPairs8[4][2][2] = {{{1, 0}, {3, 0}}, {{2, 1}, {3, 1}}, {
 //   3 : all : (I + L)[W | Ut] = Diag(beta)[K Gamma | V]; W tile w per wavefront, Ut on chain
 //   A1: chain: U = Ut - W S, (q Gamma) S   | gate: gate and decays of chunk n+1, k sf
 //   A2: chain: O += P U, state update      | gate: k r, eB, anchored keys (all but adjacent pairs)
-template <int DVS, bool FROM_Z, typename Tout>
+//
+// SEG instantiations serve the passes of the segment-parallel form (one
+// workgroup per segment; identity entry state, zero values, outputs skipped,
+// per-segment states); the plain instantiation compiles all of that out.
+template <int DVS, bool FROM_Z, typename Tout, bool SEG>
 __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int ns, int xcd_map) {
   using namespace mf;
   using Ly = Layout<DVS>;
@@ -238,18 +243,22 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
   float* sGC = reinterpret_cast<float*>(smem + Ly::GC);
   float* sBeta = reinterpret_cast<float*>(smem + Ly::BT);
 
-  // workgroup -> (b*H + h, slice); slices of one head share an XCD (and its L2)
-  int bh, sl;
+  // workgroup -> ((b*H + h) * nseg + segment, slice); the slices of one head and
+  // segment share an XCD (and its L2)
+  int bh, sl, sg;
   {
     const int x = blockIdx.x;
+    int bhs;
     if (xcd_map) {
       const int idx = x >> 3;
       sl = idx % ns;
-      bh = (idx / ns) * 8 + (x & 7);
+      bhs = (idx / ns) * 8 + (x & 7);
     } else {
       sl = x % ns;
-      bh = x / ns;
+      bhs = x / ns;
     }
+    bh = SEG ? bhs / a.nseg : bhs;
+    sg = SEG ? bhs % a.nseg : 0;
   }
   const int h = bh % a.H;
   const int b = bh / a.H;
@@ -270,7 +279,11 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
     c0 = 2 * l;    // gate layout: channels c0, c0+1
   };
   relane();
-  const int nch = (T + C - 1) / C;
+  // this workgroup's chunks: segment sg of the sequence (all of it for one segment)
+  const int nch_all = (T + C - 1) / C;
+  const int seg_chunks = (SEG && a.seg_chunks > 0) ? a.seg_chunks : nch_all;
+  const int c_begin = SEG ? min(sg * seg_chunks, nch_all) : 0;
+  const int nch = SEG ? min(c_begin + seg_chunks, nch_all) : nch_all;
 
   // L^T / P^T tile for pair (i, j): rows s of tile j, columns t of tile i
   auto lp_tile = [&](int i, int j, f32x4& accL, f32x4& accP) {
@@ -339,13 +352,16 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
     for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        S[ct][v] = (owns_v && a.S_in)
-                       ? a.S_in[(static_cast<int64_t>(bh) * DK + 16 * ct + 4 * g4 + v) * DK + j0 + 16 * wv + r16]
-                       : 0.f;
+        S[ct][v] = !owns_v                ? 0.f
+                   : (SEG && a.S_identity) ? ((16 * ct + 4 * g4 + v == j0 + 16 * wv + r16) ? 1.f : 0.f)
+                   : a.S_in                ? a.S_in[((SEG && a.S_in_seg ? static_cast<int64_t>(bh) * a.nseg + sg
+                                                                        : static_cast<int64_t>(bh)) * DK +
+                                                     16 * ct + 4 * g4 + v) * DK + j0 + 16 * wv + r16]
+                                           : 0.f;
     lds_barrier();  // prologue: operand tiles of chunk 0 (gate wavefronts)
     lds_barrier();
 
-    for (int ch = 0; ch < nch; ++ch) {
+    for (int ch = c_begin; ch < nch; ++ch) {
       const int t0 = ch * C;
       const int n = min(C, T - t0);
       const int64_t row0 = (static_cast<int64_t>(b) * T + t0) * H + h;
@@ -431,28 +447,30 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
 
       // ---- A2: O += P U (stored), S = Diag(Gamma_C) S + (K Gamma_C / Gamma)^T U
       if (owns_v) {
-        const auto ro = rsrc(static_cast<Tout*>(a.o) + row0 * DK + j0, (span - 1) * DK * ES + DVS * ES);
-        const s16x4 z4 = {0, 0, 0, 0};
+        if (!(SEG && a.o_skip)) {  // outputs (segment passes that only need states skip them)
+          const auto ro = rsrc(static_cast<Tout*>(a.o) + row0 * DK + j0, (span - 1) * DK * ES + DVS * ES);
+          const s16x4 z4 = {0, 0, 0, 0};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          f32x4 acc = O[i];
-          const uint16_t* Pr = &sP[(16 * i + r16) * TS + 4 * g4];
+          for (int i = 0; i < 4; ++i) {
+            f32x4 acc = O[i];
+            const uint16_t* Pr = &sP[(16 * i + r16) * TS + 4 * g4];
 #pragma unroll
-          for (int m = 0; m + 1 <= i; m += 2)
-            acc = mma32(cat(lds64(Pr + 16 * m), lds64(Pr + 16 * m + 16)), cat(Ub[m], Ub[m + 1]), acc);
-          // the unpaired last tile runs on the same 16x16x32 shape, zero-padded: an
-          // accumulator produced by one MFMA shape is never fed to the other shape
-          if ((i & 1) == 0) acc = mma32(cat(lds64(Pr + 16 * i), z4), cat(Ub[i], z4), acc);
-          // rows t >= n lie past the end of the resource's range (H * DK >= DVS), so
-          // the hardware drops their stores: no branch splits the MFMA sequence
+            for (int m = 0; m + 1 <= i; m += 2)
+              acc = mma32(cat(lds64(Pr + 16 * m), lds64(Pr + 16 * m + 16)), cat(Ub[m], Ub[m + 1]), acc);
+            // the unpaired last tile runs on the same 16x16x32 shape, zero-padded: an
+            // accumulator produced by one MFMA shape is never fed to the other shape
+            if ((i & 1) == 0) acc = mma32(cat(lds64(Pr + 16 * i), z4), cat(Ub[i], z4), acc);
+            // rows t >= n lie past the end of the resource's range (H * DK >= DVS), so
+            // the hardware drops their stores: no branch splits the MFMA sequence
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int t = 16 * i + 4 * g4 + v;
-            const int voff = (t * H * DK + 16 * wv + r16) * ES;
-            if (ES == 2)
-              __builtin_amdgcn_raw_buffer_store_b16(f2bf(a.scale * acc[v]), ro, voff, 0, 0);
-            else
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a.scale * acc[v]), ro, voff, 0, 0);
+            for (int v = 0; v < 4; ++v) {
+              const int t = 16 * i + 4 * g4 + v;
+              const int voff = (t * H * DK + 16 * wv + r16) * ES;
+              if (ES == 2)
+                __builtin_amdgcn_raw_buffer_store_b16(f2bf(a.scale * acc[v]), ro, voff, 0, 0);
+              else
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a.scale * acc[v]), ro, voff, 0, 0);
+            }
           }
         }
 #pragma unroll
@@ -470,12 +488,14 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
     }
 
     relane();
-    if (a.S_out && owns_v) {
+    // final state: per (b, h); per (b, h, segment); or from the last segment only
+    if (a.S_out && owns_v && (!SEG || a.S_out_mode != 2 || sg == a.nseg - 1)) {
+      const int64_t base = (SEG && a.S_out_mode == 1) ? static_cast<int64_t>(bh) * a.nseg + sg : bh;
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-          a.S_out[(static_cast<int64_t>(bh) * DK + 16 * ct + 4 * g4 + v) * DK + j0 + 16 * wv + r16] = S[ct][v];
+          a.S_out[(base * DK + 16 * ct + 4 * g4 + v) * DK + j0 + 16 * wv + r16] = S[ct][v];
     }
   } else {
     // =========================== gate wavefronts ============================
@@ -662,19 +682,19 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
     };
 
     // ---- prologue: operand tiles of chunk 0
-    if (T > 0) {
-      load_tile<DVS, FROM_Z>(R, a, b, h, 0, i, ln, j0);
-      if (T >= C)
-        gate_a1(0, std::true_type{});
+    if (c_begin < nch) {
+      load_tile<DVS, FROM_Z, SEG>(R, a, b, h, c_begin * C, i, ln, j0);
+      if (T - c_begin * C >= C)
+        gate_a1(c_begin * C, std::true_type{});
       else
-        gate_a1(0, std::false_type{});
+        gate_a1(c_begin * C, std::false_type{});
     }
     lds_barrier();
     relane();
-    if (T > 0) gate_a2();
+    if (c_begin < nch) gate_a2();
     lds_barrier();
 
-    for (int ch = 0; ch < nch; ++ch) {
+    for (int ch = c_begin; ch < nch; ++ch) {
       const int t0 = ch * C;
       const bool more = ch + 1 < nch;
 
@@ -688,9 +708,9 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
       // as fast as memory takes them, so this phase (which waits for the state chain)
       // carries most of them; values and beta follow in phase 3.
       if (more) {
-        load_part<DVS, FROM_Z, 0>(R, a, b, h, t0 + C, i, ln, j0);
-        load_part<DVS, FROM_Z, 1>(R, a, b, h, t0 + C, i, ln, j0);
-        load_part<DVS, FROM_Z, 2>(R, a, b, h, t0 + C, i, ln, j0);
+        load_part<DVS, FROM_Z, 0, SEG>(R, a, b, h, t0 + C, i, ln, j0);
+        load_part<DVS, FROM_Z, 1, SEG>(R, a, b, h, t0 + C, i, ln, j0);
+        load_part<DVS, FROM_Z, 2, SEG>(R, a, b, h, t0 + C, i, ln, j0);
       }
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
@@ -710,7 +730,7 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
       relane();
 
       // ---- 3: W column tile wv
-      if (more) load_part<DVS, FROM_Z, 3>(R, a, b, h, t0 + C, i, ln, j0);
+      if (more) load_part<DVS, FROM_Z, 3, SEG>(R, a, b, h, t0 + C, i, ln, j0);
       {
         f32x4 unused[4];
         solve(std::integral_constant<int, 1>{}, unused);
@@ -742,9 +762,9 @@ bool chunk_mfma_supports(const ChunkArgs& a) {
   return a.in_bf16 && a.dk == 128 && a.dv == 128 && a.chunk == 64 && a.H <= 65536;
 }
 
-template <int DVS, bool FROM_Z, typename Tout>
+template <int DVS, bool FROM_Z, typename Tout, bool SEG>
 static hipError_t launch_mfma_t(const ChunkArgs& a, hipStream_t st, int ns) {
-  auto kern = chunk_mfma_kernel<DVS, FROM_Z, Tout>;
+  auto kern = chunk_mfma_kernel<DVS, FROM_Z, Tout, SEG>;
   constexpr int bytes = mf::Layout<DVS>::BYTES;
   static bool attr_set = false;  // set once per instantiation (idempotent if raced)
   if (!attr_set) {
@@ -753,7 +773,7 @@ static hipError_t launch_mfma_t(const ChunkArgs& a, hipStream_t st, int ns) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int64_t nbh = static_cast<int64_t>(a.B) * a.H;
+  const int64_t nbh = static_cast<int64_t>(a.B) * a.H * a.nseg;  // (b, h, segment) units
   const int64_t nblocks = nbh * ns;
   const int xcd_map = (nbh % 8 == 0) ? 1 : 0;
   hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(nblocks)), dim3(512), bytes, st, a, ns, xcd_map);
@@ -762,14 +782,23 @@ static hipError_t launch_mfma_t(const ChunkArgs& a, hipStream_t st, int ns) {
 
 template <int DVS>
 static hipError_t launch_mfma_d(const ChunkArgs& a, hipStream_t st, int ns) {
+  const bool seg = a.nseg > 1 || a.seg_chunks > 0 || a.S_in_seg || a.S_out_mode != 0 || a.S_identity ||
+                   a.v_zero || a.o_skip;
+  if (seg) {  // segment passes: fused gate only
+    if (!a.from_z) return hipErrorNotSupported;
+    return a.out_bf16 ? launch_mfma_t<DVS, true, bf16_t, true>(a, st, ns)
+                      : launch_mfma_t<DVS, true, float, true>(a, st, ns);
+  }
   if (a.from_z)
-    return a.out_bf16 ? launch_mfma_t<DVS, true, bf16_t>(a, st, ns) : launch_mfma_t<DVS, true, float>(a, st, ns);
-  return a.out_bf16 ? launch_mfma_t<DVS, false, bf16_t>(a, st, ns) : launch_mfma_t<DVS, false, float>(a, st, ns);
+    return a.out_bf16 ? launch_mfma_t<DVS, true, bf16_t, false>(a, st, ns)
+                      : launch_mfma_t<DVS, true, float, false>(a, st, ns);
+  return a.out_bf16 ? launch_mfma_t<DVS, false, bf16_t, false>(a, st, ns)
+                    : launch_mfma_t<DVS, false, float, false>(a, st, ns);
 }
 
 hipError_t launch_chunk_mfma(const ChunkArgs& a, hipStream_t st) {
   if (!chunk_mfma_supports(a)) return hipErrorNotSupported;
-  const int64_t nbh = static_cast<int64_t>(a.B) * a.H;
+  const int64_t nbh = static_cast<int64_t>(a.B) * a.H * a.nseg;  // (b, h, segment) units
   if (nbh == 0) return hipSuccess;
   // value-column slices: enough workgroups to cover the 256 compute units,
   // at most 64 columns per slice (the state slice then fits the registers)

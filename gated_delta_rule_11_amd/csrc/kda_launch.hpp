@@ -29,6 +29,15 @@ struct ChunkArgs {
   int B, T, H, dk, dv, chunk;
   float scale;
   bool in_bf16, out_bf16, from_z;
+  // Segment-parallel passes (MFMA path only; the defaults give the plain call).
+  // Segment p covers chunks [p seg_chunks, (p + 1) seg_chunks) of every sequence.
+  int nseg = 1;
+  int seg_chunks = 0;       // 0: the whole sequence
+  bool S_in_seg = false;    // S_in is [B, H, nseg, dk, dv]: one entry state per segment
+  int S_out_mode = 0;       // 0: [B, H, dk, dv]; 1: [B, H, nseg, dk, dv]; 2: last segment into [B, H, dk, dv]
+  bool S_identity = false;  // every segment starts from the identity (dv == dk)
+  bool v_zero = false;      // values taken as zero (v is not read)
+  bool o_skip = false;      // outputs are not written
 };
 
 struct DecodeArgs {
@@ -69,6 +78,16 @@ struct DecodeShape {
   static_assert(NJ * NR == NTHREADS, "threads must split evenly");
 };
 
+// Entry states of the segments: E_0 = S_in (or 0), E_{p+1} = M_p E_p + St_p.
+struct SegScanArgs {
+  const float* S_in;  // [BH, dk, dv] or nullptr
+  const float* St;    // [BH, nseg, dk, dv], end states from the zero state
+  const float* M;     // [BH, nseg, dk, dk], segment transitions
+  float* E;           // [BH, nseg, dk, dv]
+  int BH, nseg, dk, dv;
+};
+
+hipError_t launch_segscan(const SegScanArgs& a, hipStream_t st);
 hipError_t launch_gate(const GateArgs& a, hipStream_t st);
 hipError_t launch_replay(const ReplayArgs& a, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);

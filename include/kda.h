@@ -58,7 +58,8 @@ typedef enum kda_status {
   KDA_ERR_UNSUPPORTED = 4, /* valid but not provided (dk, dv, chunk, ...)    */
   KDA_ERR_ALIAS = 5,       /* outputs overlap inputs in a forbidden way      */
   KDA_ERR_HIP = 6,         /* the HIP runtime reported an error at launch    */
-  KDA_ERR_ALIGN = 7        /* a pointer is not aligned as required           */
+  KDA_ERR_ALIGN = 7,       /* a pointer is not aligned as required           */
+  KDA_ERR_WORKSPACE = 8    /* the caller's workspace is smaller than needed  */
 } kda_status;
 
 typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
@@ -150,6 +151,39 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v,
                            const float* A, float g_min, float* S, void* o,
                            kda_dtype o_dtype, int N, int H, int dk, int dv,
                            float scale, void* stream);
+
+/*
+ * kda_chunk_fwd_z_segmented -- kda_chunk_fwd_z for few, long sequences.
+ *
+ * Same inputs, outputs and result as kda_chunk_fwd_z (within the bf16
+ * tolerance: the arithmetic is regrouped).  The sequence is cut into
+ * `segments` chunk-aligned segments that run in parallel, using the fragment
+ * decomposition of "Kimi K3 reading notes", section 7: each segment from the
+ * zero state gives its end state S~_p; from the identity with zero values, its
+ * transition M_p (a dk x dk map); a scan gives the true entry states
+ * E_{p+1} = M_p E_p + S~_p (E_0 = S_in); each segment then runs from E_p and
+ * writes its outputs, the last one S_out.  About three times the work of one
+ * pass, for `segments` times the parallelism: the form for small B*H and long
+ * T (a million tokens on 8 heads), where one pass leaves most of the GPU idle.
+ *
+ * Applies to the MFMA shape (bf16 inputs, dk = dv = 128, chunk 64; see
+ * kda_chunk_uses_mfma); other shapes return KDA_ERR_UNSUPPORTED when
+ * segments > 1.  segments == 1, or T within one segment's length, runs the
+ * plain kda_chunk_fwd_z (no workspace needed).
+ *
+ * workspace: caller-owned device memory, 16-byte aligned, at least
+ * kda_chunk_fwd_z_segmented_workspace_bytes(B, H, dk, dv, segments) bytes
+ * (KDA_ERR_WORKSPACE otherwise), overlapping no argument; its contents on
+ * entry do not matter and are overwritten.  S_out may equal S_in.
+ */
+size_t kda_chunk_fwd_z_segmented_workspace_bytes(int B, int H, int dk, int dv, int segments);
+kda_status kda_chunk_fwd_z_segmented(const void* q, const void* k, const void* v,
+                                     const void* beta, const void* z, kda_dtype in_dtype,
+                                     const float* A, float g_min, const float* S_in,
+                                     void* o, kda_dtype o_dtype, float* S_out, int B,
+                                     int T, int H, int dk, int dv, int chunk, float scale,
+                                     int segments, void* workspace, size_t workspace_bytes,
+                                     void* stream);
 
 /*
  * kda_decode_replay -- speculative-decoding state replay in one launch

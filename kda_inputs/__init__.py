@@ -12,7 +12,11 @@ the workloads themselves are synthetic):
 * q, k ~ N(0, 1) per channel, then L2-normalised per (b, t, h) in fp64 as
   x / sqrt(|x|^2 + 1e-6) (the divisor is stripped from the page; this is the
   reading taken), then rounded to the storage dtype.
-* v ~ N(0, 1), z ~ N(0, 1) * z_scale, beta = sigmoid(N(0, 1)).
+* v ~ N(0, 1), z ~ N(0, 1) * z_scale + z_mean, beta = sigmoid(N(0, 1)).
+  z_mean = 0 (the workloads) puts the gate logit near 0, so most key
+  channels lose about half their remaining log-range per token and the state
+  forgets within one chunk; a negative z_mean (long-memory test cases) makes
+  the decay slow, so the state carried across chunks and segments matters.
 * A ~ N(0, 0.5^2) per (head, key channel), stored fp32.
 * S0 ~ N(0, s0_std^2) per (b, h) state, stored fp32 (absent when s0_std == 0).
 
@@ -102,6 +106,7 @@ class PrefillSpec:
     dtype: str            # storage dtype of q, k, v, z, beta: "f32" | "bf16"
     z_scale: float = 1.0
     s0_std: float = 0.0   # 0 -> no incoming state (zeros)
+    z_mean: float = 0.0   # offset of the decay logits z (negative: slow decay, long memory)
     seed: int = 1000
 
 
@@ -151,6 +156,8 @@ def _draw_block(spec: PrefillSpec, b: int, h: int, blk: int, t0: int, t1: int) -
             x = _l2norm_rows(x)
         elif name == "z":
             x = x * spec.z_scale
+            if spec.z_mean:
+                x = x + spec.z_mean
         out[name] = round_storage(x, spec.dtype)
     rng = np.random.default_rng([spec.seed, _TAG["beta"], b, h, blk])
     out["beta"] = round_storage(_sigmoid(rng.standard_normal(n)), spec.dtype)
@@ -223,9 +230,10 @@ def prefill_inputs(spec: PrefillSpec, b_sel: Optional[Sequence[int]] = None,
     return out
 
 
-def small_spec(B, H, T, dk, dv, chunk, dtype, seed, z_scale=1.0, s0_std=0.0, name="custom") -> PrefillSpec:
+def small_spec(B, H, T, dk, dv, chunk, dtype, seed, z_scale=1.0, s0_std=0.0, name="custom",
+               z_mean=0.0) -> PrefillSpec:
     return PrefillSpec(name, B=B, H=H, T=T, dk=dk, dv=dv, chunk=chunk, dtype=dtype, z_scale=z_scale,
-                       s0_std=s0_std, seed=seed)
+                       s0_std=s0_std, seed=seed, z_mean=z_mean)
 
 
 # ----------------------------------------------------------------------------

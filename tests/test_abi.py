@@ -13,7 +13,7 @@ import gated_delta_rule_11_amd as kda
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_UNSUPPORTED, ERR_ALIAS, ERR_HIP, ERR_ALIGN = range(8)
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_UNSUPPORTED, ERR_ALIAS, ERR_HIP, ERR_ALIGN, ERR_WORKSPACE = range(9)
 F32, BF16 = 0, 1
 
 
@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for s in range(8):
+    for s in range(9):
         assert L.kda_status_string(s).decode().startswith("KDA_")
     assert b"unknown" in L.kda_status_string(99)
     assert L.kda_version() >= 100
@@ -169,3 +169,26 @@ def test_replay_validation(L):
     assert replay(L, acc=ctypes.c_void_p(0x80000002)) == ERR_ALIGN
     assert replay(L, S_snap=ctypes.c_void_p(0x70000008)) == ERR_ALIGN
     assert replay(L, Nn=0) == OK
+
+
+
+def chunk_seg(L, segs=4, ws=P(10), wsb=1 << 30, B=1, T=1024, H=2, c=64, it=BF16, dk=128, **kw):
+    args = dict(q=P(0), k=P(1), v=P(2), beta=P(3), z=P(4), A=P(8), S_in=P(5), o=P(6), S_out=P(7))
+    args.update(kw)
+    return L.kda_chunk_fwd_z_segmented(args["q"], args["k"], args["v"], args["beta"], args["z"], it, args["A"], -5.0,
+                                       args["S_in"], args["o"], BF16, args["S_out"], B, T, H, dk, 128, c, 1.0,
+                                       segs, ws, wsb, N)
+
+
+def test_segmented_validation(L):
+    need = L.kda_chunk_fwd_z_segmented_workspace_bytes(1, 2, 128, 128, 4)
+    assert need == 1 * 2 * 4 * (2 * 128 * 128 + 128 * 128) * 4
+    assert L.kda_chunk_fwd_z_segmented_workspace_bytes(1, 2, 128, 128, 0) == 0
+    assert chunk_seg(L, segs=0) == ERR_SHAPE
+    assert chunk_seg(L, ws=None) == ERR_NULL
+    assert chunk_seg(L, wsb=need - 4) == ERR_WORKSPACE
+    assert chunk_seg(L, ws=ctypes.c_void_p(0xa0000008)) == ERR_ALIGN
+    assert chunk_seg(L, ws=P(6)) == ERR_ALIAS                     # workspace over the output
+    assert chunk_seg(L, it=F32) == ERR_UNSUPPORTED                # segments need the MFMA shape
+    assert chunk_seg(L, dk=64) == ERR_UNSUPPORTED
+    assert chunk_seg(L, B=0) == OK

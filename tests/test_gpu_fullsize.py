@@ -2,6 +2,8 @@
 benchmark times (fused gate, bf16 inputs and bf16 outputs), checked against
 the fp64 oracle on sampled (batch, head) sequences computed one by one over
 their whole length."""
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -40,6 +42,13 @@ def _prefill_sampled(spec, samples):
 
 def test_prefill_32k_sampled():
     _prefill_sampled(ki.PREFILL_32K, [(0, 0), (1, 17), (3, 31)])
+
+
+def test_prefill_32k_slow_decay_sampled():
+    """The 32K-token workload's shape with decay logits centred at -6: the
+    state is carried over many chunks before it fades."""
+    spec = replace(ki.PREFILL_32K, name=ki.PREFILL_32K.name + "_slow", z_mean=-6.0)
+    _prefill_sampled(spec, [(0, 3), (2, 30)])
 
 
 def test_prefill_1m_sampled():

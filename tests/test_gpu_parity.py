@@ -95,6 +95,31 @@ def test_edge_shapes(T, dk, dv, chunk, dtype, s0):
         assert eo <= TOL[dtype] and es <= TOL[dtype]
 
 
+LONG = [(128, 128, 64, "bf16"), (128, 128, 64, "f32"), (128, 128, 16, "bf16"), (64, 32, 16, "f32"),
+        (32, 128, 64, "f32")]
+
+
+@pytest.mark.parametrize("dk,dv,chunk,dtype", LONG)
+def test_long_memory(dk, dv, chunk, dtype):
+    """Slow decay (decay logits centred at -6): the entry state and the state
+    carried across many chunks still shape the outputs."""
+    spec = ki.small_spec(1, 3, 1500, dk, dv, chunk, dtype, seed=2200 + dk + chunk, s0_std=0.5, z_mean=-6.0)
+    say(f"case long memory dk={dk} dv={dv} chunk={chunk} {dtype}")
+    d = ki.prefill_inputs(spec)
+    dd = dev_inputs(d, dtype)
+    o_ref, S_ref = oracle_ref(d, spec)
+    f = f64_inputs(d, dtype)
+    o_0, _ = oracle.forward_z(f["q"], f["k"], f["v"], f["beta"], f["z"], f["A"], -5.0, None)
+    gap = rel_l2(o_0, o_ref)
+    say(f"  entry state dropped: rel-L2 {gap:.3e} from the true outputs")
+    assert gap > 10 * TOL[dtype]
+    for path in ("z", "G"):
+        o, S = run_gpu(dd, spec, path)
+        eo, es = rel_l2(host64(o), o_ref), rel_l2(host64(S), S_ref)
+        say(f"  path={path} rel-L2 o={eo:.3e} S={es:.3e}")
+        assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_state_in_place(dtype):
     """S_out == S_in: the state is read before it is overwritten."""

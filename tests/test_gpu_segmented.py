@@ -1,0 +1,149 @@
+"""GPU parity of the segment-parallel prefill (kda_chunk_fwd_z_segmented)
+against the fp64 oracle, and against the one-pass GPU prefill on the same
+inputs.  Tolerance: relative L2 1e-2 (bf16 inputs), separately for o and the
+final state; the segmented form regroups the arithmetic, so it is compared to
+the one-pass kernel at the same tolerance, not bit for bit (segments == 1 is
+the one-pass kernel itself and is compared exactly)."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_11_amd as kda
+import kda_inputs as ki
+import oracle
+from tests._gpu import DEV, TOL, dev_inputs, f64_inputs, host64, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _spec(B, H, T, seed, z_scale=1.0, s0_std=0.0, z_mean=0.0):
+    return ki.small_spec(B, H, T, 128, 128, 64, "bf16", seed=seed, z_scale=z_scale, s0_std=s0_std, z_mean=z_mean)
+
+
+def _plain(dd, S0, o_dtype=torch.bfloat16):
+    o, S = kda.chunk_fwd_z(dd["q"], dd["k"], dd["v"], dd["beta"], dd["z"], dd["A"], -5.0, 64, S_in=S0,
+                           o_dtype=o_dtype)
+    torch.cuda.synchronize()
+    return o, S
+
+
+def _seg(dd, S0, segments, o_dtype=torch.bfloat16, **kw):
+    o, S = kda.chunk_fwd_z_segmented(dd["q"], dd["k"], dd["v"], dd["beta"], dd["z"], dd["A"], segments, -5.0, 64,
+                                     S_in=S0, o_dtype=o_dtype, **kw)
+    torch.cuda.synchronize()
+    return o, S
+
+
+CASES = [  # B, H, T, segments, z_mean, s0_std
+    (1, 2, 1024, 4, 0.0, 0.0),          # four equal segments, fast decay
+    (1, 2, 1024, 4, -6.0, 0.0),         # the same with slow decay: segment boundaries carry state
+    (1, 2, 1000, 3, -6.0, 0.5),         # ragged last chunk and last segment, given entry state
+    (2, 3, 64 * 9 + 17, 7, -4.0, 0.5),  # seven segments over ten chunks (two chunks, last one short)
+    (1, 1, 512, 8, -8.0, 1.0),          # one chunk per segment, slowest decay: transitions matter most
+    (1, 2, 200, 100, -6.0, 0.5),        # more segments than chunks: one chunk each
+]
+
+
+@pytest.mark.parametrize("B,H,T,segs,zm,s0", CASES)
+def test_segmented_vs_oracle(B, H, T, segs, zm, s0):
+    spec = _spec(B, H, T, seed=4100 + T + segs, z_mean=zm, s0_std=s0)
+    say(f"case segmented B={B} H={H} T={T} segments={segs} z_mean={zm} s0_std={s0}")
+    d = ki.prefill_inputs(spec)
+    dd = dev_inputs(d, spec.dtype)
+    o, S = _seg(dd, dd["S0"], segs, o_dtype=torch.float32)
+    f = f64_inputs(d, spec.dtype)
+    o_ref, S_ref = oracle.forward_z(f["q"], f["k"], f["v"], f["beta"], f["z"], f["A"], -5.0, f["S0"])
+    eo, es = rel_l2(host64(o), o_ref), rel_l2(host64(S), S_ref)
+    say(f"  rel-L2 vs oracle o={eo:.3e} S={es:.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+    o1, S1 = _plain(dd, dd["S0"], o_dtype=torch.float32)
+    eo1, es1 = rel_l2(host64(o), host64(o1)), rel_l2(host64(S), host64(S1))
+    say(f"  rel-L2 vs one-pass kernel o={eo1:.3e} S={es1:.3e}")
+    assert eo1 <= TOL["bf16"] and es1 <= TOL["bf16"]
+    if zm < 0:
+        # the case is sensitive to the state carried into the last segment: the
+        # oracle run over that segment alone, from the zero state, is far off
+        nch = (T + 63) // 64
+        t_last = ((nch - 1) // ((nch + segs - 1) // segs)) * ((nch + segs - 1) // segs) * 64
+        cut = {n: np.ascontiguousarray(f[n][:, t_last:]) for n in ("q", "k", "v", "beta", "z")}
+        o_cut, _ = oracle.forward_z(cut["q"], cut["k"], cut["v"], cut["beta"], cut["z"], f["A"], -5.0, None)
+        gap = rel_l2(o_cut, o_ref[:, t_last:])
+        say(f"  last segment from zero state: rel-L2 {gap:.3e} from the true outputs")
+        assert gap > 10 * TOL["bf16"]
+
+
+def test_one_segment_is_the_one_pass_kernel():
+    spec = _spec(1, 2, 777, seed=4200, s0_std=0.5)
+    say("case segments=1 T=777")
+    dd = dev_inputs(ki.prefill_inputs(spec), spec.dtype)
+    o, S = _seg(dd, dd["S0"], 1)
+    o1, S1 = _plain(dd, dd["S0"])
+    assert torch.equal(o, o1) and torch.equal(S, S1)
+
+
+def test_in_place_state_and_no_state():
+    spec = _spec(1, 2, 640, seed=4300, s0_std=0.5)
+    say("case segments=5 in-place S and S_out=None")
+    d = ki.prefill_inputs(spec)
+    dd = dev_inputs(d, spec.dtype)
+    o_ref, S_ref = _seg(dd, dd["S0"], 5)
+    S_io = dd["S0"].clone()
+    o, S = _seg(dd, S_io, 5, S_out=S_io)
+    assert S.data_ptr() == S_io.data_ptr()
+    assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
+    o2, S2 = _seg(dd, dd["S0"], 5, want_state=False)
+    assert S2 is None and torch.equal(o2, o_ref)
+
+
+def test_workspace_reuse_and_dirty_workspace():
+    spec = _spec(2, 2, 900, seed=4400, s0_std=0.5)
+    say("case segments=4 caller workspace, filled with garbage between calls")
+    dd = dev_inputs(ki.prefill_inputs(spec), spec.dtype)
+    need = kda.chunk_fwd_z_segmented_workspace_bytes(2, 2, 128, 128, 4)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    ws.fill_(0x7f)  # large finite fp32 values everywhere
+    o1, S1 = _seg(dd, dd["S0"], 4, workspace=ws)
+    ws.fill_(0x3c)
+    o2, S2 = _seg(dd, dd["S0"], 4, workspace=ws)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    with pytest.raises(kda.KDAError, match="WORKSPACE"):
+        _seg(dd, dd["S0"], 4, workspace=ws[: need - 16])
+
+
+def _dev_rel_l2(x, ref):
+    """Relative L2 on the device in fp64 (the 1M-token outputs are too large to copy)."""
+    x, ref = x.double(), ref.double()
+    return float(torch.linalg.vector_norm(x - ref) / torch.linalg.vector_norm(ref))
+
+
+@pytest.mark.parametrize("z_mean", [0.0, -6.0])
+def test_prefill_1m_segmented_sampled(z_mean):
+    """The 1M-token, 8-head prefill (and a slow-decay variant of it) in 64 segments."""
+    spec = ki.PREFILL_1M if z_mean == 0.0 else replace(ki.PREFILL_1M, name=ki.PREFILL_1M.name + "_slow",
+                                                        z_mean=z_mean)
+    segs = 64
+    say(f"case {spec.name}: segments={segs}, generating inputs")
+    d = ki.prefill_inputs(spec)
+    dd = dev_inputs(d, spec.dtype)
+    say("  GPU runs (segmented, one-pass)")
+    o, S = _seg(dd, dd["S0"], segs)
+    o1, S1 = _plain(dd, dd["S0"])
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(S).all())
+    eo1, es1 = _dev_rel_l2(o, o1), _dev_rel_l2(S, S1)
+    say(f"  all heads, rel-L2 vs one-pass kernel o={eo1:.3e} S={es1:.3e}")
+    assert eo1 <= TOL["bf16"] and es1 <= TOL["bf16"]
+    b, h = 0, 3
+    say(f"  oracle b={b} h={h} T={spec.T}")
+    sub = {k: np.ascontiguousarray(d[k][b:b + 1, :, h:h + 1]) for k in ("q", "k", "v", "z", "beta")}
+    sub["A"] = np.ascontiguousarray(d["A"][h:h + 1])
+    sub["S0"] = None if d["S0"] is None else np.ascontiguousarray(d["S0"][b:b + 1, h:h + 1])
+    f = f64_inputs(sub, spec.dtype)
+    o_ref, S_ref = oracle.forward_z(f["q"], f["k"], f["v"], f["beta"], f["z"], f["A"], -5.0, f["S0"])
+    eo = rel_l2(host64(o[b:b + 1, :, h:h + 1]), o_ref)
+    es = rel_l2(host64(S[b:b + 1, h:h + 1]), S_ref)
+    say(f"  b={b} h={h} rel-L2 vs oracle o={eo:.3e} S={es:.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+    del dd, o, S, o1, S1
+    torch.cuda.empty_cache()
