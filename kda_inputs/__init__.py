@@ -17,6 +17,10 @@ the workloads themselves are synthetic):
   channels lose about half their remaining log-range per token and the state
   forgets within one chunk; a negative z_mean (long-memory test cases) makes
   the decay slow, so the state carried across chunks and segments matters.
+* raw = True (inputs of the fused-prologue entry points): q and k are NOT
+  normalised: each token row is N(0, 1) times a magnitude 10^U(-3.5, 0.5)
+  drawn per row (norms from about 4e-3 to 36, so the 1e-6 regulariser
+  matters at the small end), and beta is a logit, N(0, 2^2), with no sigmoid.
 * A ~ N(0, 0.5^2) per (head, key channel), stored fp32.
 * S0 ~ N(0, s0_std^2) per (b, h) state, stored fp32 (absent when s0_std == 0).
 
@@ -91,6 +95,17 @@ def _l2norm_rows(x: np.ndarray) -> np.ndarray:
     return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + L2_EPS)
 
 
+def _raw_rows(rng, x: np.ndarray) -> np.ndarray:
+    """Un-normalised rows: x times a per-row magnitude 10^U(-3.5, 0.5)."""
+    mag = 10.0 ** rng.uniform(-3.5, 0.5, x.shape[:-1] + (1,))
+    return x * mag
+
+
+def _beta_draw(rng, shape, raw: bool) -> np.ndarray:
+    x = rng.standard_normal(shape)
+    return 2.0 * x if raw else _sigmoid(x)
+
+
 # ----------------------------------------------------------------------------
 # workload specs
 # ----------------------------------------------------------------------------
@@ -107,6 +122,7 @@ class PrefillSpec:
     z_scale: float = 1.0
     s0_std: float = 0.0   # 0 -> no incoming state (zeros)
     z_mean: float = 0.0   # offset of the decay logits z (negative: slow decay, long memory)
+    raw: bool = False     # q, k un-normalised and beta a logit (fused-prologue inputs)
     seed: int = 1000
 
 
@@ -121,6 +137,7 @@ class DecodeSpec:
     dtype: str
     s_std: float = 0.1
     seed: int = 1004
+    raw: bool = False     # q, k un-normalised and beta a logit (fused-prologue inputs)
 
 
 # The five workloads: a tiny fp32 case, a 4K-token prefill, the 32K-token
@@ -153,14 +170,14 @@ def _draw_block(spec: PrefillSpec, b: int, h: int, blk: int, t0: int, t1: int) -
         rng = np.random.default_rng([spec.seed, _TAG[name], b, h, blk])
         x = rng.standard_normal((n, width))
         if name in ("q", "k"):
-            x = _l2norm_rows(x)
+            x = _raw_rows(rng, x) if spec.raw else _l2norm_rows(x)
         elif name == "z":
             x = x * spec.z_scale
             if spec.z_mean:
                 x = x + spec.z_mean
         out[name] = round_storage(x, spec.dtype)
     rng = np.random.default_rng([spec.seed, _TAG["beta"], b, h, blk])
-    out["beta"] = round_storage(_sigmoid(rng.standard_normal(n)), spec.dtype)
+    out["beta"] = round_storage(_beta_draw(rng, n, spec.raw), spec.dtype)
     return out
 
 
@@ -231,9 +248,9 @@ def prefill_inputs(spec: PrefillSpec, b_sel: Optional[Sequence[int]] = None,
 
 
 def small_spec(B, H, T, dk, dv, chunk, dtype, seed, z_scale=1.0, s0_std=0.0, name="custom",
-               z_mean=0.0) -> PrefillSpec:
+               z_mean=0.0, raw=False) -> PrefillSpec:
     return PrefillSpec(name, B=B, H=H, T=T, dk=dk, dv=dv, chunk=chunk, dtype=dtype, z_scale=z_scale,
-                       s0_std=s0_std, seed=seed, z_mean=z_mean)
+                       s0_std=s0_std, seed=seed, z_mean=z_mean, raw=raw)
 
 
 # ----------------------------------------------------------------------------
@@ -246,10 +263,10 @@ def decode_step_inputs(spec: DecodeSpec, step: int, n_sel: Optional[Sequence[int
         rng = np.random.default_rng([spec.seed, _TAG[name], step])
         x = rng.standard_normal((spec.N, spec.H, width))
         if name in ("q", "k"):
-            x = _l2norm_rows(x)
+            x = _raw_rows(rng, x) if spec.raw else _l2norm_rows(x)
         out[name] = round_storage(x, spec.dtype)
     rng = np.random.default_rng([spec.seed, _TAG["beta"], step])
-    out["beta"] = round_storage(_sigmoid(rng.standard_normal((spec.N, spec.H))), spec.dtype)
+    out["beta"] = round_storage(_beta_draw(rng, (spec.N, spec.H), spec.raw), spec.dtype)
     if n_sel is not None:
         n_sel = list(n_sel)
         out = {k: np.ascontiguousarray(v[n_sel]) for k, v in out.items()}

@@ -15,6 +15,13 @@ What it computes (definitions cited by page title and section):
 * Gate (Eq. 5), "Kimi K3 reading notes", section 2: g = g_min *
   sigmoid(exp(A^h) z), alpha = exp(g), g_min = -5.
 * Decode: one step of the same recurrence per sequence, state carried.
+* Fused prologue (the step before the recurrence): queries and keys get the
+  regularised L2 normalisation of "the paper and proofs side by side",
+  section 2.1.1 (Equations 2-6, "Preparing the queries, keys, values, and
+  decay"), and the write strength beta, which must lie in (0, 1)
+  ("architecture, derivations and a pinned-source audit", section 4.2), is
+  taken from a logit through the logistic sigmoid.  Plain numpy in fp64,
+  followed by the C recurrence.
 * Draft replay, "Kimi K3: architecture, derivations and a pinned-source
   audit", section 10.3 (KDA state replay for speculative decoding): the
   drafted tokens of each sequence run from a cached state that is itself
@@ -34,6 +41,7 @@ import numpy as np
 from . import build as _build
 
 G_MIN = -5.0
+L2_EPS = 1e-6   # the regulariser of the query/key normalisation (paper-and-proofs page, section 2.1.1)
 
 _DP = ctypes.POINTER(ctypes.c_double)
 
@@ -47,6 +55,33 @@ def _p(a: Optional[np.ndarray]):
 
 def _f64(a):
     return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
+
+
+def l2_normalise(x: np.ndarray) -> np.ndarray:
+    """Regularised L2 normalisation over the last axis, in fp64.
+
+    "Kimi K3: the paper and proofs side by side", section 2.1.1 (Equations
+    2-6): each coordinate is divided by a regularised norm with 1e-6 inside,
+    so the result has norm strictly below one and a zero vector stays zero.
+    The divisor itself did not survive extraction; the reading taken is
+    sqrt(sum of squares + 1e-6), the one form with both stated properties
+    whose regulariser is a plain additive 1e-6."""
+    x = _f64(x)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + L2_EPS)
+
+
+def sigmoid(x: np.ndarray) -> np.ndarray:
+    """Logistic sigmoid 1 / (1 + e^-x) in fp64: the map from a write-strength
+    logit onto (0, 1) (the pages fix beta in (0, 1), not the map; this is
+    the reading taken)."""
+    x = _f64(x)
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def prologue(q_raw, k_raw, beta_logit) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """The fused prologue: (q_hat, k_hat, beta) from un-normalised q, k [..., dk]
+    and beta logits [...]."""
+    return l2_normalise(q_raw), l2_normalise(k_raw), sigmoid(beta_logit)
 
 
 class Oracle:
@@ -137,6 +172,19 @@ class Oracle:
         return o, committed
 
 
+    def forward_z_prologue(self, q_raw, k_raw, v, beta_logit, z, A, g_min: float = G_MIN, S0=None,
+                           scale: float = 1.0, nthreads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+        """``prologue`` then ``forward_z``: the prefill of the fused-prologue entry point."""
+        q, k, beta = prologue(q_raw, k_raw, beta_logit)
+        return self.forward_z(q, k, v, beta, z, A, g_min, S0, scale, nthreads)
+
+    def decode_prologue(self, q_raw, k_raw, v, z, beta_logit, A, S0, g_min: float = G_MIN, scale: float = 1.0,
+                        nthreads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+        """``prologue`` then the decode protocol (``decode``): [steps, N, H, ...] inputs."""
+        q, k, beta = prologue(q_raw, k_raw, beta_logit)
+        return _decode(self, q, k, v, z, beta, A, S0, g_min, scale, nthreads)
+
+
 _default: Optional[Oracle] = None
 
 
@@ -163,6 +211,12 @@ def forward_z(q, k, v, beta, z, A, g_min: float = G_MIN, S0=None, scale: float =
 
 def decode(q, k, v, z, beta, A, S0, g_min: float = G_MIN, scale: float = 1.0,
            nthreads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """Decode protocol on the default build (see ``_decode``)."""
+    return _decode(default(), q, k, v, z, beta, A, S0, g_min, scale, nthreads)
+
+
+def _decode(orc: "Oracle", q, k, v, z, beta, A, S0, g_min: float = G_MIN, scale: float = 1.0,
+            nthreads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
     """Decode protocol: ``steps`` consecutive single-token updates.
 
     q, k, z: [steps, N, H, dk]; v: [steps, N, H, dv]; beta: [steps, N, H];
@@ -174,8 +228,8 @@ def decode(q, k, v, z, beta, A, S0, g_min: float = G_MIN, scale: float = 1.0,
     outs = []
     for s in range(steps):
         # [N, H, d] -> [B=N, T=1, H, d]
-        o, S = forward_z(q[s][:, None], k[s][:, None], v[s][:, None], beta[s][:, None], z[s][:, None], A,
-                         g_min, S, scale, nthreads)
+        o, S = orc.forward_z(q[s][:, None], k[s][:, None], v[s][:, None], beta[s][:, None], z[s][:, None], A,
+                             g_min, S, scale, nthreads)
         outs.append(o[:, 0])
     return np.stack(outs) if outs else np.zeros((0,) + S.shape[:2] + (S.shape[-1],)), S
 
@@ -185,3 +239,13 @@ def replay(q, k, v, z, beta, A, S_snapshot, accepted, g_min: float = G_MIN, scal
            nthreads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
     """Speculative-decoding replay (see ``Oracle.replay``) on the default build."""
     return default().replay(q, k, v, z, beta, A, S_snapshot, accepted, g_min, scale, nthreads)
+
+
+def forward_z_prologue(q_raw, k_raw, v, beta_logit, z, A, g_min: float = G_MIN, S0=None, scale: float = 1.0,
+                       nthreads: int = 0):
+    return default().forward_z_prologue(q_raw, k_raw, v, beta_logit, z, A, g_min, S0, scale, nthreads)
+
+
+def decode_prologue(q_raw, k_raw, v, z, beta_logit, A, S0, g_min: float = G_MIN, scale: float = 1.0,
+                    nthreads: int = 0):
+    return default().decode_prologue(q_raw, k_raw, v, z, beta_logit, A, S0, g_min, scale, nthreads)

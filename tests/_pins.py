@@ -418,4 +418,90 @@ def pin_replay(orc):
                 assert not np.allclose(np.array(Sall), S[n, h])
 
 
+# ----------------------------------------------------------------------------
+# fused prologue: regularised L2 normalisation of q, k and beta from a logit
+# ----------------------------------------------------------------------------
+def pin_prologue_normalisation(orc):
+    """Paper-and-proofs page, section 2.1.1 (Equations 2-6): the normalised
+    vector keeps its direction, has norm strictly below one, and a zero
+    vector stays zero; with the regulariser eps = 1e-6 under the root, the
+    squared norm of the result is s / (s + eps) for s = |x|^2, so a vector of
+    norm 1e-3 comes out with norm 1/sqrt(2), a large one with norm 1 - eps/(2s),
+    and a tiny one is scaled by 1/sqrt(eps) = 1000.  Normalisation is per token
+    row (the last axis), never across tokens."""
+    import oracle as O
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((3, 7, 2, 16))
+    x *= 10.0 ** rng.uniform(-5, 3, (3, 7, 2, 1))
+    x[1, 3, 0] = 0.0
+    y = O.l2_normalise(x)
+    assert np.array_equal(y[1, 3, 0], np.zeros(16))                     # zero stays zero
+    n_in = np.linalg.norm(x, axis=-1)
+    n_out = np.linalg.norm(y, axis=-1)
+    assert np.all(n_out < 1.0)
+    s = n_in ** 2
+    np.testing.assert_allclose(n_out ** 2, s / (s + 1e-6), rtol=1e-13, atol=0)
+    nz = n_in > 0
+    cosine = np.sum(x * y, axis=-1)[nz] / (n_in[nz] * n_out[nz])
+    np.testing.assert_allclose(cosine, 1.0, rtol=0, atol=1e-14)       # direction kept
+    e = np.zeros(16)
+    e[0] = 1e-3
+    assert abs(np.linalg.norm(O.l2_normalise(e)) - 1.0 / math.sqrt(2.0)) < 1e-12
+    e[0] = 1e4
+    assert abs(O.l2_normalise(e)[0] - (1.0 - 0.5e-14)) < 1e-15
+    e[0] = 1e-9
+    assert abs(O.l2_normalise(e)[0] / 1e-9 - 1000.0) < 1e-6
+    # rows are independent: scaling one token's row leaves the others unchanged
+    x2 = x.copy()
+    x2[0, 2, 1] *= 7.0
+    y2 = O.l2_normalise(x2)
+    mask = np.ones(x.shape[:-1], bool)
+    mask[0, 2, 1] = False
+    assert np.array_equal(y2[mask], y[mask])
+
+
+def pin_prologue_beta(orc):
+    """beta in (0, 1) ("architecture, derivations and a pinned-source audit",
+    section 4.2) from its logit by the logistic sigmoid: 1/2 at 0, symmetric
+    (sigma(-x) = 1 - sigma(x)), increasing, and inverted by the log-odds."""
+    import oracle as O
+    assert O.sigmoid(0.0) == 0.5
+    x = np.linspace(-30, 30, 601)
+    b = O.sigmoid(x)
+    assert np.all((b > 0) & (b < 1)) and np.all(np.diff(b) > 0)
+    np.testing.assert_allclose(O.sigmoid(-x) + b, 1.0, rtol=0, atol=1e-15)
+    mid = np.abs(x) < 15
+    np.testing.assert_allclose(np.log(b[mid] / (1 - b[mid])), x[mid], rtol=0, atol=1e-9)
+
+
+def pin_prologue_forward(orc):
+    """The prefill with the prologue fused: for rows of large norm the
+    regulariser is negligible, so it equals the plain prefill on exactly
+    unit-normalised q, k with beta = e^x / (1 + e^x) computed apart; scaling
+    the raw rows by any factor above that regime changes nothing; and the
+    decode form steps the same recurrence token by token."""
+    rng = np.random.default_rng(43)
+    B, T, H, dk, dv = 2, 9, 2, 6, 5
+    q = rng.standard_normal((B, T, H, dk)) * 50.0
+    k = rng.standard_normal((B, T, H, dk)) * 50.0
+    v = rng.standard_normal((B, T, H, dv))
+    bl = rng.standard_normal((B, T, H)) * 2.0
+    z = rng.standard_normal((B, T, H, dk))
+    A = rng.standard_normal((H, dk)) * 0.5
+    S0 = rng.standard_normal((B, H, dk, dv)) * 0.3
+    o, S = orc.forward_z_prologue(q, k, v, bl, z, A, -5.0, S0)
+    unit = lambda x: x / np.linalg.norm(x, axis=-1, keepdims=True)
+    ou, Su = orc.forward_z(unit(q), unit(k), v, np.exp(bl) / (1.0 + np.exp(bl)), z, A, -5.0, S0)
+    np.testing.assert_allclose(o, ou, rtol=0, atol=1e-8)
+    np.testing.assert_allclose(S, Su, rtol=0, atol=1e-8)
+    o3, S3 = orc.forward_z_prologue(q * 1e3, k * 1e3, v, bl, z, A, -5.0, S0)
+    np.testing.assert_allclose(o3, o, rtol=0, atol=1e-9)
+    np.testing.assert_allclose(S3, S, rtol=0, atol=1e-9)
+    # decode form: [steps, N, H, ...] with the batch entries as sequences
+    tm = lambda x: np.ascontiguousarray(np.moveaxis(x, 1, 0))
+    od, Sd = orc.decode_prologue(tm(q), tm(k), tm(v), tm(z), tm(bl), A, S0)
+    np.testing.assert_allclose(od, tm(o), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(Sd, S, rtol=0, atol=1e-12)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

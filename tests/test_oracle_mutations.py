@@ -6,6 +6,7 @@ import shutil
 import subprocess
 import tempfile
 
+import numpy as np
 import pytest
 
 import oracle
@@ -66,3 +67,32 @@ def test_mutation_is_caught(name, workdir):
         except AssertionError:
             failed.append(pin.__name__)
     assert failed, f"no pin catches the planted mistake {name}"
+
+
+# The prologue is numpy code (oracle.l2_normalise, oracle.sigmoid): plant its
+# plausible mistakes by swapping the function, on the CPU, and require a pin
+# to fail.
+PROLOGUE_MUTATIONS = {
+    "eps_outside_root": ("l2_normalise", lambda x: x / (np.sqrt(np.sum(x * x, axis=-1, keepdims=True)) + 1e-6)),
+    "eps_1e-3": ("l2_normalise", lambda x: x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + 1e-3)),
+    "no_root": ("l2_normalise", lambda x: x / (np.sum(x * x, axis=-1, keepdims=True) + 1e-6)),
+    "norm_over_tokens": ("l2_normalise", lambda x: x / np.sqrt(np.sum(x * x, axis=-3, keepdims=True) + 1e-6)),
+    "no_normalisation": ("l2_normalise", lambda x: np.asarray(x, float) * 1.0),
+    "sigmoid_sign": ("sigmoid", lambda x: 1.0 / (1.0 + np.exp(np.asarray(x, float)))),
+    "beta_tanh": ("sigmoid", lambda x: 0.5 * (1.0 + np.tanh(np.asarray(x, float)))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PROLOGUE_MUTATIONS))
+def test_prologue_mutation_is_caught(name, monkeypatch):
+    attr, fn = PROLOGUE_MUTATIONS[name]
+    monkeypatch.setattr(oracle, attr, fn)
+    failed = []
+    for pin in _pins.ALL_PINS:
+        if not pin.__name__.startswith("pin_prologue"):
+            continue
+        try:
+            pin(oracle.default())
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"prologue mutation {name} passed every prologue pin"
