@@ -208,6 +208,27 @@ def main():
         log(f"replay of {nd} drafts: {rep_ms:.3f} ms (vs {replay['same_tokens_as_decode_steps_ms']:.3f} ms "
             f"for {nd} decode steps)")
 
+    # ---------------- fused prologue (reported beside the step, not part of it) ----------------
+    # The same prefill with q, k normalised and beta = sigmoid(logit) inside the kernel
+    # (kda_chunk_fwd_z_prologue); the resident inputs stand in for raw ones (the kernel's
+    # work does not depend on their values).
+    prologue = None
+    if run_pre:
+        def pro():
+            kda.chunk_fwd_z_prologue(P["q"], P["k"], P["v"], P["beta"], P["z"], P["A"], -5.0, ps.chunk,
+                                     S_in=P["S0"], o=o_pre, S_out=S_pre, stream=stream)
+        pro()
+        pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+        for r0, r1 in pev:
+            r0.record(stream)
+            pro()
+            r1.record(stream)
+        torch.cuda.synchronize()
+        pro_ms = float(np.mean([r0.elapsed_time(r1) for r0, r1 in pev]))
+        prologue = {"ms": round(pro_ms, 4), "tokens_per_s": round(ps.B * ps.T / (pro_ms / 1e3), 1),
+                    "vs_plain_prefill": round(pro_ms / float(np.mean(pre_ms)), 4)}
+        log(f"fused-prologue prefill: {pro_ms:.3f} ms ({prologue['vs_plain_prefill']:.3f} x the plain prefill)")
+
     # ---------------- 1M-token prefill (reported beside the step, not part of it) ----------------
     # B=1, H=8, T=2^20: one pass of the chunk kernel has 8 sequences for 256 compute units;
     # the segment-parallel form runs 16 segments per sequence side by side.
@@ -326,6 +347,7 @@ def main():
         "cpu_baseline": cpu,
         "replay": replay,
         "long_context": long_ctx,
+        "prologue": prologue,
     }
     # a profiling run that timed one path reports nothing for the other
     if not run_dec:

@@ -58,6 +58,10 @@ def lib() -> ctypes.CDLL:
     L.kda_decode_step.restype = I
     L.kda_decode_replay.argtypes = [P, P, P, P, P, I, P, F, P, P, P, I, P, I, I, I, I, I, F, P]
     L.kda_decode_replay.restype = I
+    L.kda_chunk_fwd_z_prologue.argtypes = L.kda_chunk_fwd_z.argtypes
+    L.kda_chunk_fwd_z_prologue.restype = I
+    L.kda_decode_step_prologue.argtypes = L.kda_decode_step.argtypes
+    L.kda_decode_step_prologue.restype = I
     L.kda_chunk_fwd_z_segmented_workspace_bytes.argtypes = [I, I, I, I, I]
     L.kda_chunk_fwd_z_segmented_workspace_bytes.restype = ctypes.c_size_t
     L.kda_chunk_fwd_z_segmented.argtypes = [P, P, P, P, P, I, P, F, P, P, I, P, I, I, I, I, I, I, F, I, P,
@@ -155,6 +159,35 @@ def chunk_fwd_z(q, k, v, beta, z, A, g_min: float = G_MIN, chunk: int = 64, S_in
                                  _p(S_in), _p(o), _dtype_code(o), _p(S_out), B, T, H, dk, dv, int(chunk),
                                  float(scale), _stream(stream)), "kda_chunk_fwd_z")
     return o, S_out
+
+
+def chunk_fwd_z_prologue(q_raw, k_raw, v, beta_logit, z, A, g_min: float = G_MIN, chunk: int = 64, S_in=None,
+                         o=None, S_out=None, o_dtype=None, scale: float = 1.0, want_state: bool = True,
+                         stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """``chunk_fwd_z`` with the prologue fused: q, k un-normalised, beta as a logit."""
+    B, T, H, dk = q_raw.shape
+    dv = v.shape[-1]
+    o, S_out = _outs(q_raw, v, o, S_out, o_dtype, want_state)
+    _dev(q_raw, k_raw, v, beta_logit, z, A, S_in, o, S_out)
+    _check(lib().kda_chunk_fwd_z_prologue(_p(q_raw), _p(k_raw), _p(v), _p(beta_logit), _p(z), _dtype_code(q_raw),
+                                          _p(A), float(g_min), _p(S_in), _p(o), _dtype_code(o), _p(S_out), B, T, H,
+                                          dk, dv, int(chunk), float(scale), _stream(stream)),
+           "kda_chunk_fwd_z_prologue")
+    return o, S_out
+
+
+def decode_step_prologue(q_raw, k_raw, v, z, beta_logit, A, S, g_min: float = G_MIN, o=None, o_dtype=None,
+                         scale: float = 1.0, stream=None) -> torch.Tensor:
+    """``decode_step`` with the prologue fused: q, k un-normalised, beta as a logit."""
+    N, H, dk = q_raw.shape
+    dv = v.shape[-1]
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=o_dtype or torch.float32, device=q_raw.device)
+    _dev(q_raw, k_raw, v, z, beta_logit, A, S, o)
+    _check(lib().kda_decode_step_prologue(_p(q_raw), _p(k_raw), _p(v), _p(z), _p(beta_logit), _dtype_code(q_raw),
+                                          _p(A), float(g_min), _p(S), _p(o), _dtype_code(o), N, H, dk, dv,
+                                          float(scale), _stream(stream)), "kda_decode_step_prologue")
+    return o
 
 
 def chunk_fwd_z_segmented_workspace_bytes(B: int, H: int, dk: int, dv: int, segments: int) -> int:

@@ -102,7 +102,7 @@ static kda_status chunk_common(const void* q, const void* k, const void* v, cons
                                kda_dtype in_dtype, const float* G, const float* A, float g_min,
                                const float* S_in, void* o, kda_dtype o_dtype, float* S_out, int B, int T, int H,
                                int dk, int dv, int chunk, float scale, bool from_z, void* stream, int segments = 1,
-                               void* ws = nullptr, size_t ws_bytes = 0) {
+                               void* ws = nullptr, size_t ws_bytes = 0, bool prologue = false) {
   if (!dtype_ok(in_dtype) || !dtype_ok(o_dtype)) return KDA_ERR_DTYPE;
   if (!sizes_ok(B, T, H, dk, dv)) return KDA_ERR_SHAPE;
   if (!dim_ok(dk) || !dim_ok(dv) || !(chunk == 16 || chunk == 64)) return KDA_ERR_UNSUPPORTED;
@@ -134,6 +134,7 @@ static kda_status chunk_common(const void* q, const void* k, const void* v, cons
   a.A = from_z ? A : nullptr; a.g_min = g_min; a.S_in = S_in; a.o = o; a.S_out = S_out;
   a.B = B; a.T = T; a.H = H; a.dk = dk; a.dv = dv; a.chunk = chunk; a.scale = scale;
   a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = o_dtype == KDA_BF16; a.from_z = from_z;
+  a.prologue = prologue;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int nch = (T + chunk - 1) / chunk;
   const int seg_chunks = (nch + segments - 1) / (segments > 0 ? segments : 1);
@@ -195,6 +196,14 @@ kda_status kda_chunk_fwd_z_segmented(const void* q, const void* k, const void* v
                       scale, true, stream, segments, workspace, workspace_bytes);
 }
 
+kda_status kda_chunk_fwd_z_prologue(const void* q, const void* k, const void* v, const void* beta_logit,
+                                    const void* z, kda_dtype in_dtype, const float* A, float g_min,
+                                    const float* S_in, void* o, kda_dtype o_dtype, float* S_out, int B, int T, int H,
+                                    int dk, int dv, int chunk, float scale, void* stream) {
+  return chunk_common(q, k, v, beta_logit, z, in_dtype, nullptr, A, g_min, S_in, o, o_dtype, S_out, B, T, H, dk, dv,
+                      chunk, scale, true, stream, 1, nullptr, 0, true);
+}
+
 kda_status kda_chunk_fwd_z(const void* q, const void* k, const void* v, const void* beta, const void* z,
                            kda_dtype in_dtype, const float* A, float g_min, const float* S_in, void* o,
                            kda_dtype o_dtype, float* S_out, int B, int T, int H, int dk, int dv, int chunk,
@@ -203,9 +212,10 @@ kda_status kda_chunk_fwd_z(const void* q, const void* k, const void* v, const vo
                       scale, true, stream);
 }
 
-kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* z, const void* beta,
-                           kda_dtype in_dtype, const float* A, float g_min, float* S, void* o, kda_dtype o_dtype,
-                           int N, int H, int dk, int dv, float scale, void* stream) {
+static kda_status decode_common(const void* q, const void* k, const void* v, const void* z, const void* beta,
+                                kda_dtype in_dtype, const float* A, float g_min, float* S, void* o,
+                                kda_dtype o_dtype, int N, int H, int dk, int dv, float scale, bool prologue,
+                                void* stream) {
   if (!dtype_ok(in_dtype) || !dtype_ok(o_dtype)) return KDA_ERR_DTYPE;
   if (!sizes_ok(N, 1, H, dk, dv)) return KDA_ERR_SHAPE;
   if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
@@ -222,8 +232,20 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
     if (overlap(rS, in) || overlap(ro, in)) return KDA_ERR_ALIAS;
   if (overlap(rS, ro)) return KDA_ERR_ALIAS;
   kda::DecodeArgs a{q, k, v, z, beta, A, g_min, S, o, N, H, dk, dv, scale, in_dtype == KDA_BF16,
-                    o_dtype == KDA_BF16};
+                    o_dtype == KDA_BF16, prologue};
   return from_hip(kda::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* z, const void* beta,
+                           kda_dtype in_dtype, const float* A, float g_min, float* S, void* o, kda_dtype o_dtype,
+                           int N, int H, int dk, int dv, float scale, void* stream) {
+  return decode_common(q, k, v, z, beta, in_dtype, A, g_min, S, o, o_dtype, N, H, dk, dv, scale, false, stream);
+}
+
+kda_status kda_decode_step_prologue(const void* q, const void* k, const void* v, const void* z, const void* beta,
+                                    kda_dtype in_dtype, const float* A, float g_min, float* S, void* o,
+                                    kda_dtype o_dtype, int N, int H, int dk, int dv, float scale, void* stream) {
+  return decode_common(q, k, v, z, beta, in_dtype, A, g_min, S, o, o_dtype, N, H, dk, dv, scale, true, stream);
 }
 
 kda_status kda_decode_replay(const void* q, const void* k, const void* v, const void* z, const void* beta,

@@ -22,6 +22,10 @@
 // Every power of two above has a non-positive exponent: Gl is non-increasing
 // in t, so no overflow is possible for any g.
 //
+// Fused prologue (a.prologue): q and k arrive un-normalised and beta as a
+// logit; each sub-chunk's rows are divided by sqrt(|x|^2 + 1e-6) in LDS and
+// beta goes through the sigmoid, before any of the above.
+//
 // One workgroup (256 threads) per (b, h, slice of DVS value columns).  The
 // value columns of the state evolve independently given (k, beta, alpha), so
 // slicing changes no arithmetic.
@@ -56,6 +60,7 @@ __global__ __launch_bounds__(NT) void chunk_generic_kernel(const ChunkArgs a) {
   __shared__ float Vs[SC][DVS], Us[SC][DVS];
   __shared__ float Lm[SC][SC], Pm[SC][SC], Tm[SC][SC];
   __shared__ float bs[SC];
+  __shared__ float rn[2][SC];  // prologue: 1 / sqrt(|k|^2 + eps), 1 / sqrt(|q|^2 + eps) per token
   __shared__ float Ss[DK][DVS];
   __shared__ float eaL[DK];
 
@@ -99,8 +104,26 @@ __global__ __launch_bounds__(NT) void chunk_generic_kernel(const ChunkArgs a) {
       const int i = e / DVS, j = e % DVS;
       Vs[i][j] = i < n ? io<Tin>::load(v, (static_cast<int64_t>(b) * a.T + t0 + i) * HDV + static_cast<int64_t>(h) * a.dv + j0 + j) : 0.f;
     }
-    if (tid < SC) bs[tid] = tid < n ? io<Tin>::load(beta, (static_cast<int64_t>(b) * a.T + t0 + tid) * a.H + h) : 0.f;
+    if (tid < SC) {
+      const float bl = tid < n ? io<Tin>::load(beta, (static_cast<int64_t>(b) * a.T + t0 + tid) * a.H + h) : 0.f;
+      bs[tid] = tid < n ? (a.prologue ? sigmoid_fast(bl) : bl) : 0.f;
+    }
     __syncthreads();
+    if (a.prologue) {  // normalise the rows of k and q (rows past n are zero and stay zero)
+      if (tid < 2 * SC) {
+        const float* row = tid < SC ? Ks[tid] : Qs[tid - SC];
+        float ss = 0.f;
+        for (int c = 0; c < DK; ++c) ss += row[c] * row[c];
+        rn[tid / SC][tid % SC] = rsqrt_fast(ss + kL2Eps);
+      }
+      __syncthreads();
+      for (int e = tid; e < SC * DK; e += NT) {
+        const int i = e / DK, c = e % DK;
+        Ks[i][c] *= rn[0][i];
+        Qs[i][c] *= rn[1][i];
+      }
+      __syncthreads();
+    }
     if (FROM_Z) {  // per-token g -> running sums within the sub-chunk
       for (int c = tid; c < DK; c += NT)
         for (int i = 1; i < n; ++i) Gl[i][c] += Gl[i - 1][c];

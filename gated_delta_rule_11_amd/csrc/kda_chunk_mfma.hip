@@ -62,7 +62,8 @@ struct Layout {
   static constexpr int EB = DT + 4 * DK * 4;            // [4][128] fp32 decay before tile i
   static constexpr int GC = EB + 4 * DK * 4;            // [128] fp32 chunk decay
   static constexpr int BT = GC + DK * 4;                // [64] fp32 beta
-  static constexpr int BYTES = BT + C * 4;
+  static constexpr int RH = BT + C * 4;                 // [64] fp32 query normalisers (fused prologue)
+  static constexpr int BYTES = RH + C * 4;
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -201,6 +202,41 @@ __device__ __forceinline__ void load_tile(RawTile<FROM_Z>& R, const ChunkArgs& a
   load_part<DVS, FROM_Z, 3, SEG>(R, a, b, h, t0, i, ln, j0);
 }
 
+// Per-token sums over the 64 lanes of a wavefront, for the fused prologue's
+// norms.  v[t] is this lane's part of token t's sum (t < 16); the result in
+// lane l is the total of token (l >> 2) & 15.  Each step pairs every lane with
+// one partner, keeps half of the tokens it still carries and adds the
+// partner's part of them: lanes l and l + 32 (swap of the wavefront halves),
+// l and l + 16 (swap of the odd and even 16-lane rows), l and 15 - l within a
+// row, l and 7 - l within an 8-lane half row; the last two steps sum the quad.
+// The partners' lane offsets, {32, 16, 15, 7, 2, 1}, span all 64 lanes once.
+__device__ __forceinline__ float wave_token_sums16(const float (&v)[16], int ln) {
+  float w[8];  // token m + 8 (lane bit 5)
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[m]), __float_as_uint(v[m + 8]), false, false);
+    w[m] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+  }
+  float x[4];  // token m + 4 (bit 4) + 8 (bit 5)
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(w[m]), __float_as_uint(w[m + 4]), false, false);
+    x[m] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+  }
+  const bool b3 = (ln & 8) != 0, b2 = (ln & 4) != 0;
+  float y[2];  // token m + 2 (bit 3) + 4 (bit 4) + 8 (bit 5)
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const float keep = b3 ? x[m + 2] : x[m], send = b3 ? x[m] : x[m + 2];
+    y[m] = keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), 0x140, 0xf, 0xf, false));
+  }
+  const float keep = b2 ? y[1] : y[0], send = b2 ? y[0] : y[1];
+  float z = keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), 0x141, 0xf, 0xf, false));
+  z += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(z), 0x4E, 0xf, 0xf, false));  // quad [2,3,0,1]
+  z += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(z), 0xB1, 0xf, 0xf, false));  // quad [1,0,3,2]
+  return z;
+}
+
 // Off-diagonal tile pairs (i, j < i) of the L / P products, per gate wavefront.
 __constant__ int8_t kOffPairs8[4][2][2] = {{{1, 0}, {3, 0}}, {{2, 1}, {3, 1}}, {{3, 2}, {-1, -1}}, {{2, 0}, {-1, -1}}};
 
@@ -220,9 +256,14 @@ __constant__ int8_t kOffPairs8[4][2][2] = {{{1, 0}, {3, 0}}, {{2, 1}, {3, 1}}, {
 // SEG instantiations serve the passes of the segment-parallel form (one
 // workgroup per segment; identity entry state, zero values, outputs skipped,
 // per-segment states); the plain instantiation compiles all of that out.
-template <int DVS, bool FROM_Z, typename Tout, bool SEG>
+// NORM instantiations fuse the prologue: the gate wavefronts take each token's
+// key norm (a lane reduction) into the factors the raw keys are multiplied by
+// anyway, compute beta = sigmoid(logit), and hand the query normalisers to the
+// state chain, which applies them to the output rows (o is linear in q_t).
+template <int DVS, bool FROM_Z, typename Tout, bool SEG, bool NORM>
 __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int ns, int xcd_map) {
   using namespace mf;
+  static_assert(!NORM || (FROM_Z && !SEG), "the fused prologue runs with the fused gate, in one pass");
   using Ly = Layout<DVS>;
   constexpr int NJT = DVS / 16;  // value-column tiles in the slice (chain wavefront w owns tile w)
   constexpr int ES = sizeof(Tout);
@@ -242,6 +283,7 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
   float* sEB = reinterpret_cast<float*>(smem + Ly::EB);
   float* sGC = reinterpret_cast<float*>(smem + Ly::GC);
   float* sBeta = reinterpret_cast<float*>(smem + Ly::BT);
+  float* sRho = reinterpret_cast<float*>(smem + Ly::RH);
 
   // workgroup -> ((b*H + h) * nseg + segment, slice); the slices of one head and
   // segment share an XCD (and its L2)
@@ -453,6 +495,8 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             f32x4 acc = O[i];
+            // prologue: query normalisers of this lane's four output rows
+            const f32x4 rho = NORM ? *reinterpret_cast<const f32x4*>(&sRho[16 * i + 4 * g4]) : f32x4{1.f, 1.f, 1.f, 1.f};
             const uint16_t* Pr = &sP[(16 * i + r16) * TS + 4 * g4];
 #pragma unroll
             for (int m = 0; m + 1 <= i; m += 2)
@@ -466,10 +510,11 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
             for (int v = 0; v < 4; ++v) {
               const int t = 16 * i + 4 * g4 + v;
               const int voff = (t * H * DK + 16 * wv + r16) * ES;
+              const float ov = NORM ? (a.scale * rho[v]) * acc[v] : a.scale * acc[v];
               if (ES == 2)
-                __builtin_amdgcn_raw_buffer_store_b16(f2bf(a.scale * acc[v]), ro, voff, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b16(f2bf(ov), ro, voff, 0, 0);
               else
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a.scale * acc[v]), ro, voff, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov), ro, voff, 0, 0);
             }
           }
         }
@@ -515,6 +560,7 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
     float D0 = 1.f, D1 = 1.f;         // A1 -> A2: decay over the tile
     uint32_t qt[16], kh[16];          // A2 -> B: q Gamma pairs, (k Gamma_C / Gamma)^T pairs
     float gc0 = 1.f, gc1 = 1.f;       // A2 -> B: Gamma_C (written by tile 0's wavefront)
+    float rho = 1.f;                  // A1 -> B (prologue): query normaliser of token (ln >> 2) & 15
 
     // gate of chunk tc: within-tile decay products, tile decays -> sD; q r -> sQR, v^T, beta
     // FULL: every token of the chunk is valid (all chunks but a ragged last one)
@@ -523,7 +569,8 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
       const int n = FULL ? C : min(C, T - tc);
       if (ln < 16) {
         const int t = 16 * i + ln;
-        sBeta[t] = (FULL || t < n) ? bf16_to_f32(static_cast<uint16_t>(R.beta)) : 0.f;
+        const float bl = bf16_to_f32(static_cast<uint16_t>(R.beta));
+        sBeta[t] = (FULL || t < n) ? (NORM ? sigmoid_fast(bl) : bl) : 0.f;
       }
       if (ln < DVS) {  // v^T, value column ln of the slice, tokens of this tile
         uint32_t w[8];
@@ -537,6 +584,25 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
         u32x4* dv = reinterpret_cast<u32x4*>(&sVT[ln * TS + 16 * i]);
         dv[0] = u32x4{w[0], w[1], w[2], w[3]};
         dv[1] = u32x4{w[4], w[5], w[6], w[7]};
+      }
+      // prologue: 1 / sqrt(|k_t|^2 + eps) of the tile's tokens (uniform values), and the
+      // query normalisers, kept for the state chain
+      float nk[16];
+#pragma unroll
+      for (int tt = 0; tt < 16; ++tt) nk[tt] = 1.f;
+      if constexpr (NORM) {
+        float pk[16], pq[16];
+#pragma unroll
+        for (int tt = 0; tt < 16; ++tt) {
+          pk[tt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, R.k[tt]),
+                                                   __builtin_bit_cast(bf16x2, R.k[tt]), 0.f, false);
+          pq[tt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, R.q[tt]),
+                                                   __builtin_bit_cast(bf16x2, R.q[tt]), 0.f, false);
+        }
+        const float rkl = rsqrt_fast(wave_token_sums16(pk, ln) + kL2Eps);
+        rho = rsqrt_fast(wave_token_sums16(pq, ln) + kL2Eps);
+#pragma unroll
+        for (int tt = 0; tt < 16; ++tt) nk[tt] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rkl), 4 * tt));
       }
       if constexpr (FROM_Z) {
         float al0[16], al1[16];
@@ -553,14 +619,14 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
           p0 *= al0[tt];
           p1 *= al1[tt];
           const uint32_t k = valid ? R.k[tt] : 0u, q = valid ? R.q[tt] : 0u;
-          kr[tt] = pack2(bflo(k) * p0, bfhi(k) * p1);
+          kr[tt] = pack2(bflo(k) * (p0 * nk[tt]), bfhi(k) * (p1 * nk[tt]));
           qr[tt] = pack2(bflo(q) * p0, bfhi(q) * p1);
         }
         float s0 = 1.f, s1 = 1.f;  // exclusive suffix products sf_t
 #pragma unroll
         for (int tt = 15; tt >= 0; --tt) {
           const uint32_t k = (FULL || 16 * i + tt < n) ? R.k[tt] : 0u;
-          ks[tt] = pack2(bflo(k) * s0, bfhi(k) * s1);
+          ks[tt] = pack2(bflo(k) * (s0 * nk[tt]), bfhi(k) * (s1 * nk[tt]));
           s0 *= al0[tt];
           s1 *= al1[tt];
         }
@@ -679,6 +745,7 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
         sGC[c0] = gc0;
         sGC[c0 + 1] = gc1;
       }
+      if (NORM && (ln & 3) == 0) sRho[16 * i + (ln >> 2)] = rho;
     };
 
     // ---- prologue: operand tiles of chunk 0
@@ -762,9 +829,9 @@ bool chunk_mfma_supports(const ChunkArgs& a) {
   return a.in_bf16 && a.dk == 128 && a.dv == 128 && a.chunk == 64 && a.H <= 65536;
 }
 
-template <int DVS, bool FROM_Z, typename Tout, bool SEG>
+template <int DVS, bool FROM_Z, typename Tout, bool SEG, bool NORM = false>
 static hipError_t launch_mfma_t(const ChunkArgs& a, hipStream_t st, int ns) {
-  auto kern = chunk_mfma_kernel<DVS, FROM_Z, Tout, SEG>;
+  auto kern = chunk_mfma_kernel<DVS, FROM_Z, Tout, SEG, NORM>;
   constexpr int bytes = mf::Layout<DVS>::BYTES;
   static bool attr_set = false;  // set once per instantiation (idempotent if raced)
   if (!attr_set) {
@@ -784,6 +851,11 @@ template <int DVS>
 static hipError_t launch_mfma_d(const ChunkArgs& a, hipStream_t st, int ns) {
   const bool seg = a.nseg > 1 || a.seg_chunks > 0 || a.S_in_seg || a.S_out_mode != 0 || a.S_identity ||
                    a.v_zero || a.o_skip;
+  if (a.prologue) {  // fused prologue: fused gate, one pass
+    if (!a.from_z || seg) return hipErrorNotSupported;
+    return a.out_bf16 ? launch_mfma_t<DVS, true, bf16_t, false, true>(a, st, ns)
+                      : launch_mfma_t<DVS, true, float, false, true>(a, st, ns);
+  }
   if (seg) {  // segment passes: fused gate only
     if (!a.from_z) return hipErrorNotSupported;
     return a.out_bf16 ? launch_mfma_t<DVS, true, bf16_t, true>(a, st, ns)

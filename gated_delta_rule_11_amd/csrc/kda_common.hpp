@@ -51,4 +51,11 @@ __device__ __forceinline__ float gate_log2(float z, float ea_l2e, float gmin_l2e
   return gmin_l2e * fast_rcp(1.0f + e);
 }
 
+// Fused prologue ("Kimi K3: the paper and proofs side by side", section 2.1.1,
+// Equations 2-6): q and k are divided by sqrt(|x|^2 + 1e-6); the write
+// strength beta in (0, 1) comes from its logit through the logistic sigmoid.
+constexpr float kL2Eps = 1e-6f;
+__device__ __forceinline__ float rsqrt_fast(float x) { return __builtin_amdgcn_rsqf(x); }  // v_rsq_f32, ~1 ulp
+__device__ __forceinline__ float sigmoid_fast(float x) { return fast_rcp(1.0f + fast_exp2(-x * kLog2e)); }
+
 }  // namespace kda

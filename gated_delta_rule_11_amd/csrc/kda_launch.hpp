@@ -38,6 +38,8 @@ struct ChunkArgs {
   bool S_identity = false;  // every segment starts from the identity (dv == dk)
   bool v_zero = false;      // values taken as zero (v is not read)
   bool o_skip = false;      // outputs are not written
+  // Fused prologue: q, k un-normalised and beta a logit (normalised / sigmoid in-kernel).
+  bool prologue = false;
 };
 
 struct DecodeArgs {
@@ -49,6 +51,7 @@ struct DecodeArgs {
   int N, H, dk, dv;
   float scale;
   bool in_bf16, out_bf16;
+  bool prologue = false;  // q, k un-normalised and beta a logit
 };
 
 struct ReplayArgs {

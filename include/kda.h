@@ -153,6 +153,31 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v,
                            float scale, void* stream);
 
 /*
+ * Fused prologue ("Kimi K3: the paper and proofs side by side", section 2.1.1,
+ * Equations 2-6, "Preparing the queries, keys, values, and decay"; write
+ * strength in (0, 1): "Kimi K3: architecture, derivations and a
+ * pinned-source audit", section 4.2).
+ *
+ * kda_chunk_fwd_z_prologue and kda_decode_step_prologue take the same
+ * arguments as kda_chunk_fwd_z and kda_decode_step, but q and k arrive
+ * un-normalised and beta as a logit.  Inside the kernels, per token:
+ *   q^ = q / sqrt(|q|^2 + 1e-6),  k^ = k / sqrt(|k|^2 + 1e-6)   (fp32 sums)
+ *   beta = 1 / (1 + e^(-beta_logit))
+ * and the step then runs on (q^, k^, beta).  A zero q or k stays zero.  The
+ * short convolution, the activation and the projections that produce these
+ * inputs are not part of the library (they need trained weights).
+ * Shapes, dtypes, layouts, validation and errors: as the plain entry points.
+ */
+kda_status kda_chunk_fwd_z_prologue(const void* q, const void* k, const void* v, const void* beta_logit,
+                                    const void* z, kda_dtype in_dtype, const float* A, float g_min,
+                                    const float* S_in, void* o, kda_dtype o_dtype, float* S_out, int B, int T,
+                                    int H, int dk, int dv, int chunk, float scale, void* stream);
+kda_status kda_decode_step_prologue(const void* q, const void* k, const void* v, const void* z,
+                                    const void* beta_logit, kda_dtype in_dtype, const float* A, float g_min,
+                                    float* S, void* o, kda_dtype o_dtype, int N, int H, int dk, int dv,
+                                    float scale, void* stream);
+
+/*
  * kda_chunk_fwd_z_segmented -- kda_chunk_fwd_z for few, long sequences.
  *
  * Same inputs, outputs and result as kda_chunk_fwd_z (within the bf16

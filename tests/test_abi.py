@@ -34,6 +34,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_z", "kda_decode_step", "kda_decode_replay",
+              "kda_chunk_fwd_z_prologue", "kda_decode_step_prologue", "kda_chunk_fwd_z_segmented",
               "kda_status_string"):
         assert n in names
 
@@ -192,3 +193,31 @@ def test_segmented_validation(L):
     assert chunk_seg(L, it=F32) == ERR_UNSUPPORTED                # segments need the MFMA shape
     assert chunk_seg(L, dk=64) == ERR_UNSUPPORTED
     assert chunk_seg(L, B=0) == OK
+
+
+def test_prologue_validation(L):
+    """The fused-prologue entry points validate exactly as the plain ones."""
+    def chunk(**kw):
+        a = dict(q=P(0), k=P(1), v=P(2), beta=P(3), z=P(4), A=P(8), S_in=P(5), o=P(6), S_out=P(7), B=1, T=100,
+                 H=2, dk=128, dv=128, chunk=64, it=BF16, gmin=-5.0)
+        a.update(kw)
+        return L.kda_chunk_fwd_z_prologue(a["q"], a["k"], a["v"], a["beta"], a["z"], a["it"], a["A"], a["gmin"],
+                                          a["S_in"], a["o"], BF16, a["S_out"], a["B"], a["T"], a["H"], a["dk"],
+                                          a["dv"], a["chunk"], 1.0, N)
+    assert chunk(q=None) == ERR_NULL
+    assert chunk(dk=48) == ERR_UNSUPPORTED
+    assert chunk(chunk=32) == ERR_UNSUPPORTED
+    assert chunk(it=7) == ERR_DTYPE
+    assert chunk(o=P(2)) == ERR_ALIAS
+    assert chunk(gmin=1.0) == ERR_UNSUPPORTED
+    assert chunk(B=0) == OK
+
+    def dec(**kw):
+        a = dict(q=P(0), k=P(1), v=P(2), z=P(3), beta=P(4), A=P(5), S=P(6), o=P(7), N=4, H=2, dk=128, dv=128)
+        a.update(kw)
+        return L.kda_decode_step_prologue(a["q"], a["k"], a["v"], a["z"], a["beta"], BF16, a["A"], -5.0, a["S"],
+                                          a["o"], BF16, a["N"], a["H"], a["dk"], a["dv"], 1.0, N)
+    assert dec(beta=None) == ERR_NULL
+    assert dec(dv=24) == ERR_UNSUPPORTED
+    assert dec(o=P(6)) == ERR_ALIAS
+    assert dec(N=0) == OK
