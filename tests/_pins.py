@@ -504,4 +504,124 @@ def pin_prologue_forward(orc):
     np.testing.assert_allclose(Sd, S, rtol=0, atol=1e-12)
 
 
+# ----------------------------------------------------------------------------
+# backward (oracle.backward): the derivative of the forward
+# ----------------------------------------------------------------------------
+def _bwd_case(rng, B=2, T=7, H=2, dk=5, dv=4):
+    q = rng.standard_normal((B, T, H, dk)) * 0.5
+    k = rng.standard_normal((B, T, H, dk)) * 0.4
+    v = rng.standard_normal((B, T, H, dv))
+    beta = rng.uniform(0.1, 0.9, (B, T, H))
+    z = rng.standard_normal((B, T, H, dk))
+    A = rng.standard_normal((H, dk)) * 0.5
+    S0 = rng.standard_normal((B, H, dk, dv)) * 0.5
+    return dict(q=q, k=k, v=v, beta=beta, z=z, A=A, S0=S0)
+
+
+def pin_backward_finite_differences(orc):
+    """Every gradient of the backward against central finite differences of the
+    C forward (an independent implementation): for L = sum(w_o o) + sum(w_S S_T)
+    and a random direction d in each input, (L(x + eps d) - L(x - eps d)) / 2 eps
+    equals <grad, d>.  The CPU laboratory of "architecture, derivations and a
+    pinned-source audit" checks its analytic state derivative the same way."""
+    import oracle.backward as OB
+    rng = np.random.default_rng(51)
+    c = _bwd_case(rng)
+    scale = 0.7
+    o, S = orc.forward_z(c["q"], c["k"], c["v"], c["beta"], c["z"], c["A"], -5.0, c["S0"], scale)
+    w_o = rng.standard_normal(o.shape)
+    w_S = rng.standard_normal(S.shape)
+    g = OB.backward_z(c["q"], c["k"], c["v"], c["beta"], c["z"], c["A"], w_o, w_S, -5.0, c["S0"], scale)
+    names = {"q": "dq", "k": "dk", "v": "dv", "beta": "dbeta", "z": "dz", "A": "dA", "S0": "dS_in"}
+    eps = 1e-6
+    for x, gname in names.items():
+        d = rng.standard_normal(c[x].shape)
+        lo = dict(c)
+        hi = dict(c)
+        lo[x] = c[x] - eps * d
+        hi[x] = c[x] + eps * d
+        Lh = OB.loss(*orc.forward_z(hi["q"], hi["k"], hi["v"], hi["beta"], hi["z"], hi["A"], -5.0, hi["S0"], scale),
+                     w_o, w_S)
+        Ll = OB.loss(*orc.forward_z(lo["q"], lo["k"], lo["v"], lo["beta"], lo["z"], lo["A"], -5.0, lo["S0"], scale),
+                     w_o, w_S)
+        fd = (Lh - Ll) / (2 * eps)
+        an = float(np.sum(g[gname] * d))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (x, fd, an)
+
+
+def pin_backward_state_derivative_printed(orc):
+    """The CPU laboratory's analytic derivative ("architecture, derivations and a
+    pinned-source audit"): for one step S_1 = M S_0 + U with M = (I - beta k k^T)
+    Diag(alpha) and U = beta k v^T, the gradient of sum(S_1^2) with respect to S_0
+    is 2 M^T (M S_0 + U)."""
+    import oracle.backward as OB
+    rng = np.random.default_rng(52)
+    c = _bwd_case(rng, B=1, T=1, H=1, dk=4, dv=3)
+    f = OB.forward_states(c["q"], c["k"], c["v"], c["beta"], c["z"], c["A"], -5.0, c["S0"])
+    S1 = f["S"][1]
+    g = OB.backward_z(c["q"], c["k"], c["v"], c["beta"], c["z"], c["A"], np.zeros((1, 1, 1, 3)), 2.0 * S1, -5.0,
+                      c["S0"])
+    k = c["k"][0, 0, 0]
+    b = c["beta"][0, 0, 0]
+    alpha = f["alpha"][0, 0, 0]
+    M = (np.eye(4) - b * np.outer(k, k)) @ np.diag(alpha)
+    U = b * np.outer(k, c["v"][0, 0, 0])
+    expected = 2 * M.T @ (M @ c["S0"][0, 0] + U)
+    np.testing.assert_allclose(g["dS_in"][0, 0], expected, rtol=0, atol=1e-13)
+
+
+def pin_backward_autograd(orc):
+    """Every gradient against torch's reverse-mode automatic differentiation (fp64,
+    CPU) of the same forward written as plain tensor operations, and the
+    backward's own forward against the C oracle."""
+    import torch
+    import oracle.backward as OB
+    rng = np.random.default_rng(53)
+    c = _bwd_case(rng, B=2, T=9, H=3, dk=6, dv=5)
+    scale = 1.3
+    t = {n: torch.tensor(a, dtype=torch.float64, requires_grad=True) for n, a in c.items()}
+    S = t["S0"]
+    outs = []
+    for i in range(c["q"].shape[1]):
+        a = torch.exp(-5.0 * torch.sigmoid(torch.exp(t["A"]) * t["z"][:, i]))     # [B, H, dk]
+        D = a[..., None] * S
+        e = t["v"][:, i] - torch.einsum("bhc,bhcj->bhj", t["k"][:, i], D)
+        S = D + t["beta"][:, i, :, None, None] * t["k"][:, i, :, :, None] * e[:, :, None, :]
+        outs.append(scale * torch.einsum("bhcj,bhc->bhj", S, t["q"][:, i]))
+    o = torch.stack(outs, dim=1)
+    w_o = torch.tensor(rng.standard_normal(tuple(o.shape)), dtype=torch.float64)
+    w_S = torch.tensor(rng.standard_normal(tuple(S.shape)), dtype=torch.float64)
+    (torch.sum(w_o * o) + torch.sum(w_S * S)).backward()
+    g = OB.backward_z(c["q"], c["k"], c["v"], c["beta"], c["z"], c["A"], w_o.numpy(), w_S.numpy(), -5.0, c["S0"],
+                      scale)
+    for n, gname in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("beta", "dbeta"), ("z", "dz"), ("A", "dA"),
+                     ("S0", "dS_in")):
+        np.testing.assert_allclose(g[gname], t[n].grad.numpy(), rtol=0, atol=1e-11, err_msg=n)
+    oc, Sc = orc.forward_z(c["q"], c["k"], c["v"], c["beta"], c["z"], c["A"], -5.0, c["S0"], scale)
+    np.testing.assert_allclose(g["o"], oc, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(g["S_T"], Sc, rtol=0, atol=1e-12)
+
+
+def pin_backward_special_cases(orc):
+    """beta = 0 leaves only the decay, so nothing flows to v and k (dv = dk = 0);
+    with every cotangent zero every gradient is zero; gradients are linear in
+    the cotangents (do, dS_out)."""
+    import oracle.backward as OB
+    rng = np.random.default_rng(54)
+    c = _bwd_case(rng)
+    w1 = rng.standard_normal((2, 7, 2, 4))
+    w2 = rng.standard_normal((2, 7, 2, 4))
+    s1 = rng.standard_normal((2, 2, 5, 4))
+    b0 = OB.backward_z(c["q"], c["k"], c["v"], np.zeros_like(c["beta"]), c["z"], c["A"], w1, s1, -5.0, c["S0"])
+    assert np.array_equal(b0["dv"], np.zeros_like(c["v"])) and np.array_equal(b0["dk"], np.zeros_like(c["k"]))
+    z0 = OB.backward_z(c["q"], c["k"], c["v"], c["beta"], c["z"], c["A"], np.zeros_like(w1), None, -5.0, c["S0"])
+    for key in ("dq", "dk", "dv", "dbeta", "dz", "dA", "dS_in"):
+        assert np.array_equal(z0[key], np.zeros_like(z0[key]))
+    ga = OB.backward_z(c["q"], c["k"], c["v"], c["beta"], c["z"], c["A"], w1, s1, -5.0, c["S0"])
+    gb = OB.backward_z(c["q"], c["k"], c["v"], c["beta"], c["z"], c["A"], w2, None, -5.0, c["S0"])
+    gs = OB.backward_z(c["q"], c["k"], c["v"], c["beta"], c["z"], c["A"], 2 * w1 - 3 * w2, 2 * s1, -5.0, c["S0"])
+    for key in ("dq", "dk", "dv", "dbeta", "dz", "dA", "dS_in"):
+        np.testing.assert_allclose(gs[key], 2 * ga[key] - 3 * gb[key], rtol=0, atol=1e-11)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -96,3 +96,42 @@ def test_prologue_mutation_is_caught(name, monkeypatch):
         except AssertionError:
             failed.append(pin.__name__)
     assert failed, f"prologue mutation {name} passed every prologue pin"
+
+
+# The backward oracle (oracle/backward.py) is numpy code: plant its plausible
+# mistakes in a copy of its source text, load that copy in place of the module's
+# backward_z, and require a backward pin to fail.
+import oracle.backward as _OB  # noqa: E402
+
+BWD_SRC = open(_OB.__file__).read()
+BACKWARD_MUTATIONS = {
+    "dq_without_scale": [("dq[:, t] = scale * np.einsum", "dq[:, t] = np.einsum")],
+    "dq_reads_old_state": [('np.einsum("bhcj,bhj->bhc", St, do[:, t])', 'np.einsum("bhcj,bhj->bhc", Sp, do[:, t])')],
+    "dk_without_erase_term": [('        dkt = dkt - np.einsum("bhcj,bhj->bhc", D, de)\n', "")],
+    "dD_sign": [("dD = dS - kt[:, :, :, None]", "dD = dS + kt[:, :, :, None]")],
+    "dS_without_decay": [("dS = alpha[:, t, :, :, None] * dD", "dS = dD")],
+    "dbeta_without_e": [('np.einsum("bhc,bhcj,bhj->bh", kt, dS, e)', 'np.einsum("bhc,bhcj->bh", kt, dS)')],
+    "sigmoid_prime_missing": [("sig[:, t] * (1.0 - sig[:, t]) * dg", "sig[:, t] * dg")],
+    "dA_without_z": [('np.einsum("bthc,bthc->hc", dx, z) * eA', "np.sum(dx, axis=(0, 1)) * eA")],
+    "dv_sign": [("dv_[:, t] = de", "dv_[:, t] = -de")],
+}
+
+
+@pytest.mark.parametrize("name", sorted(BACKWARD_MUTATIONS))
+def test_backward_mutation_is_caught(name, monkeypatch):
+    src = BWD_SRC
+    for old, new in BACKWARD_MUTATIONS[name]:
+        assert src.count(old) == 1, f"mutation anchor not unique/found: {old!r}"
+        src = src.replace(old, new)
+    ns = {"__name__": "oracle_backward_mutant"}
+    exec(compile(src, f"<{name}>", "exec"), ns)
+    monkeypatch.setattr(_OB, "backward_z", ns["backward_z"])
+    failed = []
+    for pin in _pins.ALL_PINS:
+        if not pin.__name__.startswith("pin_backward"):
+            continue
+        try:
+            pin(oracle.default())
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"backward mutation {name} passed every backward pin"
