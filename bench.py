@@ -229,6 +229,31 @@ def main():
                     "vs_plain_prefill": round(pro_ms / float(np.mean(pre_ms)), 4)}
         log(f"fused-prologue prefill: {pro_ms:.3f} ms ({prologue['vs_plain_prefill']:.3f} x the plain prefill)")
 
+    # ---------------- backward (reported beside the step, not part of it) ----------------
+    # Gradients of the 32K prefill for an upstream gradient of the outputs (the resident
+    # outputs stand in for it): the checkpointing forward plus the backward kernel.
+    backward = None
+    if run_pre:
+        bw_ws = torch.empty(kda.lib().kda_chunk_bwd_z_workspace_bytes(ps.B, ps.T, ps.H, ps.dk, ps.dv),
+                            dtype=torch.uint8, device=dev)
+
+        def bwd():
+            kda.chunk_bwd_z(P["q"], P["k"], P["v"], P["beta"], P["z"], P["A"], o_pre, None, -5.0, P["S0"],
+                            workspace=bw_ws, stream=stream)
+        bwd()
+        bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(3)]
+        for r0, r1 in bev:
+            r0.record(stream)
+            bwd()
+            r1.record(stream)
+        torch.cuda.synchronize()
+        bw_ms = float(np.mean([r0.elapsed_time(r1) for r0, r1 in bev]))
+        backward = {"ms": round(bw_ms, 3), "tokens_per_s": round(ps.B * ps.T / (bw_ms / 1e3), 1),
+                    "vs_forward_prefill": round(bw_ms / float(np.mean(pre_ms)), 2)}
+        log(f"backward: {bw_ms:.2f} ms ({backward['vs_forward_prefill']:.1f} x the forward prefill)")
+        del bw_ws
+        torch.cuda.empty_cache()
+
     # ---------------- 1M-token prefill (reported beside the step, not part of it) ----------------
     # B=1, H=8, T=2^20: one pass of the chunk kernel has 8 sequences for 256 compute units;
     # the segment-parallel form runs 16 segments per sequence side by side.
@@ -348,6 +373,7 @@ def main():
         "replay": replay,
         "long_context": long_ctx,
         "prologue": prologue,
+        "backward": backward,
     }
     # a profiling run that timed one path reports nothing for the other
     if not run_dec:

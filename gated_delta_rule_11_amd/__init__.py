@@ -62,6 +62,11 @@ def lib() -> ctypes.CDLL:
     L.kda_chunk_fwd_z_prologue.restype = I
     L.kda_decode_step_prologue.argtypes = L.kda_decode_step.argtypes
     L.kda_decode_step_prologue.restype = I
+    L.kda_chunk_bwd_z_workspace_bytes.argtypes = [I, I, I, I, I]
+    L.kda_chunk_bwd_z_workspace_bytes.restype = ctypes.c_size_t
+    L.kda_chunk_bwd_z.argtypes = [P, P, P, P, P, I, P, F, P, P, I, P, P, P, P, P, P, P, P, I, I, I, I, I, F, P,
+                                  ctypes.c_size_t, P]
+    L.kda_chunk_bwd_z.restype = I
     L.kda_chunk_fwd_z_segmented_workspace_bytes.argtypes = [I, I, I, I, I]
     L.kda_chunk_fwd_z_segmented_workspace_bytes.restype = ctypes.c_size_t
     L.kda_chunk_fwd_z_segmented.argtypes = [P, P, P, P, P, I, P, F, P, P, I, P, I, I, I, I, I, I, F, I, P,
@@ -188,6 +193,34 @@ def decode_step_prologue(q_raw, k_raw, v, z, beta_logit, A, S, g_min: float = G_
                                           _p(A), float(g_min), _p(S), _p(o), _dtype_code(o), N, H, dk, dv,
                                           float(scale), _stream(stream)), "kda_decode_step_prologue")
     return o
+
+
+def chunk_bwd_z(q, k, v, beta, z, A, d_o, dS_out=None, g_min: float = G_MIN, S_in=None, scale: float = 1.0,
+                want_dS_in: bool = True, workspace=None, stream=None) -> dict:
+    """Backward of ``chunk_fwd_z``: gradients (fp32) of a loss given dL/do (``d_o``)
+    and optionally dL/dS_out.  Returns a dict with dq, dk, dv, dbeta, dz, dA and
+    dS_in (None unless ``want_dS_in``)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    f32 = torch.float32
+    out = {"dq": torch.empty((B, T, H, dk), dtype=f32, device=dev),
+           "dk": torch.empty((B, T, H, dk), dtype=f32, device=dev),
+           "dv": torch.empty((B, T, H, dv), dtype=f32, device=dev),
+           "dbeta": torch.empty((B, T, H), dtype=f32, device=dev),
+           "dz": torch.empty((B, T, H, dk), dtype=f32, device=dev),
+           "dA": torch.empty((H, dk), dtype=f32, device=dev),
+           "dS_in": torch.empty((B, H, dk, dv), dtype=f32, device=dev) if want_dS_in else None}
+    need = int(lib().kda_chunk_bwd_z_workspace_bytes(B, T, H, dk, dv))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _dev(q, k, v, beta, z, A, d_o, dS_out, S_in, workspace, *[t for t in out.values() if t is not None])
+    _check(lib().kda_chunk_bwd_z(_p(q), _p(k), _p(v), _p(beta), _p(z), _dtype_code(q), _p(A), float(g_min), _p(S_in),
+                                 _p(d_o), _dtype_code(d_o), _p(dS_out), _p(out["dq"]), _p(out["dk"]), _p(out["dv"]),
+                                 _p(out["dbeta"]), _p(out["dz"]), _p(out["dA"]), _p(out["dS_in"]), B, T, H, dk, dv,
+                                 float(scale), _p(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(stream)), "kda_chunk_bwd_z")
+    return out
 
 
 def chunk_fwd_z_segmented_workspace_bytes(B: int, H: int, dk: int, dv: int, segments: int) -> int:

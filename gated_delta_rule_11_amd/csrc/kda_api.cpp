@@ -196,6 +196,64 @@ kda_status kda_chunk_fwd_z_segmented(const void* q, const void* k, const void* v
                       scale, true, stream, segments, workspace, workspace_bytes);
 }
 
+size_t kda_chunk_bwd_z_workspace_bytes(int B, int T, int H, int dk, int dv) {
+  if (B < 0 || T < 0 || H < 0 || dk < 0 || dv < 0) return 0;
+  const size_t bh = size_t(B) * size_t(H), sz = size_t(dk) * size_t(dv);
+  const size_t nblk = (size_t(T) + 63) / 64;
+  return (bh * (nblk + 3) * sz + bh * size_t(dk)) * 4;
+}
+
+kda_status kda_chunk_bwd_z(const void* q, const void* k, const void* v, const void* beta, const void* z,
+                           kda_dtype in_dtype, const float* A, float g_min, const float* S_in, const void* d_o,
+                           kda_dtype do_dtype, const float* dS_out, float* dq, float* dk_, float* dv_, float* dbeta,
+                           float* dz, float* dA, float* dS_in, int B, int T, int H, int dk, int dv, float scale,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(in_dtype) || !dtype_ok(do_dtype)) return KDA_ERR_DTYPE;
+  if (!sizes_ok(B, T, H, dk, dv)) return KDA_ERR_SHAPE;
+  if (!dim_ok(dk) || !dim_ok(dv)) return KDA_ERR_UNSUPPORTED;
+  if (!isfinite(scale) || !isfinite(g_min) || g_min > 0.f || g_min < -5.f) return KDA_ERR_UNSUPPORTED;
+  const int64_t ntok = int64_t(B) * T * H, bh = int64_t(B) * H;
+  if (bh == 0) return KDA_OK;
+  if (!A || !dA) return KDA_ERR_NULL;
+  if (ntok > 0 && (!q || !k || !v || !beta || !z || !d_o || !dq || !dk_ || !dv_ || !dbeta || !dz))
+    return KDA_ERR_NULL;
+  if (!workspace) return KDA_ERR_NULL;
+  if (!all_aligned({q, k, v, z, A, S_in, d_o, dS_out, dq, dk_, dv_, dz, dA, dS_in, workspace}, beta,
+                   esize(in_dtype)) ||
+      !aligned(dbeta, 4))
+    return KDA_ERR_ALIGN;
+  if (workspace_bytes < kda_chunk_bwd_z_workspace_bytes(B, T, H, dk, dv)) return KDA_ERR_WORKSPACE;
+  const int64_t ein = esize(in_dtype), edo = esize(do_dtype), nstate = bh * dk * dv;
+  const Range ins[] = {{q, ntok * dk * ein}, {k, ntok * dk * ein}, {v, ntok * dv * ein}, {beta, ntok * ein},
+                       {z, ntok * dk * ein}, {A, int64_t(H) * dk * 4}, {S_in, nstate * 4}, {d_o, ntok * dv * edo},
+                       {dS_out, nstate * 4}};
+  const Range outs[] = {{dq, ntok * dk * 4}, {dk_, ntok * dk * 4}, {dv_, ntok * dv * 4}, {dbeta, ntok * 4},
+                        {dz, ntok * dk * 4}, {dA, int64_t(H) * dk * 4}, {dS_in, nstate * 4},
+                        {workspace, int64_t(kda_chunk_bwd_z_workspace_bytes(B, T, H, dk, dv))}};
+  for (const Range& o : outs) {
+    for (const Range& in : ins)
+      if (overlap(o, in)) return KDA_ERR_ALIAS;
+    for (const Range& o2 : outs)
+      if (&o2 != &o && overlap(o, o2)) return KDA_ERR_ALIAS;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t nblk = (int64_t(T) + 63) / 64;
+  float* ckpt = static_cast<float*>(workspace);
+  float* scratch = ckpt + bh * nblk * dk * dv;
+  float* dA_part = scratch + bh * 3 * dk * dv;
+  // forward pass that only leaves the state entering every 64-token block
+  kda::ChunkArgs f{};
+  f.q = q; f.k = k; f.v = v; f.beta = beta; f.z = z; f.A = A; f.g_min = g_min; f.S_in = S_in;
+  f.o = dq;  // never written (outputs skipped)
+  f.S_out = nullptr; f.B = B; f.T = T; f.H = H; f.dk = dk; f.dv = dv; f.chunk = 64; f.scale = scale;
+  f.in_bf16 = in_dtype == KDA_BF16; f.out_bf16 = false; f.from_z = true; f.o_skip = true; f.S_ckpt = ckpt;
+  hipError_t e = kda::chunk_mfma_supports(f) ? kda::launch_chunk_mfma(f, st) : kda::launch_chunk_generic(f, st);
+  if (e != hipSuccess) return from_hip(e);
+  kda::BwdArgs bwa{q, k, v, beta, z, A, g_min, d_o, dS_out, ckpt, scratch, dA_part, dq, dk_, dv_, dbeta, dz, dA,
+                   dS_in, B, T, H, dk, dv, scale, in_dtype == KDA_BF16, do_dtype == KDA_BF16};
+  return from_hip(kda::launch_chunk_bwd(bwa, st));
+}
+
 kda_status kda_chunk_fwd_z_prologue(const void* q, const void* k, const void* v, const void* beta_logit,
                                     const void* z, kda_dtype in_dtype, const float* A, float g_min,
                                     const float* S_in, void* o, kda_dtype o_dtype, float* S_out, int B, int T, int H,

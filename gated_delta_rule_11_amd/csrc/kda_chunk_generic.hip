@@ -78,6 +78,10 @@ __global__ __launch_bounds__(NT) void chunk_generic_kernel(const ChunkArgs a) {
 
   for (int t0 = 0; t0 < a.T; t0 += SC) {
     const int n = min(SC, a.T - t0);
+    if (a.S_ckpt && t0 % 64 == 0) {  // backward checkpoint: the state entering this 64-token block
+      float* ck = a.S_ckpt + (static_cast<int64_t>(bh) * ((a.T + 63) / 64) + t0 / 64) * DK * a.dv;
+      for (int e = tid; e < DK * DVS; e += NT) ck[(e / DVS) * a.dv + j0 + e % DVS] = Ss[e / DVS][e % DVS];
+    }
     // 1. load the sub-chunk; Gl = log2-decay summed from the sub-chunk start
     for (int e = tid; e < SC * DK; e += NT) {
       const int i = e / DK, c = e % DK;
@@ -183,7 +187,7 @@ __global__ __launch_bounds__(NT) void chunk_generic_kernel(const ChunkArgs a) {
     // 6. o = scale ((Q * 2^Gl) S + P U)
     for (int e = tid; e < SC * DVS; e += NT) {
       const int i = e / DVS, j = e % DVS;
-      if (i < n) {
+      if (i < n && !a.o_skip) {
         float acc = 0.f;
         for (int c = 0; c < DK; ++c) acc += Qs[i][c] * fast_exp2(Gl[i][c]) * Ss[c][j];
         for (int s = 0; s <= i; ++s) acc += Pm[i][s] * Us[s][j];

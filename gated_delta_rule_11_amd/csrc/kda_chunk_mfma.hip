@@ -409,6 +409,13 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
       const int64_t row0 = (static_cast<int64_t>(b) * T + t0) * H + h;
       const int64_t span = static_cast<int64_t>(n - 1) * H + 1;
 
+      if (SEG && a.S_ckpt && owns_v) {  // backward checkpoint: the state entering this chunk
+        float* ck = a.S_ckpt + (static_cast<int64_t>(bh) * nch_all + ch) * DK * DK;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) ck[(16 * ct + 4 * g4 + v) * DK + j0 + 16 * wv + r16] = S[ct][v];
+      }
       lds_barrier();  // B
       relane();
 
@@ -850,7 +857,7 @@ static hipError_t launch_mfma_t(const ChunkArgs& a, hipStream_t st, int ns) {
 template <int DVS>
 static hipError_t launch_mfma_d(const ChunkArgs& a, hipStream_t st, int ns) {
   const bool seg = a.nseg > 1 || a.seg_chunks > 0 || a.S_in_seg || a.S_out_mode != 0 || a.S_identity ||
-                   a.v_zero || a.o_skip;
+                   a.v_zero || a.o_skip || a.S_ckpt;
   if (a.prologue) {  // fused prologue: fused gate, one pass
     if (!a.from_z || seg) return hipErrorNotSupported;
     return a.out_bf16 ? launch_mfma_t<DVS, true, bf16_t, false, true>(a, st, ns)

@@ -40,6 +40,9 @@ struct ChunkArgs {
   bool o_skip = false;      // outputs are not written
   // Fused prologue: q, k un-normalised and beta a logit (normalised / sigmoid in-kernel).
   bool prologue = false;
+  // Checkpoints for the backward pass: the state entering every 64-token block,
+  // [B, H, ceil(T / 64), dk, dv] (MFMA path: segment instantiation, one segment).
+  float* S_ckpt = nullptr;
 };
 
 struct DecodeArgs {
@@ -91,6 +94,25 @@ struct SegScanArgs {
 };
 
 hipError_t launch_segscan(const SegScanArgs& a, hipStream_t st);
+
+// Backward pass of the fused-gate prefill (fp32 gradients).
+struct BwdArgs {
+  const void *q, *k, *v, *beta, *z;  // [B, T, H, d], beta [B, T, H]
+  const float* A;                    // [H, dk]
+  float g_min;
+  const void* d_o;                   // [B, T, H, dv]
+  const float* dS_out;               // [B, H, dk, dv] or nullptr
+  const float* ckpt;                 // [B, H, nblk, dk, dv]: state entering each 64-token block
+  float* scratch;                    // [B, H, 3, dk, dv]: states entering sub-chunks 1..3 of a block
+  float* dA_part;                    // [B, H, dk]
+  float *grad_q, *grad_k, *grad_v, *grad_beta, *grad_z;  // fp32 gradients, layouts of the inputs
+  float* grad_A;                                          // [H, dk]
+  float* grad_S_in;                                       // [B, H, dk, dv] or nullptr
+  int B, T, H, dk, dv;
+  float scale;
+  bool in_bf16, do_bf16;
+};
+hipError_t launch_chunk_bwd(const BwdArgs& a, hipStream_t st);
 hipError_t launch_gate(const GateArgs& a, hipStream_t st);
 hipError_t launch_replay(const ReplayArgs& a, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);

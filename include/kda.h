@@ -178,6 +178,37 @@ kda_status kda_decode_step_prologue(const void* q, const void* k, const void* v,
                                     float scale, void* stream);
 
 /*
+ * kda_chunk_bwd_z -- backward pass of kda_chunk_fwd_z (training).
+ *
+ * Given the forward's inputs and dL/do (d_o [B,T,H,dv], dtype do_dtype) and
+ * optionally dL/dS_out (dS_out [B,H,dk,dv] fp32, NULL = the final state does not
+ * enter the loss), writes the gradients of L with respect to every input, in
+ * fp32, in the layouts of the inputs: dq, dk, dz [B,T,H,dk]; dv [B,T,H,dv];
+ * dbeta [B,T,H]; dA [H,dk] (summed over batch and tokens); dS_in [B,H,dk,dv]
+ * (may be NULL).  S_in may be NULL (zero state), as in the forward.
+ *
+ * The derivative is the chain rule of the forward recurrence ("Kimi K3: the
+ * paper and proofs side by side", section 2.1.1, Equation 1, and the bounded
+ * gate of "Kimi K3 reading notes", section 2), computed chunkwise: a forward
+ * pass keeps the state entering every 64-token block in the workspace, then
+ * one workgroup per (b, h) walks the blocks backwards in 16-token sub-chunks,
+ * in fp32 (matrix cores with fp32 operands).
+ *
+ * Supported: dk, dv in {16, 32, 64, 128}; in_dtype, do_dtype in {f32, bf16};
+ * g_min in [-5, 0] (16 g_min >= -80 keeps every in-sub-chunk decay ratio in
+ * the fp32 range).  workspace: caller-owned device memory, 16-byte aligned, of
+ * kda_chunk_bwd_z_workspace_bytes(B, T, H, dk, dv) bytes; contents on entry do
+ * not matter.  No output may overlap an input, another output or the workspace.
+ */
+size_t kda_chunk_bwd_z_workspace_bytes(int B, int T, int H, int dk, int dv);
+kda_status kda_chunk_bwd_z(const void* q, const void* k, const void* v, const void* beta, const void* z,
+                           kda_dtype in_dtype, const float* A, float g_min, const float* S_in,
+                           const void* d_o, kda_dtype do_dtype, const float* dS_out, float* dq, float* dk,
+                           float* dv, float* dbeta, float* dz, float* dA, float* dS_in, int B, int T, int H,
+                           int dk_dim, int dv_dim, float scale, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
  * kda_chunk_fwd_z_segmented -- kda_chunk_fwd_z for few, long sequences.
  *
  * Same inputs, outputs and result as kda_chunk_fwd_z (within the bf16

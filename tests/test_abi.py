@@ -35,6 +35,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("kda_gate", "kda_chunk_fwd", "kda_chunk_fwd_z", "kda_decode_step", "kda_decode_replay",
               "kda_chunk_fwd_z_prologue", "kda_decode_step_prologue", "kda_chunk_fwd_z_segmented",
+              "kda_chunk_bwd_z",
               "kda_status_string"):
         assert n in names
 
@@ -221,3 +222,26 @@ def test_prologue_validation(L):
     assert dec(dv=24) == ERR_UNSUPPORTED
     assert dec(o=P(6)) == ERR_ALIAS
     assert dec(N=0) == OK
+
+
+def test_backward_validation(L):
+    need = L.kda_chunk_bwd_z_workspace_bytes(2, 100, 3, 64, 32)
+    assert need == (2 * 3 * (2 + 3) * 64 * 32 + 2 * 3 * 64) * 4
+
+    def bwd(**kw):
+        a = dict(q=P(0), k=P(1), v=P(2), beta=P(3), z=P(4), A=P(5), S_in=None, do=P(6), dS_out=None, dq=P(7),
+                 dk=P(8), dv=P(9), dbeta=P(10), dz=P(11), dA=P(12), dS_in=None, B=2, T=100, H=3, dk_=64, dv_=32,
+                 gmin=-5.0, ws=P(13), wsb=need, it=F32)
+        a.update(kw)
+        return L.kda_chunk_bwd_z(a["q"], a["k"], a["v"], a["beta"], a["z"], a["it"], a["A"], a["gmin"], a["S_in"],
+                                 a["do"], F32, a["dS_out"], a["dq"], a["dk"], a["dv"], a["dbeta"], a["dz"], a["dA"],
+                                 a["dS_in"], a["B"], a["T"], a["H"], a["dk_"], a["dv_"], 1.0, a["ws"], a["wsb"], N)
+    assert bwd(dq=None) == ERR_NULL
+    assert bwd(ws=None) == ERR_NULL
+    assert bwd(wsb=need - 4) == ERR_WORKSPACE
+    assert bwd(gmin=-5.5) == ERR_UNSUPPORTED       # the backward needs 16 g_min >= -80
+    assert bwd(dk_=48) == ERR_UNSUPPORTED
+    assert bwd(dq=P(0)) == ERR_ALIAS               # gradient over an input
+    assert bwd(dk=P(7)) == ERR_ALIAS               # two gradients on one buffer
+    assert bwd(ws=P(11)) == ERR_ALIAS              # workspace over a gradient
+    assert bwd(B=0) == OK
