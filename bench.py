@@ -214,9 +214,12 @@ def main():
     # work does not depend on their values).
     prologue = None
     if run_pre:
+        o_pro = torch.empty_like(o_pre)  # its own outputs: o_pre and S_pre are checked against the oracle below
+        S_pro = torch.empty_like(S_pre)
+
         def pro():
             kda.chunk_fwd_z_prologue(P["q"], P["k"], P["v"], P["beta"], P["z"], P["A"], -5.0, ps.chunk,
-                                     S_in=P["S0"], o=o_pre, S_out=S_pre, stream=stream)
+                                     S_in=P["S0"], o=o_pro, S_out=S_pro, stream=stream)
         pro()
         pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
         for r0, r1 in pev:
@@ -228,6 +231,7 @@ def main():
         prologue = {"ms": round(pro_ms, 4), "tokens_per_s": round(ps.B * ps.T / (pro_ms / 1e3), 1),
                     "vs_plain_prefill": round(pro_ms / float(np.mean(pre_ms)), 4)}
         log(f"fused-prologue prefill: {pro_ms:.3f} ms ({prologue['vs_plain_prefill']:.3f} x the plain prefill)")
+        del o_pro, S_pro
 
     # ---------------- backward (reported beside the step, not part of it) ----------------
     # Gradients of the 32K prefill for an upstream gradient of the outputs (the resident

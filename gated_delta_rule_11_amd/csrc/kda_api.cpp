@@ -200,7 +200,9 @@ size_t kda_chunk_bwd_z_workspace_bytes(int B, int T, int H, int dk, int dv) {
   if (B < 0 || T < 0 || H < 0 || dk < 0 || dv < 0) return 0;
   const size_t bh = size_t(B) * size_t(H), sz = size_t(dk) * size_t(dv);
   const size_t nblk = (size_t(T) + 63) / 64;
-  return (bh * (nblk + 3) * sz + bh * size_t(dk)) * 4;
+  const size_t nsp = size_t(kda::chunk_bwd_slices(B, H, dv));
+  const size_t parts = nsp == 2 ? bh * size_t(T) * (3 * size_t(dk) + 1) : 0;  // second slice's key-side parts
+  return (bh * (nblk + 3) * sz + bh * nsp * size_t(dk) + parts) * 4;
 }
 
 kda_status kda_chunk_bwd_z(const void* q, const void* k, const void* v, const void* beta, const void* z,
@@ -241,6 +243,8 @@ kda_status kda_chunk_bwd_z(const void* q, const void* k, const void* v, const vo
   float* ckpt = static_cast<float*>(workspace);
   float* scratch = ckpt + bh * nblk * dk * dv;
   float* dA_part = scratch + bh * 3 * dk * dv;
+  const int nsp = kda::chunk_bwd_slices(B, H, dv);
+  float* parts = dA_part + bh * nsp * dk;
   // forward pass that only leaves the state entering every 64-token block
   kda::ChunkArgs f{};
   f.q = q; f.k = k; f.v = v; f.beta = beta; f.z = z; f.A = A; f.g_min = g_min; f.S_in = S_in;
@@ -251,6 +255,12 @@ kda_status kda_chunk_bwd_z(const void* q, const void* k, const void* v, const vo
   if (e != hipSuccess) return from_hip(e);
   kda::BwdArgs bwa{q, k, v, beta, z, A, g_min, d_o, dS_out, ckpt, scratch, dA_part, dq, dk_, dv_, dbeta, dz, dA,
                    dS_in, B, T, H, dk, dv, scale, in_dtype == KDA_BF16, do_dtype == KDA_BF16};
+  if (nsp == 2) {
+    bwa.part_q = parts;
+    bwa.part_k = parts + ntok * dk;
+    bwa.part_z = parts + 2 * ntok * dk;
+    bwa.part_beta = parts + 3 * ntok * dk;
+  }
   return from_hip(kda::launch_chunk_bwd(bwa, st));
 }
 

@@ -61,28 +61,54 @@ struct Layout {
                        DP = TT + 16 * RS, DT0 = DP + 16 * RS, DT1 = DT0 + 16 * RS, DM = DT1 + 16 * RS,
                        Y = DM + 16 * RS, DAL = Y + 16 * RS;
   // vectors
-  static constexpr int BETA = DAL + 16 * RS, GL = BETA + 16, DGL = GL + DK;
-  static constexpr int FLOATS = DGL + DK;
+  static constexpr int BETA = DAL + 16 * RS, GL = BETA + 16, DGL = GL + DK, EA = DGL + DK;
+  // [16][RK]: sigma(e^A z) and e^A z of the sub-chunk, kept for the gate's derivative
+  static constexpr int SG = EA + DK, XZ = SG + 16 * RK;
+  static constexpr int FLOATS = XZ + 16 * RK;
   static constexpr int BYTES = FLOATS * 4;
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 }  // namespace bw
 
+// Four consecutive elements (16-byte aligned for fp32, 8-byte for bf16) as fp32.
+template <typename T> struct io4;
+template <> struct io4<float> {
+  __device__ __forceinline__ static f32x4 load(const float* p, int64_t i) {
+    return *reinterpret_cast<const f32x4*>(p + i);
+  }
+};
+template <> struct io4<bf16_t> {
+  __device__ __forceinline__ static f32x4 load(const bf16_t* p, int64_t i) {
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    const u32x2_t u = *reinterpret_cast<const u32x2_t*>(p + i);
+    return f32x4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u), __uint_as_float(u[1] << 16),
+                 __uint_as_float(u[1] & 0xffff0000u)};
+  }
+};
+
 __device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Workgroup barrier ordering LDS only: the next sub-chunk's inputs stay in flight across it.
 __device__ __forceinline__ void bw_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+// Workgroup barrier that also orders global memory (the recomputed states in the scratch).
+__device__ __forceinline__ void bw_barrier_global() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-template <int DK, int DV, typename Tin, typename Tdo>
+template <int DK, int DV, int NSP, typename Tin, typename Tdo>
 __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
   using namespace bw;
-  using Ly = Layout<DK, DV>;
-  constexpr int NKT = DK / 16, NVT = DV / 16;
+  constexpr int DVS = DV / NSP;  // value columns of this workgroup's slice
+  using Ly = Layout<DK, DVS>;
+  constexpr int NKT = DK / 16, NVT = DVS / 16;
   constexpr int RK = Ly::RK, RV = Ly::RV, RS = Ly::RS;
   extern __shared__ __attribute__((aligned(16))) float sm[];
   float* sKt = sm + Ly::KT;
@@ -101,7 +127,6 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
   float* sU = sm + Ly::U;
   float* sdU = sm + Ly::DU;
   float* sAL = sm + Ly::AL;
-  float* sL = sm + Ly::L;
   float* sP = sm + Ly::P;
   float* sM = sm + Ly::M;
   float* sT = sm + Ly::TT;
@@ -114,10 +139,14 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
   float* sBeta = sm + Ly::BETA;
   float* sGl = sm + Ly::GL;
   float* sdGl = sm + Ly::DGL;
+  float* sEA = sm + Ly::EA;
+  float* sSig = sm + Ly::SG;
+  float* sXz = sm + Ly::XZ;
 
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.x / NSP, sp = blockIdx.x % NSP;
   const int h = bh % a.H, b = bh / a.H;
   const int T = a.T, H = a.H;
+  const int j0 = sp * DVS;  // first value column of the slice
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // Lane coordinates are re-derived through an opaque copy after every barrier,
   // so that the LDS and global addresses built from them are formed where they
@@ -132,13 +161,15 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
     r16 = ln & 15;
   };
   relane();
-  const bool own_j = wv < NVT;  // value-column tile jt = wv (state by columns)
+  const bool own_j = wv < NVT;  // value-column tile jt = wv of the slice (state by columns)
   const bool own_c = wv < NKT;  // key-row tile ct = wv (state transposed)
   const int jt = wv, ct = wv;
+  // wavefronts with no value tile of their own take the 16 x 16 products
+  constexpr int W_DP = NW - 1, W_DT0 = NW - 2, W_DT1 = NW - 3;
   const int nblk = (T + CK - 1) / CK;
   const int64_t SZ = static_cast<int64_t>(DK) * DV;
   const float* ckpt = a.ckpt + static_cast<int64_t>(bh) * nblk * SZ;
-  float* scratch = a.scratch + static_cast<int64_t>(bh) * 3 * SZ;
+  float* scratch = a.scratch + static_cast<int64_t>(bh) * 3 * SZ;  // the slices write disjoint columns
   const Tin* q = static_cast<const Tin*>(a.q);
   const Tin* k = static_cast<const Tin*>(a.k);
   const Tin* v = static_cast<const Tin*>(a.v);
@@ -146,106 +177,189 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
   const Tin* beta = static_cast<const Tin*>(a.beta);
   const Tdo* d_o = static_cast<const Tdo*>(a.d_o);
   const float g_min = a.g_min;
+  // key-side gradients: the whole value range (one slice) or this slice's part of it
+  float* const gq = sp == 0 ? a.grad_q : a.part_q;
+  float* const gk = sp == 0 ? a.grad_k : a.part_k;
+  float* const gz = sp == 0 ? a.grad_z : a.part_z;
+  float* const gbeta = sp == 0 ? a.grad_beta : a.part_beta;
 
-  // state by value-column tile: Sc[ct'][v] = S[16 ct' + 4 g4 + v][16 jt + r16]
-  // state transposed by key-row tile: St[jt'][v] = S[16 ct + r16][16 jt' + 4 g4 + v]
+  // state by value-column tile: Sc[ct'][e] = S[16 ct' + 4 g4 + e][j0 + 16 jt + r16]
+  // state transposed by key-row tile: St[jt'][e] = S[16 ct + r16][j0 + 16 jt' + 4 g4 + e]
   f32x4 Sc[NKT], St[NVT], dSc[NKT], dSt[NVT];
   auto load_state = [&](const float* src, f32x4 (&C)[NKT], f32x4 (&Tr)[NVT]) {
 #pragma unroll
     for (int c2 = 0; c2 < NKT; ++c2)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) C[c2][e] = (own_j && src) ? src[(16 * c2 + 4 * g4 + e) * DV + 16 * jt + r16] : 0.f;
+      for (int e = 0; e < 4; ++e)
+        C[c2][e] = (own_j && src) ? src[(16 * c2 + 4 * g4 + e) * DV + j0 + 16 * jt + r16] : 0.f;
 #pragma unroll
     for (int j2 = 0; j2 < NVT; ++j2) {
       if (own_c && src) {
-        Tr[j2] = *reinterpret_cast<const f32x4*>(src + (16 * ct + r16) * DV + 16 * j2 + 4 * g4);
+        Tr[j2] = *reinterpret_cast<const f32x4*>(src + (16 * ct + r16) * DV + j0 + 16 * j2 + 4 * g4);
       } else {
         Tr[j2] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
   };
 
-  float dA_acc = 0.f;  // thread c < DK: this (b, h)'s part of dA[h][c]
-  const float eA = tid < DK ? __expf(a.A[h * DK + tid]) : 0.f;
+  float dA_acc = 0.f;  // thread c < DK: this workgroup's part of dA[h][c]
 
-  // ---- sub-chunk inputs into LDS; BWD also loads q and dO
-  auto load_sub = [&](int t0, int n, bool BWD) {
-    if (tid < DK) {  // key channel c: gate, running log-decay, scaled keys (and queries)
-      const int c = tid;
-      float G = 0.f;
-#pragma unroll 2
-      for (int t = 0; t < SC; ++t) {
-        const bool ok = t < n;
-        const int64_t row = (static_cast<int64_t>(b) * T + t0 + t) * H + h;
-        const float kv = ok ? io<Tin>::load(k, row * DK + c) : 0.f;
-        const float zv = ok ? io<Tin>::load(z, row * DK + c) : 0.f;
-        const float g = ok ? g_min / (1.f + __expf(-eA * zv)) : 0.f;
-        G += g;
-        const float Gm = __expf(G);
-        sKt[t * RK + c] = kv * Gm;
-        sKb[t * RK + c] = kv * __expf(-G);
-        sG[t * RK + c] = G;
-        if (BWD) sQt[t * RK + c] = (ok ? io<Tin>::load(q, row * DK + c) : 0.f) * Gm;
+  // ---- sub-chunk inputs.  The raw values of the next sub-chunk in processing order are
+  // loaded into registers while the current one is processed, four consecutive channels
+  // per load (token offsets clamped to the sub-chunk's last valid token, padding zeroed
+  // later: no branch around a load).
+  constexpr int NQK = SC * DK / 4, NQV = SC * DVS / 4;  // quads of the key side, the value side
+  static_assert(NQK <= NT && NQV <= NT, "one quad per thread");
+  f32x4 pk = {}, pz = {}, pq = {}, pv = {}, po = {};
+  float pb = 0.f;
+  auto fetch = [&](int t0, int n, bool BWD) {
+    {
+      const int e = min(tid, NQK - 1) * 4, t = e / DK, c = e % DK;
+      const int64_t row = (static_cast<int64_t>(b) * T + t0 + min(t, n - 1)) * H + h;
+      pk = io4<Tin>::load(k, row * DK + c);
+      pz = io4<Tin>::load(z, row * DK + c);
+      if (BWD) pq = io4<Tin>::load(q, row * DK + c);
+    }
+    {
+      const int e = min(tid, NQV - 1) * 4, t = e / DVS, j = e % DVS;
+      const int64_t row = (static_cast<int64_t>(b) * T + t0 + min(t, n - 1)) * H + h;
+      pv = io4<Tin>::load(v, row * DV + j0 + j);
+      if (BWD) po = io4<Tdo>::load(d_o, row * DV + j0 + j);
+    }
+    pb = io<Tin>::load(beta, (static_cast<int64_t>(b) * T + t0 + min(ln & 15, n - 1)) * H + h);
+  };
+  // the sub-chunk after (blk, s, BWD) in processing order: each block recomputes its
+  // sub-chunks 0 .. nsub-2 forwards, then runs nsub-1 .. 0 backwards; blocks go last first
+  auto nsub_of = [&](int blk) { return (min(CK, T - blk * CK) + SC - 1) / SC; };
+  auto fetch_after = [&](int blk, int s, bool BWD) {
+    const int ns = nsub_of(blk);
+    int nb = blk, nsb;
+    bool nbwd;
+    if (!BWD) {
+      nbwd = s + 1 >= ns - 1;
+      nsb = nbwd ? ns - 1 : s + 1;
+    } else if (s > 0) {
+      nbwd = true;
+      nsb = s - 1;
+    } else {
+      if (blk == 0) return;
+      nb = blk - 1;
+      const int ns2 = nsub_of(nb);
+      nbwd = ns2 == 1;
+      nsb = 0;  // its first recompute sub-chunk, or its only sub-chunk
+    }
+    const int t0 = nb * CK + nsb * SC;
+    fetch(t0, min(SC, T - t0), nbwd);
+  };
+
+  // ---- sub-chunk (blk, s) into LDS from the prefetched registers; BWD also takes q and dO.
+  // Three steps: every thread stores its elements and computes the gate; one thread per key
+  // channel sums the log-decay over the tokens; every thread scales its elements.
+  auto load_sub = [&](int blk, int s, int t0, int n, bool BWD) {
+    const f32x4 kv = pk, zv = pz, qv = pq, vv = pv, ov = po;
+    const float bt = pb;
+    fetch_after(blk, s, BWD);
+    if (tid < NQK) {
+      const int e = tid * 4, t = e / DK, c = e % DK;
+      const bool ok = t < n;
+      const int o = t * RK + c;
+      f32x4 gg, sg4, xz;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xz[i] = sEA[c + i] * zv[i];
+        sg4[i] = 1.f / (1.f + __expf(-xz[i]));
+        gg[i] = ok ? g_min * sg4[i] : 0.f;
       }
-      const float gl = __expf(G);
-      sGl[c] = gl;
-      // Kh = k e^(G_last - G) = Kb e^(G_last)
-#pragma unroll 4
-      for (int t = 0; t < SC; ++t) sKh[t * RK + c] = sKb[t * RK + c] * gl;
-    } else if (tid < DK + DV) {  // value column j
-      const int j = tid - DK;
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(sKt + o) = ok ? kv : zero;  // raw until step 3
+      if (BWD) *reinterpret_cast<f32x4*>(sQt + o) = ok ? qv : zero;
+      *reinterpret_cast<f32x4*>(sG + o) = gg;
+      *reinterpret_cast<f32x4*>(sSig + o) = sg4;
+      *reinterpret_cast<f32x4*>(sXz + o) = xz;
+    }
+    if (tid < NQV) {
+      const int e = tid * 4, t = e / DVS, j = e % DVS;
+      const bool ok = t < n;
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(sV + t * RV + j) = ok ? vv : zero;
+      if (BWD) *reinterpret_cast<f32x4*>(sdO + t * RV + j) = ok ? a.scale * ov : zero;
+    }
+    if (tid < SC) sBeta[tid] = tid < n ? bt : 0.f;
+    bw_barrier();
+    relane();
+    if (tid < DK) {  // running log-decay over the sub-chunk
+      float G = 0.f;
 #pragma unroll
       for (int t = 0; t < SC; ++t) {
-        const bool ok = t < n;
-        const int64_t row = (static_cast<int64_t>(b) * T + t0 + t) * H + h;
-        sV[t * RV + j] = ok ? io<Tin>::load(v, row * DV + j) : 0.f;
-        if (BWD) sdO[t * RV + j] = ok ? a.scale * io<Tdo>::load(d_o, row * DV + j) : 0.f;
+        G += sG[t * RK + tid];
+        sG[t * RK + tid] = G;
       }
-    } else if (tid >= 256 && tid < 256 + SC) {
-      const int t = tid - 256;
-      sBeta[t] = t < n ? io<Tin>::load(beta, (static_cast<int64_t>(b) * T + t0 + t) * H + h) : 0.f;
+      sGl[tid] = __expf(G);
+    }
+    bw_barrier();
+    relane();
+#pragma unroll
+    for (int i = 0; i < (SC * DK + NT - 1) / NT; ++i) {
+      const int e = tid + i * NT, t = e / DK, c = e % DK;
+      if (SC * DK % NT != 0 && e >= SC * DK) break;
+      const int o = t * RK + c;
+      const float G = sG[o], kv = sKt[o];
+      const float Gm = __expf(G), Gi = __expf(-G);
+      const float kb = kv * Gi;
+      sKt[o] = kv * Gm;
+      sKb[o] = kb;
+      sKh[o] = kb * sGl[c];  // k e^(G_last - G)
+      if (BWD) sQt[o] = sQt[o] * Gm;
     }
   };
 
-  // ---- AL = Kt Kb^T (wave 0), AP = Qt Kb^T (wave 1, BWD); masked L, P
-  auto lp = [&](bool BWD) {
+  // ---- wave 0: AL = Kt Kb^T, then M = (I + L)^-1 and T = M Diag(beta) from lane broadcasts of
+  // the accumulators (L[t][m] sits in lane m + 16 (t / 4), slot t % 4); wave 1 (BWD): P = lower(Qt Kb^T)
+  auto lp_inverse = [&](bool BWD) {
     if (wv == 0 || (BWD && wv == 1)) {
       const float* X = wv == 0 ? sKt : sQt;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-      for (int kb = 0; kb < DK / 4; ++kb) acc = mma4(X[r16 * RK + 4 * kb + g4], sKb[r16 * RK + 4 * kb + g4], acc);
+      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int kb = 0; kb < DK / 4; kb += 2) {
+        acc0 = mma4(X[r16 * RK + 4 * kb + g4], sKb[r16 * RK + 4 * kb + g4], acc0);
+        acc1 = mma4(X[r16 * RK + 4 * kb + 4 + g4], sKb[r16 * RK + 4 * kb + 4 + g4], acc1);
+      }
       // acc[e] = X[t][s] with t = 4 g4 + e, s = r16
+      if (wv == 1) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 4 * g4 + e, s = r16;
-        if (wv == 0) {
-          sAL[t * RS + s] = acc[e];
-          sL[t * RS + s] = s < t ? sBeta[t] * acc[e] : 0.f;
-        } else {
-          sP[t * RS + s] = s <= t ? acc[e] : 0.f;
+        for (int e = 0; e < 4; ++e) {
+          const int t = 4 * g4 + e;
+          sP[t * RS + r16] = r16 <= t ? acc0[e] + acc1[e] : 0.f;
         }
-      }
-    }
-  };
-
-  // ---- M = (I + L)^-1 (forward substitution, one column per lane), T = M Diag(beta)
-  auto inverse = [&]() {
-    if (wv == 0 && ln < SC) {
-      const int s = ln;
-      float x[SC];
+      } else {
+        float lv[4];
 #pragma unroll
-      for (int t = 0; t < SC; ++t) {
-        float acc = (t == s) ? 1.f : 0.f;
+        for (int e = 0; e < 4; ++e) {
+          const int t = 4 * g4 + e;
+          const float al = acc0[e] + acc1[e];
+          if (BWD) sAL[t * RS + r16] = al;
+          lv[e] = r16 < t ? sBeta[t] * al : 0.f;
+        }
+        // column s = ln of the inverse (lanes 0..15), right-looking
+        float x[SC];
 #pragma unroll
-        for (int m = 0; m < t; ++m) acc -= sL[t * RS + m] * x[m];
-        x[t] = acc;
-        __builtin_amdgcn_sched_barrier(0);  // keep each row's reads with its row
-      }
-      const float bs = sBeta[s];
+        for (int r = 0; r < SC; ++r) x[r] = (r == ln) ? 1.f : 0.f;
 #pragma unroll
-      for (int t = 0; t < SC; ++t) {
-        sM[t * RS + s] = x[t];
-        sT[t * RS + s] = x[t] * bs;
+        for (int m = 0; m < SC - 1; ++m) {
+#pragma unroll
+          for (int r = m + 1; r < SC; ++r) {
+            const float l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv[r % 4]), m + 16 * (r / 4)));
+            x[r] -= l * x[m];
+          }
+        }
+        if (ln < SC) {
+          const float bs = sBeta[ln];
+#pragma unroll
+          for (int t = 0; t < SC; ++t) {
+            sM[t * RS + ln] = x[t];
+            sT[t * RS + ln] = x[t] * bs;
+          }
+        }
       }
     }
   };
@@ -266,33 +380,56 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
     }
   };
 
-  // ---- X[:, jt] += sum_c A[t][c] Y[c][jt] with Y held by columns (B operand = the lane's element e)
+  // ---- X[:, jt] += sum_c A[t][c] Y[c][jt], Y held by columns (B operand = the lane's element e);
+  // two accumulators so that consecutive products do not wait on each other
   auto over_c = [&](const float* Asrc, const f32x4 (&Y)[NKT], f32x4 acc) {
+    f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c2 = 0; c2 < NKT; ++c2) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc = mma4(Asrc[r16 * RK + 16 * c2 + 4 * g4 + e], Y[c2][e], acc);
-      __builtin_amdgcn_sched_barrier(0);  // bound how far operand reads run ahead (registers)
+      for (int e = 0; e < 4; e += 2) {
+        acc = mma4(Asrc[r16 * RK + 16 * c2 + 4 * g4 + e], Y[c2][e], acc);
+        acc2 = mma4(Asrc[r16 * RK + 16 * c2 + 4 * g4 + e + 1], Y[c2][e + 1], acc2);
+      }
     }
-    return acc;
+    return acc + acc2;
   };
-  // ---- X[:, ct] += sum_j A[t][j] Y[ct][j] with Y held transposed
+  // ---- X[:, ct] += sum_j A[t][j] Y[ct][j], Y held transposed
   auto over_j = [&](const float* Asrc, const f32x4 (&Y)[NVT], f32x4 acc) {
+    f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j2 = 0; j2 < NVT; ++j2) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc = mma4(Asrc[r16 * RV + 16 * j2 + 4 * g4 + e], Y[j2][e], acc);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int e = 0; e < 4; e += 2) {
+        acc = mma4(Asrc[r16 * RV + 16 * j2 + 4 * g4 + e], Y[j2][e], acc);
+        acc2 = mma4(Asrc[r16 * RV + 16 * j2 + 4 * g4 + e + 1], Y[j2][e + 1], acc2);
+      }
     }
-    return acc;
+    return acc + acc2;
+  };
+  // ---- 16 x 16 tile: sum over K of A[r][k] B[c][k] (both row-major with stride RSTR)
+  auto mm_nt = [&](const float* Ap, const float* Bp, int K, int RSTR) {
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int kb = 0; kb < K / 4; kb += 2) {
+      acc0 = mma4(Ap[r16 * RSTR + 4 * kb + g4], Bp[r16 * RSTR + 4 * kb + g4], acc0);
+      acc1 = mma4(Ap[r16 * RSTR + 4 * kb + 4 + g4], Bp[r16 * RSTR + 4 * kb + 4 + g4], acc1);
+    }
+    return acc0 + acc1;
   };
 
+  if (tid < DK) sEA[tid] = __expf(a.A[h * DK + tid]);
   // dS_out
   load_state(a.dS_out ? a.dS_out + static_cast<int64_t>(bh) * SZ : nullptr, dSc, dSt);
 
+  if (nblk > 0) {  // the first sub-chunk in processing order
+    const int ns = nsub_of(nblk - 1);
+    const int t0 = (nblk - 1) * CK + (ns > 1 ? 0 : ns - 1) * SC;
+    fetch(t0, min(SC, T - t0), ns == 1);
+  }
   for (int blk = nblk - 1; blk >= 0; --blk) {
     const int b0 = blk * CK;
-    const int nsub = min(CK, T - b0 + 0) > 0 ? (min(CK, T - b0) + SC - 1) / SC : 0;
+    const int nsub = (min(CK, T - b0) + SC - 1) / SC;
 
     // ===== recompute the states entering sub-chunks 1 .. nsub-1 of the block
     load_state(ckpt + static_cast<int64_t>(blk) * SZ, Sc, St);
@@ -301,13 +438,10 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
       const int n = min(SC, T - t0);
       bw_barrier();
       relane();
-      load_sub(t0, n, false);
+      load_sub(blk, s, t0, n, false);
       bw_barrier();
       relane();
-      lp(false);
-      bw_barrier();
-      relane();
-      inverse();
+      lp_inverse(false);
       bw_barrier();
       relane();
       f32x4 Ut;
@@ -316,7 +450,7 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
       relane();
       if (own_j) {
         // U[:, jt] = Ut - W S[:, jt];  S_next[c][jt] = Gam_last[c] S + sum_t Kh[t][c] U[t][jt]
-        f32x4 negU = over_c(sW, Sc, f32x4{-Ut[0], -Ut[1], -Ut[2], -Ut[3]});  // = W S - Ut = -U
+        const f32x4 negU = over_c(sW, Sc, f32x4{-Ut[0], -Ut[1], -Ut[2], -Ut[3]});  // = W S - Ut = -U
         float* dst = scratch + static_cast<int64_t>(s) * SZ;
 #pragma unroll
         for (int c2 = 0; c2 < NKT; ++c2) {
@@ -327,28 +461,26 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
           for (int e = 0; e < 4; ++e) acc = mma4(-sKh[(4 * g4 + e) * RK + 16 * c2 + r16], negU[e], acc);
           Sc[c2] = acc;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) dst[(16 * c2 + 4 * g4 + e) * DV + 16 * jt + r16] = acc[e];
-          __builtin_amdgcn_sched_barrier(0);
+          for (int e = 0; e < 4; ++e) dst[(16 * c2 + 4 * g4 + e) * DV + j0 + 16 * jt + r16] = acc[e];
         }
       }
     }
 
-    // ===== sub-chunks of the block, last first (the barrier at the top of each
-    // makes the scratch states written above visible to every wavefront)
+    bw_barrier_global();  // the recomputed states in the scratch, visible to every wavefront
+    relane();
+
+    // ===== sub-chunks of the block, last first
     for (int s = nsub - 1; s >= 0; --s) {
       const int t0 = b0 + s * SC;
       const int n = min(SC, T - t0);
       bw_barrier();
-      relane();  // scratch states written, LDS free
+      relane();
       load_state(s == 0 ? ckpt + static_cast<int64_t>(blk) * SZ : scratch + static_cast<int64_t>(s - 1) * SZ, Sc,
                  St);
-      load_sub(t0, n, true);
+      load_sub(blk, s, t0, n, true);
       bw_barrier();
       relane();
-      lp(true);
-      bw_barrier();
-      relane();
-      inverse();
+      lp_inverse(true);
       bw_barrier();
       relane();
       f32x4 Ut;
@@ -356,12 +488,10 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
       bw_barrier();
       relane();
 
-      // ---- U, dU (by value-column tile); dQt (by key-row tile)
-      f32x4 Uc = {0.f, 0.f, 0.f, 0.f}, dUc = {0.f, 0.f, 0.f, 0.f}, dQt = {0.f, 0.f, 0.f, 0.f};
+      // ---- U, dU (by value-column tile); dQt = dO S^T (by key-row tile)
+      f32x4 dUc = {0.f, 0.f, 0.f, 0.f}, dQt = {0.f, 0.f, 0.f, 0.f};
       if (own_j) {
         const f32x4 WS = over_c(sW, Sc, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int e = 0; e < 4; ++e) Uc[e] = Ut[e] - WS[e];
         // dU = P^T dO + Kh dS_next
         f32x4 acc = over_c(sKh, dSc, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
@@ -369,15 +499,15 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
         dUc = acc;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          sU[(4 * g4 + e) * RV + 16 * jt + r16] = Uc[e];
+          sU[(4 * g4 + e) * RV + 16 * jt + r16] = Ut[e] - WS[e];
           sdU[(4 * g4 + e) * RV + 16 * jt + r16] = dUc[e];
         }
       }
-      if (own_c) dQt = over_j(sdO, St, dQt);  // dO S^T
+      if (own_c) dQt = over_j(sdO, St, dQt);
       bw_barrier();
       relane();
 
-      // ---- dKh, dW, dGam_last (by key-row tile); dP (wave 0); then dS in both layouts
+      // ---- dKh, dW, dGam_last (key-row tiles); dP, dU V^T (16 x 16); dS in both layouts
       if (own_c) {
         const f32x4 dKh = over_j(sU, dSt, f32x4{0.f, 0.f, 0.f, 0.f});
         const f32x4 ndW = over_j(sdU, St, f32x4{0.f, 0.f, 0.f, 0.f});  // dU S^T = -dW
@@ -386,7 +516,7 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
           sdKh[(4 * g4 + e) * RK + 16 * ct + r16] = dKh[e];
           sdW[(4 * g4 + e) * RK + 16 * ct + r16] = -ndW[e];
         }
-        float part = 0.f;  // sum_j dS_next[c][j] S[c][j], c = 16 ct + r16
+        float part = 0.f;  // sum over the slice's j of dS_next[c][j] S[c][j], c = 16 ct + r16
 #pragma unroll
         for (int j2 = 0; j2 < NVT; ++j2)
 #pragma unroll
@@ -395,52 +525,53 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
         part += __shfl_xor(part, 32);
         if (g4 == 0) sdGl[16 * ct + r16] = part;
       }
-      if (wv == NW - 1) {  // dP = lower(dO U^T)
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-        for (int kb = 0; kb < DV / 4; ++kb) acc = mma4(sdO[r16 * RV + 4 * kb + g4], sU[r16 * RV + 4 * kb + g4], acc);
+      if (wv == W_DP) {  // dP = lower(dO U^T)
+        const f32x4 acc = mm_nt(sdO, sU, DVS, RV);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = 4 * g4 + e;
           sdP[t * RS + r16] = r16 <= t ? acc[e] : 0.f;
         }
       }
+      if (wv == W_DT0) {  // dU V^T
+        const f32x4 acc = mm_nt(sdU, sV, DVS, RV);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sdT0[(4 * g4 + e) * RS + r16] = acc[e];
+      }
       // dS = Qt^T dO + Diag(Gam_last) dS_next - W^T dU
       if (own_j) {
 #pragma unroll
         for (int c2 = 0; c2 < NKT; ++c2) {
-          f32x4 acc;
+          f32x4 acc, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc[e] = sGl[16 * c2 + 4 * g4 + e] * dSc[c2][e];
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb)
             acc = mma4(sQt[(4 * kb + g4) * RK + 16 * c2 + r16], sdO[(4 * kb + g4) * RV + 16 * jt + r16], acc);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc = mma4(-sW[(4 * g4 + e) * RK + 16 * c2 + r16], dUc[e], acc);
-          dSc[c2] = acc;
-          __builtin_amdgcn_sched_barrier(0);
+          for (int e = 0; e < 4; ++e) acc2 = mma4(-sW[(4 * g4 + e) * RK + 16 * c2 + r16], dUc[e], acc2);
+          dSc[c2] = acc + acc2;
         }
       }
       if (own_c) {
         const float gl = sGl[16 * ct + r16];
 #pragma unroll
         for (int j2 = 0; j2 < NVT; ++j2) {
-          f32x4 acc;
+          f32x4 acc, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc[e] = gl * dSt[j2][e];
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb) {
             acc = mma4(sdO[(4 * kb + g4) * RV + 16 * j2 + r16], sQt[(4 * kb + g4) * RK + 16 * ct + r16], acc);
-            acc = mma4(-sdU[(4 * kb + g4) * RV + 16 * j2 + r16], sW[(4 * kb + g4) * RK + 16 * ct + r16], acc);
+            acc2 = mma4(-sdU[(4 * kb + g4) * RV + 16 * j2 + r16], sW[(4 * kb + g4) * RK + 16 * ct + r16], acc2);
           }
-          dSt[j2] = acc;
-          __builtin_amdgcn_sched_barrier(0);
+          dSt[j2] = acc + acc2;
         }
       }
       bw_barrier();
       relane();
 
-      // ---- dV (by value-column tile, stored); dT parts (waves 6, 7); dKt from W (by key-row tile)
+      // ---- dV (value-column tiles, stored); dT's second part dW Kt^T; dKt = T^T dW (key-row tiles)
       if (own_j) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -448,89 +579,84 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = 4 * g4 + e;
-          if (t < n) a.grad_v[((static_cast<int64_t>(b) * T + t0 + t) * H + h) * DV + 16 * jt + r16] = acc[e];
+          if (t < n) a.grad_v[((static_cast<int64_t>(b) * T + t0 + t) * H + h) * DV + j0 + 16 * jt + r16] = acc[e];
         }
       }
-      if (wv == NW - 2 || wv == NW - 1) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (wv == NW - 2) {  // dU V^T
-#pragma unroll 8
-          for (int kb = 0; kb < DV / 4; ++kb) acc = mma4(sdU[r16 * RV + 4 * kb + g4], sV[r16 * RV + 4 * kb + g4], acc);
-        } else {  // dW Kt^T
-#pragma unroll 8
-          for (int kb = 0; kb < DK / 4; ++kb) acc = mma4(sdW[r16 * RK + 4 * kb + g4], sKt[r16 * RK + 4 * kb + g4], acc);
-        }
-        float* dst = wv == NW - 2 ? sdT0 : sdT1;
+      if (wv == W_DT1) {  // dW Kt^T
+        const f32x4 acc = mm_nt(sdW, sKt, DK, RK);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dst[(4 * g4 + e) * RS + r16] = acc[e];
+        for (int e = 0; e < 4; ++e) sdT1[(4 * g4 + e) * RS + r16] = acc[e];
       }
-      f32x4 dKt = {0.f, 0.f, 0.f, 0.f};
+      f32x4 dKt = {0.f, 0.f, 0.f, 0.f}, dKb = {0.f, 0.f, 0.f, 0.f};
       if (own_c) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 4; ++kb) {
           dKt = mma4(sT[(4 * kb + g4) * RS + r16], sdW[(4 * kb + g4) * RK + 16 * ct + r16], dKt);
+          // the parts of dQt and dKb that do not wait for dL
+          dQt = mma4(sdP[r16 * RS + 4 * kb + g4], sKb[(4 * kb + g4) * RK + 16 * ct + r16], dQt);
+          dKb = mma4(sdP[(4 * kb + g4) * RS + r16], sQt[(4 * kb + g4) * RK + 16 * ct + r16], dKb);
+        }
       }
       bw_barrier();
       relane();
 
-      // ---- dM = dT Diag(beta) -> LDS (wave 0)
+      // ---- wave 0: dM = dT Diag(beta), Y = M^T dM, dL = -strict_lower(Y M^T), dAL = Diag(beta) dL,
+      // dbeta; one wavefront end to end (its own LDS writes are read back in order)
       if (wv == 0) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = 4 * g4 + e;
           sdM[t * RS + r16] = (sdT0[t * RS + r16] + sdT1[t * RS + r16]) * sBeta[r16];
         }
-      }
-      bw_barrier();
-      relane();
-      // Y = M^T dM (wave 0)
-      if (wv == 0) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) acc = mma4(sM[(4 * kb + g4) * RS + r16], sdM[(4 * kb + g4) * RS + r16], acc);
 #pragma unroll
         for (int e = 0; e < 4; ++e) sY[(4 * g4 + e) * RS + r16] = acc[e];
-      }
-      bw_barrier();
-      relane();
-      // dL = -strict_lower(Y M^T) (over dM, free again); dAL = Diag(beta) dL (wave 0)
-      if (wv == 0) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) acc = mma4(sY[r16 * RS + 4 * kb + g4], sM[r16 * RS + 4 * kb + g4], acc);
+        float dlv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = 4 * g4 + e;
-          const float dl = r16 < t ? -acc[e] : 0.f;
-          sdM[t * RS + r16] = dl;
-          sdAL[t * RS + r16] = dl * sBeta[t];
+          dlv[e] = r16 < t ? -acc[e] : 0.f;
+          sdAL[t * RS + r16] = dlv[e] * sBeta[t];
+        }
+        // dbeta_u = sum_t dT[t][u] M[t][u] + sum_s dL[u][s] AL[u][s]: the second sum is a row
+        // sum of the lanes' products, reduced over the 16 lanes of each row group
+        float rs[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 4 * g4 + e;
+          float x = dlv[e] * sAL[t * RS + r16];
+          x += __shfl_xor(x, 1);
+          x += __shfl_xor(x, 2);
+          x += __shfl_xor(x, 4);
+          x += __shfl_xor(x, 8);
+          rs[e] = x;  // row t's sum, in every lane of the row group
+        }
+        if (r16 == 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sY[(4 * g4 + e) * RS + 16] = rs[e];  // spare column 16 of Y
+        }
+        if (ln < SC) {
+          const int u = ln;
+          float db = sY[u * RS + 16];
+#pragma unroll
+          for (int t = 0; t < SC; ++t) db += (sdT0[t * RS + u] + sdT1[t * RS + u]) * sM[t * RS + u];
+          if (u < n) gbeta[(static_cast<int64_t>(b) * T + t0 + u) * H + h] = db;
         }
       }
       bw_barrier();
       relane();
-      // dbeta_u = sum_t dT[t][u] M[t][u] + sum_s dL[u][s] AL[u][s] (lanes 0..15 of wave 1)
-      if (wv == 1 && ln < SC) {
-        const int u = ln;
-        float db = 0.f;
-#pragma unroll
-        for (int t = 0; t < SC; ++t) db += (sdT0[t * RS + u] + sdT1[t * RS + u]) * sM[t * RS + u];
-#pragma unroll
-        for (int s2 = 0; s2 < SC; ++s2) db += sdM[u * RS + s2] * sAL[u * RS + s2];
-        if (u < n) a.grad_beta[(static_cast<int64_t>(b) * T + t0 + u) * H + h] = db;
-      }
 
-      // ---- dKt += dAL Kb; dKb = dAL^T Kt + dP^T Qt; dQt += dP Kb (by key-row tile)
+      // ---- dKt += dAL Kb; dKb += dAL^T Kt (key-row tiles) -> LDS with dQt
       if (own_c) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
           dKt = mma4(sdAL[r16 * RS + 4 * kb + g4], sKb[(4 * kb + g4) * RK + 16 * ct + r16], dKt);
-          dQt = mma4(sdP[r16 * RS + 4 * kb + g4], sKb[(4 * kb + g4) * RK + 16 * ct + r16], dQt);
-        }
-        f32x4 dKb = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
           dKb = mma4(sdAL[(4 * kb + g4) * RS + r16], sKt[(4 * kb + g4) * RK + 16 * ct + r16], dKb);
-          dKb = mma4(sdP[(4 * kb + g4) * RS + r16], sQt[(4 * kb + g4) * RK + 16 * ct + r16], dKb);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -543,36 +669,40 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
       bw_barrier();
       relane();
 
-      // ---- per key channel: dq, dk, dG -> dg (reverse cumulative sum) -> dz, dA
+      // ---- every element: dq, dk and dG (over G, no longer needed)
+#pragma unroll
+      for (int i = 0; i < (SC * DK + NT - 1) / NT; ++i) {
+        const int e = tid + i * NT, t = e / DK, c = e % DK;
+        if (SC * DK % NT != 0 && e >= SC * DK) break;
+        const int o = t * RK + c;
+        const float Gm = __expf(sG[o]);
+        const float dqt = sdQt[o], dkt = sdKt[o], dkb = sdKb[o], dkh = sdKh[o];
+        sG[o] = dqt * sQt[o] + dkt * sKt[o] - dkb * sKb[o] - dkh * sKh[o];
+        if (t < n) {
+          const int64_t row = (static_cast<int64_t>(b) * T + t0 + t) * H + h;
+          gq[row * DK + c] = dqt * Gm;
+          gk[row * DK + c] = dkt * Gm + dkb / Gm + dkh * sGl[c] / Gm;
+        }
+      }
+      bw_barrier();
+      relane();
+      // ---- per key channel: dg = reverse cumulative sum of dG (the last token also carries
+      // Gam_last's uses), then dz = dg g_min sigma (1 - sigma) e^A and dA += dz z
       if (tid < DK) {
         const int c = tid;
-        const float gl = sGl[c];
-        float tail = 0.f;
-#pragma unroll 2
-        for (int t = 0; t < SC; ++t) {
-          const int o = t * RK + c;
-          const float Gm = __expf(sG[o]);
-          const float dqt = sdQt[o], dkt = sdKt[o], dkb = sdKb[o], dkh = sdKh[o];
-          const float Kh_ = sKh[o];
-          sG[o] = dqt * sQt[o] + dkt * sKt[o] - dkb * sKb[o] - dkh * Kh_;  // dG (G is no longer needed)
-          tail += dkh * Kh_;
-          if (t < n) {
-            const int64_t row = (static_cast<int64_t>(b) * T + t0 + t) * H + h;
-            a.grad_q[row * DK + c] = dqt * Gm;
-            a.grad_k[row * DK + c] = dkt * Gm + dkb / Gm + dkh * gl / Gm;
-          }
-        }
-        float run = tail + sdGl[c] * gl;  // dG at the last token also carries Gam_last's uses
-#pragma unroll 2
+        float run = sdGl[c] * sGl[c];
+#pragma unroll
+        for (int t = 0; t < SC; ++t) run += sdKh[t * RK + c] * sKh[t * RK + c];
+        const float ea = sEA[c];
+#pragma unroll 4
         for (int t = SC - 1; t >= 0; --t) {
-          run += sG[t * RK + c];
+          const int o = t * RK + c;
+          run += sG[o];
           if (t < n) {
-            const int64_t row = (static_cast<int64_t>(b) * T + t0 + t) * H + h;
-            const float zv = io<Tin>::load(z, row * DK + c);
-            const float sg = 1.f / (1.f + __expf(-eA * zv));
+            const float sg = sSig[o];
             const float dx = run * g_min * sg * (1.f - sg);
-            a.grad_z[row * DK + c] = dx * eA;
-            dA_acc += dx * eA * zv;
+            gz[(static_cast<int64_t>(b) * T + t0 + t) * H * DK + static_cast<int64_t>(h) * DK + c] = dx * ea;
+            dA_acc += dx * sXz[o];
           }
         }
       }
@@ -584,25 +714,40 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
 #pragma unroll
     for (int c2 = 0; c2 < NKT; ++c2)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dst[(16 * c2 + 4 * g4 + e) * DV + 16 * jt + r16] = dSc[c2][e];
+      for (int e = 0; e < 4; ++e) dst[(16 * c2 + 4 * g4 + e) * DV + j0 + 16 * jt + r16] = dSc[c2][e];
   }
-  if (tid < DK) a.dA_part[static_cast<int64_t>(bh) * DK + tid] = dA_acc;
+  if (tid < DK) a.dA_part[(static_cast<int64_t>(bh) * NSP + sp) * DK + tid] = dA_acc;
+}
+
+// The second value slice's parts of the key-side gradients, added to the first's.
+// Two addends: the sum is the same in either order.
+__global__ void add_parts_kernel(float* __restrict__ out, const float* __restrict__ part, int64_t n) {
+  const int64_t i4 = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
+  if (i4 + 4 <= n) {
+    f32x4 o = *reinterpret_cast<f32x4*>(out + i4);
+    const f32x4 p = *reinterpret_cast<const f32x4*>(part + i4);
+    *reinterpret_cast<f32x4*>(out + i4) = o + p;
+  } else {
+    for (int64_t i = i4; i < n; ++i) out[i] += part[i];
+  }
 }
 
 // dA[h][c] = sum over b of the per-(b, h) parts (fixed order: deterministic)
-__global__ void dA_reduce_kernel(const float* __restrict__ part, float* __restrict__ dA, int B, int H, int dk) {
+__global__ void dA_reduce_kernel(const float* __restrict__ part, float* __restrict__ dA, int B, int H, int dk,
+                                 int nsp) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= H * dk) return;
   const int h = i / dk, c = i % dk;
   float s = 0.f;
-  for (int b = 0; b < B; ++b) s += part[(static_cast<int64_t>(b) * H + h) * dk + c];
+  for (int b = 0; b < B; ++b)
+    for (int p = 0; p < nsp; ++p) s += part[((static_cast<int64_t>(b) * H + h) * nsp + p) * dk + c];
   dA[i] = s;
 }
 
-template <int DK, int DV, typename Tin, typename Tdo>
+template <int DK, int DV, int NSP, typename Tin, typename Tdo>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
-  auto kern = chunk_bwd_kernel<DK, DV, Tin, Tdo>;
-  constexpr int bytes = bw::Layout<DK, DV>::BYTES;
+  auto kern = chunk_bwd_kernel<DK, DV, NSP, Tin, Tdo>;
+  constexpr int bytes = bw::Layout<DK, DV / NSP>::BYTES;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -610,19 +755,42 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3(a.B * a.H), dim3(bw::NT), bytes, st, a);
+  hipLaunchKernelGGL(kern, dim3(a.B * a.H * NSP), dim3(bw::NT), bytes, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (NSP == 2) {
+    const int64_t ntok = static_cast<int64_t>(a.B) * a.T * a.H;
+    const struct { float* out; const float* part; int64_t n; } adds[] = {
+        {a.grad_q, a.part_q, ntok * a.dk}, {a.grad_k, a.part_k, ntok * a.dk}, {a.grad_z, a.part_z, ntok * a.dk},
+        {a.grad_beta, a.part_beta, ntok}};
+    for (const auto& ad : adds) {
+      if (ad.n == 0) continue;
+      const int64_t nthr = (ad.n + 3) / 4;
+      hipLaunchKernelGGL(add_parts_kernel, dim3(static_cast<uint32_t>((nthr + 255) / 256)), dim3(256), 0, st, ad.out,
+                         ad.part, ad.n);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int n = a.H * a.dk;
-  hipLaunchKernelGGL(dA_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, st, a.dA_part, a.grad_A, a.B, a.H, a.dk);
+  hipLaunchKernelGGL(dA_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, st, a.dA_part, a.grad_A, a.B, a.H, a.dk,
+                     NSP);
   return hipGetLastError();
+}
+
+template <int DK, int DV, int NSP>
+static hipError_t launch_bwd_s(const BwdArgs& a, hipStream_t st) {
+  if (a.in_bf16)
+    return a.do_bf16 ? launch_bwd_t<DK, DV, NSP, bf16_t, bf16_t>(a, st) : launch_bwd_t<DK, DV, NSP, bf16_t, float>(a, st);
+  return a.do_bf16 ? launch_bwd_t<DK, DV, NSP, float, bf16_t>(a, st) : launch_bwd_t<DK, DV, NSP, float, float>(a, st);
 }
 
 template <int DK, int DV>
 static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
-  if (a.in_bf16)
-    return a.do_bf16 ? launch_bwd_t<DK, DV, bf16_t, bf16_t>(a, st) : launch_bwd_t<DK, DV, bf16_t, float>(a, st);
-  return a.do_bf16 ? launch_bwd_t<DK, DV, float, bf16_t>(a, st) : launch_bwd_t<DK, DV, float, float>(a, st);
+  if constexpr (DV >= 64) {
+    if (a.part_q) return launch_bwd_s<DK, DV, 2>(a, st);  // two value slices
+  }
+  return launch_bwd_s<DK, DV, 1>(a, st);
 }
 
 template <int DK>
@@ -634,6 +802,11 @@ static hipError_t launch_bwd_k(const BwdArgs& a, hipStream_t st) {
     case 128: return launch_bwd_d<DK, 128>(a, st);
   }
   return hipErrorInvalidValue;
+}
+
+int chunk_bwd_slices(int B, int H, int dv) {
+  // two value slices when one workgroup per (b, h) would leave compute units idle
+  return (dv >= 64 && static_cast<int64_t>(B) * H < 256) ? 2 : 1;
 }
 
 hipError_t launch_chunk_bwd(const BwdArgs& a, hipStream_t st) {

@@ -111,7 +111,10 @@ struct BwdArgs {
   int B, T, H, dk, dv;
   float scale;
   bool in_bf16, do_bf16;
+  // second value slice's parts of dq, dk, dz, dbeta (nullptr: one slice, see chunk_bwd_slices)
+  float *part_q = nullptr, *part_k = nullptr, *part_z = nullptr, *part_beta = nullptr;
 };
+int chunk_bwd_slices(int B, int H, int dv);
 hipError_t launch_chunk_bwd(const BwdArgs& a, hipStream_t st);
 hipError_t launch_gate(const GateArgs& a, hipStream_t st);
 hipError_t launch_replay(const ReplayArgs& a, hipStream_t st);
