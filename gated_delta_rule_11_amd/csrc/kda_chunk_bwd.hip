@@ -202,7 +202,7 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
     }
   };
 
-  float dA_acc = 0.f;  // thread c < DK: this workgroup's part of dA[h][c]
+  float dA_acc = 0.f;  // lanes 4c .. 4c + 3: this workgroup's part of dA[h][c]
 
   // ---- sub-chunk inputs.  The raw values of the next sub-chunk in processing order are
   // loaded into registers while the current one is processed, four consecutive channels
@@ -686,22 +686,38 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
       }
       bw_barrier();
       relane();
-      // ---- per key channel: dg = reverse cumulative sum of dG (the last token also carries
-      // Gam_last's uses), then dz = dg g_min sigma (1 - sigma) e^A and dA += dz z
-      if (tid < DK) {
-        const int c = tid;
-        float run = sdGl[c] * sGl[c];
+      // ---- dg = reverse cumulative sum of dG over the sub-chunk (the last token also carries
+      // Gam_last's uses), then dz = dg g_min sigma (1 - sigma) e^A and dA += dz z.  Four lanes
+      // per key channel, four tokens each: suffix sums in a lane, then across the quad.
+      if (tid < 4 * DK) {
+        const int c = tid >> 2, qd = tid & 3;
+        float dg[4], tail = 0.f;
 #pragma unroll
-        for (int t = 0; t < SC; ++t) run += sdKh[t * RK + c] * sKh[t * RK + c];
+        for (int i = 0; i < 4; ++i) {
+          const int o = (4 * qd + i) * RK + c;
+          dg[i] = sG[o];
+          tail += sdKh[o] * sKh[o];
+        }
+#pragma unroll
+        for (int i = 2; i >= 0; --i) dg[i] += dg[i + 1];  // suffix sums within the lane's tokens
+        tail += __shfl_xor(tail, 1);
+        tail += __shfl_xor(tail, 2);
+        float later = 0.f;  // the sums of the quad's later lanes (later tokens)
+#pragma unroll
+        for (int r = 1; r < 4; ++r) {
+          const float x = __shfl(dg[0], (ln & ~3) + r);
+          later += r > qd ? x : 0.f;
+        }
+        const float base = sdGl[c] * sGl[c] + tail + later;
         const float ea = sEA[c];
-#pragma unroll 4
-        for (int t = SC - 1; t >= 0; --t) {
-          const int o = t * RK + c;
-          run += sG[o];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 4 * qd + i;
           if (t < n) {
+            const int o = t * RK + c;
             const float sg = sSig[o];
-            const float dx = run * g_min * sg * (1.f - sg);
-            gz[(static_cast<int64_t>(b) * T + t0 + t) * H * DK + static_cast<int64_t>(h) * DK + c] = dx * ea;
+            const float dx = (base + dg[i]) * g_min * sg * (1.f - sg);
+            gz[((static_cast<int64_t>(b) * T + t0 + t) * H + h) * DK + c] = dx * ea;
             dA_acc += dx * sXz[o];
           }
         }
@@ -716,7 +732,10 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) dst[(16 * c2 + 4 * g4 + e) * DV + j0 + 16 * jt + r16] = dSc[c2][e];
   }
-  if (tid < DK) a.dA_part[(static_cast<int64_t>(bh) * NSP + sp) * DK + tid] = dA_acc;
+  // dA: the four lanes of each key channel hold parts over their tokens
+  dA_acc += __shfl_xor(dA_acc, 1);
+  dA_acc += __shfl_xor(dA_acc, 2);
+  if (tid < 4 * DK && (tid & 3) == 0) a.dA_part[(static_cast<int64_t>(bh) * NSP + sp) * DK + (tid >> 2)] = dA_acc;
 }
 
 // The second value slice's parts of the key-side gradients, added to the first's.
