@@ -193,11 +193,11 @@ __device__ __forceinline__ void load_part(RawTile<FROM_Z>& R, const ChunkArgs& a
   }
 }
 
-template <int DVS, bool FROM_Z, bool SEG>
+template <int DVS, bool FROM_Z, bool SEG, bool STO>
 __device__ __forceinline__ void load_tile(RawTile<FROM_Z>& R, const ChunkArgs& a, int b, int h, int t0, int i,
                                           int ln, int j0) {
   load_part<DVS, FROM_Z, 0, SEG>(R, a, b, h, t0, i, ln, j0);
-  load_part<DVS, FROM_Z, 1, SEG>(R, a, b, h, t0, i, ln, j0);
+  if constexpr (!STO) load_part<DVS, FROM_Z, 1, SEG>(R, a, b, h, t0, i, ln, j0);
   load_part<DVS, FROM_Z, 2, SEG>(R, a, b, h, t0, i, ln, j0);
   load_part<DVS, FROM_Z, 3, SEG>(R, a, b, h, t0, i, ln, j0);
 }
@@ -260,10 +260,15 @@ __constant__ int8_t kOffPairs8[4][2][2] = {{{1, 0}, {3, 0}}, {{2, 1}, {3, 1}}, {
 // key norm (a lane reduction) into the factors the raw keys are multiplied by
 // anyway, compute beta = sigmoid(logit), and hand the query normalisers to the
 // state chain, which applies them to the output rows (o is linear in q_t).
-template <int DVS, bool FROM_Z, typename Tout, bool SEG, bool NORM>
+//
+// STO (state only) instantiations serve the segment passes that write no outputs
+// (end states, transitions, backward checkpoints): no queries are loaded and neither
+// P nor (q Gamma) S is formed.
+template <int DVS, bool FROM_Z, typename Tout, bool SEG, bool NORM, bool STO>
 __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int ns, int xcd_map) {
   using namespace mf;
   static_assert(!NORM || (FROM_Z && !SEG), "the fused prologue runs with the fused gate, in one pass");
+  static_assert(!STO || SEG, "state-only passes are segment passes");
   using Ly = Layout<DVS>;
   constexpr int NJT = DVS / 16;  // value-column tiles in the slice (chain wavefront w owns tile w)
   constexpr int ES = sizeof(Tout);
@@ -337,7 +342,7 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
       const int cb = 32 * kb + 8 * g4;
       const u32x4 A = lds128(Ar + cb);
       accL = mma32(A, lds128(&sKR[(16 * i + r16) * RS + cb]), accL);
-      accP = mma32(A, lds128(&sQR[(16 * i + r16) * RS + cb]), accP);
+      if constexpr (!STO) accP = mma32(A, lds128(&sQR[(16 * i + r16) * RS + cb]), accP);
     }
   };
 
@@ -435,7 +440,7 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
           lv[v] = s < r16 ? bt * dL[v] : 0.f;
           pv[v] = s <= r16 ? dP[v] : 0.f;
         }
-        *reinterpret_cast<s16x4*>(&sP[(16 * i + r16) * TS + 16 * i + 4 * g4]) = cvt4(pv);
+        if constexpr (!STO) *reinterpret_cast<s16x4*>(&sP[(16 * i + r16) * TS + 16 * i + 4 * g4]) = cvt4(pv);
         // X_ii = (I + L_ii)^-1, one column per lane (lanes 0..15), right-looking; L[r][m]
         // is broadcast from the accumulator lane that holds it (lane r + 16 (m / 4), slot m % 4)
         float x[16];
@@ -485,9 +490,11 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
         for (int i = 0; i < 4; ++i) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
           const uint16_t* Qr = &sQt[(16 * i + r16) * RS + 4 * g4];
+          if constexpr (!STO) {
 #pragma unroll
-          for (int cp = 0; cp < 4; ++cp)
-            acc = mma32(cat(lds64(Qr + 32 * cp), lds64(Qr + 32 * cp + 16)), cat(Sb[2 * cp], Sb[2 * cp + 1]), acc);
+            for (int cp = 0; cp < 4; ++cp)
+              acc = mma32(cat(lds64(Qr + 32 * cp), lds64(Qr + 32 * cp + 16)), cat(Sb[2 * cp], Sb[2 * cp + 1]), acc);
+          }
           O[i] = acc;
         }
       }
@@ -496,7 +503,7 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
 
       // ---- A2: O += P U (stored), S = Diag(Gamma_C) S + (K Gamma_C / Gamma)^T U
       if (owns_v) {
-        if (!(SEG && a.o_skip)) {  // outputs (segment passes that only need states skip them)
+        if (!STO && !(SEG && a.o_skip)) {  // outputs (passes that only need states skip them)
           const auto ro = rsrc(static_cast<Tout*>(a.o) + row0 * DK + j0, (span - 1) * DK * ES + DVS * ES);
           const s16x4 z4 = {0, 0, 0, 0};
 #pragma unroll
@@ -668,8 +675,9 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
         D0 = fast_exp2(last0 - base0);
         D1 = fast_exp2(last1 - base1);
       }
+      if constexpr (!STO)
 #pragma unroll
-      for (int tt = 0; tt < 16; ++tt) *reinterpret_cast<uint32_t*>(&sQR[(16 * i + tt) * RS + c0]) = qr[tt];
+        for (int tt = 0; tt < 16; ++tt) *reinterpret_cast<uint32_t*>(&sQR[(16 * i + tt) * RS + c0]) = qr[tt];
       // k sf of this tile is the anchored-key slot (i + 1, i) as it stands (no tile
       // in between); the scaled slots read it back in the next phase
       if (i < 3) {
@@ -740,8 +748,9 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
 
     // tiles the state chain reads until the end of a chunk (written once it is done)
     auto gate_b = [&]() {
+      if constexpr (!STO)
 #pragma unroll
-      for (int tt = 0; tt < 16; ++tt) *reinterpret_cast<uint32_t*>(&sQt[(16 * i + tt) * RS + c0]) = qt[tt];
+        for (int tt = 0; tt < 16; ++tt) *reinterpret_cast<uint32_t*>(&sQt[(16 * i + tt) * RS + c0]) = qt[tt];
       u32x4* d = reinterpret_cast<u32x4*>(&sKhT[c0 * TS + 16 * i]);
       d[0] = u32x4{kh[0], kh[1], kh[2], kh[3]};
       d[1] = u32x4{kh[4], kh[5], kh[6], kh[7]};
@@ -757,7 +766,7 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
 
     // ---- prologue: operand tiles of chunk 0
     if (c_begin < nch) {
-      load_tile<DVS, FROM_Z, SEG>(R, a, b, h, c_begin * C, i, ln, j0);
+      load_tile<DVS, FROM_Z, SEG, STO>(R, a, b, h, c_begin * C, i, ln, j0);
       if (T - c_begin * C >= C)
         gate_a1(c_begin * C, std::true_type{});
       else
@@ -783,7 +792,7 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
       // carries most of them; values and beta follow in phase 3.
       if (more) {
         load_part<DVS, FROM_Z, 0, SEG>(R, a, b, h, t0 + C, i, ln, j0);
-        load_part<DVS, FROM_Z, 1, SEG>(R, a, b, h, t0 + C, i, ln, j0);
+        if constexpr (!STO) load_part<DVS, FROM_Z, 1, SEG>(R, a, b, h, t0 + C, i, ln, j0);
         load_part<DVS, FROM_Z, 2, SEG>(R, a, b, h, t0 + C, i, ln, j0);
       }
 #pragma unroll
@@ -798,7 +807,7 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
 #pragma unroll
         for (int v = 0; v < 4; ++v) nl[v] = -bt * oL[v];
         *reinterpret_cast<s16x4*>(&sLm[t * TS + 16 * pj + 4 * g4]) = cvt4(nl);
-        *reinterpret_cast<s16x4*>(&sP[t * TS + 16 * pj + 4 * g4]) = cvt4(oP);
+        if constexpr (!STO) *reinterpret_cast<s16x4*>(&sP[t * TS + 16 * pj + 4 * g4]) = cvt4(oP);
       }
       lds_barrier();
       relane();
@@ -836,9 +845,9 @@ bool chunk_mfma_supports(const ChunkArgs& a) {
   return a.in_bf16 && a.dk == 128 && a.dv == 128 && a.chunk == 64 && a.H <= 65536;
 }
 
-template <int DVS, bool FROM_Z, typename Tout, bool SEG, bool NORM = false>
+template <int DVS, bool FROM_Z, typename Tout, bool SEG, bool NORM = false, bool STO = false>
 static hipError_t launch_mfma_t(const ChunkArgs& a, hipStream_t st, int ns) {
-  auto kern = chunk_mfma_kernel<DVS, FROM_Z, Tout, SEG, NORM>;
+  auto kern = chunk_mfma_kernel<DVS, FROM_Z, Tout, SEG, NORM, STO>;
   constexpr int bytes = mf::Layout<DVS>::BYTES;
   static bool attr_set = false;  // set once per instantiation (idempotent if raced)
   if (!attr_set) {
@@ -865,6 +874,7 @@ static hipError_t launch_mfma_d(const ChunkArgs& a, hipStream_t st, int ns) {
   }
   if (seg) {  // segment passes: fused gate only
     if (!a.from_z) return hipErrorNotSupported;
+    if (a.o_skip) return launch_mfma_t<DVS, true, bf16_t, true, false, true>(a, st, ns);  // no outputs
     return a.out_bf16 ? launch_mfma_t<DVS, true, bf16_t, true>(a, st, ns)
                       : launch_mfma_t<DVS, true, float, true>(a, st, ns);
   }
