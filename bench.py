@@ -50,9 +50,9 @@ DECODE_BYTES_PER_SEQ_HEAD = 2 * 128 * 128 * 4 + 4 * 128 * 2 + 2 + 128 * 2
 # sources it was taken on are unchanged (sha256 of the listed files), else null.
 MEASURED_TRAFFIC = {
     "prefill": {"files": ["gated_delta_rule_11_amd/csrc/kda_chunk_mfma.hip", "gated_delta_rule_11_amd/csrc/kda_common.hpp"],
-                "sha256": "7ee4a31ec521a00e", "bytes": 5.454e9},
+                "sha256": "51b14846cf2a98af", "bytes": 5.474e9},
     "decode": {"files": ["gated_delta_rule_11_amd/csrc/kda_decode.hip", "gated_delta_rule_11_amd/csrc/kda_common.hpp"],
-               "sha256": "03354a1f412561c7", "bytes": 1.0849e9},
+               "sha256": "289f3a27b8b3e623", "bytes": 1.0849e9},
 }
 
 
@@ -83,6 +83,9 @@ def main():
                          "(outside the timed region) so a counter pass can scale FETCH_SIZE/WRITE_SIZE")
     ap.add_argument("--no-long", action="store_true",
                     help="skip the 1M-token single-sequence prefill reported beside the step")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="counter runs: skip everything reported beside the step (replay, fused prologue, "
+                         "backward, 1M-token prefill) so that only the step's kernels are profiled")
     ap.add_argument("--cpu-sample-batches", type=int, default=4,
                     help="batch entries (all heads, all tokens) the oracle runs for the CPU baseline")
     args = ap.parse_args()
@@ -186,7 +189,7 @@ def main():
     # state, with seeded accepted-prefix lengths: one kda_decode_replay launch against the
     # 8 kda_decode_step launches that would advance (and then need rolling back) the state.
     replay = None
-    if run_dec:
+    if run_dec and not args.no_extras:
         nd = 8
         snap = S_dec.clone()
         acc = torch.from_numpy(np.random.default_rng(ds.seed).integers(0, nd + 1, ds.N).astype(np.int32)).to(dev)
@@ -213,7 +216,7 @@ def main():
     # (kda_chunk_fwd_z_prologue); the resident inputs stand in for raw ones (the kernel's
     # work does not depend on their values).
     prologue = None
-    if run_pre:
+    if run_pre and not args.no_extras:
         o_pro = torch.empty_like(o_pre)  # its own outputs: o_pre and S_pre are checked against the oracle below
         S_pro = torch.empty_like(S_pre)
 
@@ -237,7 +240,7 @@ def main():
     # Gradients of the 32K prefill for an upstream gradient of the outputs (the resident
     # outputs stand in for it): the checkpointing forward plus the backward kernel.
     backward = None
-    if run_pre:
+    if run_pre and not args.no_extras:
         bw_ws = torch.empty(kda.lib().kda_chunk_bwd_z_workspace_bytes(ps.B, ps.T, ps.H, ps.dk, ps.dv),
                             dtype=torch.uint8, device=dev)
 
@@ -262,7 +265,7 @@ def main():
     # B=1, H=8, T=2^20: one pass of the chunk kernel has 8 sequences for 256 compute units;
     # the segment-parallel form runs 16 segments per sequence side by side.
     long_ctx = None
-    if run_pre and not args.no_long:
+    if run_pre and not args.no_long and not args.no_extras:
         ls = ki.PREFILL_1M
         t0 = time.time()
         ld = ki.prefill_inputs(ls)
