@@ -39,6 +39,8 @@ BF16_PEAK_TFLOPS = 2500.0
 # T V and P U), and bytes: q, k, v, z (bf16) + beta (bf16) + o (bf16).
 PREFILL_FLOP_PER_TOKEN_HEAD = 2 * (3 * 128 * 128 + 64 * (1.5 * 128 + 128))
 PREFILL_BYTES_PER_TOKEN_HEAD = 4 * 128 * 2 + 2 + 128 * 2
+# Backward per token-head: read q, k, v, z, dO, beta (bf16); write dq, dk, dz, dv (fp32) and dbeta (fp32).
+BACKWARD_BYTES_PER_TOKEN_HEAD = 5 * 128 * 2 + 2 + 4 * 128 * 4 + 4
 # Decode per (sequence, head) per step: state read + write (fp32), q, k, v, z
 # (bf16), beta (bf16), o (bf16).
 DECODE_BYTES_PER_SEQ_HEAD = 2 * 128 * 128 * 4 + 4 * 128 * 2 + 2 + 128 * 2
@@ -231,7 +233,10 @@ def main():
             r1.record(stream)
         torch.cuda.synchronize()
         pro_ms = float(np.mean([r0.elapsed_time(r1) for r0, r1 in pev]))
+        pro_bytes = ps.B * ps.T * ps.H * PREFILL_BYTES_PER_TOKEN_HEAD + 2 * ps.B * ps.H * ps.dk * ps.dv * 4
         prologue = {"ms": round(pro_ms, 4), "tokens_per_s": round(ps.B * ps.T / (pro_ms / 1e3), 1),
+                    "achieved_GBps": round(pro_bytes / (pro_ms / 1e3) / 1e9, 1),
+                    "frac_hbm": round(pro_bytes / (pro_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                     "vs_plain_prefill": round(pro_ms / float(np.mean(pre_ms)), 4)}
         log(f"fused-prologue prefill: {pro_ms:.3f} ms ({prologue['vs_plain_prefill']:.3f} x the plain prefill)")
         del o_pro, S_pro
@@ -255,7 +260,10 @@ def main():
             r1.record(stream)
         torch.cuda.synchronize()
         bw_ms = float(np.mean([r0.elapsed_time(r1) for r0, r1 in bev]))
+        bw_bytes = ps.B * ps.T * ps.H * BACKWARD_BYTES_PER_TOKEN_HEAD + 2 * ps.B * ps.H * ps.dk * ps.dv * 4
         backward = {"ms": round(bw_ms, 3), "tokens_per_s": round(ps.B * ps.T / (bw_ms / 1e3), 1),
+                    "algorithmic_bytes": bw_bytes, "achieved_GBps": round(bw_bytes / (bw_ms / 1e3) / 1e9, 1),
+                    "frac_hbm": round(bw_bytes / (bw_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                     "vs_forward_prefill": round(bw_ms / float(np.mean(pre_ms)), 2)}
         log(f"backward: {bw_ms:.2f} ms ({backward['vs_forward_prefill']:.1f} x the forward prefill)")
         del bw_ws
@@ -293,7 +301,10 @@ def main():
         seg_ms = timed(lambda: kda.chunk_fwd_z_segmented(*largs, nseg, -5.0, ls.chunk, o=o_l, S_out=S_l,
                                                          workspace=ws, stream=stream), 5)
         one_ms = timed(lambda: kda.chunk_fwd_z(*largs, -5.0, ls.chunk, o=o_l, S_out=S_l, stream=stream), 2)
+        l_bytes = ls.B * ls.T * ls.H * PREFILL_BYTES_PER_TOKEN_HEAD + 2 * ls.B * ls.H * ls.dk * ls.dv * 4
         long_ctx = {"workload": ls.name, "segments": nseg, "ms": round(seg_ms, 3),
+                    "achieved_GBps": round(l_bytes / (seg_ms / 1e3) / 1e9, 1),
+                    "frac_hbm": round(l_bytes / (seg_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                     "tokens_per_s": round(ls.B * ls.T / (seg_ms / 1e3), 1), "one_pass_ms": round(one_ms, 3)}
         log(f"1M-token prefill: {seg_ms:.2f} ms in {nseg} segments, {one_ms:.2f} ms in one pass")
         del L, o_l, S_l, ws, largs
