@@ -767,15 +767,12 @@ template <int DK, int DV, int NSP, typename Tin, typename Tdo>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   auto kern = chunk_bwd_kernel<DK, DV, NSP, Tin, Tdo>;
   constexpr int bytes = bw::Layout<DK, DV / NSP>::BYTES;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(kern, dim3(a.B * a.H * NSP), dim3(bw::NT), bytes, st, a);
-  hipError_t e = hipGetLastError();
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = set_lds_limit(reinterpret_cast<const void*>(kern), bytes, lds_set);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(static_cast<int64_t>(a.B) * a.H * NSP)), dim3(bw::NT), bytes,
+                     st, a);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (NSP == 2) {
     const int64_t ntok = static_cast<int64_t>(a.B) * a.T * a.H;

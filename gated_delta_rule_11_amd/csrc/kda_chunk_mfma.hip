@@ -43,6 +43,7 @@ constexpr int DK = 128;        // key / value head dim
 constexpr int RS = DK + 8;     // row stride (bf16 elements) of [token][channel] tiles
 constexpr int TS = C + 8;      // row stride of [channel][token] tiles
 constexpr int XS = 24;         // row stride of the 16x16 diagonal inverses
+constexpr int LFS = 20;        // row stride (floats) of the fp32 (L_ii)^T copies: conflict-free column writes
 
 // pair (i, j <= i) of 16-token tiles -> slot of its anchored key tile
 __host__ __device__ constexpr int slot(int i, int j) { return i * (i + 1) / 2 + j; }
@@ -63,7 +64,8 @@ struct Layout {
   static constexpr int GC = EB + 4 * DK * 4;            // [128] fp32 chunk decay
   static constexpr int BT = GC + DK * 4;                // [64] fp32 beta
   static constexpr int RH = BT + C * 4;                 // [64] fp32 query normalisers (fused prologue)
-  static constexpr int BYTES = RH + C * 4;
+  static constexpr int LF = RH + C * 4;                 // [4][16][LFS] fp32 (L_ii)^T, one per chain wavefront
+  static constexpr int BYTES = LF + 4 * 16 * LFS * 4;
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -289,6 +291,7 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
   float* sGC = reinterpret_cast<float*>(smem + Ly::GC);
   float* sBeta = reinterpret_cast<float*>(smem + Ly::BT);
   float* sRho = reinterpret_cast<float*>(smem + Ly::RH);
+  float* sLf = reinterpret_cast<float*>(smem + Ly::LF);
 
   // workgroup -> ((b*H + h) * nseg + segment, slice); the slices of one head and
   // segment share an XCD (and its L2)
@@ -317,7 +320,7 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
   // that the addresses built from them are computed where they are used
   // instead of being hoisted out of the chunk loop and held in registers.
   int ln, g4, r16, c0;
-  auto relane = [&]() {
+  auto relane = [&]() __attribute__((always_inline)) {
     int l = threadIdx.x & 63;
     asm volatile("" : "+v"(l));
     ln = l;
@@ -333,7 +336,7 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
   const int nch = SEG ? min(c_begin + seg_chunks, nch_all) : nch_all;
 
   // L^T / P^T tile for pair (i, j): rows s of tile j, columns t of tile i
-  auto lp_tile = [&](int i, int j, f32x4& accL, f32x4& accP) {
+  auto lp_tile = [&](int i, int j, f32x4& accL, f32x4& accP) __attribute__((always_inline)) {
     accL = f32x4{0.f, 0.f, 0.f, 0.f};
     accP = f32x4{0.f, 0.f, 0.f, 0.f};
     const uint16_t* Ar = sKA + (slot(i, j) * 16 + r16) * RS;
@@ -430,8 +433,7 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
         f32x4 dL, dP;
         lp_tile(i, i, dL, dP);
         const float bt = sBeta[16 * i + r16];
-        // lane (t = r16, g4): P[t][s] and beta_t L[t][s] for s = 4 g4 + v (masked); the L
-        // values sit in a plain array, whose elements are scalars for the broadcasts below
+        // lane (t = r16, g4): P[t][s] and beta_t L[t][s] for s = 4 g4 + v (masked)
         f32x4 pv;
         float lv[4];
 #pragma unroll
@@ -441,17 +443,25 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
           pv[v] = s <= r16 ? dP[v] : 0.f;
         }
         if constexpr (!STO) *reinterpret_cast<s16x4*>(&sP[(16 * i + r16) * TS + 16 * i + 4 * g4]) = cvt4(pv);
-        // X_ii = (I + L_ii)^-1, one column per lane (lanes 0..15), right-looking; L[r][m]
-        // is broadcast from the accumulator lane that holds it (lane r + 16 (m / 4), slot m % 4)
+        // X_ii = (I + L_ii)^-1, one column per lane (lanes 0..15), right-looking: once x[m]
+        // is final, column m of L is applied to the rows below it.  The columns of L come
+        // from this wavefront's fp32 copy of (L_ii)^T in LDS, read at wave-uniform addresses
+        // (broadcasts); only this wavefront touches the copy, and its LDS accesses complete
+        // in order, so no barrier is needed between the writes and the reads.
+        float* Lt = sLf + wv * 16 * LFS;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) Lt[(4 * g4 + v) * LFS + r16] = lv[v];
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[r] = (r == ln) ? 1.f : 0.f;
 #pragma unroll
         for (int m = 0; m < 15; ++m) {
 #pragma unroll
-          for (int r = m + 1; r < 16; ++r) {
-            const float l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv[m % 4]), r + 16 * (m / 4)));
-            x[r] -= l * x[m];
+          for (int q4 = (m + 1) / 4; q4 < 4; ++q4) {
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(Lt + m * LFS + 4 * q4);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (4 * q4 + u > m) x[4 * q4 + u] -= l4[u] * x[m];
           }
         }
         if (ln < 16) {
@@ -578,7 +588,7 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
 
     // gate of chunk tc: within-tile decay products, tile decays -> sD; q r -> sQR, v^T, beta
     // FULL: every token of the chunk is valid (all chunks but a ragged last one)
-    auto gate_a1 = [&](int tc, auto full_c) {
+    auto gate_a1 = [&](int tc, auto full_c) __attribute__((always_inline)) {
       constexpr bool FULL = decltype(full_c)::value;
       const int n = FULL ? C : min(C, T - tc);
       if (ln < 16) {
@@ -689,7 +699,7 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
     };
 
     // k r, anchored keys, eB (sD complete and the k r storage free)
-    auto gate_a2 = [&]() {
+    auto gate_a2 = [&]() __attribute__((always_inline)) {
       float d0[4], d1[4];
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
@@ -747,7 +757,7 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
     };
 
     // tiles the state chain reads until the end of a chunk (written once it is done)
-    auto gate_b = [&]() {
+    auto gate_b = [&]() __attribute__((always_inline)) {
       if constexpr (!STO)
 #pragma unroll
         for (int tt = 0; tt < 16; ++tt) *reinterpret_cast<uint32_t*>(&sQt[(16 * i + tt) * RS + c0]) = qt[tt];
@@ -849,13 +859,9 @@ template <int DVS, bool FROM_Z, typename Tout, bool SEG, bool NORM = false, bool
 static hipError_t launch_mfma_t(const ChunkArgs& a, hipStream_t st, int ns) {
   auto kern = chunk_mfma_kernel<DVS, FROM_Z, Tout, SEG, NORM, STO>;
   constexpr int bytes = mf::Layout<DVS>::BYTES;
-  static bool attr_set = false;  // set once per instantiation (idempotent if raced)
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = set_lds_limit(reinterpret_cast<const void*>(kern), bytes, lds_set);
+  if (e != hipSuccess) return e;
   const int64_t nbh = static_cast<int64_t>(a.B) * a.H * a.nseg;  // (b, h, segment) units
   const int64_t nblocks = nbh * ns;
   const int xcd_map = (nbh % 8 == 0) ? 1 : 0;

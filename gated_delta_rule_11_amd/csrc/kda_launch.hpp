@@ -3,6 +3,8 @@
 // the ABI layer (non-null where required, sizes in the supported set).
 #pragma once
 
+#include <atomic>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -94,6 +96,19 @@ struct SegScanArgs {
 };
 
 hipError_t launch_segscan(const SegScanArgs& a, hipStream_t st);
+
+// Raise a kernel's dynamic LDS limit on the current device, once per device (the
+// setting is per device); `done` is the kernel's bit set of devices already set up.
+inline hipError_t set_lds_limit(const void* kern, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t{1} << dev) : 0;
+  if (bit && (done.load(std::memory_order_relaxed) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_relaxed);
+  return e;
+}
 
 // Backward pass of the fused-gate prefill (fp32 gradients).
 struct BwdArgs {
