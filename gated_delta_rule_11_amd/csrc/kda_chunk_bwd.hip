@@ -34,6 +34,8 @@
 // in registers twice: by value-column tile (wavefront w owns columns 16 w..)
 // for the products that contract over key channels, and transposed, by key-row
 // tile, for those that contract over value channels.
+#include <type_traits>
+
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
 
@@ -64,26 +66,43 @@ struct Layout {
   static constexpr int BETA = DAL + 16 * RS, GL = BETA + 16, DGL = GL + DK, EA = DGL + DK;
   // [16][RK]: sigma(e^A z) and e^A z of the sub-chunk, kept for the gate's derivative
   static constexpr int SG = EA + DK, XZ = SG + 16 * RK;
-  static constexpr int FLOATS = XZ + 16 * RK;
+  // [16][LS]: L^T for the inverse's column reads (LS a multiple of 4: 16-byte rows)
+  static constexpr int LS = 20, LT = XZ + 16 * RK;
+  static constexpr int FLOATS = LT + 16 * LS;
   static constexpr int BYTES = FLOATS * 4;
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 }  // namespace bw
 
-// Four consecutive elements (16-byte aligned for fp32, 8-byte for bf16) as fp32.
+// Four consecutive elements (16-byte aligned for fp32, 8-byte for bf16), loaded raw
+// (so that a prefetch does not wait for its data) and widened to fp32 where used.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 template <typename T> struct io4;
 template <> struct io4<float> {
-  __device__ __forceinline__ static f32x4 load(const float* p, int64_t i) {
-    return *reinterpret_cast<const f32x4*>(p + i);
-  }
+  typedef f32x4 raw;
+  __device__ __forceinline__ static raw load(const float* p, int64_t i) { return *reinterpret_cast<const f32x4*>(p + i); }
+  __device__ __forceinline__ static f32x4 wide(raw r) { return r; }
 };
 template <> struct io4<bf16_t> {
-  __device__ __forceinline__ static f32x4 load(const bf16_t* p, int64_t i) {
-    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-    const u32x2_t u = *reinterpret_cast<const u32x2_t*>(p + i);
+  typedef u32x2_t raw;
+  __device__ __forceinline__ static raw load(const bf16_t* p, int64_t i) {
+    return *reinterpret_cast<const u32x2_t*>(p + i);
+  }
+  __device__ __forceinline__ static f32x4 wide(raw u) {
     return f32x4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u), __uint_as_float(u[1] << 16),
                  __uint_as_float(u[1] & 0xffff0000u)};
   }
+};
+template <typename T> struct io1;
+template <> struct io1<float> {
+  typedef float raw;
+  __device__ __forceinline__ static raw load(const float* p, int64_t i) { return p[i]; }
+  __device__ __forceinline__ static float wide(raw r) { return r; }
+};
+template <> struct io1<bf16_t> {
+  typedef uint16_t raw;
+  __device__ __forceinline__ static raw load(const bf16_t* p, int64_t i) { return p[i].bits; }
+  __device__ __forceinline__ static float wide(raw r) { return bf16_to_f32(r); }
 };
 
 __device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c) {
@@ -142,6 +161,7 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
   float* sEA = sm + Ly::EA;
   float* sSig = sm + Ly::SG;
   float* sXz = sm + Ly::XZ;
+  float* sLt = sm + Ly::LT;
 
   const int bh = blockIdx.x / NSP, sp = blockIdx.x % NSP;
   const int h = bh % a.H, b = bh / a.H;
@@ -210,8 +230,9 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
   // later: no branch around a load).
   constexpr int NQK = SC * DK / 4, NQV = SC * DVS / 4;  // quads of the key side, the value side
   static_assert(NQK <= NT && NQV <= NT, "one quad per thread");
-  f32x4 pk = {}, pz = {}, pq = {}, pv = {}, po = {};
-  float pb = 0.f;
+  typename io4<Tin>::raw pk = {}, pz = {}, pq = {}, pv = {};
+  typename io4<Tdo>::raw po = {};
+  typename io1<Tin>::raw pb = {};
   auto fetch = [&](int t0, int n, bool BWD) {
     {
       const int e = min(tid, NQK - 1) * 4, t = e / DK, c = e % DK;
@@ -226,7 +247,7 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
       pv = io4<Tin>::load(v, row * DV + j0 + j);
       if (BWD) po = io4<Tdo>::load(d_o, row * DV + j0 + j);
     }
-    pb = io<Tin>::load(beta, (static_cast<int64_t>(b) * T + t0 + min(ln & 15, n - 1)) * H + h);
+    pb = io1<Tin>::load(beta, (static_cast<int64_t>(b) * T + t0 + min(ln & 15, n - 1)) * H + h);
   };
   // the sub-chunk after (blk, s, BWD) in processing order: each block recomputes its
   // sub-chunks 0 .. nsub-2 forwards, then runs nsub-1 .. 0 backwards; blocks go last first
@@ -256,12 +277,14 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
   // Three steps: every thread stores its elements and computes the gate; one thread per key
   // channel sums the log-decay over the tokens; every thread scales its elements.
   auto load_sub = [&](int blk, int s, int t0, int n, bool BWD) {
-    const f32x4 kv = pk, zv = pz, qv = pq, vv = pv, ov = po;
-    const float bt = pb;
+    const auto kr = pk, zr = pz, qr = pq, vr = pv;
+    const auto orw = po;
+    const auto br = pb;
     fetch_after(blk, s, BWD);
     if (tid < NQK) {
       const int e = tid * 4, t = e / DK, c = e % DK;
       const bool ok = t < n;
+      const f32x4 kv = io4<Tin>::wide(kr), zv = io4<Tin>::wide(zr), qv = io4<Tin>::wide(qr);
       const int o = t * RK + c;
       f32x4 gg, sg4, xz;
 #pragma unroll
@@ -280,11 +303,12 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
     if (tid < NQV) {
       const int e = tid * 4, t = e / DVS, j = e % DVS;
       const bool ok = t < n;
+      const f32x4 vv = io4<Tin>::wide(vr), ov = io4<Tdo>::wide(orw);
       const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
       *reinterpret_cast<f32x4*>(sV + t * RV + j) = ok ? vv : zero;
       if (BWD) *reinterpret_cast<f32x4*>(sdO + t * RV + j) = ok ? a.scale * ov : zero;
     }
-    if (tid < SC) sBeta[tid] = tid < n ? bt : 0.f;
+    if (tid < SC) sBeta[tid] = tid < n ? io1<Tin>::wide(br) : 0.f;
     bw_barrier();
     relane();
     if (tid < DK) {  // running log-decay over the sub-chunk
@@ -313,43 +337,64 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
     }
   };
 
-  // ---- wave 0: AL = Kt Kb^T, then M = (I + L)^-1 and T = M Diag(beta) from lane broadcasts of
-  // the accumulators (L[t][m] sits in lane m + 16 (t / 4), slot t % 4); wave 1 (BWD): P = lower(Qt Kb^T)
+  // ---- 16 x 16 tile: sum over K of A[r][k] B[c][k] (both row-major with stride RSTR).
+  // Any assignment of the K channels to the K / 4 products' lane groups gives the same
+  // sum; lane group g4 takes channels (K / 4) g4 .. (K / 4) g4 + K / 4 - 1, so each lane
+  // reads its operands as contiguous 16-byte vectors.
+  auto mm_nt = [&](const float* Ap, const float* Bp, auto k_c, int RSTR) {
+    constexpr int K = decltype(k_c)::value, KQ = K / 4;
+    static_assert(KQ % 4 == 0, "16-byte operand reads");
+    const float* ar = Ap + r16 * RSTR + KQ * g4;
+    const float* br = Bp + r16 * RSTR + KQ * g4;
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int qd = 0; qd < KQ / 4; ++qd) {
+      const f32x4 av = *reinterpret_cast<const f32x4*>(ar + 4 * qd);
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(br + 4 * qd);
+      acc0 = mma4(av[0], bv[0], acc0);
+      acc1 = mma4(av[1], bv[1], acc1);
+      acc0 = mma4(av[2], bv[2], acc0);
+      acc1 = mma4(av[3], bv[3], acc1);
+    }
+    return acc0 + acc1;
+  };
+
+  // ---- wave 0: AL = Kt Kb^T, then M = (I + L)^-1 and T = M Diag(beta); wave 1 (BWD):
+  // P = lower(Qt Kb^T).  The inverse takes one column per lane (lanes 0..15),
+  // right-looking: once x[m] is final, column m of L is applied to the rows below it,
+  // read from an fp32 copy of L^T in LDS at a wave-uniform address (a broadcast).  Only
+  // wave 0 touches the copy and its LDS accesses complete in order: no barrier between.
   auto lp_inverse = [&](bool BWD) {
     if (wv == 0 || (BWD && wv == 1)) {
-      const float* X = wv == 0 ? sKt : sQt;
-      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-      for (int kb = 0; kb < DK / 4; kb += 2) {
-        acc0 = mma4(X[r16 * RK + 4 * kb + g4], sKb[r16 * RK + 4 * kb + g4], acc0);
-        acc1 = mma4(X[r16 * RK + 4 * kb + 4 + g4], sKb[r16 * RK + 4 * kb + 4 + g4], acc1);
-      }
+      const f32x4 acc = mm_nt(wv == 0 ? sKt : sQt, sKb, std::integral_constant<int, DK>{}, RK);
       // acc[e] = X[t][s] with t = 4 g4 + e, s = r16
       if (wv == 1) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = 4 * g4 + e;
-          sP[t * RS + r16] = r16 <= t ? acc0[e] + acc1[e] : 0.f;
+          sP[t * RS + r16] = r16 <= t ? acc[e] : 0.f;
         }
       } else {
-        float lv[4];
+        f32x4 lv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = 4 * g4 + e;
-          const float al = acc0[e] + acc1[e];
-          if (BWD) sAL[t * RS + r16] = al;
-          lv[e] = r16 < t ? sBeta[t] * al : 0.f;
+          if (BWD) sAL[t * RS + r16] = acc[e];
+          lv[e] = r16 < t ? sBeta[t] * acc[e] : 0.f;
         }
-        // column s = ln of the inverse (lanes 0..15), right-looking
+        // L^T[s][t] = L[t][s]: row r16 of the copy, columns 4 g4 .. 4 g4 + 3
+        *reinterpret_cast<f32x4*>(sLt + r16 * Ly::LS + 4 * g4) = lv;
         float x[SC];
 #pragma unroll
         for (int r = 0; r < SC; ++r) x[r] = (r == ln) ? 1.f : 0.f;
 #pragma unroll
         for (int m = 0; m < SC - 1; ++m) {
 #pragma unroll
-          for (int r = m + 1; r < SC; ++r) {
-            const float l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv[r % 4]), m + 16 * (r / 4)));
-            x[r] -= l * x[m];
+          for (int q4 = (m + 1) / 4; q4 < 4; ++q4) {
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(sLt + m * Ly::LS + 4 * q4);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (4 * q4 + u > m) x[4 * q4 + u] -= l4[u] * x[m];
           }
         }
         if (ln < SC) {
@@ -407,16 +452,7 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
     }
     return acc + acc2;
   };
-  // ---- 16 x 16 tile: sum over K of A[r][k] B[c][k] (both row-major with stride RSTR)
-  auto mm_nt = [&](const float* Ap, const float* Bp, int K, int RSTR) {
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int kb = 0; kb < K / 4; kb += 2) {
-      acc0 = mma4(Ap[r16 * RSTR + 4 * kb + g4], Bp[r16 * RSTR + 4 * kb + g4], acc0);
-      acc1 = mma4(Ap[r16 * RSTR + 4 * kb + 4 + g4], Bp[r16 * RSTR + 4 * kb + 4 + g4], acc1);
-    }
-    return acc0 + acc1;
-  };
+
 
   if (tid < DK) sEA[tid] = __expf(a.A[h * DK + tid]);
   // dS_out
@@ -526,7 +562,7 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
         if (g4 == 0) sdGl[16 * ct + r16] = part;
       }
       if (wv == W_DP) {  // dP = lower(dO U^T)
-        const f32x4 acc = mm_nt(sdO, sU, DVS, RV);
+        const f32x4 acc = mm_nt(sdO, sU, std::integral_constant<int, DVS>{}, RV);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = 4 * g4 + e;
@@ -534,7 +570,7 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
         }
       }
       if (wv == W_DT0) {  // dU V^T
-        const f32x4 acc = mm_nt(sdU, sV, DVS, RV);
+        const f32x4 acc = mm_nt(sdU, sV, std::integral_constant<int, DVS>{}, RV);
 #pragma unroll
         for (int e = 0; e < 4; ++e) sdT0[(4 * g4 + e) * RS + r16] = acc[e];
       }
@@ -583,7 +619,7 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
         }
       }
       if (wv == W_DT1) {  // dW Kt^T
-        const f32x4 acc = mm_nt(sdW, sKt, DK, RK);
+        const f32x4 acc = mm_nt(sdW, sKt, std::integral_constant<int, DK>{}, RK);
 #pragma unroll
         for (int e = 0; e < 4; ++e) sdT1[(4 * g4 + e) * RS + r16] = acc[e];
       }
@@ -675,13 +711,13 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
         const int e = tid + i * NT, t = e / DK, c = e % DK;
         if (SC * DK % NT != 0 && e >= SC * DK) break;
         const int o = t * RK + c;
-        const float Gm = __expf(sG[o]);
+        const float Gm = __expf(sG[o]), Gi = __expf(-sG[o]);
         const float dqt = sdQt[o], dkt = sdKt[o], dkb = sdKb[o], dkh = sdKh[o];
         sG[o] = dqt * sQt[o] + dkt * sKt[o] - dkb * sKb[o] - dkh * sKh[o];
         if (t < n) {
           const int64_t row = (static_cast<int64_t>(b) * T + t0 + t) * H + h;
           gq[row * DK + c] = dqt * Gm;
-          gk[row * DK + c] = dkt * Gm + dkb / Gm + dkh * sGl[c] / Gm;
+          gk[row * DK + c] = dkt * Gm + (dkb + dkh * sGl[c]) * Gi;
         }
       }
       bw_barrier();
