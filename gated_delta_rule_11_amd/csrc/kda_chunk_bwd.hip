@@ -290,7 +290,7 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         xz[i] = sEA[c + i] * zv[i];
-        sg4[i] = 1.f / (1.f + __expf(-xz[i]));
+        sg4[i] = fast_rcp(1.f + __expf(-xz[i]));
         gg[i] = ok ? g_min * sg4[i] : 0.f;
       }
       const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -347,14 +347,21 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
     const float* ar = Ap + r16 * RSTR + KQ * g4;
     const float* br = Bp + r16 * RSTR + KQ * g4;
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    // the reads of the next four channels go out before the products of the current ones
+    f32x4 av = *reinterpret_cast<const f32x4*>(ar), bv = *reinterpret_cast<const f32x4*>(br);
 #pragma unroll
     for (int qd = 0; qd < KQ / 4; ++qd) {
-      const f32x4 av = *reinterpret_cast<const f32x4*>(ar + 4 * qd);
-      const f32x4 bv = *reinterpret_cast<const f32x4*>(br + 4 * qd);
+      f32x4 an = av, bn = bv;
+      if (qd + 1 < KQ / 4) {
+        an = *reinterpret_cast<const f32x4*>(ar + 4 * qd + 4);
+        bn = *reinterpret_cast<const f32x4*>(br + 4 * qd + 4);
+      }
       acc0 = mma4(av[0], bv[0], acc0);
       acc1 = mma4(av[1], bv[1], acc1);
       acc0 = mma4(av[2], bv[2], acc0);
       acc1 = mma4(av[3], bv[3], acc1);
+      av = an;
+      bv = bn;
     }
     return acc0 + acc1;
   };
