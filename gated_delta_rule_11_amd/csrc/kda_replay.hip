@@ -18,25 +18,11 @@
 
 namespace kda {
 
-template <int DK, int DV, typename Tin>
-struct ReplayToken {
-  using Sh = DecodeShape<DK, DV>;
-  float kc[Sh::RPT], qc[Sh::RPT], zc[Sh::RPT], vc[4], bt;
-
-  __device__ __forceinline__ void load(const Tin* q, const Tin* k, const Tin* v, const Tin* z, const Tin* beta,
-                                       int64_t tok, int rg, int j4) {
-#pragma unroll
-    for (int i = 0; i < Sh::RPT; ++i) {
-      const int c = rg + Sh::NR * i;
-      kc[i] = io<Tin>::load(k, tok * DK + c);
-      qc[i] = io<Tin>::load(q, tok * DK + c);
-      zc[i] = io<Tin>::load(z, tok * DK + c);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) vc[e] = io<Tin>::load(v, tok * DV + 4 * j4 + e);
-    bt = io<Tin>::load(beta, tok);
-  }
-};
+// Drafted tokens staged in LDS per group: their keys, queries, decays and values are
+// read from HBM once per workgroup (coalesced, one element per thread) instead of by
+// every thread that uses them, and each decay is formed once instead of once per
+// value-column group.
+constexpr int kReplayGroup = 8;
 
 template <int DK, int DV, typename Tin, typename Tout>
 __global__ __launch_bounds__(decode_threads(DK, DV)) void replay_kernel(
@@ -45,15 +31,27 @@ __global__ __launch_bounds__(decode_threads(DK, DV)) void replay_kernel(
     const float* __restrict__ S_snap, Tout* __restrict__ o, float* __restrict__ S_commit,
     const int* __restrict__ accepted, int n_draft, int N, int H, float scale) {
   using Sh = DecodeShape<DK, DV>;
+  constexpr int DG = kReplayGroup;
   const int nh = blockIdx.x;  // n * H + h
   const int n = nh / H;
   const int h = nh % H;
   const int tid = threadIdx.x;
+  // thread (rg, j4) owns value columns 4 j4 .. 4 j4 + 3 of rows rg + NR i (the decode
+  // step's layout, so that replaying a draft gives bit for bit what a decode step
+  // gives); the staged keys, queries and decays are stored permuted, channel c at
+  // position (c % NR) RPT + c / NR, so that a thread's rows are contiguous in LDS
   const int j4 = tid % Sh::NJ;
   const int rg = tid / Sh::NJ;
+  const int r0 = Sh::RPT * rg;
   // accepted prefix length, clamped to [0, n_draft]
   const int m = min(max(accepted[n], 0), n_draft);
 
+  __shared__ __attribute__((aligned(16))) float kS[DG][DK];
+  __shared__ __attribute__((aligned(16))) float qS[DG][DK];
+  __shared__ __attribute__((aligned(16))) float aS[DG][DK];  // decays alpha
+  __shared__ __attribute__((aligned(16))) float vS[DG][DV];
+  __shared__ float bS[DG];
+  __shared__ float eaS[DK];  // e^A log2 e
   // two sets of reduction slots, alternating between steps: one barrier per step
   __shared__ float red_r[2][Sh::NR][DV];
   __shared__ float red_y[2][Sh::NR][DV];
@@ -68,62 +66,76 @@ __global__ __launch_bounds__(decode_threads(DK, DV)) void replay_kernel(
 #pragma unroll
     for (int i = 0; i < Sh::RPT; ++i) __builtin_nontemporal_store(s[i], &Cp[(rg + Sh::NR * i) * Sh::NJ + j4]);
   }
-  float ea[Sh::RPT];
-#pragma unroll
-  for (int i = 0; i < Sh::RPT; ++i) ea[i] = __expf(A[h * DK + rg + Sh::NR * i]) * kLog2e;
+  for (int c = tid; c < DK; c += Sh::NTHREADS) eaS[c] = __expf(A[h * DK + c]) * kLog2e;
 
-  ReplayToken<DK, DV, Tin> cur, nxt;
-  if (n_draft > 0) cur.load(q, k, v, z, beta, static_cast<int64_t>(n) * H + h, rg, j4);
-  for (int t = 0; t < n_draft; ++t) {
-    const int64_t tok = (static_cast<int64_t>(t) * N + n) * H + h;
-    // the next drafted token's vectors are in flight while this one is processed
-    if (t + 1 < n_draft) nxt.load(q, k, v, z, beta, tok + static_cast<int64_t>(N) * H, rg, j4);
-    const int buf = t & 1;
-
-    float r[4] = {0.f, 0.f, 0.f, 0.f}, y[4] = {0.f, 0.f, 0.f, 0.f};
-    float kq = 0.f;
-#pragma unroll
-    for (int i = 0; i < Sh::RPT; ++i) {
-      const float ac = fast_exp2(gate_log2(cur.zc[i], ea[i], gmin_l2e));
-      s[i].x *= ac; s[i].y *= ac; s[i].z *= ac; s[i].w *= ac;
-      r[0] += cur.kc[i] * s[i].x; r[1] += cur.kc[i] * s[i].y; r[2] += cur.kc[i] * s[i].z; r[3] += cur.kc[i] * s[i].w;
-      y[0] += cur.qc[i] * s[i].x; y[1] += cur.qc[i] * s[i].y; y[2] += cur.qc[i] * s[i].z; y[3] += cur.qc[i] * s[i].w;
-      kq += cur.kc[i] * cur.qc[i];
+  for (int g0 = 0; g0 < n_draft; g0 += DG) {
+    const int nd = min(DG, n_draft - g0);
+    __syncthreads();  // the previous group's staged values are no longer read (and eaS is written)
+    for (int e = tid; e < nd * DK; e += Sh::NTHREADS) {
+      const int t = e / DK, c = e % DK;
+      const int pc = (c % Sh::NR) * Sh::RPT + c / Sh::NR;
+      const int64_t tok = (static_cast<int64_t>(g0 + t) * N + n) * H + h;
+      kS[t][pc] = io<Tin>::load(k, tok * DK + c);
+      qS[t][pc] = io<Tin>::load(q, tok * DK + c);
+      aS[t][pc] = fast_exp2(gate_log2(io<Tin>::load(z, tok * DK + c), eaS[c], gmin_l2e));
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      red_r[buf][rg][4 * j4 + e] = r[e];
-      red_y[buf][rg][4 * j4 + e] = y[e];
+    for (int e = tid; e < nd * DV; e += Sh::NTHREADS) {
+      const int t = e / DV, j = e % DV;
+      vS[t][j] = io<Tin>::load(v, ((static_cast<int64_t>(g0 + t) * N + n) * H + h) * DV + j);
     }
-    if (j4 == 0) red_kq[buf][rg] = kq;
+    if (tid < nd) bS[tid] = io<Tin>::load(beta, (static_cast<int64_t>(g0 + tid) * N + n) * H + h);
     __syncthreads();
-    float rt[4] = {0.f, 0.f, 0.f, 0.f}, yt[4] = {0.f, 0.f, 0.f, 0.f};
-    float kqt = 0.f;
+
+    for (int t = 0; t < nd; ++t) {
+      const int tg = g0 + t;
+      const int64_t tok = (static_cast<int64_t>(tg) * N + n) * H + h;
+      const int buf = tg & 1;
+      float r[4] = {0.f, 0.f, 0.f, 0.f}, y[4] = {0.f, 0.f, 0.f, 0.f};
+      float kq = 0.f;
 #pragma unroll
-    for (int g = 0; g < Sh::NR; ++g) {
+      for (int i = 0; i < Sh::RPT; ++i) {
+        const float ac = aS[t][r0 + i], kc = kS[t][r0 + i], qc = qS[t][r0 + i];
+        s[i].x *= ac; s[i].y *= ac; s[i].z *= ac; s[i].w *= ac;
+        r[0] += kc * s[i].x; r[1] += kc * s[i].y; r[2] += kc * s[i].z; r[3] += kc * s[i].w;
+        y[0] += qc * s[i].x; y[1] += qc * s[i].y; y[2] += qc * s[i].z; y[3] += qc * s[i].w;
+        kq += kc * qc;
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        rt[e] += red_r[buf][g][4 * j4 + e];
-        yt[e] += red_y[buf][g][4 * j4 + e];
+        red_r[buf][rg][4 * j4 + e] = r[e];
+        red_y[buf][rg][4 * j4 + e] = y[e];
       }
-      kqt += red_kq[buf][g];
-    }
-    float ev[4];
+      if (j4 == 0) red_kq[buf][rg] = kq;
+      __syncthreads();
+      float rt[4] = {0.f, 0.f, 0.f, 0.f}, yt[4] = {0.f, 0.f, 0.f, 0.f};
+      float kqt = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) ev[e] = cur.bt * (cur.vc[e] - rt[e]);
+      for (int gg = 0; gg < Sh::NR; ++gg) {
 #pragma unroll
-    for (int i = 0; i < Sh::RPT; ++i) {
-      s[i].x += cur.kc[i] * ev[0]; s[i].y += cur.kc[i] * ev[1]; s[i].z += cur.kc[i] * ev[2]; s[i].w += cur.kc[i] * ev[3];
-    }
-    if (rg == 0) {
+        for (int e = 0; e < 4; ++e) {
+          rt[e] += red_r[buf][gg][4 * j4 + e];
+          yt[e] += red_y[buf][gg][4 * j4 + e];
+        }
+        kqt += red_kq[buf][gg];
+      }
+      const float bt = bS[t];
+      float ev[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) io<Tout>::store(o, tok * DV + 4 * j4 + e, scale * (yt[e] + ev[e] * kqt));
-    }
-    if (t + 1 == m) {
+      for (int e = 0; e < 4; ++e) ev[e] = bt * (vS[t][4 * j4 + e] - rt[e]);
 #pragma unroll
-      for (int i = 0; i < Sh::RPT; ++i) __builtin_nontemporal_store(s[i], &Cp[(rg + Sh::NR * i) * Sh::NJ + j4]);
+      for (int i = 0; i < Sh::RPT; ++i) {
+        const float kc = kS[t][r0 + i];
+        s[i].x += kc * ev[0]; s[i].y += kc * ev[1]; s[i].z += kc * ev[2]; s[i].w += kc * ev[3];
+      }
+      if (rg == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) io<Tout>::store(o, tok * DV + 4 * j4 + e, scale * (yt[e] + ev[e] * kqt));
+      }
+      if (tg + 1 == m) {
+#pragma unroll
+        for (int i = 0; i < Sh::RPT; ++i) __builtin_nontemporal_store(s[i], &Cp[(rg + Sh::NR * i) * Sh::NJ + j4]);
+      }
     }
-    if (t + 1 < n_draft) cur = nxt;
   }
 }
 
