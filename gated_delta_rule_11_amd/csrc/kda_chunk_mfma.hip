@@ -248,12 +248,13 @@ __constant__ int8_t kOffPairs8[4][2][2] = {{{1, 0}, {3, 0}}, {{2, 1}, {3, 1}}, {
 //                          tiles of chunk n+1 while the chain wavefronts update the state.
 // Each role runs its own loop (no register of one role is merged with the other's),
 // and both loops pass the same barriers:
-//   B : gate: write q Gamma, (k Gamma_C/Gamma)^T, Gamma_C of chunk n
-//   2 : all : L, P tiles; chain: diagonal tiles + inverses; gate: off-diagonal tiles and
+//   2 : all : L, P tiles; chain: diagonal tiles + inverses; gate: (k Gamma_C/Gamma)^T and
+//             Gamma_C of chunk n (read in A2), off-diagonal tiles and
 //             the prefetch of chunk n+1 (in flight until A1)
 //   3 : all : (I + L)[W | Ut] = Diag(beta)[K Gamma | V]; W tile w per wavefront, Ut on chain
 //   A1: chain: U = Ut - W S, (q Gamma) S   | gate: gate and decays of chunk n+1, k sf
-//   A2: chain: O += P U, state update      | gate: k r, eB, anchored keys (all but adjacent pairs)
+//   A2: chain: O += P U, state update      | gate: k r, q r, q Gamma, eB, anchored keys (all but
+//                                          |       adjacent pairs) of chunk n+1
 //
 // SEG instantiations serve the passes of the segment-parallel form (one
 // workgroup per segment; identity entry state, zero values, outputs skipped,
@@ -424,7 +425,6 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
 #pragma unroll
           for (int v = 0; v < 4; ++v) ck[(16 * ct + 4 * g4 + v) * DK + j0 + 16 * wv + r16] = S[ct][v];
       }
-      lds_barrier();  // B
       relane();
 
       // ---- 2: diagonal L, P tiles of tile wv and the inverse of (I + L_ii)
@@ -582,9 +582,9 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
     RawTile<FROM_Z> R;
     uint32_t kr[16], qr[16], ks[16];  // A1 -> A2: bf16 pairs of k r, q r, k sf
     float D0 = 1.f, D1 = 1.f;         // A1 -> A2: decay over the tile
-    uint32_t qt[16], kh[16];          // A2 -> B: q Gamma pairs, (k Gamma_C / Gamma)^T pairs
-    float gc0 = 1.f, gc1 = 1.f;       // A2 -> B: Gamma_C (written by tile 0's wavefront)
-    float rho = 1.f;                  // A1 -> B (prologue): query normaliser of token (ln >> 2) & 15
+    uint32_t kh[16];                  // A2 -> 2: (k Gamma_C / Gamma)^T pairs
+    float gc0 = 1.f, gc1 = 1.f;       // A2 -> 2: Gamma_C (written by tile 0's wavefront)
+    float rho = 1.f;                  // A1 -> 2 (prologue): query normaliser of token (ln >> 2) & 15
 
     // gate of chunk tc: within-tile decay products, tile decays -> sD; q r -> sQR, v^T, beta
     // FULL: every token of the chunk is valid (all chunks but a ragged last one)
@@ -685,9 +685,6 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
         D0 = fast_exp2(last0 - base0);
         D1 = fast_exp2(last1 - base1);
       }
-      if constexpr (!STO)
-#pragma unroll
-        for (int tt = 0; tt < 16; ++tt) *reinterpret_cast<uint32_t*>(&sQR[(16 * i + tt) * RS + c0]) = qr[tt];
       // k sf of this tile is the anchored-key slot (i + 1, i) as it stands (no tile
       // in between); the scaled slots read it back in the next phase
       if (i < 3) {
@@ -744,7 +741,13 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
 #pragma unroll
       for (int tt = 0; tt < 16; ++tt) {
         *reinterpret_cast<uint32_t*>(&sKR[(16 * i + tt) * RS + c0]) = kr[tt];
-        qt[tt] = pack2(bflo(qr[tt]) * eB0, bfhi(qr[tt]) * eB1);
+        if constexpr (!STO) {
+          // q r (read by the next phase 2) and q Gamma (read by the next A1); the state
+          // chain's reads of the current chunk's q Gamma ended with A1
+          *reinterpret_cast<uint32_t*>(&sQR[(16 * i + tt) * RS + c0]) = qr[tt];
+          *reinterpret_cast<uint32_t*>(&sQt[(16 * i + tt) * RS + c0]) =
+              pack2(bflo(qr[tt]) * eB0, bfhi(qr[tt]) * eB1);
+        }
       }
 #pragma unroll
       for (int tp = 0; tp < 8; ++tp) {
@@ -756,11 +759,8 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
       gc1 = af1 * D1;
     };
 
-    // tiles the state chain reads until the end of a chunk (written once it is done)
+    // tiles the state chain reads in A2 (written once the previous chunk's A2 is done)
     auto gate_b = [&]() __attribute__((always_inline)) {
-      if constexpr (!STO)
-#pragma unroll
-        for (int tt = 0; tt < 16; ++tt) *reinterpret_cast<uint32_t*>(&sQt[(16 * i + tt) * RS + c0]) = qt[tt];
       u32x4* d = reinterpret_cast<u32x4*>(&sKhT[c0 * TS + 16 * i]);
       d[0] = u32x4{kh[0], kh[1], kh[2], kh[3]};
       d[1] = u32x4{kh[4], kh[5], kh[6], kh[7]};
@@ -792,9 +792,7 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
       const bool more = ch + 1 < nch;
 
       relane();
-      gate_b();  // B
-      lds_barrier();
-      relane();
+      gate_b();
 
       // ---- 2: off-diagonal L, P tiles; keys, queries and gate inputs of the next chunk,
       // in flight until A1.  All workgroups load at once here and the loads issue only
