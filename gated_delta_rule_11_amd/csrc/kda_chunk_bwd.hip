@@ -190,6 +190,7 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
   const int64_t SZ = static_cast<int64_t>(DK) * DV;
   const float* ckpt = a.ckpt + static_cast<int64_t>(bh) * nblk * SZ;
   float* scratch = a.scratch + static_cast<int64_t>(bh) * 3 * SZ;  // the slices write disjoint columns
+  float* const mcache = a.mcache ? a.mcache + (static_cast<int64_t>(bh) * NSP + sp) * kBwdMCacheFloats : nullptr;
   const Tin* q = static_cast<const Tin*>(a.q);
   const Tin* k = static_cast<const Tin*>(a.k);
   const Tin* v = static_cast<const Tin*>(a.v);
@@ -371,7 +372,29 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
   // right-looking: once x[m] is final, column m of L is applied to the rows below it,
   // read from an fp32 copy of L^T in LDS at a wave-uniform address (a broadcast).  Only
   // wave 0 touches the copy and its LDS accesses complete in order: no barrier between.
-  auto lp_inverse = [&](bool BWD) {
+  // cw (recompute): also leave M and AL in the cache slot; cached (backward): take M and
+  // AL as prefetched from the slot the recompute filled instead of forming them again.
+  f32x4 pre_m = {}, pre_al = {};  // wave 0: lane (g4, r16) holds row 4 g4 + e, column r16
+  auto prefetch_m = [&](const float* cr) {
+    if (wv == 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pre_m[e] = cr[(4 * g4 + e) * 16 + r16];
+        pre_al[e] = cr[256 + (4 * g4 + e) * 16 + r16];
+      }
+    }
+  };
+  auto lp_inverse = [&](bool BWD, float* cw, bool cached) {
+    if (wv == 0 && cached) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 4 * g4 + e;
+        sM[t * RS + r16] = pre_m[e];
+        sT[t * RS + r16] = pre_m[e] * sBeta[r16];
+        sAL[t * RS + r16] = pre_al[e];
+      }
+      return;
+    }
     if (wv == 0 || (BWD && wv == 1)) {
       const f32x4 acc = mm_nt(wv == 0 ? sKt : sQt, sKb, std::integral_constant<int, DK>{}, RK);
       // acc[e] = X[t][s] with t = 4 g4 + e, s = r16
@@ -387,6 +410,7 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
         for (int e = 0; e < 4; ++e) {
           const int t = 4 * g4 + e;
           if (BWD) sAL[t * RS + r16] = acc[e];
+          if (cw) cw[256 + t * 16 + r16] = acc[e];
           lv[e] = r16 < t ? sBeta[t] * acc[e] : 0.f;
         }
         // L^T[s][t] = L[t][s]: row r16 of the copy, columns 4 g4 .. 4 g4 + 3
@@ -410,6 +434,7 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
           for (int t = 0; t < SC; ++t) {
             sM[t * RS + ln] = x[t];
             sT[t * RS + ln] = x[t] * bs;
+            if (cw) cw[t * 16 + ln] = x[t];
           }
         }
       }
@@ -484,7 +509,7 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
       load_sub(blk, s, t0, n, false);
       bw_barrier();
       relane();
-      lp_inverse(false);
+      lp_inverse(false, mcache ? mcache + s * 512 : nullptr, false);
       bw_barrier();
       relane();
       f32x4 Ut;
@@ -523,7 +548,8 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
       load_sub(blk, s, t0, n, true);
       bw_barrier();
       relane();
-      lp_inverse(true);
+      lp_inverse(true, nullptr, mcache && s + 1 < nsub);
+      if (mcache && s > 0) prefetch_m(mcache + (s - 1) * 512);  // for the next sub-chunk
       bw_barrier();
       relane();
       f32x4 Ut;
