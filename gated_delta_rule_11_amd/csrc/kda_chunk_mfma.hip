@@ -98,6 +98,18 @@ __device__ __forceinline__ s16x4 cvt4(f32x4 x) {
 __device__ __forceinline__ s16x4 lds64(const uint16_t* p) {
   return __builtin_bit_cast(s16x4, *reinterpret_cast<const u32x2*>(p));
 }
+// One 8-byte LDS read per call, for the state chain's operand reads in A1 and A2.  They
+// go through a volatile LDS pointer so that the compiler keeps each one a single
+// ds_read_b64: paired into one ds_read2_b64 (two addresses 32 bytes apart, as these
+// tiles are read), the same lanes take eight cycles of bank conflicts per instruction
+// on gfx950, while two separate reads at these strides take none (measured with the
+// LDS bank-conflict counter).  Elsewhere (the solve) the pairing stays: there the
+// volatile reads' fixed order cost more than the conflicts.
+typedef __attribute__((address_space(3))) const volatile u32x2 lds_u32x2;
+__device__ __forceinline__ s16x4 lds64u(const uint16_t* p) {
+  const u32x2 v = *(lds_u32x2*)(p);  // a plain volatile load (a bit-cast of the lvalue would drop it)
+  return __builtin_bit_cast(s16x4, v);
+}
 __device__ __forceinline__ u32x4 lds128(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ u32x4 cat(s16x4 lo, s16x4 hi) {
   const u32x2 l = __builtin_bit_cast(u32x2, lo), h = __builtin_bit_cast(u32x2, hi);
@@ -493,7 +505,7 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
           const uint16_t* Wr = &sW[(16 * i + r16) * RS + 4 * g4];
 #pragma unroll
           for (int cp = 0; cp < 4; ++cp)
-            acc = mma32(cat(lds64(Wr + 32 * cp), lds64(Wr + 32 * cp + 16)), cat(Sb[2 * cp], Sb[2 * cp + 1]), acc);
+            acc = mma32(cat(lds64u(Wr + 32 * cp), lds64u(Wr + 32 * cp + 16)), cat(Sb[2 * cp], Sb[2 * cp + 1]), acc);
           Ub[i] = cvt4(acc);
         }
 #pragma unroll
@@ -503,7 +515,7 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
           if constexpr (!STO) {
 #pragma unroll
             for (int cp = 0; cp < 4; ++cp)
-              acc = mma32(cat(lds64(Qr + 32 * cp), lds64(Qr + 32 * cp + 16)), cat(Sb[2 * cp], Sb[2 * cp + 1]), acc);
+              acc = mma32(cat(lds64u(Qr + 32 * cp), lds64u(Qr + 32 * cp + 16)), cat(Sb[2 * cp], Sb[2 * cp + 1]), acc);
           }
           O[i] = acc;
         }
@@ -524,10 +536,10 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
             const uint16_t* Pr = &sP[(16 * i + r16) * TS + 4 * g4];
 #pragma unroll
             for (int m = 0; m + 1 <= i; m += 2)
-              acc = mma32(cat(lds64(Pr + 16 * m), lds64(Pr + 16 * m + 16)), cat(Ub[m], Ub[m + 1]), acc);
+              acc = mma32(cat(lds64u(Pr + 16 * m), lds64u(Pr + 16 * m + 16)), cat(Ub[m], Ub[m + 1]), acc);
             // the unpaired last tile runs on the same 16x16x32 shape, zero-padded: an
             // accumulator produced by one MFMA shape is never fed to the other shape
-            if ((i & 1) == 0) acc = mma32(cat(lds64(Pr + 16 * i), z4), cat(Ub[i], z4), acc);
+            if ((i & 1) == 0) acc = mma32(cat(lds64u(Pr + 16 * i), z4), cat(Ub[i], z4), acc);
             // rows t >= n lie past the end of the resource's range (H * DK >= DVS), so
             // the hardware drops their stores: no branch splits the MFMA sequence
 #pragma unroll
@@ -548,8 +560,8 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
 #pragma unroll
           for (int v = 0; v < 4; ++v) acc[v] = S[ct][v] * sGC[16 * ct + 4 * g4 + v];
           const uint16_t* Kr = &sKhT[(16 * ct + r16) * TS + 4 * g4];
-          acc = mma32(cat(lds64(Kr), lds64(Kr + 16)), cat(Ub[0], Ub[1]), acc);
-          acc = mma32(cat(lds64(Kr + 32), lds64(Kr + 48)), cat(Ub[2], Ub[3]), acc);
+          acc = mma32(cat(lds64u(Kr), lds64u(Kr + 16)), cat(Ub[0], Ub[1]), acc);
+          acc = mma32(cat(lds64u(Kr + 32), lds64u(Kr + 48)), cat(Ub[2], Ub[3]), acc);
           S[ct] = acc;
         }
       }
