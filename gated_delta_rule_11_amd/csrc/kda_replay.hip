@@ -25,7 +25,7 @@ namespace kda {
 constexpr int kReplayGroup = 8;
 
 template <int DK, int DV, typename Tin, typename Tout>
-__global__ __launch_bounds__(decode_threads(DK, DV)) void replay_kernel(
+__global__ __launch_bounds__(decode_threads(DK, DV), 3) void replay_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
     const Tin* __restrict__ z, const Tin* __restrict__ beta, const float* __restrict__ A, float gmin_l2e,
     const float* __restrict__ S_snap, Tout* __restrict__ o, float* __restrict__ S_commit,
@@ -94,6 +94,9 @@ __global__ __launch_bounds__(decode_threads(DK, DV)) void replay_kernel(
       float kq = 0.f;
 #pragma unroll
       for (int i = 0; i < Sh::RPT; ++i) {
+        // the staged rows are read eight at a time: reading all of them ahead of the
+        // products held 48 more registers across the step and halved the occupancy
+        if (i % 8 == 0 && i > 0) asm volatile("" ::: "memory");
         const float ac = aS[t][r0 + i], kc = kS[t][r0 + i], qc = qS[t][r0 + i];
         s[i].x *= ac; s[i].y *= ac; s[i].z *= ac; s[i].w *= ac;
         r[0] += kc * s[i].x; r[1] += kc * s[i].y; r[2] += kc * s[i].z; r[3] += kc * s[i].w;
@@ -109,7 +112,7 @@ __global__ __launch_bounds__(decode_threads(DK, DV)) void replay_kernel(
       __syncthreads();
       float rt[4] = {0.f, 0.f, 0.f, 0.f}, yt[4] = {0.f, 0.f, 0.f, 0.f};
       float kqt = 0.f;
-#pragma unroll
+#pragma unroll 2
       for (int gg = 0; gg < Sh::NR; ++gg) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
