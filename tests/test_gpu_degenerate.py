@@ -9,7 +9,12 @@ inputs, 1e-2 for bf16), plus the results that are exact:
 * beta = 0: the state only decays and is never written;
 * q = 0: every output is exactly zero; v = 0 with a zero entry state: the
   state and the outputs stay exactly zero;
-* many heads (H = 1024 for the prefill, 2048 for the decode): large strides.
+* many heads (H = 1024 for the prefill, 2048 for the decode): large strides;
+* head counts that select each launch shape of the matrix-core prefill: four
+  32-column slices per head (B*H = 64 with the XCD-grouped workgroup order,
+  B*H = 75 without it) and two 64-column slices in plain order (B*H = 130),
+  for the fused gate and the precomputed gate (the segment passes' shapes are
+  covered in test_gpu_segmented).
 """
 import numpy as np
 import pytest
@@ -147,3 +152,30 @@ def test_backward_no_decay_and_floor(dtype):
             assert e <= TOL[dtype], (n, e)
         if g_min == 0.0:
             assert float(g["dz"].abs().max()) == 0.0 and float(g["dA"].abs().max()) == 0.0
+
+
+@pytest.mark.parametrize("B,H", [(2, 32), (3, 25), (2, 65)])
+def test_head_counts_select_launch_shapes(B, H):
+    spec = ki.small_spec(B, H, 64 + 17, 128, 128, 64, "bf16", seed=7800 + B * H, s0_std=0.1)
+    say(f"case launch shape B={B} H={H} T={spec.T} (fused gate, precomputed gate, 2 segments)")
+    d = ki.prefill_inputs(spec)
+    dd = dev_inputs(d, spec.dtype)
+    o, S, o_ref, S_ref = _prefill(d, spec, -5.0, dd)
+    eo, es = rel_l2(host64(o), o_ref), rel_l2(host64(S), S_ref)
+    say(f"  fused gate rel-L2 o={eo:.3e} S={es:.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+    G = kda.gate(dd["z"], dd["A"], -5.0, spec.chunk)
+    o2, S2 = kda.chunk_fwd(dd["q"], dd["k"], dd["v"], dd["beta"], G, spec.chunk, S_in=dd["S0"],
+                           o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    eo, es = rel_l2(host64(o2), o_ref), rel_l2(host64(S2), S_ref)
+    say(f"  precomputed gate rel-L2 o={eo:.3e} S={es:.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+    # two segments of one chunk each: 128 (b, h, segment) units in the XCD-grouped order,
+    # 150 and 260 in plain order
+    o3, S3 = kda.chunk_fwd_z_segmented(dd["q"], dd["k"], dd["v"], dd["beta"], dd["z"], dd["A"], 2, -5.0,
+                                       spec.chunk, S_in=dd["S0"], o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    eo, es = rel_l2(host64(o3), o_ref), rel_l2(host64(S3), S_ref)
+    say(f"  two segments rel-L2 o={eo:.3e} S={es:.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]

@@ -43,6 +43,8 @@ CASES = [  # B, H, T, segments, z_mean, s0_std
     (2, 3, 64 * 9 + 17, 7, -4.0, 0.5),  # seven segments over ten chunks (two chunks, last one short)
     (1, 1, 512, 8, -8.0, 1.0),          # one chunk per segment, slowest decay: transitions matter most
     (1, 2, 200, 100, -6.0, 0.5),        # more segments than chunks: one chunk each
+    (1, 8, 64 * 16, 8, -6.0, 0.3),      # 64 (b, h, segment) units: four 32-column slices, XCD-grouped order
+    (3, 5, 64 * 10 - 9, 5, -6.0, 0.3),  # 75 units: four 32-column slices, plain order; ragged end
 ]
 
 
