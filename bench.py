@@ -354,7 +354,7 @@ def main():
         rel_o = float(np.linalg.norm(o_gpu - o_ref) / np.linalg.norm(o_ref))
         rel_S = float(np.linalg.norm(S_gpu - S_ref) / np.linalg.norm(S_ref))
         log(f"cpu baseline {cdt:.1f}s -> {cpu_tps:.1f} tokens/s; sample parity rel-L2 o={rel_o:.2e} S={rel_S:.2e}")
-        whole = "the whole workload" if nb == ps.B else f"batch entries 0-{nb - 1} of {ps.B}"
+        whole = f"the whole workload ({ps.B} batch entries)" if nb == ps.B else f"batch entries 0-{nb - 1} of {ps.B}"
         cpu = {"value": round(cpu_tps, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
                "sample": f"prefill {whole}: all {ps.H} heads, all {ps.T} tokens (fp64 token loop, "
                          f"{cdt:.1f}s)",
