@@ -241,6 +241,31 @@ def main():
         log(f"fused-prologue prefill: {pro_ms:.3f} ms ({prologue['vs_plain_prefill']:.3f} x the plain prefill)")
         del o_pro, S_pro
 
+    # ---------------- standalone gate (reported beside the step, not part of it) ----------------
+    # kda_gate on the 32K workload: z in (bf16), chunk-local log-decay sums G out (fp32).  The
+    # timed prefill fuses this step; the standalone kernel feeds kda_chunk_fwd.
+    gate = None
+    if run_pre and not args.no_extras:
+        G_out = torch.empty((ps.B, ps.T, ps.H, ps.dk), dtype=torch.float32, device=dev)
+
+        def gate_call():
+            kda.gate(P["z"], P["A"], -5.0, ps.chunk, out=G_out, stream=stream)
+        gate_call()
+        gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+        for r0, r1 in gev:
+            r0.record(stream)
+            gate_call()
+            r1.record(stream)
+        torch.cuda.synchronize()
+        gate_ms = float(np.mean([r0.elapsed_time(r1) for r0, r1 in gev]))
+        in_es = 2 if ps.dtype == "bf16" else 4
+        gate_bytes = ps.B * ps.T * ps.H * ps.dk * (in_es + 4) + ps.H * ps.dk * 4
+        gate = {"ms": round(gate_ms, 4), "algorithmic_bytes": gate_bytes,
+                "achieved_GBps": round(gate_bytes / (gate_ms / 1e3) / 1e9, 1),
+                "frac_hbm": round(gate_bytes / (gate_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"standalone gate: {gate_ms:.3f} ms, {gate['achieved_GBps']:.0f} GB/s")
+        del G_out
+
     # ---------------- backward (reported beside the step, not part of it) ----------------
     # Gradients of the 32K prefill for an upstream gradient of the outputs (the resident
     # outputs stand in for it): the checkpointing forward plus the backward kernel.
@@ -391,6 +416,7 @@ def main():
         "replay": replay,
         "long_context": long_ctx,
         "prologue": prologue,
+        "gate": gate,
         "backward": backward,
     }
     # a profiling run that timed one path reports nothing for the other
