@@ -264,7 +264,32 @@ def main():
                 "achieved_GBps": round(gate_bytes / (gate_ms / 1e3) / 1e9, 1),
                 "frac_hbm": round(gate_bytes / (gate_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
         log(f"standalone gate: {gate_ms:.3f} ms, {gate['achieved_GBps']:.0f} GB/s")
-        del G_out
+        # the unfused path: kda_gate, then kda_chunk_fwd reading G (fp32) in place of z
+        o_unf = torch.empty_like(o_pre)
+        S_unf = torch.empty_like(S_pre)
+
+        def unfused():
+            kda.gate(P["z"], P["A"], -5.0, ps.chunk, out=G_out, stream=stream)
+            kda.chunk_fwd(P["q"], P["k"], P["v"], P["beta"], G_out, ps.chunk, S_in=P["S0"], o=o_unf, S_out=S_unf,
+                          stream=stream)
+        unfused()
+        uev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+                torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+        for r0, r1, r2 in uev:
+            r0.record(stream)
+            kda.gate(P["z"], P["A"], -5.0, ps.chunk, out=G_out, stream=stream)
+            r1.record(stream)
+            kda.chunk_fwd(P["q"], P["k"], P["v"], P["beta"], G_out, ps.chunk, S_in=P["S0"], o=o_unf, S_out=S_unf,
+                          stream=stream)
+            r2.record(stream)
+        torch.cuda.synchronize()
+        unf_chunk_ms = float(np.mean([r1.elapsed_time(r2) for _, r1, r2 in uev]))
+        unf_ms = float(np.mean([r0.elapsed_time(r2) for r0, _, r2 in uev]))
+        gate["unfused_prefill"] = {"chunk_fwd_ms": round(unf_chunk_ms, 4), "gate_plus_chunk_fwd_ms": round(unf_ms, 4),
+                                   "vs_fused_prefill": round(unf_ms / float(np.mean(pre_ms)), 4)}
+        log(f"unfused prefill: gate + chunk_fwd {unf_ms:.3f} ms (chunk_fwd {unf_chunk_ms:.3f} ms), "
+            f"{gate['unfused_prefill']['vs_fused_prefill']:.3f} x the fused prefill")
+        del G_out, o_unf, S_unf
 
     # ---------------- backward (reported beside the step, not part of it) ----------------
     # Gradients of the 32K prefill for an upstream gradient of the outputs (the resident
