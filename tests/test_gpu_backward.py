@@ -81,6 +81,38 @@ def test_backward_empty_and_deterministic():
         assert torch.equal(g1[name], g2[name]), name
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_one_slice_many_heads(dtype):
+    """B*H = 256 at d_k = d_v = 128 runs one value slice per head (two slices are
+    for fewer heads): all heads on the GPU, three sampled heads against the
+    oracle.  With B = 1 a head's dA comes from that head alone."""
+    B, H, T = 1, 256, 70
+    spec = ki.small_spec(B, H, T, 128, 128, 64, dtype, seed=6300, s0_std=0.2, z_mean=-4.0)
+    say(f"case backward one slice B={B} H={H} T={T} {dtype}")
+    d = ki.prefill_inputs(spec)
+    do, dS = _cot(spec, 5, True)
+    dd = dev_inputs(d, dtype)
+    g = kda.chunk_bwd_z(dd["q"], dd["k"], dd["v"], dd["beta"], dd["z"], dd["A"], dev(do, dtype), dev(dS, "f32"),
+                        -5.0, dd["S0"])
+    torch.cuda.synchronize()
+    for h in (0, 97, 255):
+        sub = {k: np.ascontiguousarray(d[k][:, :, h:h + 1]) for k in ("q", "k", "v", "z", "beta")}
+        sub["A"] = np.ascontiguousarray(d["A"][h:h + 1])
+        sub["S0"] = np.ascontiguousarray(d["S0"][:, h:h + 1])
+        f = f64_inputs(sub, dtype)
+        ref = OB.backward_z(f["q"], f["k"], f["v"], f["beta"], f["z"], f["A"],
+                            ki.to_f64(np.ascontiguousarray(do[:, :, h:h + 1]), dtype),
+                            np.ascontiguousarray(dS[:, h:h + 1]).astype(np.float64), -5.0, f["S0"])
+        errs = {}
+        for name in ("dq", "dk", "dv", "dbeta", "dz"):
+            errs[name] = rel_l2(host64(g[name][:, :, h:h + 1]), ref[name])
+        errs["dA"] = rel_l2(host64(g["dA"][h:h + 1]), ref["dA"])
+        errs["dS_in"] = rel_l2(host64(g["dS_in"][:, h:h + 1]), ref["dS_in"])
+        say(f"  h={h} rel-L2 " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+        for name, e in errs.items():
+            assert e <= TOL[dtype], (h, name, e)
+
+
 def test_backward_32k_sampled():
     """The 32K-token workload (B=4, H=32, bf16), whole batch on the GPU, against
     the oracle on one sampled (b, h) sequence over its full length (every
