@@ -94,8 +94,9 @@ __global__ __launch_bounds__(decode_threads(DK, DV), 3) void replay_kernel(
       float kq = 0.f;
 #pragma unroll
       for (int i = 0; i < Sh::RPT; ++i) {
-        // the staged rows are read eight at a time: reading all of them ahead of the
-        // products held 48 more registers across the step and halved the occupancy
+        // the staged rows are read eight at a time: reading all 48 values ahead of the
+        // products (the compiler's choice) kept the kernel at two wavefronts per SIMD
+        // instead of the three the launch bound asks for
         if (i % 8 == 0 && i > 0) asm volatile("" ::: "memory");
         const float ac = aS[t][r0 + i], kc = kS[t][r0 + i], qc = qS[t][r0 + i];
         s[i].x *= ac; s[i].y *= ac; s[i].z *= ac; s[i].w *= ac;
