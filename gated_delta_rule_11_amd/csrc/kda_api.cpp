@@ -32,10 +32,11 @@ bool overlap(Range a, Range b) {
   return a0 < b0 + static_cast<uintptr_t>(b.bytes) && b0 < a0 + static_cast<uintptr_t>(a.bytes);
 }
 
-// Checks B, T, H, dk, dv and returns false when any product overflows the
-// supported index range.
+// Checks B, T, H, dk, dv and returns false when a size is out of range (negative
+// B or T; H, dk or dv below 1) or any product overflows the supported index range.
+// The head dims are checked here, before the products below divide by them.
 bool sizes_ok(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv) {
-  if (B < 0 || T < 0 || H < 1) return false;
+  if (B < 0 || T < 0 || H < 1 || dk < 1 || dv < 1) return false;
   if (B * H > 0x7fffffffLL) return false;
   if (H * dk > 0x7fffffffLL || H * dv > 0x7fffffffLL) return false;
   if (B > 0 && T > 0 && B * T > kMaxElems / (H * (dk > dv ? dk : dv))) return false;

@@ -53,7 +53,8 @@ extern "C" {
 typedef enum kda_status {
   KDA_OK = 0,
   KDA_ERR_NULL = 1,        /* a required pointer is NULL                     */
-  KDA_ERR_SHAPE = 2,       /* a size is negative or too large                */
+  KDA_ERR_SHAPE = 2,       /* a size is negative, zero where it must be at
+                              least 1 (H, N, dk, dv), or too large           */
   KDA_ERR_DTYPE = 3,       /* dtype enum out of range                        */
   KDA_ERR_UNSUPPORTED = 4, /* valid but not provided (dk, dv, chunk, ...)    */
   KDA_ERR_ALIAS = 5,       /* outputs overlap inputs in a forbidden way      */

@@ -250,3 +250,24 @@ def test_backward_validation(L):
     assert bwd(dk=P(7)) == ERR_ALIAS               # two gradients on one buffer
     assert bwd(ws=P(11)) == ERR_ALIAS              # workspace over a gradient
     assert bwd(B=0) == OK
+
+
+def test_zero_head_dims_rejected(L):
+    """A head dim (or H, N) of zero is a shape error on every entry point.  The size
+    checks divide by the head dims, so a zero once stopped the caller's process with
+    an integer division by zero instead of returning a status."""
+    for kw in ({"dk": 0}, {"dk": 0, "T": 0}):
+        assert gate(L, **kw) == ERR_SHAPE, kw
+    for kw in ({"dk": 0}, {"dv": 0}, {"dk": 0, "dv": 0}, {"dv": 0, "T": 0}):
+        assert chunk(L, **kw) == ERR_SHAPE, kw
+        assert chunk_z(L, **kw) == ERR_SHAPE, kw
+    for kw in ({"dk": 0}, {"dv": 0}, {"H": 0}):
+        assert decode(L, **kw) == ERR_SHAPE, kw
+        assert replay(L, **kw) == ERR_SHAPE, kw
+    assert chunk_seg(L, dk=0) == ERR_SHAPE
+    assert L.kda_chunk_fwd_z_prologue(P(0), P(1), P(2), P(3), P(4), BF16, P(8), -5.0, P(5), P(6), BF16, P(7), 1, 100,
+                                      2, 128, 0, 64, 1.0, N) == ERR_SHAPE
+    assert L.kda_decode_step_prologue(P(0), P(1), P(2), P(3), P(4), BF16, P(5), -5.0, P(6), P(7), BF16, 4, 2, 0, 128,
+                                      1.0, N) == ERR_SHAPE
+    assert L.kda_chunk_bwd_z(P(0), P(1), P(2), P(3), P(4), F32, P(5), -5.0, None, P(6), F32, None, P(7), P(8), P(9),
+                             P(10), P(11), P(12), None, 2, 100, 3, 0, 32, 1.0, P(13), 1 << 30, N) == ERR_SHAPE
