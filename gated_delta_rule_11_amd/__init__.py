@@ -106,6 +106,28 @@ def _dev(*ts):
             raise KDAError("tensors must be contiguous")
 
 
+_F32 = (torch.float32,)
+_IO = (torch.float32, torch.bfloat16)
+
+
+def _shapes(what: str, *specs):
+    """The C ABI takes raw pointers and trusts the sizes it is given, so every
+    tensor's shape and dtype are checked here, before any pointer is passed:
+    specs are (name, tensor or None, expected shape, allowed dtypes)."""
+    dev = None
+    for name, t, shape, dtypes in specs:
+        if t is None:
+            continue
+        if tuple(t.shape) != tuple(shape):
+            raise KDAError(f"{what}: {name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if t.dtype not in dtypes:
+            raise KDAError(f"{what}: {name} has dtype {t.dtype}, expected {' or '.join(map(str, dtypes))}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise KDAError(f"{what}: {name} is on {t.device}, the other tensors on {dev}")
+
+
 def _p(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -121,10 +143,21 @@ def gate(z: torch.Tensor, A: torch.Tensor, g_min: float = G_MIN, chunk: int = 1,
     B, T, H, dk = z.shape
     if out is None:
         out = torch.empty((B, T, H, dk), dtype=torch.float32, device=z.device)
+    _shapes("kda_gate", ("z", z, (B, T, H, dk), _IO), ("A", A, (H, dk), _F32), ("out", out, (B, T, H, dk), _F32))
     _dev(z, A, out)
     _check(lib().kda_gate(_p(z), _dtype_code(z), _p(A), float(g_min), B, T, H, dk, int(chunk), _p(out),
                           _stream(stream)), "kda_gate")
     return out
+
+
+def _chunk_shapes(what, q, k, v, beta, z=None, A=None, G=None, S_in=None, o=None, S_out=None):
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    io = (q.dtype,) if q.dtype in _IO else _IO
+    _shapes(what, ("q", q, (B, T, H, dk), _IO), ("k", k, (B, T, H, dk), io), ("v", v, (B, T, H, dv), io),
+            ("beta", beta, (B, T, H), io), ("z", z, (B, T, H, dk), io), ("A", A, (H, dk), _F32),
+            ("G", G, (B, T, H, dk), _F32), ("S_in", S_in, (B, H, dk, dv), _F32), ("o", o, (B, T, H, dv), _IO),
+            ("S_out", S_out, (B, H, dk, dv), _F32))
 
 
 def _outs(q, v, o, S_out, o_dtype, want_state):
@@ -144,6 +177,7 @@ def chunk_fwd(q, k, v, beta, G, chunk: int = 64, S_in=None, o=None, S_out=None, 
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     o, S_out = _outs(q, v, o, S_out, o_dtype, want_state)
+    _chunk_shapes("kda_chunk_fwd", q, k, v, beta, G=G, S_in=S_in, o=o, S_out=S_out)
     _dev(q, k, v, beta, G, S_in, o, S_out)
     _check(lib().kda_chunk_fwd(_p(q), _p(k), _p(v), _p(beta), _dtype_code(q), _p(G), _p(S_in), _p(o),
                                _dtype_code(o), _p(S_out), B, T, H, dk, dv, int(chunk), float(scale),
@@ -159,6 +193,7 @@ def chunk_fwd_z(q, k, v, beta, z, A, g_min: float = G_MIN, chunk: int = 64, S_in
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     o, S_out = _outs(q, v, o, S_out, o_dtype, want_state)
+    _chunk_shapes("kda_chunk_fwd_z", q, k, v, beta, z=z, A=A, S_in=S_in, o=o, S_out=S_out)
     _dev(q, k, v, beta, z, A, S_in, o, S_out)
     _check(lib().kda_chunk_fwd_z(_p(q), _p(k), _p(v), _p(beta), _p(z), _dtype_code(q), _p(A), float(g_min),
                                  _p(S_in), _p(o), _dtype_code(o), _p(S_out), B, T, H, dk, dv, int(chunk),
@@ -173,6 +208,7 @@ def chunk_fwd_z_prologue(q_raw, k_raw, v, beta_logit, z, A, g_min: float = G_MIN
     B, T, H, dk = q_raw.shape
     dv = v.shape[-1]
     o, S_out = _outs(q_raw, v, o, S_out, o_dtype, want_state)
+    _chunk_shapes("kda_chunk_fwd_z_prologue", q_raw, k_raw, v, beta_logit, z=z, A=A, S_in=S_in, o=o, S_out=S_out)
     _dev(q_raw, k_raw, v, beta_logit, z, A, S_in, o, S_out)
     _check(lib().kda_chunk_fwd_z_prologue(_p(q_raw), _p(k_raw), _p(v), _p(beta_logit), _p(z), _dtype_code(q_raw),
                                           _p(A), float(g_min), _p(S_in), _p(o), _dtype_code(o), _p(S_out), B, T, H,
@@ -188,6 +224,7 @@ def decode_step_prologue(q_raw, k_raw, v, z, beta_logit, A, S, g_min: float = G_
     dv = v.shape[-1]
     if o is None:
         o = torch.empty((N, H, dv), dtype=o_dtype or torch.float32, device=q_raw.device)
+    _decode_shapes("kda_decode_step_prologue", q_raw, k_raw, v, z, beta_logit, A, S, o)
     _dev(q_raw, k_raw, v, z, beta_logit, A, S, o)
     _check(lib().kda_decode_step_prologue(_p(q_raw), _p(k_raw), _p(v), _p(z), _p(beta_logit), _dtype_code(q_raw),
                                           _p(A), float(g_min), _p(S), _p(o), _dtype_code(o), N, H, dk, dv,
@@ -214,6 +251,9 @@ def chunk_bwd_z(q, k, v, beta, z, A, d_o, dS_out=None, g_min: float = G_MIN, S_i
     need = int(lib().kda_chunk_bwd_z_workspace_bytes(B, T, H, dk, dv))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _chunk_shapes("kda_chunk_bwd_z", q, k, v, beta, z=z, A=A, S_in=S_in)
+    _shapes("kda_chunk_bwd_z", ("q", q, q.shape, _IO), ("d_o", d_o, (B, T, H, dv), _IO),
+            ("dS_out", dS_out, (B, H, dk, dv), _F32))
     _dev(q, k, v, beta, z, A, d_o, dS_out, S_in, workspace, *[t for t in out.values() if t is not None])
     _check(lib().kda_chunk_bwd_z(_p(q), _p(k), _p(v), _p(beta), _p(z), _dtype_code(q), _p(A), float(g_min), _p(S_in),
                                  _p(d_o), _dtype_code(d_o), _p(dS_out), _p(out["dq"]), _p(out["dk"]), _p(out["dv"]),
@@ -241,6 +281,7 @@ def chunk_fwd_z_segmented(q, k, v, beta, z, A, segments: int, g_min: float = G_M
     need = chunk_fwd_z_segmented_workspace_bytes(B, H, dk, dv, segments)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _chunk_shapes("kda_chunk_fwd_z_segmented", q, k, v, beta, z=z, A=A, S_in=S_in, o=o, S_out=S_out)
     _dev(q, k, v, beta, z, A, S_in, o, S_out, workspace)
     _check(lib().kda_chunk_fwd_z_segmented(_p(q), _p(k), _p(v), _p(beta), _p(z), _dtype_code(q), _p(A),
                                            float(g_min), _p(S_in), _p(o), _dtype_code(o), _p(S_out), B, T, H, dk,
@@ -248,6 +289,15 @@ def chunk_fwd_z_segmented(q, k, v, beta, z, A, segments: int, g_min: float = G_M
                                            workspace.numel() * workspace.element_size(), _stream(stream)),
            "kda_chunk_fwd_z_segmented")
     return o, S_out
+
+
+def _decode_shapes(what, q, k, v, z, beta, A, S, o):
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    io = (q.dtype,) if q.dtype in _IO else _IO
+    _shapes(what, ("q", q, (N, H, dk), _IO), ("k", k, (N, H, dk), io), ("v", v, (N, H, dv), io),
+            ("z", z, (N, H, dk), io), ("beta", beta, (N, H), io), ("A", A, (H, dk), _F32),
+            ("S", S, (N, H, dk, dv), _F32), ("o", o, (N, H, dv), _IO))
 
 
 def decode_step(q, k, v, z, beta, A, S, g_min: float = G_MIN, o=None, o_dtype=None, scale: float = 1.0,
@@ -258,6 +308,7 @@ def decode_step(q, k, v, z, beta, A, S, g_min: float = G_MIN, o=None, o_dtype=No
     dv = v.shape[-1]
     if o is None:
         o = torch.empty((N, H, dv), dtype=o_dtype or torch.float32, device=q.device)
+    _decode_shapes("kda_decode_step", q, k, v, z, beta, A, S, o)
     _dev(q, k, v, z, beta, A, S, o)
     _check(lib().kda_decode_step(_p(q), _p(k), _p(v), _p(z), _p(beta), _dtype_code(q), _p(A), float(g_min),
                                  _p(S), _p(o), _dtype_code(o), N, H, dk, dv, float(scale), _stream(stream)),
@@ -278,8 +329,12 @@ def decode_replay(q, k, v, z, beta, A, S_snapshot, accepted, g_min: float = G_MI
         o = torch.empty((n_draft, N, H, dv), dtype=o_dtype or torch.float32, device=q.device)
     if S_commit is None:
         S_commit = torch.empty_like(S_snapshot)
-    if accepted.dtype != torch.int32:
-        raise KDAError("decode_replay: accepted must be int32")
+    io = (q.dtype,) if q.dtype in _IO else _IO
+    _shapes("kda_decode_replay", ("q", q, (n_draft, N, H, dk), _IO), ("k", k, (n_draft, N, H, dk), io),
+            ("v", v, (n_draft, N, H, dv), io), ("z", z, (n_draft, N, H, dk), io), ("beta", beta, (n_draft, N, H), io),
+            ("A", A, (H, dk), _F32), ("S_snapshot", S_snapshot, (N, H, dk, dv), _F32),
+            ("accepted", accepted, (N,), (torch.int32,)), ("o", o, (n_draft, N, H, dv), _IO),
+            ("S_commit", S_commit, (N, H, dk, dv), _F32))
     _dev(q, k, v, z, beta, A, S_snapshot, accepted, o, S_commit)
     _check(lib().kda_decode_replay(_p(q), _p(k), _p(v), _p(z), _p(beta), _dtype_code(q), _p(A), float(g_min),
                                    _p(S_snapshot), _p(accepted), _p(o), _dtype_code(o), _p(S_commit), n_draft, N,

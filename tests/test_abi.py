@@ -149,6 +149,35 @@ def test_binding_refuses_cpu_tensors(L):
         kda.gate(z, A, chunk=1, out=torch.zeros(1, 4, 1, 16))
 
 
+def test_binding_checks_shapes_and_dtypes():
+    """The library takes raw pointers and trusts the sizes it is given; the binding
+    refuses tensors whose shape or dtype disagree with the call before passing a
+    pointer (checked with CPU tensors: the shape check comes first)."""
+    import torch
+    B, T, H, dk, dv = 1, 8, 2, 16, 32
+    q = torch.zeros(B, T, H, dk, dtype=torch.bfloat16)
+    v = torch.zeros(B, T, H, dv, dtype=torch.bfloat16)
+    beta = torch.zeros(B, T, H, dtype=torch.bfloat16)
+    A = torch.zeros(H, dk)
+    cases = [
+        (lambda: kda.gate(q, A, out=torch.zeros(B, T, H, dk - 1)), "out has shape"),
+        (lambda: kda.gate(q, A.bfloat16()), "A has dtype"),
+        (lambda: kda.chunk_fwd_z(q, q[:, :4], v, beta, q, A), "k has shape"),
+        (lambda: kda.chunk_fwd_z(q, q.float(), v, beta, q, A), "k has dtype"),
+        (lambda: kda.chunk_fwd_z(q, q, v, beta[..., :1], q, A), "beta has shape"),
+        (lambda: kda.chunk_fwd_z(q, q, v, beta, q, A, S_in=torch.zeros(B, H, dv, dk)), "S_in has shape"),
+        (lambda: kda.chunk_fwd_z(q, q, v, beta, q, A, o=torch.zeros(B, T, H, dk)), "o has shape"),
+        (lambda: kda.chunk_fwd(q, q, v, beta, q, 16), "G has dtype"),
+        (lambda: kda.chunk_bwd_z(q, q, v, beta, q, A, q), "d_o has shape"),
+        (lambda: kda.decode_step(q[0], q[0], v[0], q[0], beta[0], A, torch.zeros(T, H, dk, dk)), "S has shape"),
+        (lambda: kda.decode_replay(q, q, v, q, beta, A, torch.zeros(T, H, dk, dv), torch.zeros(T, dtype=torch.int64)),
+         "accepted has dtype"),
+    ]
+    for call, msg in cases:
+        with pytest.raises(kda.KDAError, match=msg):
+            call()
+
+
 def replay(L, q=P(0), k=P(1), v=P(2), z=P(3), beta=P(4), it=BF16, A=P(5), gmin=-5.0, S_snap=P(6),
            acc=P(7), o=P(8), ot=BF16, S_commit=P(9), n_draft=4, Nn=4, H=2, dk=128, dv=128, scale=1.0):
     return L.kda_decode_replay(q, k, v, z, beta, it, A, gmin, S_snap, acc, o, ot, S_commit, n_draft, Nn, H, dk, dv,
