@@ -15,6 +15,7 @@ Entry points (same names as the C ABI):
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from typing import Optional, Tuple
 
@@ -128,6 +129,19 @@ def _shapes(what: str, *specs):
             raise KDAError(f"{what}: {name} is on {t.device}, the other tensors on {dev}")
 
 
+def _on_tensor_device(fn):
+    """Run a call with the device of its first tensor argument current: the library
+    launches on the current device, on that device's current stream."""
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        t = next((a for a in args if isinstance(a, torch.Tensor)), None)
+        if t is None or not t.is_cuda:
+            return fn(*args, **kwargs)
+        with torch.cuda.device(t.device):
+            return fn(*args, **kwargs)
+    return wrapper
+
+
 def _p(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -137,6 +151,7 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
+@_on_tensor_device
 def gate(z: torch.Tensor, A: torch.Tensor, g_min: float = G_MIN, chunk: int = 1,
          out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """G [B,T,H,dk] fp32: chunk-local sums of g = g_min*sigmoid(exp(A) z)."""
@@ -170,6 +185,7 @@ def _outs(q, v, o, S_out, o_dtype, want_state):
     return o, S_out
 
 
+@_on_tensor_device
 def chunk_fwd(q, k, v, beta, G, chunk: int = 64, S_in=None, o=None, S_out=None, o_dtype=None,
               scale: float = 1.0, want_state: bool = True, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked prefill from the chunk-local sums G of kda_gate (same chunk).
@@ -185,6 +201,7 @@ def chunk_fwd(q, k, v, beta, G, chunk: int = 64, S_in=None, o=None, S_out=None, 
     return o, S_out
 
 
+@_on_tensor_device
 def chunk_fwd_z(q, k, v, beta, z, A, g_min: float = G_MIN, chunk: int = 64, S_in=None, o=None, S_out=None,
                 o_dtype=None, scale: float = 1.0, want_state: bool = True,
                 stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
@@ -201,6 +218,7 @@ def chunk_fwd_z(q, k, v, beta, z, A, g_min: float = G_MIN, chunk: int = 64, S_in
     return o, S_out
 
 
+@_on_tensor_device
 def chunk_fwd_z_prologue(q_raw, k_raw, v, beta_logit, z, A, g_min: float = G_MIN, chunk: int = 64, S_in=None,
                          o=None, S_out=None, o_dtype=None, scale: float = 1.0, want_state: bool = True,
                          stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
@@ -217,6 +235,7 @@ def chunk_fwd_z_prologue(q_raw, k_raw, v, beta_logit, z, A, g_min: float = G_MIN
     return o, S_out
 
 
+@_on_tensor_device
 def decode_step_prologue(q_raw, k_raw, v, z, beta_logit, A, S, g_min: float = G_MIN, o=None, o_dtype=None,
                          scale: float = 1.0, stream=None) -> torch.Tensor:
     """``decode_step`` with the prologue fused: q, k un-normalised, beta as a logit."""
@@ -232,6 +251,7 @@ def decode_step_prologue(q_raw, k_raw, v, z, beta_logit, A, S, g_min: float = G_
     return o
 
 
+@_on_tensor_device
 def chunk_bwd_z(q, k, v, beta, z, A, d_o, dS_out=None, g_min: float = G_MIN, S_in=None, scale: float = 1.0,
                 want_dS_in: bool = True, workspace=None, stream=None) -> dict:
     """Backward of ``chunk_fwd_z``: gradients (fp32) of a loss given dL/do (``d_o``)
@@ -268,6 +288,7 @@ def chunk_fwd_z_segmented_workspace_bytes(B: int, H: int, dk: int, dv: int, segm
     return int(lib().kda_chunk_fwd_z_segmented_workspace_bytes(B, H, dk, dv, int(segments)))
 
 
+@_on_tensor_device
 def chunk_fwd_z_segmented(q, k, v, beta, z, A, segments: int, g_min: float = G_MIN, chunk: int = 64, S_in=None,
                           o=None, S_out=None, o_dtype=None, scale: float = 1.0, want_state: bool = True,
                           workspace=None, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
@@ -300,6 +321,7 @@ def _decode_shapes(what, q, k, v, z, beta, A, S, o):
             ("S", S, (N, H, dk, dv), _F32), ("o", o, (N, H, dv), _IO))
 
 
+@_on_tensor_device
 def decode_step(q, k, v, z, beta, A, S, g_min: float = G_MIN, o=None, o_dtype=None, scale: float = 1.0,
                 stream=None) -> torch.Tensor:
     """One token per sequence; S [N,H,dk,dv] fp32 is updated in place.
@@ -316,6 +338,7 @@ def decode_step(q, k, v, z, beta, A, S, g_min: float = G_MIN, o=None, o_dtype=No
     return o
 
 
+@_on_tensor_device
 def decode_replay(q, k, v, z, beta, A, S_snapshot, accepted, g_min: float = G_MIN, o=None, o_dtype=None,
                   S_commit=None, scale: float = 1.0, stream=None):
     """Speculative-decoding replay: the drafted tokens q, k, z [n_draft,N,H,dk],
