@@ -34,9 +34,12 @@ bool overlap(Range a, Range b) {
 
 // Checks B, T, H, dk, dv and returns false when a size is out of range (negative
 // B or T; H, dk or dv below 1) or any product overflows the supported index range.
-// The head dims are checked here, before the products below divide by them.
+// The head dims are checked here, before the products below divide by them.  T is
+// kept 64 below INT_MAX so that token offsets rounded up to a whole chunk (T + 63,
+// a chunk start + 64) stay within 32 bits in the kernels.
+constexpr int64_t kMaxT = 0x7fffffffLL - 64;
 bool sizes_ok(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv) {
-  if (B < 0 || T < 0 || H < 1 || dk < 1 || dv < 1) return false;
+  if (B < 0 || T < 0 || H < 1 || dk < 1 || dv < 1 || T > kMaxT) return false;
   if (B * H > 0x7fffffffLL) return false;
   if (H * dk > 0x7fffffffLL || H * dv > 0x7fffffffLL) return false;
   if (B > 0 && T > 0 && B * T > kMaxElems / (H * (dk > dv ? dk : dv))) return false;
@@ -138,8 +141,10 @@ static kda_status chunk_common(const void* q, const void* k, const void* v, cons
   a.prologue = prologue;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int nch = (T + chunk - 1) / chunk;
-  const int seg_chunks = (nch + segments - 1) / (segments > 0 ? segments : 1);
-  const int nseg = seg_chunks > 0 ? (nch + seg_chunks - 1) / seg_chunks : 1;
+  // chunks per segment and segments (more segments than chunks: one chunk each); in
+  // 64 bits, since segments may be as large as INT_MAX
+  const int seg_chunks = int((int64_t(nch) + segments - 1) / (segments > 0 ? segments : 1));
+  const int nseg = seg_chunks > 0 ? int((int64_t(nch) + seg_chunks - 1) / seg_chunks) : 1;
   if (!kda::chunk_mfma_supports(a)) {
     if (segments > 1) return KDA_ERR_UNSUPPORTED;
     return from_hip(kda::launch_chunk_generic(a, st));

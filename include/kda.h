@@ -34,7 +34,8 @@
  *    (the last chunk may be partial); input dtype KDA_F32 or KDA_BF16 (q, k,
  *    v, z, beta share it); output dtype KDA_F32 or KDA_BF16.  Anything else
  *    returns KDA_ERR_UNSUPPORTED.  Sizes are limited so that every element
- *    index fits in 63 bits and B*H, N*H fit in 31 bits.
+ *    index fits in 63 bits and B*H, N*H fit in 31 bits; T (and n_draft) is at
+ *    most 2^31 - 65.  Larger sizes return KDA_ERR_SHAPE.
  *  - Alignment: tensor base pointers 16-byte aligned (beta: its element
  *    size).  Allocator pointers and token slices of contiguous tensors with
  *    d >= 16 satisfy this.  Otherwise KDA_ERR_ALIGN.

@@ -300,3 +300,18 @@ def test_zero_head_dims_rejected(L):
                                       1.0, N) == ERR_SHAPE
     assert L.kda_chunk_bwd_z(P(0), P(1), P(2), P(3), P(4), F32, P(5), -5.0, None, P(6), F32, None, P(7), P(8), P(9),
                              P(10), P(11), P(12), None, 2, 100, 3, 0, 32, 1.0, P(13), 1 << 30, N) == ERR_SHAPE
+
+
+def test_token_count_limit(L):
+    """T (and n_draft) is at most 2^31 - 65: the kernels round token offsets up to a
+    whole chunk in 32 bits.  Just below the limit the sizes pass (the calls below
+    then stop at a NULL pointer, before anything launches)."""
+    big = (1 << 31) - 65
+    small = dict(B=1, H=1, dk=16, dv=16)
+    assert chunk(L, T=big + 1, **small) == ERR_SHAPE
+    assert chunk(L, T=big, q=None, **small) == ERR_NULL
+    assert chunk_z(L, T=big + 1, **small) == ERR_SHAPE
+    assert gate(L, T=big + 1, B=1, H=1, dk=16) == ERR_SHAPE
+    assert gate(L, T=big, B=1, H=1, dk=16, z=None) == ERR_NULL
+    assert replay(L, n_draft=big + 1, Nn=1, H=1, dk=16, dv=16) == ERR_SHAPE
+    assert replay(L, n_draft=big, Nn=1, H=1, dk=16, dv=16, q=None) == ERR_NULL
