@@ -91,6 +91,8 @@ def main():
     ap.add_argument("--cpu-sample-batches", type=int, default=4,
                     help="batch entries (all heads, all tokens) the oracle runs for the CPU baseline")
     args = ap.parse_args()
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("--steps must be at least 1 and --warmup at least 0")
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} (WORLD_SIZE={world}) is not supported; "
