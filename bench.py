@@ -243,6 +243,35 @@ def main():
         log(f"fused-prologue prefill: {pro_ms:.3f} ms ({prologue['vs_plain_prefill']:.3f} x the plain prefill)")
         del o_pro, S_pro
 
+    # ---------------- the two small configurations (reported beside the step) ----------------
+    # The tiny fp32 case and the 4K-token bf16 prefill, each one kda_chunk_fwd_z launch with
+    # its inputs resident; mean of 20 launches after one warm-up.
+    small = None
+    if run_pre and not args.no_extras:
+        small = {}
+        for cs in (ki.TINY_F32, ki.PREFILL_4K):
+            cd = ki.prefill_inputs(cs)
+            C = {k: to_dev(cd[k], cs.dtype) for k in ("q", "k", "v", "z", "beta")}
+            C["A"] = to_dev(cd["A"], "f32")
+            S0c = to_dev(cd["S0"], "f32")
+            oc = torch.empty((cs.B, cs.T, cs.H, cs.dv), dtype=torch.float32 if cs.dtype == "f32" else torch.bfloat16,
+                             device=dev)
+            Sc = torch.empty((cs.B, cs.H, cs.dk, cs.dv), dtype=torch.float32, device=dev)
+
+            def small_call():
+                kda.chunk_fwd_z(C["q"], C["k"], C["v"], C["beta"], C["z"], C["A"], -5.0, cs.chunk, S_in=S0c, o=oc,
+                                S_out=Sc, stream=stream)
+            small_call()
+            sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+            for r0, r1 in sev:
+                r0.record(stream)
+                small_call()
+                r1.record(stream)
+            torch.cuda.synchronize()
+            sms = float(np.mean([r0.elapsed_time(r1) for r0, r1 in sev]))
+            small[cs.name] = {"ms": round(sms, 4), "tokens_per_s": round(cs.B * cs.T / (sms / 1e3), 1)}
+        log(f"small configurations: {small}")
+
     # ---------------- standalone gate (reported beside the step, not part of it) ----------------
     # kda_gate on the 32K workload: z in (bf16), chunk-local log-decay sums G out (fp32).  The
     # timed prefill fuses this step; the standalone kernel feeds kda_chunk_fwd.
@@ -411,6 +440,28 @@ def main():
                "sample": f"prefill {whole}: all {ps.H} heads, all {ps.T} tokens (fp64 token loop, "
                          f"{cdt:.1f}s)",
                "sample_parity_rel_l2": {"o": rel_o, "S": rel_S}}
+        # the oracle's rate on the other configurations (context for the GPU figures of
+        # each; the decode one on a sample of the sequences: all 64 steps, 32 of 256)
+        per = {}
+        for cs in (ki.TINY_F32, ki.PREFILL_4K):
+            cd = ki.prefill_inputs(cs)
+            cf = {k: ki.to_f64(cd[k], cs.dtype) for k in ("q", "k", "v", "z", "beta")}
+            c0 = time.perf_counter()
+            oracle.forward_z(cf["q"], cf["k"], cf["v"], cf["beta"], cf["z"], cd["A"].astype(np.float64), -5.0,
+                             None if cd["S0"] is None else cd["S0"].astype(np.float64), nthreads=cores)
+            cdt2 = time.perf_counter() - c0
+            per[cs.name] = {"tokens_per_s": round(cs.B * cs.T / cdt2, 1), "s": round(cdt2, 3)}
+        n_s = 32
+        dd_s = ki.decode_inputs(ki.DECODE_256, n_sel=range(n_s))
+        df = {k: ki.to_f64(dd_s[k], ki.DECODE_256.dtype) for k in ("q", "k", "v", "z", "beta")}
+        c0 = time.perf_counter()
+        oracle.decode(df["q"], df["k"], df["v"], df["z"], df["beta"], dd_s["A"].astype(np.float64),
+                      dd_s["S0"].astype(np.float64), nthreads=cores)
+        cdt2 = time.perf_counter() - c0
+        per[ki.DECODE_256.name] = {"tokens_per_s": round(n_s * ki.DECODE_256.steps / cdt2, 1), "s": round(cdt2, 3),
+                                   "sample": f"{n_s} of {ki.DECODE_256.N} sequences, all {ki.DECODE_256.steps} steps"}
+        cpu["per_config"] = per
+        log(f"oracle on the other configurations: {per}")
 
     out = {
         "metric": METRIC,
@@ -443,6 +494,7 @@ def main():
         "replay": replay,
         "long_context": long_ctx,
         "prologue": prologue,
+        "small_configs": small,
         "gate": gate,
         "backward": backward,
     }
