@@ -72,6 +72,75 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def stats(ms):
+    """min / median / max of a list of per-rep times in ms."""
+    a = np.asarray(ms, dtype=np.float64)
+    return {"min": round(float(a.min()), 4), "median": round(float(np.median(a)), 4), "max": round(float(a.max()), 4),
+            "reps": int(a.size)}
+
+
+def _run(cmd, timeout=20):
+    import subprocess
+    try:
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=timeout)
+        return r.stdout if r.returncode == 0 else None
+    except (OSError, subprocess.SubprocessError):
+        return None
+
+
+def source_sha256():
+    """sha256 of the library's sources (kernels, C ABI, header): identifies the code measured."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_delta_rule_11_amd", "csrc")
+    for f in sorted(os.listdir(csrc)) + ["../../include/kda.h"]:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def environment(torch):
+    """Accelerator, kernel and compiler versions and the timing convention of this run."""
+    p = torch.cuda.get_device_properties(0)
+    env = {"gpu": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+           "hbm_GiB": round(p.total_memory / 2 ** 30, 1), "torch": torch.__version__, "hip_runtime": torch.version.hip}
+    try:
+        with open("/opt/rocm/.info/version") as fh:
+            env["rocm"] = fh.read().strip()
+    except OSError:
+        env["rocm"] = None
+    hv = _run(["/opt/rocm/bin/hipcc", "--version"])
+    env["hipcc"] = next((l.strip() for l in (hv or "").splitlines() if "clang version" in l), None)
+    clk = _run(["/opt/rocm/bin/rocm-smi", "--showclocks"])
+    env["clocks"] = [l.split(":", 1)[-1].strip() for l in (clk or "").splitlines()
+                     if "sclk" in l or "mclk" in l or "fclk" in l][:3] or None
+    env["library_sources_sha256"] = source_sha256()
+    try:
+        import json as _json
+        with open(os.path.join(ROOT, "gated_delta_rule_11_amd", "build_info.json")) as fh:
+            env["build"] = _json.load(fh)
+    except (OSError, ValueError):
+        env["build"] = None
+    env["timing"] = ("HIP events recorded on the launch stream around each launch (decode: around the 64 steps); "
+                     "warm-up launches first; min / median / max over the timed reps; value from the median")
+    return env
+
+
+def cpu_info():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), None)
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return {"model": model, "os_cpu_count": os.cpu_count(), "affinity": affinity,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,6 +207,12 @@ def main():
     o_pre = torch.empty((ps.B, ps.T, ps.H, ps.dv), dtype=torch.bfloat16, device=dev)
     S_pre = torch.empty((ps.B, ps.H, ps.dk, ps.dv), dtype=torch.float32, device=dev)
 
+    def workspace(B, T, H, dk, dv, chunk):
+        """The chunked prefill's workspace, allocated outside any timed region (None if unneeded)."""
+        need = kda.chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk)
+        return torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+    ws_pre = workspace(ps.B, ps.T, ps.H, ps.dk, ps.dv, ps.chunk)
+
     t0 = time.time()
     dd = ki.decode_inputs(ds)
     log(f"decode inputs generated in {time.time() - t0:.1f}s")
@@ -153,7 +228,7 @@ def main():
         if not run_pre:
             return
         kda.chunk_fwd_z(P["q"], P["k"], P["v"], P["beta"], P["z"], P["A"], -5.0, ps.chunk, S_in=P["S0"],
-                        o=o_pre, S_out=S_pre, stream=stream)
+                        o=o_pre, S_out=S_pre, workspace=ws_pre, stream=stream)
 
     def decode_pass():
         if not run_dec:
@@ -161,6 +236,17 @@ def main():
         for s in range(ds.steps):
             kda.decode_step(D["q"][s], D["k"][s], D["v"][s], D["z"][s], D["beta"][s], D["A"], S_dec, -5.0,
                             o=o_dec[s], stream=stream)
+
+    def timed(fn, reps):
+        """One untimed call, then `reps` calls each bracketed by HIP events on the launch stream."""
+        fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for r0, r1 in evs:
+            r0.record(stream)
+            fn()
+            r1.record(stream)
+        torch.cuda.synchronize()
+        return [r0.elapsed_time(r1) for r0, r1 in evs]
 
     # ---------------- warmup ----------------
     for _ in range(args.warmup):
@@ -200,18 +286,13 @@ def main():
         o_rep = torch.empty((nd, ds.N, ds.H, ds.dv), dtype=torch.bfloat16, device=dev)
         S_rep = torch.empty_like(snap)
         rep_args = (D["q"][:nd], D["k"][:nd], D["v"][:nd], D["z"][:nd], D["beta"][:nd], D["A"], snap, acc)
-        kda.decode_replay(*rep_args, o=o_rep, S_commit=S_rep, stream=stream)
-        rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
-        for r0, r1 in rev:
-            r0.record(stream)
-            kda.decode_replay(*rep_args, o=o_rep, S_commit=S_rep, stream=stream)
-            r1.record(stream)
-        torch.cuda.synchronize()
-        rep_ms = float(np.mean([r0.elapsed_time(r1) for r0, r1 in rev]))
+        rep_t = stats(timed(lambda: kda.decode_replay(*rep_args, o=o_rep, S_commit=S_rep, stream=stream), 10))
+        rep_ms = rep_t["median"]
         rep_bytes = ds.N * ds.H * (2 * ds.dk * ds.dv * 4 + nd * (3 * ds.dk * 2 + ds.dv * 2 + 2 + ds.dv * 2))
         replay = {"n_draft": nd, "ms": round(rep_ms, 4), "tokens_per_s": round(ds.N * nd / (rep_ms / 1e3), 1),
                   "algorithmic_bytes": rep_bytes, "achieved_GBps": round(rep_bytes / (rep_ms / 1e3) / 1e9, 1),
-                  "same_tokens_as_decode_steps_ms": round(float(np.mean(dec_ms)) * nd / ds.steps, 4)}
+                  "same_tokens_as_decode_steps_ms": round(float(np.median(dec_ms)) * nd / ds.steps, 4),
+                  "frac_hbm": round(rep_bytes / (rep_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4), "times_ms": rep_t}
         log(f"replay of {nd} drafts: {rep_ms:.3f} ms (vs {replay['same_tokens_as_decode_steps_ms']:.3f} ms "
             f"for {nd} decode steps)")
 
@@ -226,26 +307,21 @@ def main():
 
         def pro():
             kda.chunk_fwd_z_prologue(P["q"], P["k"], P["v"], P["beta"], P["z"], P["A"], -5.0, ps.chunk,
-                                     S_in=P["S0"], o=o_pro, S_out=S_pro, stream=stream)
-        pro()
-        pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
-        for r0, r1 in pev:
-            r0.record(stream)
-            pro()
-            r1.record(stream)
-        torch.cuda.synchronize()
-        pro_ms = float(np.mean([r0.elapsed_time(r1) for r0, r1 in pev]))
+                                     S_in=P["S0"], o=o_pro, S_out=S_pro, workspace=ws_pre, stream=stream)
+        pro_t = stats(timed(pro, 5))
+        pro_ms = pro_t["median"]
         pro_bytes = ps.B * ps.T * ps.H * PREFILL_BYTES_PER_TOKEN_HEAD + 2 * ps.B * ps.H * ps.dk * ps.dv * 4
         prologue = {"ms": round(pro_ms, 4), "tokens_per_s": round(ps.B * ps.T / (pro_ms / 1e3), 1),
                     "achieved_GBps": round(pro_bytes / (pro_ms / 1e3) / 1e9, 1),
                     "frac_hbm": round(pro_bytes / (pro_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-                    "vs_plain_prefill": round(pro_ms / float(np.mean(pre_ms)), 4)}
+                    "vs_plain_prefill": round(pro_ms / float(np.median(pre_ms)), 4), "times_ms": pro_t}
         log(f"fused-prologue prefill: {pro_ms:.3f} ms ({prologue['vs_plain_prefill']:.3f} x the plain prefill)")
         del o_pro, S_pro
 
     # ---------------- the two small configurations (reported beside the step) ----------------
-    # The tiny fp32 case and the 4K-token bf16 prefill, each one kda_chunk_fwd_z launch with
-    # its inputs resident; mean of 20 launches after one warm-up.
+    # The tiny fp32 case and the 4K-token bf16 prefill, each one kda_chunk_fwd_z call with
+    # its inputs resident (20 timed calls after one warm-up).  The 4K-token prefill has
+    # B*H = 8, so the call runs the segment-parallel form; its one-pass time is given too.
     small = None
     if run_pre and not args.no_extras:
         small = {}
@@ -257,19 +333,20 @@ def main():
             oc = torch.empty((cs.B, cs.T, cs.H, cs.dv), dtype=torch.float32 if cs.dtype == "f32" else torch.bfloat16,
                              device=dev)
             Sc = torch.empty((cs.B, cs.H, cs.dk, cs.dv), dtype=torch.float32, device=dev)
+            wsc = workspace(cs.B, cs.T, cs.H, cs.dk, cs.dv, cs.chunk)
 
             def small_call():
                 kda.chunk_fwd_z(C["q"], C["k"], C["v"], C["beta"], C["z"], C["A"], -5.0, cs.chunk, S_in=S0c, o=oc,
-                                S_out=Sc, stream=stream)
-            small_call()
-            sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
-            for r0, r1 in sev:
-                r0.record(stream)
-                small_call()
-                r1.record(stream)
-            torch.cuda.synchronize()
-            sms = float(np.mean([r0.elapsed_time(r1) for r0, r1 in sev]))
-            small[cs.name] = {"ms": round(sms, 4), "tokens_per_s": round(cs.B * cs.T / (sms / 1e3), 1)}
+                                S_out=Sc, workspace=wsc, stream=stream)
+            st_ = stats(timed(small_call, 20))
+            small[cs.name] = {"ms": st_["median"], "tokens_per_s": round(cs.B * cs.T / (st_["median"] / 1e3), 1),
+                              "times_ms": st_,
+                              "workspace_bytes": 0 if wsc is None else int(wsc.numel())}
+            if wsc is not None:
+                one = stats(timed(lambda: kda.chunk_fwd_z_segmented(
+                    C["q"], C["k"], C["v"], C["beta"], C["z"], C["A"], 1, -5.0, cs.chunk, S_in=S0c, o=oc, S_out=Sc,
+                    stream=stream), 20))
+                small[cs.name]["one_pass_ms"] = one["median"]
         log(f"small configurations: {small}")
 
     # ---------------- standalone gate (reported beside the step, not part of it) ----------------
@@ -281,19 +358,13 @@ def main():
 
         def gate_call():
             kda.gate(P["z"], P["A"], -5.0, ps.chunk, out=G_out, stream=stream)
-        gate_call()
-        gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
-        for r0, r1 in gev:
-            r0.record(stream)
-            gate_call()
-            r1.record(stream)
-        torch.cuda.synchronize()
-        gate_ms = float(np.mean([r0.elapsed_time(r1) for r0, r1 in gev]))
+        gate_t = stats(timed(gate_call, 10))
+        gate_ms = gate_t["median"]
         in_es = 2 if ps.dtype == "bf16" else 4
         gate_bytes = ps.B * ps.T * ps.H * ps.dk * (in_es + 4) + ps.H * ps.dk * 4
         gate = {"ms": round(gate_ms, 4), "algorithmic_bytes": gate_bytes,
                 "achieved_GBps": round(gate_bytes / (gate_ms / 1e3) / 1e9, 1),
-                "frac_hbm": round(gate_bytes / (gate_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+                "frac_hbm": round(gate_bytes / (gate_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4), "times_ms": gate_t}
         log(f"standalone gate: {gate_ms:.3f} ms, {gate['achieved_GBps']:.0f} GB/s")
         # the unfused path: kda_gate, then kda_chunk_fwd reading G (fp32) in place of z
         o_unf = torch.empty_like(o_pre)
@@ -302,7 +373,7 @@ def main():
         def unfused():
             kda.gate(P["z"], P["A"], -5.0, ps.chunk, out=G_out, stream=stream)
             kda.chunk_fwd(P["q"], P["k"], P["v"], P["beta"], G_out, ps.chunk, S_in=P["S0"], o=o_unf, S_out=S_unf,
-                          stream=stream)
+                          workspace=ws_pre, stream=stream)
         unfused()
         uev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
                 torch.cuda.Event(enable_timing=True)) for _ in range(5)]
@@ -311,13 +382,13 @@ def main():
             kda.gate(P["z"], P["A"], -5.0, ps.chunk, out=G_out, stream=stream)
             r1.record(stream)
             kda.chunk_fwd(P["q"], P["k"], P["v"], P["beta"], G_out, ps.chunk, S_in=P["S0"], o=o_unf, S_out=S_unf,
-                          stream=stream)
+                          workspace=ws_pre, stream=stream)
             r2.record(stream)
         torch.cuda.synchronize()
-        unf_chunk_ms = float(np.mean([r1.elapsed_time(r2) for _, r1, r2 in uev]))
-        unf_ms = float(np.mean([r0.elapsed_time(r2) for r0, _, r2 in uev]))
+        unf_chunk_ms = float(np.median([r1.elapsed_time(r2) for _, r1, r2 in uev]))
+        unf_ms = float(np.median([r0.elapsed_time(r2) for r0, _, r2 in uev]))
         gate["unfused_prefill"] = {"chunk_fwd_ms": round(unf_chunk_ms, 4), "gate_plus_chunk_fwd_ms": round(unf_ms, 4),
-                                   "vs_fused_prefill": round(unf_ms / float(np.mean(pre_ms)), 4)}
+                                   "vs_fused_prefill": round(unf_ms / float(np.median(pre_ms)), 4)}
         log(f"unfused prefill: gate + chunk_fwd {unf_ms:.3f} ms (chunk_fwd {unf_chunk_ms:.3f} ms), "
             f"{gate['unfused_prefill']['vs_fused_prefill']:.3f} x the fused prefill")
         del G_out, o_unf, S_unf
@@ -333,19 +404,13 @@ def main():
         def bwd():
             kda.chunk_bwd_z(P["q"], P["k"], P["v"], P["beta"], P["z"], P["A"], o_pre, None, -5.0, P["S0"],
                             workspace=bw_ws, stream=stream)
-        bwd()
-        bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(3)]
-        for r0, r1 in bev:
-            r0.record(stream)
-            bwd()
-            r1.record(stream)
-        torch.cuda.synchronize()
-        bw_ms = float(np.mean([r0.elapsed_time(r1) for r0, r1 in bev]))
+        bw_t = stats(timed(bwd, 3))
+        bw_ms = bw_t["median"]
         bw_bytes = ps.B * ps.T * ps.H * BACKWARD_BYTES_PER_TOKEN_HEAD + 2 * ps.B * ps.H * ps.dk * ps.dv * 4
         backward = {"ms": round(bw_ms, 3), "tokens_per_s": round(ps.B * ps.T / (bw_ms / 1e3), 1),
                     "algorithmic_bytes": bw_bytes, "achieved_GBps": round(bw_bytes / (bw_ms / 1e3) / 1e9, 1),
                     "frac_hbm": round(bw_bytes / (bw_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-                    "vs_forward_prefill": round(bw_ms / float(np.mean(pre_ms)), 2)}
+                    "vs_forward_prefill": round(bw_ms / float(np.median(pre_ms)), 2), "times_ms": bw_t}
         log(f"backward: {bw_ms:.2f} ms ({backward['vs_forward_prefill']:.1f} x the forward prefill)")
         del bw_ws
         torch.cuda.empty_cache()
@@ -364,31 +429,29 @@ def main():
         del ld
         o_l = torch.empty((ls.B, ls.T, ls.H, ls.dv), dtype=torch.bfloat16, device=dev)
         S_l = torch.empty((ls.B, ls.H, ls.dk, ls.dv), dtype=torch.float32, device=dev)
-        nseg = max(1, -(-128 // (ls.B * ls.H)))
+        nseg = 16
         ws = torch.empty(kda.chunk_fwd_z_segmented_workspace_bytes(ls.B, ls.H, ls.dk, ls.dv, nseg),
                          dtype=torch.uint8, device=dev)
+        ws_auto = workspace(ls.B, ls.T, ls.H, ls.dk, ls.dv, ls.chunk)
         largs = (L["q"], L["k"], L["v"], L["beta"], L["z"], L["A"])
-
-        def timed(fn, reps):
-            fn()
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-            for r0, r1 in evs:
-                r0.record(stream)
-                fn()
-                r1.record(stream)
-            torch.cuda.synchronize()
-            return float(np.mean([r0.elapsed_time(r1) for r0, r1 in evs]))
-
-        seg_ms = timed(lambda: kda.chunk_fwd_z_segmented(*largs, nseg, -5.0, ls.chunk, o=o_l, S_out=S_l,
-                                                         workspace=ws, stream=stream), 5)
-        one_ms = timed(lambda: kda.chunk_fwd_z(*largs, -5.0, ls.chunk, o=o_l, S_out=S_l, stream=stream), 2)
+        auto_t = stats(timed(lambda: kda.chunk_fwd_z(*largs, -5.0, ls.chunk, o=o_l, S_out=S_l, workspace=ws_auto,
+                                                     stream=stream), 5))
+        seg_t = stats(timed(lambda: kda.chunk_fwd_z_segmented(*largs, nseg, -5.0, ls.chunk, o=o_l, S_out=S_l,
+                                                              workspace=ws, stream=stream), 5))
+        one_t = stats(timed(lambda: kda.chunk_fwd_z_segmented(*largs, 1, -5.0, ls.chunk, o=o_l, S_out=S_l,
+                                                              stream=stream), 2))
+        auto_ms, seg_ms, one_ms = auto_t["median"], seg_t["median"], one_t["median"]
         l_bytes = ls.B * ls.T * ls.H * PREFILL_BYTES_PER_TOKEN_HEAD + 2 * ls.B * ls.H * ls.dk * ls.dv * 4
-        long_ctx = {"workload": ls.name, "segments": nseg, "ms": round(seg_ms, 3),
-                    "achieved_GBps": round(l_bytes / (seg_ms / 1e3) / 1e9, 1),
-                    "frac_hbm": round(l_bytes / (seg_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-                    "tokens_per_s": round(ls.B * ls.T / (seg_ms / 1e3), 1), "one_pass_ms": round(one_ms, 3)}
-        log(f"1M-token prefill: {seg_ms:.2f} ms in {nseg} segments, {one_ms:.2f} ms in one pass")
-        del L, o_l, S_l, ws, largs
+        long_ctx = {"workload": ls.name, "entry_point": "kda_chunk_fwd_z", "ms": round(auto_ms, 3),
+                    "achieved_GBps": round(l_bytes / (auto_ms / 1e3) / 1e9, 1),
+                    "frac_hbm": round(l_bytes / (auto_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "tokens_per_s": round(ls.B * ls.T / (auto_ms / 1e3), 1), "times_ms": auto_t,
+                    "workspace_bytes": 0 if ws_auto is None else int(ws_auto.numel()),
+                    "explicit_segments": {"segments": nseg, "ms": round(seg_ms, 3)},
+                    "one_pass_ms": round(one_ms, 3)}
+        log(f"1M-token prefill: kda_chunk_fwd_z {auto_ms:.2f} ms; {seg_ms:.2f} ms in {nseg} segments; "
+            f"{one_ms:.2f} ms in one pass")
+        del L, o_l, S_l, ws, ws_auto, largs
         torch.cuda.empty_cache()
 
     if args.copy_calibration_mib > 0:
@@ -401,8 +464,8 @@ def main():
         log(f"copy calibration: {nbytes} bytes device-to-device")
         del src, dst
 
-    pre_avg_s = max(float(np.mean(pre_ms)) / 1e3, 1e-9)
-    dec_avg_s = max(float(np.mean(dec_ms)) / 1e3, 1e-9)
+    pre_avg_s = max(float(np.median(pre_ms)) / 1e3, 1e-9)
+    dec_avg_s = max(float(np.median(dec_ms)) / 1e3, 1e-9)
     tokens = ps.B * ps.T
     token_heads = tokens * ps.H
     prefill_tps = tokens / pre_avg_s
@@ -420,7 +483,9 @@ def main():
     if not args.no_cpu_baseline and run_pre:
         import oracle
         nb = max(1, min(ps.B, args.cpu_sample_batches))
-        cores = max(1, min(16, os.cpu_count() or 1))
+        # every CPU this job may use: its affinity set, capped by OMP_NUM_THREADS where the
+        # host sets it to the job's share
+        cores = oracle.default_threads()
         f = {k: ki.to_f64(pd[k][0:nb], ps.dtype) for k in ("q", "k", "v", "z", "beta")}
         A64 = pd["A"].astype(np.float64)
         S064 = pd["S0"][0:nb].astype(np.float64)
@@ -436,7 +501,7 @@ def main():
         rel_S = float(np.linalg.norm(S_gpu - S_ref) / np.linalg.norm(S_ref))
         log(f"cpu baseline {cdt:.1f}s -> {cpu_tps:.1f} tokens/s; sample parity rel-L2 o={rel_o:.2e} S={rel_S:.2e}")
         whole = f"the whole workload ({ps.B} batch entries)" if nb == ps.B else f"batch entries 0-{nb - 1} of {ps.B}"
-        cpu = {"value": round(cpu_tps, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+        cpu = {"value": round(cpu_tps, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle", "host": cpu_info(),
                "sample": f"prefill {whole}: all {ps.H} heads, all {ps.T} tokens (fp64 token loop, "
                          f"{cdt:.1f}s)",
                "sample_parity_rel_l2": {"o": rel_o, "S": rel_S}}
@@ -460,6 +525,16 @@ def main():
         cdt2 = time.perf_counter() - c0
         per[ki.DECODE_256.name] = {"tokens_per_s": round(n_s * ki.DECODE_256.steps / cdt2, 1), "s": round(cdt2, 3),
                                    "sample": f"{n_s} of {ki.DECODE_256.N} sequences, all {ki.DECODE_256.steps} steps"}
+        # one thread on the 4K-token prefill: the oracle's per-core rate
+        cs = ki.PREFILL_4K
+        cd = ki.prefill_inputs(cs)
+        cf = {k: ki.to_f64(cd[k], cs.dtype) for k in ("q", "k", "v", "z", "beta")}
+        c0 = time.perf_counter()
+        oracle.forward_z(cf["q"], cf["k"], cf["v"], cf["beta"], cf["z"], cd["A"].astype(np.float64), -5.0, None,
+                         nthreads=1)
+        cdt2 = time.perf_counter() - c0
+        per[cs.name + "_one_thread"] = {"tokens_per_s": round(cs.B * cs.T / cdt2, 1), "s": round(cdt2, 3),
+                                        "threads": 1}
         cpu["per_config"] = per
         log(f"oracle on the other configurations: {per}")
 
@@ -480,6 +555,8 @@ def main():
                    "seq_len": ps.T, "heads": ps.H, "d_k": ps.dk, "d_v": ps.dv, "chunk": ps.chunk,
                    "parallelism": "single GPU"},
         "prefill_ms": round(pre_avg_s * 1e3, 4),
+        "prefill_times_ms": stats(pre_ms),
+        "environment": environment(torch),
         "roofline": {"bound": "hbm", "achieved": round(pre_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(pre_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("prefill"),
                      "kernel": "chunk prefill (kda_chunk_fwd_z)",
@@ -487,6 +564,7 @@ def main():
                      "mfma_tflops_algorithmic": round(pre_flops / pre_avg_s / 1e12, 2),
                      "mfma_frac_algorithmic": round(pre_flops / pre_avg_s / 1e12 / BF16_PEAK_TFLOPS, 4)},
         "decode": {"value": round(decode_tps, 1), "unit": "tokens/s", "ms_per_64_steps": round(dec_avg_s * 1e3, 4),
+                   "times_ms": stats(dec_ms),
                    "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                 "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("decode"),
                                 "algorithmic_bytes_per_launch": dec_bytes}},

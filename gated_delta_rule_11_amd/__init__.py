@@ -8,6 +8,7 @@ library is not built or when a tensor is not on a GPU.
 
 Entry points (same names as the C ABI):
   gate(z, A, g_min, chunk)                        -> G           (kda_gate)
+  chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk) -> bytes     (kda_chunk_fwd_workspace_bytes)
   chunk_fwd(q, k, v, beta, G, chunk, ...)         -> (o, S_out)  (kda_chunk_fwd)
   chunk_fwd_z(q, k, v, beta, z, A, g_min, chunk)  -> (o, S_out)  (kda_chunk_fwd_z)
   decode_step(q, k, v, z, beta, A, S, g_min)      -> o           (kda_decode_step; S updated in place)
@@ -21,7 +22,8 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["gate", "chunk_fwd", "chunk_fwd_z", "decode_step", "chunk_uses_mfma", "lib", "KDAError", "LIB_PATH", "G_MIN"]
+__all__ = ["gate", "chunk_fwd", "chunk_fwd_z", "chunk_fwd_workspace_bytes", "decode_step", "chunk_uses_mfma", "lib",
+           "KDAError", "LIB_PATH", "G_MIN"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 G_MIN = -5.0
@@ -51,9 +53,12 @@ def lib() -> ctypes.CDLL:
     L.kda_chunk_uses_mfma.restype = I
     L.kda_gate.argtypes = [P, I, P, F, I, I, I, I, I, P, P]
     L.kda_gate.restype = I
-    L.kda_chunk_fwd.argtypes = [P, P, P, P, I, P, P, P, I, P, I, I, I, I, I, I, F, P]
+    Z = ctypes.c_size_t
+    L.kda_chunk_fwd_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    L.kda_chunk_fwd_workspace_bytes.restype = Z
+    L.kda_chunk_fwd.argtypes = [P, P, P, P, I, P, P, P, I, P, I, I, I, I, I, I, F, P, Z, P]
     L.kda_chunk_fwd.restype = I
-    L.kda_chunk_fwd_z.argtypes = [P, P, P, P, P, I, P, F, P, P, I, P, I, I, I, I, I, I, F, P]
+    L.kda_chunk_fwd_z.argtypes = [P, P, P, P, P, I, P, F, P, P, I, P, I, I, I, I, I, I, F, P, Z, P]
     L.kda_chunk_fwd_z.restype = I
     L.kda_decode_step.argtypes = [P, P, P, P, P, I, P, F, P, P, I, I, I, I, I, F, P]
     L.kda_decode_step.restype = I
@@ -175,6 +180,25 @@ def _chunk_shapes(what, q, k, v, beta, z=None, A=None, G=None, S_in=None, o=None
             ("S_out", S_out, (B, H, dk, dv), _F32))
 
 
+def chunk_fwd_workspace_bytes(B: int, T: int, H: int, dk: int, dv: int, chunk: int) -> int:
+    """Device bytes kda_chunk_fwd / kda_chunk_fwd_z / kda_chunk_fwd_z_prologue need
+    as workspace for these sizes (0: none)."""
+    return int(lib().kda_chunk_fwd_workspace_bytes(int(B), int(T), int(H), int(dk), int(dv), int(chunk)))
+
+
+def _workspace(workspace, q, v, chunk):
+    """(pointer, bytes) of the caller's workspace, or of a new one of the queried
+    size (None, 0 when the call needs none)."""
+    B, T, H, dk = q.shape
+    if workspace is None:
+        need = chunk_fwd_workspace_bytes(B, T, H, dk, v.shape[-1], chunk)
+        if need == 0:
+            return None, 0, None
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _dev(workspace)
+    return _p(workspace), workspace.numel() * workspace.element_size(), workspace
+
+
 def _outs(q, v, o, S_out, o_dtype, want_state):
     B, T, H, _ = q.shape
     dv = v.shape[-1]
@@ -187,50 +211,57 @@ def _outs(q, v, o, S_out, o_dtype, want_state):
 
 @_on_tensor_device
 def chunk_fwd(q, k, v, beta, G, chunk: int = 64, S_in=None, o=None, S_out=None, o_dtype=None,
-              scale: float = 1.0, want_state: bool = True, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+              scale: float = 1.0, want_state: bool = True, workspace=None,
+              stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked prefill from the chunk-local sums G of kda_gate (same chunk).
+    ``workspace``: a device tensor of at least ``chunk_fwd_workspace_bytes``
+    bytes, or None (one is allocated when the call needs it).
     Returns (o [B,T,H,dv], S_out [B,H,dk,dv] or None)."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     o, S_out = _outs(q, v, o, S_out, o_dtype, want_state)
     _chunk_shapes("kda_chunk_fwd", q, k, v, beta, G=G, S_in=S_in, o=o, S_out=S_out)
     _dev(q, k, v, beta, G, S_in, o, S_out)
+    wp, wb, _keep = _workspace(workspace, q, v, chunk)
     _check(lib().kda_chunk_fwd(_p(q), _p(k), _p(v), _p(beta), _dtype_code(q), _p(G), _p(S_in), _p(o),
-                               _dtype_code(o), _p(S_out), B, T, H, dk, dv, int(chunk), float(scale),
+                               _dtype_code(o), _p(S_out), B, T, H, dk, dv, int(chunk), float(scale), wp, wb,
                                _stream(stream)), "kda_chunk_fwd")
     return o, S_out
 
 
 @_on_tensor_device
 def chunk_fwd_z(q, k, v, beta, z, A, g_min: float = G_MIN, chunk: int = 64, S_in=None, o=None, S_out=None,
-                o_dtype=None, scale: float = 1.0, want_state: bool = True,
+                o_dtype=None, scale: float = 1.0, want_state: bool = True, workspace=None,
                 stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked prefill with the gate fused (decay logits z, A, g_min).
+    ``workspace``: as ``chunk_fwd``.
     Returns (o [B,T,H,dv], S_out [B,H,dk,dv] or None)."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     o, S_out = _outs(q, v, o, S_out, o_dtype, want_state)
     _chunk_shapes("kda_chunk_fwd_z", q, k, v, beta, z=z, A=A, S_in=S_in, o=o, S_out=S_out)
     _dev(q, k, v, beta, z, A, S_in, o, S_out)
+    wp, wb, _keep = _workspace(workspace, q, v, chunk)
     _check(lib().kda_chunk_fwd_z(_p(q), _p(k), _p(v), _p(beta), _p(z), _dtype_code(q), _p(A), float(g_min),
                                  _p(S_in), _p(o), _dtype_code(o), _p(S_out), B, T, H, dk, dv, int(chunk),
-                                 float(scale), _stream(stream)), "kda_chunk_fwd_z")
+                                 float(scale), wp, wb, _stream(stream)), "kda_chunk_fwd_z")
     return o, S_out
 
 
 @_on_tensor_device
 def chunk_fwd_z_prologue(q_raw, k_raw, v, beta_logit, z, A, g_min: float = G_MIN, chunk: int = 64, S_in=None,
                          o=None, S_out=None, o_dtype=None, scale: float = 1.0, want_state: bool = True,
-                         stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                         workspace=None, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """``chunk_fwd_z`` with the prologue fused: q, k un-normalised, beta as a logit."""
     B, T, H, dk = q_raw.shape
     dv = v.shape[-1]
     o, S_out = _outs(q_raw, v, o, S_out, o_dtype, want_state)
     _chunk_shapes("kda_chunk_fwd_z_prologue", q_raw, k_raw, v, beta_logit, z=z, A=A, S_in=S_in, o=o, S_out=S_out)
     _dev(q_raw, k_raw, v, beta_logit, z, A, S_in, o, S_out)
+    wp, wb, _keep = _workspace(workspace, q_raw, v, chunk)
     _check(lib().kda_chunk_fwd_z_prologue(_p(q_raw), _p(k_raw), _p(v), _p(beta_logit), _p(z), _dtype_code(q_raw),
                                           _p(A), float(g_min), _p(S_in), _p(o), _dtype_code(o), _p(S_out), B, T, H,
-                                          dk, dv, int(chunk), float(scale), _stream(stream)),
+                                          dk, dv, int(chunk), float(scale), wp, wb, _stream(stream)),
            "kda_chunk_fwd_z_prologue")
     return o, S_out
 

@@ -48,6 +48,25 @@ def _compile(src, verbose):
     return obj
 
 
+def _write_build_info():
+    """Record which commit the library was built from (and whether its sources had
+    uncommitted changes) next to it; the benchmark reports it."""
+    import json
+
+    def git(*a):
+        try:
+            r = subprocess.run(["git", "-C", ROOT] + list(a), capture_output=True, text=True, timeout=20)
+            return r.stdout.strip() if r.returncode == 0 else None
+        except (OSError, subprocess.SubprocessError):
+            return None
+    head = git("rev-parse", "HEAD")
+    dirty = git("status", "--porcelain", "--", "gated_delta_rule_11_amd/csrc", "include")
+    info = {"commit": head, "sources_modified_since_commit": bool(dirty) if dirty is not None else None,
+            "arch": ARCH, "hipcc": HIPCC}
+    with open(os.path.join(HERE, "build_info.json"), "w") as fh:
+        json.dump(info, fh)
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
@@ -59,6 +78,7 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    _write_build_info()
     return LIB
 
 

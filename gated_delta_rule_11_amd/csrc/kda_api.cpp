@@ -49,6 +49,11 @@ bool sizes_ok(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv) {
 
 kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
 
+// g_min accepted by the gate and the chunked prefill: 16 g_min >= -86.4 keeps the
+// decay of any 16-token tile (and so its reciprocal) a normal fp32 number.
+constexpr float kGminFloor = -5.4f;
+bool gmin_ok(float g) { return isfinite(g) && g <= 0.f && g >= kGminFloor; }
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 // Tensor bases 16-byte aligned, beta to its element size (NULL passes).
@@ -68,16 +73,16 @@ const char* kda_status_string(int s) {
     case KDA_ERR_NULL: return "KDA_ERR_NULL: a required pointer is NULL";
     case KDA_ERR_SHAPE: return "KDA_ERR_SHAPE: a size is negative or too large";
     case KDA_ERR_DTYPE: return "KDA_ERR_DTYPE: unknown dtype";
-    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: head dim, chunk or parameter outside the supported set";
-    case KDA_ERR_ALIAS: return "KDA_ERR_ALIAS: an output overlaps an input";
-    case KDA_ERR_HIP: return "KDA_ERR_HIP: the HIP runtime reported a launch error";
-    case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN: a tensor pointer is not 16-byte aligned";
     case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: the workspace is smaller than required";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: head dim, chunk or parameter outside the supported set";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP: the HIP runtime reported a launch error";
+    case KDA_ERR_ALIAS: return "KDA_ERR_ALIAS: an output overlaps an input";
+    case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN: a tensor pointer is not 16-byte aligned";
   }
   return "unknown kda_status";
 }
 
-int kda_version(void) { return 100; }
+int kda_version(void) { return 200; }
 
 int kda_chunk_uses_mfma(kda_dtype in_dtype, int dk, int dv, int chunk) {
   kda::ChunkArgs a{};
@@ -90,7 +95,7 @@ kda_status kda_gate(const void* z, kda_dtype z_dtype, const float* A, float g_mi
   if (!dtype_ok(z_dtype)) return KDA_ERR_DTYPE;
   if (!sizes_ok(B, T, H, dk, dk)) return KDA_ERR_SHAPE;
   if (!dim_ok(dk) || !(chunk == 1 || chunk == 16 || chunk == 64)) return KDA_ERR_UNSUPPORTED;
-  if (!isfinite(g_min) || g_min > 0.f) return KDA_ERR_UNSUPPORTED;
+  if (!gmin_ok(g_min)) return KDA_ERR_UNSUPPORTED;
   const int64_t n = int64_t(B) * T * H * dk;
   if (n == 0) return KDA_OK;
   if (!z || !A || !G) return KDA_ERR_NULL;
@@ -102,36 +107,102 @@ kda_status kda_gate(const void* z, kda_dtype z_dtype, const float* A, float g_mi
   return from_hip(kda::launch_gate(a, static_cast<hipStream_t>(stream)));
 }
 
-static kda_status chunk_common(const void* q, const void* k, const void* v, const void* beta, const void* z,
-                               kda_dtype in_dtype, const float* G, const float* A, float g_min,
-                               const float* S_in, void* o, kda_dtype o_dtype, float* S_out, int B, int T, int H,
-                               int dk, int dv, int chunk, float scale, bool from_z, void* stream, int segments = 1,
-                               void* ws = nullptr, size_t ws_bytes = 0, bool prologue = false) {
+}  // extern "C"
+
+namespace {
+
+// Segments of a segment-parallel prefill: `seg_chunks` chunks each (more segments
+// than chunks: one chunk each), `nseg` of them non-empty.  In 64 bits, since the
+// requested count may be as large as INT_MAX.
+struct SegLayout {
+  int nseg;
+  int seg_chunks;
+};
+SegLayout seg_layout(int64_t nch, int64_t segments) {
+  if (segments < 1) segments = 1;
+  const int64_t sc = (nch + segments - 1) / segments;
+  if (sc <= 0) return {1, 0};
+  return {int((nch + sc - 1) / sc), int(sc)};
+}
+
+// Workspace of the segment-parallel form, in floats: the end states from the zero
+// state St and the transitions M of every segment but the last (whose are never
+// used), then the entry states E of every segment.
+int64_t seg_ws_floats(int64_t bh, int64_t nseg, int64_t dk, int64_t dv) {
+  if (nseg <= 1) return 0;
+  return bh * ((nseg - 1) * (dk * dv + dk * dk) + nseg * dk * dv);
+}
+
+// Launch form the chunked prefill picks from the sizes alone.  One pass runs one
+// workgroup per (b, h, value-column slice) and walks the whole sequence; when B*H
+// is too small to occupy the compute units even with narrow slices, the sequence is
+// cut into segments ("Kimi K3 reading notes", section 7).  The segment-parallel form
+// does about three passes' work (end states, transitions, then outputs), so it pays
+// only once it multiplies the parallelism well beyond that: here when at least
+// kMinSegs segments of at least kMinSegChunks chunks each fit, with the two
+// 64-column slices per (b, h, segment) of the widest launch filling kFillUnits.
+constexpr int64_t kFillUnits = 256;   // compute units of the MI355X
+constexpr int64_t kMinSegs = 4;
+constexpr int64_t kMinSegChunks = 4;
+int64_t auto_segments(int64_t B, int64_t T, int64_t H, int dk, int dv, int chunk) {
+  kda::ChunkArgs a{};
+  a.dk = dk; a.dv = dv; a.chunk = chunk; a.in_bf16 = true; a.H = int(H);
+  if (!kda::chunk_mfma_supports(a)) return 1;  // the segment passes exist on the matrix-core path only
+  const int64_t bh = B * H, nch = (T + chunk - 1) / chunk;
+  if (bh <= 0 || nch <= 0) return 1;
+  int64_t segs = kFillUnits / (2 * bh);
+  segs = segs < nch / kMinSegChunks ? segs : nch / kMinSegChunks;
+  return segs >= kMinSegs ? segs : 1;
+}
+
+bool chunk_args_ok(int B, int T, int H, int dk, int dv, int chunk) {
+  return sizes_ok(B, T, H, dk, dv) && dim_ok(dk) && dim_ok(dv) && (chunk == 16 || chunk == 64);
+}
+
+// `segments` > 0: exactly that many segments (kda_chunk_fwd_z_segmented); 0: the
+// automatic choice, whose workspace kda_chunk_fwd_workspace_bytes sizes; < 0: an
+// invalid count (KDA_ERR_SHAPE).
+kda_status chunk_common(const void* q, const void* k, const void* v, const void* beta, const void* z,
+                        kda_dtype in_dtype, const float* G, const float* A, float g_min, const float* S_in, void* o,
+                        kda_dtype o_dtype, float* S_out, int B, int T, int H, int dk, int dv, int chunk, float scale,
+                        bool from_z, int segments, void* ws, size_t ws_bytes, bool prologue, void* stream) {
   if (!dtype_ok(in_dtype) || !dtype_ok(o_dtype)) return KDA_ERR_DTYPE;
   if (!sizes_ok(B, T, H, dk, dv)) return KDA_ERR_SHAPE;
   if (!dim_ok(dk) || !dim_ok(dv) || !(chunk == 16 || chunk == 64)) return KDA_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return KDA_ERR_UNSUPPORTED;
-  if (from_z && (!isfinite(g_min) || g_min > 0.f || g_min < -5.5f)) return KDA_ERR_UNSUPPORTED;
-  const int64_t ntok = int64_t(B) * T * H;
-  const int64_t nstate = int64_t(B) * H * dk * dv;
-  if (int64_t(B) * H == 0) return KDA_OK;
+  if (from_z && !gmin_ok(g_min)) return KDA_ERR_UNSUPPORTED;
+  if (segments < 0) return KDA_ERR_SHAPE;
+  const int64_t bh = int64_t(B) * H;
+  const int64_t ntok = bh * T;
+  const int64_t nstate = bh * dk * dv;
+  const int64_t nch = (int64_t(T) + chunk - 1) / chunk;
+  // the caller's workspace must hold what the chosen form needs
+  const bool auto_form = segments == 0;
+  const SegLayout lay = seg_layout(nch, auto_form ? auto_segments(B, T, H, dk, dv, chunk) : segments);
+  const int64_t need = seg_ws_floats(bh, lay.nseg, dk, dv) * 4;
+  if (bh == 0) return KDA_OK;
   if (ntok > 0) {
     if (!q || !k || !v || !beta || !o) return KDA_ERR_NULL;
     if (from_z ? (!z || !A) : !G) return KDA_ERR_NULL;
   }
-  if (!all_aligned({q, k, v, z, G, A, o, S_in, S_out}, beta, esize(in_dtype))) return KDA_ERR_ALIGN;
+  if (need > 0 && !ws) return KDA_ERR_NULL;
+  if (!all_aligned({q, k, v, z, G, A, o, S_in, S_out, need > 0 ? ws : nullptr}, beta, esize(in_dtype)))
+    return KDA_ERR_ALIGN;
+  if (ws_bytes < size_t(need)) return KDA_ERR_WORKSPACE;
   const int64_t ein = esize(in_dtype);
   const Range rq{q, ntok * dk * ein}, rk{k, ntok * dk * ein}, rv{v, ntok * dv * ein}, rb{beta, ntok * ein};
   const Range rz{from_z ? z : nullptr, ntok * dk * ein}, rG{from_z ? nullptr : G, ntok * dk * 4};
   const Range rA{from_z ? A : nullptr, int64_t(H) * dk * 4};
   const Range ro{o, ntok * dv * int64_t(esize(o_dtype))};
   const Range rSi{S_in, nstate * 4}, rSo{S_out, nstate * 4};
+  const Range rw{need > 0 ? ws : nullptr, need};
   for (Range in : {rq, rk, rv, rb, rz, rG, rA, rSi})
     if (overlap(ro, in)) return KDA_ERR_ALIAS;
   for (Range in : {rq, rk, rv, rb, rz, rG, rA, ro})
     if (overlap(rSo, in)) return KDA_ERR_ALIAS;
   if (overlap(rSo, rSi) && S_out != S_in) return KDA_ERR_ALIAS;
-  if (segments < 1) return KDA_ERR_SHAPE;
+  for (Range in : {rq, rk, rv, rb, rz, rG, rA, ro, rSi, rSo})
+    if (overlap(rw, in)) return KDA_ERR_ALIAS;
 
   kda::ChunkArgs a{};
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.G = from_z ? nullptr : G; a.z = from_z ? z : nullptr;
@@ -140,39 +211,29 @@ static kda_status chunk_common(const void* q, const void* k, const void* v, cons
   a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = o_dtype == KDA_BF16; a.from_z = from_z;
   a.prologue = prologue;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int nch = (T + chunk - 1) / chunk;
-  // chunks per segment and segments (more segments than chunks: one chunk each); in
-  // 64 bits, since segments may be as large as INT_MAX
-  const int seg_chunks = int((int64_t(nch) + segments - 1) / (segments > 0 ? segments : 1));
-  const int nseg = seg_chunks > 0 ? int((int64_t(nch) + seg_chunks - 1) / seg_chunks) : 1;
   if (!kda::chunk_mfma_supports(a)) {
-    if (segments > 1) return KDA_ERR_UNSUPPORTED;
+    if (!auto_form && lay.nseg > 1) return KDA_ERR_UNSUPPORTED;
     return from_hip(kda::launch_chunk_generic(a, st));
   }
-  if (nseg <= 1) return from_hip(kda::launch_chunk_mfma(a, st));
+  // the segment passes take the fused gate without the prologue; the automatic form
+  // runs the other variants in one pass
+  if (lay.nseg <= 1 || !from_z || prologue) return from_hip(kda::launch_chunk_mfma(a, st));
 
-  // Segment-parallel form ("Kimi K3 reading notes", section 7): each segment from the
-  // zero state (end states St), each segment's transition from the identity with zero
-  // values (M), the entry states by a scan, then each segment from its entry state.
-  const int64_t bh = int64_t(B) * H;
-  const int64_t nSt = bh * nseg * dk * dv, nM = bh * nseg * dk * dk;
-  if (!ws) return KDA_ERR_NULL;
-  if (!aligned(ws, 16)) return KDA_ERR_ALIGN;
-  if (ws_bytes < size_t(2 * nSt + nM) * 4) return KDA_ERR_WORKSPACE;
-  const Range rw{ws, int64_t(2 * nSt + nM) * 4};
-  for (Range in : {rq, rk, rv, rb, rz, rA, ro, rSi, rSo})
-    if (overlap(rw, in)) return KDA_ERR_ALIAS;
+  // Segment-parallel form ("Kimi K3 reading notes", section 7): the segments but the
+  // last from the zero state (end states St) and from the identity with zero values
+  // (transitions M), the entry states E by a scan, then every segment from its entry
+  // state, writing the outputs and, from the last one, the final state.
+  const int nseg = lay.nseg;
   float* St = static_cast<float*>(ws);
-  float* M = St + nSt;
-  float* E = M + nM;
-  a.nseg = nseg;
-  a.seg_chunks = seg_chunks;
+  float* M = St + bh * (nseg - 1) * dk * dv;
+  float* E = M + bh * (nseg - 1) * dk * dk;
+  a.seg_chunks = lay.seg_chunks;
   kda::ChunkArgs pa = a;  // pass A: end states from the zero state
-  pa.S_in = nullptr; pa.S_out = St; pa.S_out_mode = 1; pa.o_skip = true;
-  kda::ChunkArgs pb = a;  // pass B: transitions (identity entry state, zero values)
-  pb.S_in = nullptr; pb.S_identity = true; pb.v_zero = true; pb.S_out = M; pb.S_out_mode = 1; pb.o_skip = true;
+  pa.nseg = nseg - 1; pa.S_in = nullptr; pa.S_out = St; pa.S_out_mode = 1; pa.o_skip = true;
+  kda::ChunkArgs pb = pa;  // pass B: transitions (identity entry state, zero values)
+  pb.S_identity = true; pb.v_zero = true; pb.S_out = M;
   kda::ChunkArgs pc = a;  // pass C: outputs and the final state from the true entry states
-  pc.S_in = E; pc.S_in_seg = true; pc.S_out_mode = 2;
+  pc.nseg = nseg; pc.S_in = E; pc.S_in_seg = true; pc.S_out_mode = 2;
   const kda::SegScanArgs sa{S_in, St, M, E, int(bh), nseg, dk, dv};
   hipError_t e = kda::launch_chunk_mfma(pa, st);
   if (e == hipSuccess) e = kda::launch_chunk_mfma(pb, st);
@@ -181,16 +242,28 @@ static kda_status chunk_common(const void* q, const void* k, const void* v, cons
   return from_hip(e);
 }
 
+}  // namespace
+
+extern "C" {
+
+size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk) {
+  if (!chunk_args_ok(B, T, H, dk, dv, chunk)) return 0;
+  const int64_t nch = (int64_t(T) + chunk - 1) / chunk;
+  const SegLayout lay = seg_layout(nch, auto_segments(B, T, H, dk, dv, chunk));
+  return size_t(seg_ws_floats(int64_t(B) * H, lay.nseg, dk, dv)) * 4;
+}
+
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* beta, kda_dtype in_dtype,
                          const float* G, const float* S_in, void* o, kda_dtype o_dtype, float* S_out, int B, int T,
-                         int H, int dk, int dv, int chunk, float scale, void* stream) {
+                         int H, int dk, int dv, int chunk, float scale, void* workspace, size_t workspace_bytes,
+                         void* stream) {
   return chunk_common(q, k, v, beta, nullptr, in_dtype, G, nullptr, -5.0f, S_in, o, o_dtype, S_out, B, T, H, dk, dv,
-                      chunk, scale, false, stream);
+                      chunk, scale, false, 0, workspace, workspace_bytes, false, stream);
 }
 
 size_t kda_chunk_fwd_z_segmented_workspace_bytes(int B, int H, int dk, int dv, int segments) {
   if (B < 0 || H < 0 || dk < 0 || dv < 0 || segments < 1) return 0;
-  return size_t(B) * size_t(H) * size_t(segments) * (2 * size_t(dk) * dv + size_t(dk) * dk) * 4;
+  return size_t(seg_ws_floats(int64_t(B) * H, segments, dk, dv)) * 4;
 }
 
 kda_status kda_chunk_fwd_z_segmented(const void* q, const void* k, const void* v, const void* beta, const void* z,
@@ -198,8 +271,9 @@ kda_status kda_chunk_fwd_z_segmented(const void* q, const void* k, const void* v
                                      kda_dtype o_dtype, float* S_out, int B, int T, int H, int dk, int dv, int chunk,
                                      float scale, int segments, void* workspace, size_t workspace_bytes,
                                      void* stream) {
+  // a count below one is a shape error (reported after the dtype checks, as every size)
   return chunk_common(q, k, v, beta, z, in_dtype, nullptr, A, g_min, S_in, o, o_dtype, S_out, B, T, H, dk, dv, chunk,
-                      scale, true, stream, segments, workspace, workspace_bytes);
+                      scale, true, segments < 1 ? -1 : segments, workspace, workspace_bytes, false, stream);
 }
 
 size_t kda_chunk_bwd_z_workspace_bytes(int B, int T, int H, int dk, int dv) {
@@ -276,17 +350,18 @@ kda_status kda_chunk_bwd_z(const void* q, const void* k, const void* v, const vo
 kda_status kda_chunk_fwd_z_prologue(const void* q, const void* k, const void* v, const void* beta_logit,
                                     const void* z, kda_dtype in_dtype, const float* A, float g_min,
                                     const float* S_in, void* o, kda_dtype o_dtype, float* S_out, int B, int T, int H,
-                                    int dk, int dv, int chunk, float scale, void* stream) {
+                                    int dk, int dv, int chunk, float scale, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
   return chunk_common(q, k, v, beta_logit, z, in_dtype, nullptr, A, g_min, S_in, o, o_dtype, S_out, B, T, H, dk, dv,
-                      chunk, scale, true, stream, 1, nullptr, 0, true);
+                      chunk, scale, true, 0, workspace, workspace_bytes, true, stream);
 }
 
 kda_status kda_chunk_fwd_z(const void* q, const void* k, const void* v, const void* beta, const void* z,
                            kda_dtype in_dtype, const float* A, float g_min, const float* S_in, void* o,
                            kda_dtype o_dtype, float* S_out, int B, int T, int H, int dk, int dv, int chunk,
-                           float scale, void* stream) {
+                           float scale, void* workspace, size_t workspace_bytes, void* stream) {
   return chunk_common(q, k, v, beta, z, in_dtype, nullptr, A, g_min, S_in, o, o_dtype, S_out, B, T, H, dk, dv, chunk,
-                      scale, true, stream);
+                      scale, true, 0, workspace, workspace_bytes, false, stream);
 }
 
 static kda_status decode_common(const void* q, const void* k, const void* v, const void* z, const void* beta,

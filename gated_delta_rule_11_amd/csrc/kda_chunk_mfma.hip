@@ -905,10 +905,12 @@ hipError_t launch_chunk_mfma(const ChunkArgs& a, hipStream_t st) {
   if (!chunk_mfma_supports(a)) return hipErrorNotSupported;
   const int64_t nbh = static_cast<int64_t>(a.B) * a.H * a.nseg;  // (b, h, segment) units
   if (nbh == 0) return hipSuccess;
-  // value-column slices: enough workgroups to cover the 256 compute units,
-  // at most 64 columns per slice (the state slice then fits the registers)
+  // value-column slices: at most 64 columns per slice (the state slice then fits the
+  // registers); narrower slices only while the grid still fits one workgroup per
+  // compute unit (256), since every slice repeats the gate wavefronts' work and a
+  // second round of workgroups would double the time
   int ns = 2;
-  while (ns < 8 && nbh * ns < 256) ns *= 2;
+  while (ns < 8 && nbh * ns * 2 <= 256) ns *= 2;
   if (nbh * ns > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   switch (ns) {
     case 2: return launch_mfma_d<64>(a, st, 2);

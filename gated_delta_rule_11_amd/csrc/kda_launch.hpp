@@ -89,8 +89,8 @@ struct DecodeShape {
 // Entry states of the segments: E_0 = S_in (or 0), E_{p+1} = M_p E_p + St_p.
 struct SegScanArgs {
   const float* S_in;  // [BH, dk, dv] or nullptr
-  const float* St;    // [BH, nseg, dk, dv], end states from the zero state
-  const float* M;     // [BH, nseg, dk, dk], segment transitions
+  const float* St;    // [BH, nseg - 1, dk, dv], end states from the zero state
+  const float* M;     // [BH, nseg - 1, dk, dk], segment transitions
   float* E;           // [BH, nseg, dk, dv]
   int BH, nseg, dk, dv;
 };

@@ -7,6 +7,8 @@
 //   E_0 = S_in,  E_{p+1} = M_p E_p + S~_p,
 // here in fp32, one workgroup per (b, h, 16-column block of the state), the
 // column block of E held in LDS while the segments are walked in order.
+// Layouts: St [BH, nseg - 1, dk, dv] and M [BH, nseg - 1, dk, dk] (the last
+// segment's are never needed), E [BH, nseg, dk, dv].
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
 
@@ -33,7 +35,8 @@ __global__ __launch_bounds__(256) void segscan_kernel(const float* __restrict__ 
   for (int j = 0; j < 8; ++j)
     e[j] = S_in ? S_in[static_cast<int64_t>(bh) * sz + static_cast<int64_t>(r) * dv + cb * kScanCols + c8 + j] : 0.f;
   for (int p = 0; p < nseg; ++p) {
-    const int64_t seg = static_cast<int64_t>(bh) * nseg + p;
+    const int64_t seg = static_cast<int64_t>(bh) * nseg + p;        // in E
+    const int64_t sm = static_cast<int64_t>(bh) * (nseg - 1) + p;   // in St and M (p < nseg - 1 below)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       E[seg * sz + static_cast<int64_t>(r) * dv + cb * kScanCols + c8 + j] = e[j];
@@ -41,8 +44,8 @@ __global__ __launch_bounds__(256) void segscan_kernel(const float* __restrict__ 
     }
     if (p + 1 == nseg) break;
     __syncthreads();
-    const float* Mr = M + seg * DK * DK + static_cast<int64_t>(r) * DK;
-    const float* Sr = St + seg * sz + static_cast<int64_t>(r) * dv + cb * kScanCols + c8;
+    const float* Mr = M + sm * DK * DK + static_cast<int64_t>(r) * DK;
+    const float* Sr = St + sm * sz + static_cast<int64_t>(r) * dv + cb * kScanCols + c8;
     float acc[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] = Sr[j];

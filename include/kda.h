@@ -51,17 +51,20 @@
 extern "C" {
 #endif
 
+/* Status codes: zero on success, negative on error.  The first six keep the
+ * numbering of the boundary's contract sketch; KDA_ERR_ALIAS and KDA_ERR_ALIGN
+ * are this library's additions. */
 typedef enum kda_status {
   KDA_OK = 0,
-  KDA_ERR_NULL = 1,        /* a required pointer is NULL                     */
-  KDA_ERR_SHAPE = 2,       /* a size is negative, zero where it must be at
-                              least 1 (H, N, dk, dv), or too large           */
-  KDA_ERR_DTYPE = 3,       /* dtype enum out of range                        */
-  KDA_ERR_UNSUPPORTED = 4, /* valid but not provided (dk, dv, chunk, ...)    */
-  KDA_ERR_ALIAS = 5,       /* outputs overlap inputs in a forbidden way      */
-  KDA_ERR_HIP = 6,         /* the HIP runtime reported an error at launch    */
-  KDA_ERR_ALIGN = 7,       /* a pointer is not aligned as required           */
-  KDA_ERR_WORKSPACE = 8    /* the caller's workspace is smaller than needed  */
+  KDA_ERR_NULL = -1,        /* a required pointer is NULL                    */
+  KDA_ERR_SHAPE = -2,       /* a size is negative, zero where it must be at
+                               least 1 (H, N, dk, dv), or too large          */
+  KDA_ERR_DTYPE = -3,       /* dtype enum out of range                       */
+  KDA_ERR_WORKSPACE = -4,   /* the caller's workspace is smaller than needed */
+  KDA_ERR_UNSUPPORTED = -5, /* valid but not provided (dk, dv, chunk, ...)   */
+  KDA_ERR_HIP = -6,         /* the HIP runtime reported an error at launch   */
+  KDA_ERR_ALIAS = -7,       /* outputs overlap inputs in a forbidden way     */
+  KDA_ERR_ALIGN = -8        /* a pointer is not aligned as required          */
 } kda_status;
 
 typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
@@ -69,7 +72,8 @@ typedef enum kda_dtype { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* kda_status_string(int status);
 
-/* Library ABI version (major * 100 + minor). */
+/* Library ABI version (major * 100 + minor): 200 since the chunked prefill
+ * takes a workspace and the status codes are negative. */
 int kda_version(void);
 
 /* 1 when kda_chunk_fwd / kda_chunk_fwd_z run the MFMA kernel (bf16 matrix
@@ -89,13 +93,29 @@ int kda_chunk_uses_mfma(kda_dtype in_dtype, int dk, int dv, int chunk);
  * (-80, 0) the same section states.
  *
  *   z      [B,T,H,dk] in z_dtype (device)     A [H,dk] fp32 (device)
- *   g_min  lower bound of g (the pages fix -5); must be finite and < 0
+ *   g_min  lower bound of g (the pages fix -5), in [-5.5, 0]: the range the
+ *          chunked prefill accepts (KDA_ERR_UNSUPPORTED otherwise)
  *   chunk  1, 16 or 64
  *   G      [B,T,H,dk] fp32 (device, written); must not overlap z or A
  */
 kda_status kda_gate(const void* z, kda_dtype z_dtype, const float* A,
                     float g_min, int B, int T, int H, int dk, int chunk,
                     float* G, void* stream);
+
+/*
+ * kda_chunk_fwd_workspace_bytes -- device scratch memory that kda_chunk_fwd,
+ * kda_chunk_fwd_z and kda_chunk_fwd_z_prologue need for these sizes (any
+ * input dtype).  0 means the call needs none (workspace may then be NULL).
+ * Pure host computation; negative or zero-sized arguments give 0.
+ *
+ * The library picks the launch form from the sizes alone: one pass over the
+ * sequence when B*H alone fills the GPU, otherwise (few, long sequences on the
+ * matrix-core path, fused gate) the segment-parallel form of "Kimi K3 reading
+ * notes", section 7, whose per-segment end states, transitions and entry
+ * states live in the workspace.  Both forms give the same result within the
+ * stated tolerance.
+ */
+size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk);
 
 /*
  * kda_chunk_fwd -- chunked prefill with state in and out, from precomputed
@@ -109,31 +129,47 @@ kda_status kda_gate(const void* z, kda_dtype z_dtype, const float* A,
  * results equal the token recurrence up to rounding.
  *
  *   q, k   [B,T,H,dk] in_dtype     v [B,T,H,dv] in_dtype     beta [B,T,H] in_dtype
- *   G      [B,T,H,dk] fp32 chunk-local sums (chunk must match kda_gate's)
+ *   G      [B,T,H,dk] fp32 chunk-local sums (chunk must match kda_gate's).
+ *          On the matrix-core path (kda_chunk_uses_mfma) every channel's
+ *          log-decay over any aligned 16-token tile, G at the tile's last
+ *          token minus G before its first, must be at least -88: the tile's
+ *          decay and its reciprocal must both be finite in fp32.  G from
+ *          kda_gate with g_min >= -5.5 always is; the bounded gate of the
+ *          pages (g_min = -5) keeps it above -80.
  *   S_in   [B,H,dk,dv] fp32 or NULL (zero state)
  *   o      [B,T,H,dv] in o_dtype (written)
  *   S_out  [B,H,dk,dv] fp32 or NULL (not written); may equal S_in exactly
  *          (in-place state update) but must not partially overlap it
  *   scale  output scale (1 for Eq. 1 as written)
+ *   workspace, workspace_bytes
+ *          caller-owned device memory, 16-byte aligned, of at least
+ *          kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk) bytes
+ *          (KDA_ERR_WORKSPACE otherwise; NULL when that is 0).  It must not
+ *          overlap any argument; its contents on entry do not matter and are
+ *          overwritten.  Calls that run concurrently need separate workspaces.
  */
 kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
                          const void* beta, kda_dtype in_dtype, const float* G,
                          const float* S_in, void* o, kda_dtype o_dtype,
                          float* S_out, int B, int T, int H, int dk, int dv,
-                         int chunk, float scale, void* stream);
+                         int chunk, float scale, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /*
  * kda_chunk_fwd_z -- the same chunked prefill with the gate fused: takes the
  * decay logits z [B,T,H,dk] (in_dtype), A [H,dk] fp32 and g_min instead of G.
  * Equal to kda_gate followed by kda_chunk_fwd up to rounding; this is the
- * path that avoids the fp32 round trip of G through memory.
+ * path that avoids the fp32 round trip of G through memory.  g_min must lie
+ * in [-5.5, 0] (16 g_min >= -88 keeps every 16-token tile's decay and its
+ * reciprocal finite in fp32); other values return KDA_ERR_UNSUPPORTED.
+ * Workspace: as kda_chunk_fwd.
  */
 kda_status kda_chunk_fwd_z(const void* q, const void* k, const void* v,
                            const void* beta, const void* z, kda_dtype in_dtype,
                            const float* A, float g_min, const float* S_in,
                            void* o, kda_dtype o_dtype, float* S_out, int B,
                            int T, int H, int dk, int dv, int chunk, float scale,
-                           void* stream);
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * kda_decode_step -- one token per sequence, state updated IN PLACE.
@@ -161,7 +197,8 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v,
  * pinned-source audit", section 4.2).
  *
  * kda_chunk_fwd_z_prologue and kda_decode_step_prologue take the same
- * arguments as kda_chunk_fwd_z and kda_decode_step, but q and k arrive
+ * arguments as kda_chunk_fwd_z (workspace included: its size is
+ * kda_chunk_fwd_workspace_bytes) and kda_decode_step, but q and k arrive
  * un-normalised and beta as a logit.  Inside the kernels, per token:
  *   q^ = q / sqrt(|q|^2 + 1e-6),  k^ = k / sqrt(|k|^2 + 1e-6)   (fp32 sums)
  *   beta = 1 / (1 + e^(-beta_logit))
@@ -173,7 +210,8 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v,
 kda_status kda_chunk_fwd_z_prologue(const void* q, const void* k, const void* v, const void* beta_logit,
                                     const void* z, kda_dtype in_dtype, const float* A, float g_min,
                                     const float* S_in, void* o, kda_dtype o_dtype, float* S_out, int B, int T,
-                                    int H, int dk, int dv, int chunk, float scale, void* stream);
+                                    int H, int dk, int dv, int chunk, float scale, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 kda_status kda_decode_step_prologue(const void* q, const void* k, const void* v, const void* z,
                                     const void* beta_logit, kda_dtype in_dtype, const float* A, float g_min,
                                     float* S, void* o, kda_dtype o_dtype, int N, int H, int dk, int dv,

@@ -57,6 +57,24 @@ def _f64(a):
     return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
 
 
+def default_threads() -> int:
+    """Worker threads of the C recurrence when a call passes nthreads = 0: the
+    CPUs this process may run on, capped by OMP_NUM_THREADS when that is set
+    (a host shared by several jobs sets it to each job's share)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def _threads(n: int) -> int:
+    return int(n) if int(n) > 0 else default_threads()
+
+
 def l2_normalise(x: np.ndarray) -> np.ndarray:
     """Regularised L2 normalisation over the last axis, in fp64.
 
@@ -124,7 +142,7 @@ class Oracle:
         o = np.zeros((B, T, H, dv))
         S = np.zeros((B, H, dk, dv))
         rc = self.lib.kda_oracle_recurrence(_p(q), _p(k), _p(v), _p(beta), _p(g), _p(S0), _p(o), _p(S),
-                                            B, T, H, dk, dv, float(scale), int(nthreads))
+                                            B, T, H, dk, dv, float(scale), _threads(nthreads))
         if rc != 0:
             raise ValueError("kda_oracle_recurrence: bad arguments")
         return o, S
@@ -138,7 +156,7 @@ class Oracle:
         o = np.zeros((B, T, H, dv))
         S = np.zeros((B, H, dk, dv))
         rc = self.lib.kda_oracle_forward_z(_p(q), _p(k), _p(v), _p(beta), _p(z), _p(A), float(g_min),
-                                           _p(S0), _p(o), _p(S), B, T, H, dk, dv, float(scale), int(nthreads))
+                                           _p(S0), _p(o), _p(S), B, T, H, dk, dv, float(scale), _threads(nthreads))
         if rc != 0:
             raise ValueError("kda_oracle_forward_z: bad arguments")
         return o, S

@@ -8,9 +8,14 @@ factorised update ("Kimi K3: the paper and proofs side by side", section
                - beta * k[i] * (sum_r k[r] * alpha[r] * S[r][j])
                + beta * k[i] * v[j]
 
-followed by the read after the update, o[j] = sum_i S'[i][j] * q[i].  It uses
-only Python floats and loops, so it shares nothing with the C oracle beyond the
-definition, and is cross-checked against it on tiny shapes.
+followed by the read after the update, o[j] = sum_i S'[i][j] * q[i].  The
+same coordinate formula is the scalar step of the CPU laboratory on "Kimi K3:
+architecture, derivations and a pinned-source audit" (section "CPU
+laboratory: recurrence, depth, experts and replay"); here it is evaluated one
+value column at a time, since the columns of the state evolve independently
+given (k, beta, alpha).  It uses only Python floats and loops, so it shares
+nothing with the C oracle beyond the definition, and is cross-checked against
+it on tiny shapes.
 """
 from __future__ import annotations
 
@@ -18,16 +23,23 @@ import math
 
 
 def step(S, q, k, v, alpha, beta):
+    """One token: returns (S', o) as nested lists."""
     dk, dv = len(S), len(S[0])
-    out = [[0.0] * dv for _ in range(dk)]
-    for i in range(dk):
-        for j in range(dv):
-            old_read = 0.0
-            for r in range(dk):
-                old_read += k[r] * alpha[r] * S[r][j]
-            out[i][j] = alpha[i] * S[i][j] - beta * k[i] * old_read + beta * k[i] * v[j]
-    o = [sum(out[i][j] * q[i] for i in range(dk)) for j in range(dv)]
-    return out, o
+    new = [[0.0] * dv for _ in range(dk)]
+    o = [0.0] * dv
+    for j in range(dv):
+        col = [alpha[i] * S[i][j] for i in range(dk)]  # column j with its key rows decayed
+        pred = 0.0
+        for i in range(dk):
+            pred += k[i] * col[i]                       # what the decayed column predicts at k
+        err = v[j] - pred
+        for i in range(dk):
+            new[i][j] = col[i] + beta * k[i] * err      # erase along k, write v
+        acc = 0.0
+        for i in range(dk):
+            acc += new[i][j] * q[i]                     # the query reads the updated column
+        o[j] = acc
+    return new, o
 
 
 def gate_alpha(z, A, g_min=-5.0):

@@ -1,5 +1,12 @@
 """Helpers for the GPU parity tests: storage arrays -> device tensors, the
-relative-L2 metric, and oracle runs on the same rounded inputs."""
+relative-L2 metric, and oracle runs on the same rounded inputs.
+
+Parity is judged per sequence and per 64-token block, not only over a whole
+tensor: at a million tokens one 64-token block is 1/16384 of the output, so a
+block that came out entirely wrong would barely move a whole-tensor relative
+L2.  ``assert_tokens`` therefore checks the relative L2 of every (b, h)
+sequence and of every 64-token block of it, and ``assert_states`` that of
+every (b, h) state, each against the same tolerance."""
 from __future__ import annotations
 
 import sys
@@ -11,6 +18,7 @@ import kda_inputs as ki
 
 DEV = "cuda:0"
 TOL = {"f32": 1e-5, "bf16": 1e-2}
+BLOCK = 64
 
 
 def say(*a):
@@ -43,11 +51,107 @@ def rel_l2(x: np.ndarray, ref: np.ndarray) -> float:
     return float(np.linalg.norm(x - ref) / nr)
 
 
+def _ratio(d2: np.ndarray, r2: np.ndarray) -> np.ndarray:
+    """sqrt(d2 / r2) elementwise; 0 where both are 0, inf where only r2 is."""
+    out = np.zeros(np.broadcast(d2, r2).shape)
+    nz = r2 > 0
+    out[nz] = np.sqrt(d2[nz] / r2[nz])
+    out[(~nz) & (d2 > 0)] = np.inf
+    return out
+
+
+def token_report(x: np.ndarray, ref: np.ndarray, block: int = BLOCK) -> dict:
+    """x, ref [B, T, H, d]: relative L2 over the whole tensor, per (b, h)
+    sequence and per (b, h, block of ``block`` tokens); the largest absolute
+    error and where it is."""
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert x.shape == ref.shape and x.ndim == 4, (x.shape, ref.shape)
+    assert np.all(np.isfinite(x)), "non-finite values in GPU output"
+    B, T, H, _ = x.shape
+    diff = x - ref
+    d2 = np.einsum("bthc,bthc->bth", diff, diff)
+    r2 = np.einsum("bthc,bthc->bth", ref, ref)
+    nb = -(-T // block)
+    pad = nb * block - T
+    if pad:
+        d2 = np.concatenate([d2, np.zeros((B, pad, H))], axis=1)
+        r2 = np.concatenate([r2, np.zeros((B, pad, H))], axis=1)
+    d2b = d2.reshape(B, nb, block, H).sum(axis=2)  # [B, nb, H]
+    r2b = r2.reshape(B, nb, block, H).sum(axis=2)
+    blk = _ratio(d2b, r2b)
+    pair = _ratio(d2b.sum(axis=1), r2b.sum(axis=1))  # [B, H]
+    whole = float(_ratio(np.array(d2b.sum()), np.array(r2b.sum())))
+    ab = np.abs(diff)
+    iw = np.unravel_index(int(np.argmax(ab)), ab.shape) if ab.size else (0, 0, 0, 0)
+    ib = np.unravel_index(int(np.argmax(blk)), blk.shape) if blk.size else (0, 0, 0)
+    ip = np.unravel_index(int(np.argmax(pair)), pair.shape) if pair.size else (0, 0)
+    return {"whole": whole, "pair_max": float(pair.max()) if pair.size else 0.0, "pair_at": tuple(map(int, ip)),
+            "block_max": float(blk.max()) if blk.size else 0.0,
+            "block_at": (int(ib[0]), int(ib[1]) * block, int(ib[2])),
+            "max_abs": float(ab.max()) if ab.size else 0.0, "max_abs_at": tuple(map(int, iw)),
+            "blocks": int(blk.size)}
+
+
+def state_report(x: np.ndarray, ref: np.ndarray) -> dict:
+    """x, ref [B, H, dk, dv]: relative L2 over the whole tensor and per (b, h)."""
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert x.shape == ref.shape and x.ndim == 4, (x.shape, ref.shape)
+    assert np.all(np.isfinite(x)), "non-finite values in GPU state"
+    diff = x - ref
+    d2 = np.einsum("bhij,bhij->bh", diff, diff)
+    r2 = np.einsum("bhij,bhij->bh", ref, ref)
+    pair = _ratio(d2, r2)
+    ip = np.unravel_index(int(np.argmax(pair)), pair.shape) if pair.size else (0, 0)
+    ab = np.abs(diff)
+    return {"whole": float(_ratio(np.array(d2.sum()), np.array(r2.sum()))),
+            "pair_max": float(pair.max()) if pair.size else 0.0, "pair_at": tuple(map(int, ip)),
+            "max_abs": float(ab.max()) if ab.size else 0.0}
+
+
+def assert_tokens(label: str, x: np.ndarray, ref: np.ndarray, tol: float, block: int = BLOCK,
+                  offset: tuple = (0, 0)) -> dict:
+    """Relative L2 <= tol over every (b, h) sequence and every ``block``-token
+    block of it (and so over the whole tensor).  ``offset`` = (b0, h0) of x
+    within the full tensor, for the printed coordinates."""
+    r = token_report(x, ref, block)
+    b0, h0 = offset
+    pb, ph = r["pair_at"]
+    bb, bt, bh = r["block_at"]
+    mb, mt, mh, mc = r["max_abs_at"]
+    say(f"  {label}: rel-L2 whole {r['whole']:.3e}; worst (b,h) {r['pair_max']:.3e} at ({pb + b0},{ph + h0}); "
+        f"worst of {r['blocks']} {block}-token blocks {r['block_max']:.3e} at (b={bb + b0}, t={bt}, h={bh + h0}); "
+        f"max-abs {r['max_abs']:.3e} at (b={mb + b0}, t={mt}, h={mh + h0}, c={mc})")
+    assert r["pair_max"] <= tol, f"{label}: sequence rel-L2 {r['pair_max']:.3e} > {tol}"
+    assert r["block_max"] <= tol, f"{label}: {block}-token block rel-L2 {r['block_max']:.3e} > {tol}"
+    return r
+
+
+def assert_states(label: str, x: np.ndarray, ref: np.ndarray, tol: float, offset: tuple = (0, 0)) -> dict:
+    """Relative L2 <= tol for every (b, h) state."""
+    r = state_report(x, ref)
+    b0, h0 = offset
+    pb, ph = r["pair_at"]
+    say(f"  {label}: rel-L2 whole {r['whole']:.3e}; worst (b,h) {r['pair_max']:.3e} at ({pb + b0},{ph + h0}); "
+        f"max-abs {r['max_abs']:.3e}")
+    assert r["pair_max"] <= tol, f"{label}: state rel-L2 {r['pair_max']:.3e} > {tol}"
+    return r
+
+
 def f64_inputs(d: dict, dtype: str) -> dict:
     out = {k: ki.to_f64(d[k], dtype) for k in ("q", "k", "v", "z", "beta")}
     out["A"] = d["A"].astype(np.float64)
     out["S0"] = None if d.get("S0") is None else d["S0"].astype(np.float64)
     return out
+
+
+def sub_inputs(d: dict, b0: int, b1: int, h0: int, h1: int) -> dict:
+    """Storage arrays of batch entries [b0, b1) and heads [h0, h1) of a prefill workload."""
+    sub = {k: np.ascontiguousarray(d[k][b0:b1, :, h0:h1]) for k in ("q", "k", "v", "z", "beta")}
+    sub["A"] = np.ascontiguousarray(d["A"][h0:h1])
+    sub["S0"] = None if d.get("S0") is None else np.ascontiguousarray(d["S0"][b0:b1, h0:h1])
+    return sub
 
 
 def dev_inputs(d: dict, dtype: str) -> dict:

@@ -278,27 +278,39 @@ def pin_superposition(orc):
 
 
 def pin_affine_composition(orc):
-    """Products of per-token affine maps (M_t, U_t), M_t = (I - beta k k^T)
-    Diag(alpha), U_t = beta k v^T, composed in order and applied to S_0 equal
-    the oracle's S_T; composition is associative (derivations page, 4.5)."""
+    """Each token is the affine map S -> M_t S + U_t with M_t = (I - beta k k^T)
+    Diag(alpha) and U_t = beta k v^T (derivations page, section 4.5, which
+    regroups these compositions into chunks; the CPU laboratory on the same page,
+    "CPU laboratory: recurrence, depth, experts and replay", composes them too).
+    Written as the linear map [[M_t, U_t], [0, I]] on [S; I] (a (dk + dv) x dv
+    block matrix), the ordered product over all tokens applied to [S_0; I] is
+    [S_T; I] of the oracle, and the product over a sequence equals the product of
+    the products over any two consecutive pieces of it: the regrouping the
+    chunked and segment-parallel forms rely on."""
     rng = np.random.default_rng(19)
     T, dk, dv = 9, 4, 3
     q, k, v, alpha, beta, S0 = _rand_seq(rng, T, dk, dv)
     o, S = run1(orc, q, k, v, alpha, beta, S0=S0)
-    trans = [((np.eye(dk) - beta[t] * np.outer(k[t], k[t])) @ np.diag(alpha[t]), beta[t] * np.outer(k[t], v[t]))
-             for t in range(T)]
 
-    def comp(later, earlier):
-        return later[0] @ earlier[0], later[0] @ earlier[1] + later[1]
+    def block(t):
+        X = np.zeros((dk + dv, dk + dv))
+        X[:dk, :dk] = (np.eye(dk) - beta[t] * np.outer(k[t], k[t])) @ np.diag(alpha[t])
+        X[:dk, dk:] = beta[t] * np.outer(k[t], v[t])
+        X[dk:, dk:] = np.eye(dv)
+        return X
 
-    agg = (np.eye(dk), np.zeros((dk, dv)))
-    for tr in trans:
-        agg = comp(tr, agg)
-    np.testing.assert_allclose(agg[0] @ S0 + agg[1], S, atol=1e-12)
-    left = comp(trans[2], comp(trans[1], trans[0]))
-    right = comp(comp(trans[2], trans[1]), trans[0])
-    for x, y in zip(left, right):
-        np.testing.assert_allclose(x, y, atol=1e-12)
+    def product(t0, t1):  # tokens t0 .. t1-1, the latest applied last (leftmost)
+        X = np.eye(dk + dv)
+        for t in range(t0, t1):
+            X = block(t) @ X
+        return X
+
+    whole = product(0, T)
+    out = whole @ np.vstack([S0, np.eye(dv)])
+    np.testing.assert_allclose(out[:dk], S, atol=1e-12)
+    np.testing.assert_allclose(out[dk:], np.eye(dv), atol=0)
+    for cut in range(T + 1):
+        np.testing.assert_allclose(product(cut, T) @ product(0, cut), whole, atol=1e-12)
 
 
 def pin_brute_force(orc):

@@ -13,7 +13,9 @@ import gated_delta_rule_11_amd as kda
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_UNSUPPORTED, ERR_ALIAS, ERR_HIP, ERR_ALIGN, ERR_WORKSPACE = range(9)
+# status codes: 0 on success, negative on error (include/kda.h)
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP, ERR_ALIAS, ERR_ALIGN = 0, -1, -2, -3, -4, -5, -6, -7, -8
+STATUSES = (OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP, ERR_ALIAS, ERR_ALIGN)
 F32, BF16 = 0, 1
 
 
@@ -45,11 +47,24 @@ def test_library_exports_every_declared_symbol(L):
         assert hasattr(L, name), name
 
 
+def test_status_codes_match_the_header(L):
+    """The numeric values above are the header's (the contract is negative codes)."""
+    text = open(HEADER).read()
+    names = {"OK": OK, "ERR_NULL": ERR_NULL, "ERR_SHAPE": ERR_SHAPE, "ERR_DTYPE": ERR_DTYPE,
+             "ERR_WORKSPACE": ERR_WORKSPACE, "ERR_UNSUPPORTED": ERR_UNSUPPORTED, "ERR_HIP": ERR_HIP,
+             "ERR_ALIAS": ERR_ALIAS, "ERR_ALIGN": ERR_ALIGN}
+    for n, val in names.items():
+        m = re.search(r"\bKDA_" + n + r"\s*=\s*(-?\d+)", text)
+        assert m and int(m.group(1)) == val, n
+        assert L.kda_status_string(val).decode().startswith("KDA_" + n)
+
+
 def test_status_strings(L):
-    for s in range(9):
+    for s in STATUSES:
         assert L.kda_status_string(s).decode().startswith("KDA_")
     assert b"unknown" in L.kda_status_string(99)
-    assert L.kda_version() >= 100
+    assert b"unknown" in L.kda_status_string(1)
+    assert L.kda_version() >= 200
 
 
 # Fake device addresses: validation must reject before any of them is used.
@@ -65,13 +80,14 @@ def gate(L, z=P(0), zt=BF16, A=P(1), gmin=-5.0, B=1, T=64, H=2, dk=128, chunk=64
 
 
 def chunk(L, q=P(0), k=P(1), v=P(2), beta=P(3), it=BF16, G=P(4), S_in=P(5), o=P(6), ot=BF16, S_out=P(7),
-          B=1, T=64, H=2, dk=128, dv=128, c=64, scale=1.0):
-    return L.kda_chunk_fwd(q, k, v, beta, it, G, S_in, o, ot, S_out, B, T, H, dk, dv, c, scale, N)
+          B=1, T=64, H=2, dk=128, dv=128, c=64, scale=1.0, ws=None, wsb=0):
+    return L.kda_chunk_fwd(q, k, v, beta, it, G, S_in, o, ot, S_out, B, T, H, dk, dv, c, scale, ws, wsb, N)
 
 
 def chunk_z(L, q=P(0), k=P(1), v=P(2), beta=P(3), z=P(4), it=BF16, A=P(8), gmin=-5.0, S_in=P(5), o=P(6), ot=BF16,
-            S_out=P(7), B=1, T=64, H=2, dk=128, dv=128, c=64, scale=1.0):
-    return L.kda_chunk_fwd_z(q, k, v, beta, z, it, A, gmin, S_in, o, ot, S_out, B, T, H, dk, dv, c, scale, N)
+            S_out=P(7), B=1, T=64, H=2, dk=128, dv=128, c=64, scale=1.0, ws=None, wsb=0):
+    return L.kda_chunk_fwd_z(q, k, v, beta, z, it, A, gmin, S_in, o, ot, S_out, B, T, H, dk, dv, c, scale, ws, wsb,
+                             N)
 
 
 def decode(L, q=P(0), k=P(1), v=P(2), z=P(3), beta=P(4), it=BF16, A=P(5), gmin=-5.0, S=P(6), o=P(7), ot=BF16,
@@ -88,6 +104,8 @@ def test_gate_validation(L):
     assert gate(L, chunk=32) == ERR_UNSUPPORTED
     assert gate(L, gmin=1.0) == ERR_UNSUPPORTED
     assert gate(L, gmin=float("nan")) == ERR_UNSUPPORTED
+    assert gate(L, gmin=-5.5) == ERR_UNSUPPORTED     # 16 g_min >= -86.4: tile decays stay normal fp32
+    assert gate(L, gmin=-5.4, z=None) == ERR_NULL    # the floor itself is accepted
     assert gate(L, z=None) == ERR_NULL
     assert gate(L, G=None) == ERR_NULL
     assert gate(L, A=None) == ERR_NULL
@@ -121,6 +139,8 @@ def test_chunk_validation(L):
     assert chunk(L, beta=ctypes.c_void_p(0x40000002), o=P(0)) == ERR_ALIAS
     assert chunk(L, B=0) == OK
     assert chunk_z(L, gmin=-6.0) == ERR_UNSUPPORTED
+    assert chunk_z(L, gmin=-5.5) == ERR_UNSUPPORTED
+    assert chunk_z(L, gmin=-5.4, q=None) == ERR_NULL
     assert chunk_z(L, gmin=0.5) == ERR_UNSUPPORTED
     assert chunk_z(L, z=None) == ERR_NULL
     assert chunk_z(L, A=None) == ERR_NULL
@@ -213,7 +233,9 @@ def chunk_seg(L, segs=4, ws=P(10), wsb=1 << 30, B=1, T=1024, H=2, c=64, it=BF16,
 
 def test_segmented_validation(L):
     need = L.kda_chunk_fwd_z_segmented_workspace_bytes(1, 2, 128, 128, 4)
-    assert need == 1 * 2 * 4 * (2 * 128 * 128 + 128 * 128) * 4
+    # end states and transitions of every segment but the last, entry states of all
+    assert need == 1 * 2 * (3 * (128 * 128 + 128 * 128) + 4 * 128 * 128) * 4
+    assert L.kda_chunk_fwd_z_segmented_workspace_bytes(1, 2, 128, 128, 1) == 0
     assert L.kda_chunk_fwd_z_segmented_workspace_bytes(1, 2, 128, 128, 0) == 0
     assert chunk_seg(L, segs=0) == ERR_SHAPE
     assert chunk_seg(L, ws=None) == ERR_NULL
@@ -233,7 +255,7 @@ def test_prologue_validation(L):
         a.update(kw)
         return L.kda_chunk_fwd_z_prologue(a["q"], a["k"], a["v"], a["beta"], a["z"], a["it"], a["A"], a["gmin"],
                                           a["S_in"], a["o"], BF16, a["S_out"], a["B"], a["T"], a["H"], a["dk"],
-                                          a["dv"], a["chunk"], 1.0, N)
+                                          a["dv"], a["chunk"], 1.0, None, 0, N)
     assert chunk(q=None) == ERR_NULL
     assert chunk(dk=48) == ERR_UNSUPPORTED
     assert chunk(chunk=32) == ERR_UNSUPPORTED
@@ -295,7 +317,7 @@ def test_zero_head_dims_rejected(L):
         assert replay(L, **kw) == ERR_SHAPE, kw
     assert chunk_seg(L, dk=0) == ERR_SHAPE
     assert L.kda_chunk_fwd_z_prologue(P(0), P(1), P(2), P(3), P(4), BF16, P(8), -5.0, P(5), P(6), BF16, P(7), 1, 100,
-                                      2, 128, 0, 64, 1.0, N) == ERR_SHAPE
+                                      2, 128, 0, 64, 1.0, None, 0, N) == ERR_SHAPE
     assert L.kda_decode_step_prologue(P(0), P(1), P(2), P(3), P(4), BF16, P(5), -5.0, P(6), P(7), BF16, 4, 2, 0, 128,
                                       1.0, N) == ERR_SHAPE
     assert L.kda_chunk_bwd_z(P(0), P(1), P(2), P(3), P(4), F32, P(5), -5.0, None, P(6), F32, None, P(7), P(8), P(9),
@@ -315,3 +337,30 @@ def test_token_count_limit(L):
     assert gate(L, T=big, B=1, H=1, dk=16, z=None) == ERR_NULL
     assert replay(L, n_draft=big + 1, Nn=1, H=1, dk=16, dv=16) == ERR_SHAPE
     assert replay(L, n_draft=big, Nn=1, H=1, dk=16, dv=16, q=None) == ERR_NULL
+
+
+def test_chunk_workspace_query_and_validation(L):
+    """kda_chunk_fwd_workspace_bytes sizes the workspace of the three chunked-prefill
+    entry points from the sizes alone; a call with less returns KDA_ERR_WORKSPACE,
+    with none KDA_ERR_NULL, and the workspace is checked for alignment and overlap."""
+    q = L.kda_chunk_fwd_workspace_bytes
+    assert q(4, 32768, 32, 128, 128, 64) == 0       # B*H = 128 fills the GPU in one pass
+    assert q(1, 64, 8, 128, 128, 64) == 0           # a single chunk: nothing to split
+    assert q(1, 4096, 32, 64, 64, 64) == 0          # the segment passes are matrix-core only
+    few = q(1, 4096, 8, 128, 128, 64)               # B*H = 8, 64 chunks: segment-parallel
+    assert few > 0 and few % 16 == 0
+    assert q(1, 1 << 20, 8, 128, 128, 64) >= few
+    for bad in ((-1, 64, 8, 128, 128, 64), (1, -1, 8, 128, 128, 64), (1, 64, 0, 128, 128, 64),
+                (1, 64, 8, 96, 128, 64), (1, 64, 8, 128, 128, 32)):
+        assert q(*bad) == 0, bad
+    kw = dict(B=1, T=4096, H=8)
+    for call in (chunk, chunk_z):
+        assert call(L, **kw) == ERR_NULL                               # no workspace at all
+        assert call(L, ws=P(10), wsb=few - 4, **kw) == ERR_WORKSPACE   # too small
+        assert call(L, ws=ctypes.c_void_p(0xb0000008), wsb=few, **kw) == ERR_ALIGN
+        assert call(L, ws=P(6), wsb=few, **kw) == ERR_ALIAS            # over the output
+        assert call(L, ws=P(7), wsb=few, **kw) == ERR_ALIAS            # over the final state
+        assert call(L, ws=P(10), wsb=few, B=0, T=4096, H=8) == OK      # nothing to do
+    # where none is needed, a NULL workspace of zero bytes is valid (the call then
+    # gets past validation; without a GPU it stops at its first HIP call)
+    assert chunk_z(L, ws=None, wsb=0, B=4, T=64, H=32) == ERR_HIP

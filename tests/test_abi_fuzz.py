@@ -23,7 +23,9 @@ from hypothesis import strategies as st  # noqa: E402
 
 import gated_delta_rule_11_amd as kda  # noqa: E402
 
-OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_UNSUPPORTED, ERR_ALIAS, ERR_HIP, ERR_ALIGN, ERR_WORKSPACE = range(9)
+# status codes (include/kda.h): 0 on success, negative on error
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP, ERR_ALIAS, ERR_ALIGN = 0, -1, -2, -3, -4, -5, -6, -7, -8
+STATUSES = (OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP, ERR_ALIAS, ERR_ALIGN)
 
 
 def _gpu_visible() -> bool:
@@ -40,7 +42,7 @@ SIZES = st.sampled_from([-(1 << 31), -3, -1, 0, 1, 2, 3, 7, 16, 17, 64, 100, 1 <
 DIMS = st.sampled_from([-16, -1, 0, 1, 8, 16, 24, 32, 48, 64, 96, 128, 256, 1 << 30])
 CHUNKS = st.sampled_from([-64, 0, 1, 15, 16, 32, 64, 128])
 DTYPES = st.sampled_from([-1, 0, 1, 2, 1 << 20])
-FLOATS = st.sampled_from([-math.inf, -6.0, -5.5, -5.0, -1.0, -0.0, 0.0, 0.5, 1.0, math.inf, math.nan])
+FLOATS = st.sampled_from([-math.inf, -6.0, -5.5, -5.4, -5.0, -1.0, -0.0, 0.0, 0.5, 1.0, math.inf, math.nan])
 SCALES = st.sampled_from([1.0, 0.0, -2.0, 1e30, math.inf, math.nan])
 
 
@@ -72,7 +74,7 @@ def L():
 
 
 def _check(status, dtypes, sizes):
-    assert status in range(9), status
+    assert status in STATUSES, status
     if any(t not in (0, 1) for t in dtypes):
         assert status == ERR_DTYPE, status
     if status == OK:
@@ -89,17 +91,23 @@ def test_fuzz_gate(L, p, zt, gmin, B, T, H, dk, chunk):
     _check(s, [zt], [B, T, H])
 
 
+WSB = st.sampled_from([0, 16, 1 << 20, 1 << 40])
+
+
 @FUZZ
-@given(p=pointers(9), it=DTYPES, ot=DTYPES, gmin=FLOATS, scale=SCALES, B=SIZES, T=SIZES, H=SIZES, dk=DIMS,
-       dv=DIMS, chunk=CHUNKS, fused=st.booleans())
-def test_fuzz_chunk(L, p, it, ot, gmin, scale, B, T, H, dk, dv, chunk, fused):
+@given(p=pointers(10), it=DTYPES, ot=DTYPES, gmin=FLOATS, scale=SCALES, B=SIZES, T=SIZES, H=SIZES, dk=DIMS,
+       dv=DIMS, chunk=CHUNKS, fused=st.booleans(), wsb=WSB)
+def test_fuzz_chunk(L, p, it, ot, gmin, scale, B, T, H, dk, dv, chunk, fused, wsb):
+    need = L.kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk)
     if fused:
         s = L.kda_chunk_fwd_z(p[0], p[1], p[2], p[3], p[4], it, p[5], gmin, p[6], p[7], ot, p[8], B, T, H, dk, dv,
-                              chunk, scale, None)
+                              chunk, scale, p[9], wsb, None)
     else:
         s = L.kda_chunk_fwd(p[0], p[1], p[2], p[3], it, p[4], p[6], p[7], ot, p[8], B, T, H, dk, dv, chunk, scale,
-                            None)
+                            p[9], wsb, None)
     _check(s, [it, ot], [B, T, H])
+    if s == OK and B > 0 and H > 0:
+        assert wsb >= need
 
 
 @FUZZ
@@ -131,11 +139,11 @@ def test_fuzz_segmented(L, p, it, ot, gmin, scale, B, T, H, dk, dv, chunk, segs,
 
 
 @FUZZ
-@given(p=pointers(9), it=DTYPES, ot=DTYPES, gmin=FLOATS, scale=SCALES, B=SIZES, T=SIZES, H=SIZES, dk=DIMS,
-       dv=DIMS, chunk=CHUNKS)
-def test_fuzz_prologue(L, p, it, ot, gmin, scale, B, T, H, dk, dv, chunk):
+@given(p=pointers(10), it=DTYPES, ot=DTYPES, gmin=FLOATS, scale=SCALES, B=SIZES, T=SIZES, H=SIZES, dk=DIMS,
+       dv=DIMS, chunk=CHUNKS, wsb=WSB)
+def test_fuzz_prologue(L, p, it, ot, gmin, scale, B, T, H, dk, dv, chunk, wsb):
     s = L.kda_chunk_fwd_z_prologue(p[0], p[1], p[2], p[3], p[4], it, p[5], gmin, p[6], p[7], ot, p[8], B, T, H, dk,
-                                   dv, chunk, scale, None)
+                                   dv, chunk, scale, p[9], wsb, None)
     _check(s, [it, ot], [B, T, H])
 
 

@@ -3,8 +3,11 @@ oracle on the same inputs (tolerances as everywhere: relative L2 1e-5 for fp32
 inputs, 1e-2 for bf16), plus the results that are exact:
 
 * g_min = 0: no decay at all (alpha = 1), the delta rule alone;
-* g_min at the limits the entry points accept (-5.5 for the forward, -5 for
+* g_min at the limits the entry points accept (-5.4 for the forward, -5 for
   the backward);
+* whole 16-token tiles at the floor of the gate (sigma saturated on every token
+  of a channel, so a tile decays by exactly e^(16 g_min)), through the fused
+  gate and through kda_gate followed by kda_chunk_fwd;
 * decay logits far in saturation (|e^A z| ~ 100: g is exactly 0 or g_min);
 * beta = 0: the state only decays and is never written;
 * q = 0: every output is exactly zero; v = 0 with a zero entry state: the
@@ -12,7 +15,8 @@ inputs, 1e-2 for bf16), plus the results that are exact:
 * many heads (H = 1024 for the prefill, 2048 for the decode): large strides;
 * head counts that select each launch shape of the matrix-core prefill: four
   32-column slices per head (B*H = 64 with the XCD-grouped workgroup order,
-  B*H = 75 without it) and two 64-column slices in plain order (B*H = 130),
+  B*H = 63 without it), eight 16-column slices (B*H = 16 grouped, 25 plain)
+  and two 64-column slices in plain order (B*H = 130),
   for the fused gate and the precomputed gate (the segment passes' shapes are
   covered in test_gpu_segmented).
 """
@@ -45,7 +49,7 @@ def _prefill(d, spec, g_min, dd=None):
 
 
 @pytest.mark.parametrize("dk,dv,chunk,dtype", SHAPES)
-@pytest.mark.parametrize("g_min", [0.0, -0.5, -5.5])
+@pytest.mark.parametrize("g_min", [0.0, -0.5, -5.4])
 def test_gate_floor(dk, dv, chunk, dtype, g_min):
     spec = ki.small_spec(1, 3, 300, dk, dv, chunk, dtype, seed=7100 + dk, s0_std=0.3)
     say(f"case g_min={g_min} dk={dk} dv={dv} chunk={chunk} {dtype}")
@@ -54,6 +58,34 @@ def test_gate_floor(dk, dv, chunk, dtype, g_min):
     eo, es = rel_l2(host64(o), o_ref), rel_l2(host64(S), S_ref)
     say(f"  rel-L2 o={eo:.3e} S={es:.3e}")
     assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+@pytest.mark.parametrize("path", ["fused gate", "kda_gate then kda_chunk_fwd"])
+@pytest.mark.parametrize("g_min", [-5.0, -5.4])
+def test_whole_tiles_at_the_floor(g_min, path):
+    """Key channels whose decay logit is +100 on every token (sigma = 1, g = g_min
+    exactly): each of their 16-token tiles decays by e^(16 g_min), whose reciprocal
+    the matrix-core kernel forms; and one whole chunk with every channel there."""
+    spec = ki.small_spec(1, 2, 64 * 3 + 20, 128, 128, 64, "bf16", seed=7150, s0_std=0.3)
+    say(f"case whole tiles at the floor g_min={g_min} via {path}")
+    d = ki.prefill_inputs(spec)
+    sat = ki.round_storage(np.full((1,), 100.0), "bf16")[0]
+    d["z"][:, :, :, [0, 5, 77, 127]] = sat
+    d["z"][:, 64:128] = sat
+    dd = dev_inputs(d, spec.dtype)
+    if path == "fused gate":
+        o, S = kda.chunk_fwd_z(dd["q"], dd["k"], dd["v"], dd["beta"], dd["z"], dd["A"], g_min, 64, S_in=dd["S0"],
+                               o_dtype=torch.float32)
+    else:
+        G = kda.gate(dd["z"], dd["A"], g_min, chunk=64)
+        o, S = kda.chunk_fwd(dd["q"], dd["k"], dd["v"], dd["beta"], G, 64, S_in=dd["S0"], o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(S).all())
+    f = f64_inputs(d, spec.dtype)
+    o_ref, S_ref = oracle.forward_z(f["q"], f["k"], f["v"], f["beta"], f["z"], f["A"], g_min, f["S0"])
+    eo, es = rel_l2(host64(o), o_ref), rel_l2(host64(S), S_ref)
+    say(f"  rel-L2 o={eo:.3e} S={es:.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("dk,dv,chunk,dtype", SHAPES)
@@ -154,7 +186,7 @@ def test_backward_no_decay_and_floor(dtype):
             assert float(g["dz"].abs().max()) == 0.0 and float(g["dA"].abs().max()) == 0.0
 
 
-@pytest.mark.parametrize("B,H", [(2, 32), (3, 25), (2, 65)])
+@pytest.mark.parametrize("B,H", [(2, 32), (3, 21), (1, 16), (1, 25), (2, 65)])
 def test_head_counts_select_launch_shapes(B, H):
     spec = ki.small_spec(B, H, 64 + 17, 128, 128, 64, "bf16", seed=7800 + B * H, s0_std=0.1)
     say(f"case launch shape B={B} H={H} T={spec.T} (fused gate, precomputed gate, 2 segments)")
@@ -171,8 +203,8 @@ def test_head_counts_select_launch_shapes(B, H):
     eo, es = rel_l2(host64(o2), o_ref), rel_l2(host64(S2), S_ref)
     say(f"  precomputed gate rel-L2 o={eo:.3e} S={es:.3e}")
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
-    # two segments of one chunk each: 128 (b, h, segment) units in the XCD-grouped order,
-    # 150 and 260 in plain order
+    # two segments of one chunk each (the last segment's pass over B*H*2 (b, h, segment)
+    # units, the first segment's over B*H)
     o3, S3 = kda.chunk_fwd_z_segmented(dd["q"], dd["k"], dd["v"], dd["beta"], dd["z"], dd["A"], 2, -5.0,
                                        spec.chunk, S_in=dd["S0"], o_dtype=torch.float32)
     torch.cuda.synchronize()

@@ -1,7 +1,11 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
 benchmark times (fused gate, bf16 inputs and bf16 outputs), checked against
-the fp64 oracle on sampled (batch, head) sequences computed one by one over
-their whole length."""
+the fp64 oracle on every (batch, head) sequence over its whole length.
+
+Each check asserts the relative L2 of every sequence and of every 64-token
+block of it (tests/_gpu.py, ``assert_tokens``), so one wrong chunk anywhere in
+a million tokens fails the test; the worst block, the worst sequence and the
+largest absolute error are printed with their coordinates."""
 from dataclasses import replace
 
 import numpy as np
@@ -11,51 +15,83 @@ import torch
 import gated_delta_rule_11_amd as kda
 import kda_inputs as ki
 import oracle
-from tests._gpu import TOL, dev_inputs, f64_inputs, host64, rel_l2, say
+from tests._gpu import (TOL, assert_states, assert_tokens, dev_inputs, f64_inputs, host64, say,
+                        sub_inputs)
 
 pytestmark = pytest.mark.gpu
 
 
-def _prefill_sampled(spec, samples):
+def _oracle_groups(d, spec, groups):
+    """Oracle outputs of each (b0, b1, h0, h1) group of sequences, one group at a time."""
+    for b0, b1, h0, h1 in groups:
+        say(f"  oracle b=[{b0},{b1}) h=[{h0},{h1}) T={spec.T}")
+        f = f64_inputs(sub_inputs(d, b0, b1, h0, h1), spec.dtype)
+        o_ref, S_ref = oracle.forward_z(f["q"], f["k"], f["v"], f["beta"], f["z"], f["A"], -5.0, f["S0"])
+        del f
+        yield (b0, b1, h0, h1), o_ref, S_ref
+
+
+def _check_runs(spec, d, runs, groups):
+    """runs: {label: (o, S)} device results of the whole workload."""
+    tol = TOL[spec.dtype]
+    for (b0, b1, h0, h1), o_ref, S_ref in _oracle_groups(d, spec, groups):
+        for label, (o, S) in runs.items():
+            assert_tokens(f"{label} o", host64(o[b0:b1, :, h0:h1]), o_ref, tol, offset=(b0, h0))
+            assert_states(f"{label} S", host64(S[b0:b1, h0:h1]), S_ref, tol, offset=(b0, h0))
+        del o_ref, S_ref
+
+
+def _prefill_all(spec):
     say(f"case {spec.name}: generating inputs")
     d = ki.prefill_inputs(spec)
     dd = dev_inputs(d, spec.dtype)
-    say(f"case {spec.name}: GPU run")
+    say(f"case {spec.name}: GPU run (kda_chunk_fwd_z, bf16 outputs)")
     o, S = kda.chunk_fwd_z(dd["q"], dd["k"], dd["v"], dd["beta"], dd["z"], dd["A"], -5.0, spec.chunk,
                            S_in=dd["S0"], o_dtype=torch.bfloat16)
     torch.cuda.synchronize()
-    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(S).all())
-    for b, h in samples:
-        say(f"  oracle b={b} h={h} T={spec.T}")
-        sub = {k: np.ascontiguousarray(d[k][b:b + 1, :, h:h + 1]) for k in ("q", "k", "v", "z", "beta")}
-        sub["A"] = np.ascontiguousarray(d["A"][h:h + 1])
-        sub["S0"] = None if d["S0"] is None else np.ascontiguousarray(d["S0"][b:b + 1, h:h + 1])
-        f = f64_inputs(sub, spec.dtype)
-        o_ref, S_ref = oracle.forward_z(f["q"], f["k"], f["v"], f["beta"], f["z"], f["A"], -5.0, f["S0"])
-        eo = rel_l2(host64(o[b:b + 1, :, h:h + 1]), o_ref)
-        es = rel_l2(host64(S[b:b + 1, h:h + 1]), S_ref)
-        say(f"  b={b} h={h} rel-L2 o={eo:.3e} S={es:.3e}")
-        assert eo <= TOL[spec.dtype] and es <= TOL[spec.dtype]
-    del dd, o, S
+    del dd
+    # every sequence, one batch entry (32 heads) at a time
+    _check_runs(spec, d, {"kda_chunk_fwd_z": (o, S)}, [(b, b + 1, 0, spec.H) for b in range(spec.B)])
+    del o, S
     torch.cuda.empty_cache()
 
 
-def test_prefill_32k_sampled():
-    _prefill_sampled(ki.PREFILL_32K, [(0, 0), (1, 17), (3, 31)])
+def test_prefill_32k_all_sequences():
+    _prefill_all(ki.PREFILL_32K)
 
 
-def test_prefill_32k_slow_decay_sampled():
+def test_prefill_32k_slow_decay_all_sequences():
     """The 32K-token workload's shape with decay logits centred at -6: the
     state is carried over many chunks before it fades."""
-    spec = replace(ki.PREFILL_32K, name=ki.PREFILL_32K.name + "_slow", z_mean=-6.0)
-    _prefill_sampled(spec, [(0, 3), (2, 30)])
+    _prefill_all(replace(ki.PREFILL_32K, name=ki.PREFILL_32K.name + "_slow", z_mean=-6.0))
 
 
-def test_prefill_1m_sampled():
-    _prefill_sampled(ki.PREFILL_1M, [(0, 5)])
+def test_prefill_1m_all_heads():
+    """The million-token, 8-head workload through kda_chunk_fwd_z (which picks
+    the segment-parallel form for 8 sequences), in one pass, and in 64 explicit
+    segments: every head, every 64-token block."""
+    spec = ki.PREFILL_1M
+    say(f"case {spec.name}: generating inputs")
+    d = ki.prefill_inputs(spec)
+    dd = dev_inputs(d, spec.dtype)
+    runs = {}
+    args = (dd["q"], dd["k"], dd["v"], dd["beta"], dd["z"], dd["A"])
+    say(f"case {spec.name}: GPU run, kda_chunk_fwd_z (the library picks the segment-parallel form)")
+    assert kda.chunk_fwd_workspace_bytes(spec.B, spec.T, spec.H, spec.dk, spec.dv, spec.chunk) > 0
+    runs["kda_chunk_fwd_z"] = kda.chunk_fwd_z(*args, -5.0, spec.chunk, S_in=dd["S0"], o_dtype=torch.bfloat16)
+    say(f"case {spec.name}: GPU run, one pass")
+    runs["one pass"] = kda.chunk_fwd_z_segmented(*args, 1, -5.0, spec.chunk, S_in=dd["S0"], o_dtype=torch.bfloat16)
+    say(f"case {spec.name}: GPU run, 64 segments")
+    runs["64 segments"] = kda.chunk_fwd_z_segmented(*args, 64, -5.0, spec.chunk, S_in=dd["S0"],
+                                                    o_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    del dd
+    _check_runs(spec, d, runs, [(0, 1, h, h + 2) for h in range(0, spec.H, 2)])
+    del runs
+    torch.cuda.empty_cache()
 
 
-def test_decode_256x32_sampled():
+def test_decode_256x32_all_sequences():
     spec = ki.DECODE_256
     say(f"case {spec.name}: generating inputs")
     d = ki.decode_inputs(spec)
@@ -67,15 +103,12 @@ def test_decode_256x32_sampled():
         outs.append(kda.decode_step(dd["q"][s], dd["k"][s], dd["v"][s], dd["z"][s], dd["beta"][s], dd["A"], S,
                                     o_dtype=torch.bfloat16))
     torch.cuda.synchronize()
-    o = torch.stack(outs)
-    n_sel = [0, 77, 255]
-    sub = {k: np.ascontiguousarray(d[k][:, n_sel]) for k in ("q", "k", "v", "z", "beta")}
-    sub["A"] = d["A"]
-    sub["S0"] = np.ascontiguousarray(d["S0"][n_sel])
-    f = f64_inputs(sub, spec.dtype)
-    say("  oracle on sequences", n_sel)
+    o = torch.stack(outs)  # [steps, N, H, dv]
+    say(f"  oracle on all {spec.N} sequences, {spec.steps} steps")
+    f = f64_inputs(d, spec.dtype)
     o_ref, S_ref = oracle.decode(f["q"], f["k"], f["v"], f["z"], f["beta"], f["A"], f["S0"])
-    eo = rel_l2(host64(o[:, n_sel]), o_ref)
-    es = rel_l2(host64(S[n_sel]), S_ref)
-    say(f"  rel-L2 o={eo:.3e} S={es:.3e}")
-    assert eo <= TOL[spec.dtype] and es <= TOL[spec.dtype]
+    tol = TOL[spec.dtype]
+    # outputs as [N, steps, H, dv]: per sequence and head, and per block of 8 steps
+    assert_tokens("decode o", host64(o.transpose(0, 1)), np.ascontiguousarray(o_ref.transpose(1, 0, 2, 3)), tol,
+                  block=8)
+    assert_states("decode S", host64(S), S_ref, tol)

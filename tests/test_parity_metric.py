@@ -1,0 +1,72 @@
+"""The parity metric of the GPU tests, on the CPU: a single wrong 64-token
+block in a million-token sequence, or one wrong sequence among many, fails
+``assert_tokens`` although the whole-tensor relative L2 stays under the
+tolerance."""
+import numpy as np
+import pytest
+
+from tests._gpu import assert_states, assert_tokens, token_report
+
+
+def _noisy(ref, rel, rng):
+    return ref + rel * rng.standard_normal(ref.shape) * np.sqrt(np.mean(ref * ref))
+
+
+def test_one_wrong_block_in_a_million_tokens_fails():
+    rng = np.random.default_rng(0)
+    T = 1 << 20
+    ref = rng.standard_normal((1, T, 1, 8))
+    x = _noisy(ref, 4e-3, rng)
+    assert_tokens("baseline", x, ref, 1e-2)
+    bad = x.copy()
+    t0 = 64 * 12345
+    bad[:, t0:t0 + 64] = 0.0  # one chunk entirely wrong (its outputs lost)
+    r = token_report(bad, ref)
+    assert r["whole"] < 1e-2            # the whole-tensor metric does not see it ...
+    assert r["block_at"] == (0, t0, 0)  # ... the per-block one does, at the right place
+    with pytest.raises(AssertionError, match="block"):
+        assert_tokens("one wrong block", bad, ref, 1e-2)
+
+
+def test_ragged_tail_block_is_checked():
+    rng = np.random.default_rng(1)
+    ref = rng.standard_normal((2, 64 * 5 + 7, 3, 4))
+    x = ref.copy()
+    x[1, -3:, 2] += 1.0  # only the 7-token tail block of one sequence
+    r = token_report(x, ref)
+    assert r["block_at"] == (1, 64 * 5, 2) and r["block_max"] > 0.1
+    with pytest.raises(AssertionError):
+        assert_tokens("tail", x, ref, 1e-2)
+
+
+def test_one_wrong_sequence_fails():
+    rng = np.random.default_rng(2)
+    ref = rng.standard_normal((4, 512, 32, 4))
+    x = _noisy(ref, 1e-3, rng)
+    x[3, :, 17] = _noisy(ref[3, :, 17], 5e-2, rng)
+    r = token_report(x, ref)
+    assert r["whole"] < 1e-2 and r["pair_at"] == (3, 17)
+    with pytest.raises(AssertionError):
+        assert_tokens("one wrong sequence", x, ref, 1e-2)
+
+
+def test_state_per_sequence_and_exact_zero():
+    rng = np.random.default_rng(3)
+    ref = rng.standard_normal((2, 64, 4, 4))
+    x = ref.copy()
+    x[1, 63] *= 1.2
+    with pytest.raises(AssertionError):
+        assert_states("one wrong state", x, ref, 1e-2)
+    z = np.zeros((1, 64, 1, 4))
+    assert token_report(z, z)["block_max"] == 0.0
+    nz = z.copy()
+    nz[0, 5, 0, 1] = 1e-30  # any nonzero output where the reference is exactly zero
+    assert token_report(nz, z)["block_max"] == np.inf
+
+
+def test_non_finite_output_fails():
+    ref = np.ones((1, 64, 1, 4))
+    x = ref.copy()
+    x[0, 3, 0, 0] = np.nan
+    with pytest.raises(AssertionError, match="non-finite"):
+        token_report(x, ref)
