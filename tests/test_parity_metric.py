@@ -28,15 +28,18 @@ def test_one_wrong_block_in_a_million_tokens_fails():
         assert_tokens("one wrong block", bad, ref, 1e-2)
 
 
-def test_ragged_tail_block_is_checked():
+def test_ragged_tail_is_checked_with_the_last_block():
     rng = np.random.default_rng(1)
     ref = rng.standard_normal((2, 64 * 5 + 7, 3, 4))
     x = ref.copy()
-    x[1, -3:, 2] += 1.0  # only the 7-token tail block of one sequence
+    x[1, -3:, 2] += 1.0  # only the last 3 tokens of one sequence
     r = token_report(x, ref)
-    assert r["block_at"] == (1, 64 * 5, 2) and r["block_max"] > 0.1
+    assert r["blocks"] == 2 * 5 * 3
+    assert r["block_at"] == (1, 64 * 4, 2) and r["block_max"] > 0.1  # the last block spans 71 tokens
     with pytest.raises(AssertionError):
         assert_tokens("tail", x, ref, 1e-2)
+    short = rng.standard_normal((1, 40, 1, 4))  # shorter than one block: one block
+    assert token_report(short, short)["blocks"] == 1
 
 
 def test_one_wrong_sequence_fails():
