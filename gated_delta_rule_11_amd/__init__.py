@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
     L.kda_decode_step.restype = I
     L.kda_decode_replay.argtypes = [P, P, P, P, P, I, P, F, P, P, P, I, P, I, I, I, I, I, F, P]
     L.kda_decode_replay.restype = I
+    L.kda_chunk_fwd_z_noalloc.argtypes = [P, P, P, P, P, I, P, F, P, P, I, P, I, I, I, I, I, I, F, P]
+    L.kda_chunk_fwd_z_noalloc.restype = I
     L.kda_chunk_fwd_z_prologue.argtypes = L.kda_chunk_fwd_z.argtypes
     L.kda_chunk_fwd_z_prologue.restype = I
     L.kda_decode_step_prologue.argtypes = L.kda_decode_step.argtypes
@@ -245,6 +247,24 @@ def chunk_fwd_z(q, k, v, beta, z, A, g_min: float = G_MIN, chunk: int = 64, S_in
     _check(lib().kda_chunk_fwd_z(_p(q), _p(k), _p(v), _p(beta), _p(z), _dtype_code(q), _p(A), float(g_min),
                                  _p(S_in), _p(o), _dtype_code(o), _p(S_out), B, T, H, dk, dv, int(chunk),
                                  float(scale), wp, wb, _stream(stream)), "kda_chunk_fwd_z")
+    return o, S_out
+
+
+@_on_tensor_device
+def chunk_fwd_z_noalloc(q, k, v, beta, z, A, g_min: float = G_MIN, chunk: int = 64, S_in=None, o=None, S_out=None,
+                        o_dtype=None, scale: float = 1.0, want_state: bool = True,
+                        stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """``chunk_fwd_z`` whose scratch memory is the library's static device array
+    (kda_chunk_fwd_z_noalloc): no workspace is allocated for the call.  Calls that
+    overlap in time on one device share that array and must not be issued."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    o, S_out = _outs(q, v, o, S_out, o_dtype, want_state)
+    _chunk_shapes("kda_chunk_fwd_z_noalloc", q, k, v, beta, z=z, A=A, S_in=S_in, o=o, S_out=S_out)
+    _dev(q, k, v, beta, z, A, S_in, o, S_out)
+    _check(lib().kda_chunk_fwd_z_noalloc(_p(q), _p(k), _p(v), _p(beta), _p(z), _dtype_code(q), _p(A), float(g_min),
+                                         _p(S_in), _p(o), _dtype_code(o), _p(S_out), B, T, H, dk, dv, int(chunk),
+                                         float(scale), _stream(stream)), "kda_chunk_fwd_z_noalloc")
     return o, S_out
 
 

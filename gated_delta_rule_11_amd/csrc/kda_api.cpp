@@ -7,6 +7,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <initializer_list>
 
 #include "../../include/kda.h"
@@ -109,6 +110,45 @@ kda_status kda_gate(const void* z, kda_dtype z_dtype, const float* A, float g_mi
 
 }  // extern "C"
 
+// ---------------------------------------------------------------------------
+// Allocation-free prefill for callers that cannot allocate device memory.
+//
+// The scratch memory of the segment-parallel form lives in a file-scope device
+// array instead of a caller workspace.  Its size bounds the automatic form's
+// need: that form cuts B*H sequences into at most 256 / (2 B H) segments, so
+// (b, h, segment) units never exceed 128, each needing at most three 128 x 128
+// fp32 matrices (end state, transition, entry state): 128 * 3 * 64 KiB = 24 MiB.
+// The loader gives every device its own copy; host code uses the address
+// hipGetSymbolAddress returns on each device, never the array's name.
+constexpr size_t kScratchBytes = KDA_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes == size_t(128) * 3 * 128 * 128 * 4, "the automatic form's largest need");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// The current device's copy of `scratch` (looked up once per device), or nullptr.
+void* scratch_on_current_device(hipError_t* err) {
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (*err != hipSuccess || !p) {
+    if (*err == hipSuccess) *err = hipErrorInvalidSymbol;
+    return nullptr;
+  }
+  g_scratch[dev].store(p, std::memory_order_release);
+  return p;
+}
+}  // namespace
+
 namespace {
 
 // Segments of a segment-parallel prefill: `seg_chunks` chunks each (more segments
@@ -165,7 +205,8 @@ bool chunk_args_ok(int B, int T, int H, int dk, int dv, int chunk) {
 kda_status chunk_common(const void* q, const void* k, const void* v, const void* beta, const void* z,
                         kda_dtype in_dtype, const float* G, const float* A, float g_min, const float* S_in, void* o,
                         kda_dtype o_dtype, float* S_out, int B, int T, int H, int dk, int dv, int chunk, float scale,
-                        bool from_z, int segments, void* ws, size_t ws_bytes, bool prologue, void* stream) {
+                        bool from_z, int segments, void* ws, size_t ws_bytes, bool prologue, void* stream,
+                        bool static_scratch = false) {
   if (!dtype_ok(in_dtype) || !dtype_ok(o_dtype)) return KDA_ERR_DTYPE;
   if (!sizes_ok(B, T, H, dk, dv)) return KDA_ERR_SHAPE;
   if (!dim_ok(dk) || !dim_ok(dv) || !(chunk == 16 || chunk == 64)) return KDA_ERR_UNSUPPORTED;
@@ -185,7 +226,8 @@ kda_status chunk_common(const void* q, const void* k, const void* v, const void*
     if (!q || !k || !v || !beta || !o) return KDA_ERR_NULL;
     if (from_z ? (!z || !A) : !G) return KDA_ERR_NULL;
   }
-  if (need > 0 && !ws) return KDA_ERR_NULL;
+  if (static_scratch) ws = nullptr;  // the library's own array, looked up after validation
+  if (need > 0 && !ws && !static_scratch) return KDA_ERR_NULL;
   if (!all_aligned({q, k, v, z, G, A, o, S_in, S_out, need > 0 ? ws : nullptr}, beta, esize(in_dtype)))
     return KDA_ERR_ALIGN;
   if (ws_bytes < size_t(need)) return KDA_ERR_WORKSPACE;
@@ -203,6 +245,11 @@ kda_status chunk_common(const void* q, const void* k, const void* v, const void*
   if (overlap(rSo, rSi) && S_out != S_in) return KDA_ERR_ALIAS;
   for (Range in : {rq, rk, rv, rb, rz, rG, rA, ro, rSi, rSo})
     if (overlap(rw, in)) return KDA_ERR_ALIAS;
+  if (static_scratch && need > 0) {
+    hipError_t e = hipSuccess;
+    ws = scratch_on_current_device(&e);
+    if (!ws) return KDA_ERR_HIP;
+  }
 
   kda::ChunkArgs a{};
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.G = from_z ? nullptr : G; a.z = from_z ? z : nullptr;
@@ -322,8 +369,8 @@ kda_status kda_chunk_bwd_z(const void* q, const void* k, const void* v, const vo
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t nblk = (int64_t(T) + 63) / 64;
   float* ckpt = static_cast<float*>(workspace);
-  float* scratch = ckpt + bh * nblk * dk * dv;
-  float* dA_part = scratch + bh * 3 * dk * dv;
+  float* sub_states = ckpt + bh * nblk * dk * dv;
+  float* dA_part = sub_states + bh * 3 * dk * dv;
   const int nsp = kda::chunk_bwd_slices(B, H, dv);
   float* mcache = dA_part + bh * nsp * dk;
   float* parts = mcache + bh * nsp * kda::kBwdMCacheFloats;
@@ -335,7 +382,7 @@ kda_status kda_chunk_bwd_z(const void* q, const void* k, const void* v, const vo
   f.in_bf16 = in_dtype == KDA_BF16; f.out_bf16 = false; f.from_z = true; f.o_skip = true; f.S_ckpt = ckpt;
   hipError_t e = kda::chunk_mfma_supports(f) ? kda::launch_chunk_mfma(f, st) : kda::launch_chunk_generic(f, st);
   if (e != hipSuccess) return from_hip(e);
-  kda::BwdArgs bwa{q, k, v, beta, z, A, g_min, d_o, dS_out, ckpt, scratch, dA_part, dq, dk_, dv_, dbeta, dz, dA,
+  kda::BwdArgs bwa{q, k, v, beta, z, A, g_min, d_o, dS_out, ckpt, sub_states, dA_part, dq, dk_, dv_, dbeta, dz, dA,
                    dS_in, B, T, H, dk, dv, scale, in_dtype == KDA_BF16, do_dtype == KDA_BF16};
   bwa.mcache = mcache;
   if (nsp == 2) {
@@ -426,6 +473,16 @@ kda_status kda_decode_replay(const void* q, const void* k, const void* v, const 
   kda::ReplayArgs a{q,        k,          v,     z, beta, A, g_min, S_snapshot, o, S_commit, accepted, n_draft, N, H,
                     dk,       dv,         scale, in_dtype == KDA_BF16, o_dtype == KDA_BF16};
   return from_hip(kda::launch_replay(a, static_cast<hipStream_t>(stream)));
+}
+
+kda_status kda_chunk_fwd_z_noalloc(const void* q, const void* k, const void* v, const void* beta, const void* z,
+                                   kda_dtype in_dtype, const float* A, float g_min, const float* S_in, void* o,
+                                   kda_dtype o_dtype, float* S_out, int B, int T, int H, int dk, int dv, int chunk,
+                                   float scale, void* stream) {
+  // a need beyond the static array is reported as a workspace error (chunk_common
+  // compares it with the array's size, after the argument checks)
+  return chunk_common(q, k, v, beta, z, in_dtype, nullptr, A, g_min, S_in, o, o_dtype, S_out, B, T, H, dk, dv, chunk,
+                      scale, true, 0, nullptr, kScratchBytes, false, stream, true);
 }
 
 }  // extern "C"

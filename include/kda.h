@@ -172,6 +172,29 @@ kda_status kda_chunk_fwd_z(const void* q, const void* k, const void* v,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kda_chunk_fwd_z_noalloc -- kda_chunk_fwd_z for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, result and validation as
+ * kda_chunk_fwd_z, without the workspace: where the call needs scratch memory
+ * (kda_chunk_fwd_workspace_bytes > 0) it uses a static array of the library's
+ * on the current device, of KDA_NOALLOC_SCRATCH_BYTES (24 MiB), which each
+ * device holds until the process ends.  A need beyond that returns
+ * KDA_ERR_WORKSPACE (the automatic launch form never needs more: it makes at
+ * most 128 (b, h, segment) units of three 128 x 128 fp32 matrices each).  The
+ * call allocates nothing.  Every call on one device
+ * shares that device's array, whose contents the call overwrites before
+ * reading: calls that overlap in time on one device (different streams, or
+ * threads) race and must not be issued; calls in order on one stream are safe.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)24 << 20)
+kda_status kda_chunk_fwd_z_noalloc(const void* q, const void* k, const void* v,
+                                   const void* beta, const void* z, kda_dtype in_dtype,
+                                   const float* A, float g_min, const float* S_in,
+                                   void* o, kda_dtype o_dtype, float* S_out, int B,
+                                   int T, int H, int dk, int dv, int chunk, float scale,
+                                   void* stream);
+
+/*
  * kda_decode_step -- one token per sequence, state updated IN PLACE.
  *
  * For n < N, h < H: gate from z and A, S[n,h] <- (I - beta k k^T)

@@ -364,3 +364,23 @@ def test_chunk_workspace_query_and_validation(L):
     # where none is needed, a NULL workspace of zero bytes is valid (the call then
     # gets past validation; without a GPU it stops at its first HIP call)
     assert chunk_z(L, ws=None, wsb=0, B=4, T=64, H=32) == ERR_HIP
+
+
+def noalloc(L, q=P(0), k=P(1), v=P(2), beta=P(3), z=P(4), it=BF16, A=P(8), gmin=-5.0, S_in=P(5), o=P(6), ot=BF16,
+            S_out=P(7), B=1, T=4096, H=8, dk=128, dv=128, c=64, scale=1.0):
+    return L.kda_chunk_fwd_z_noalloc(q, k, v, beta, z, it, A, gmin, S_in, o, ot, S_out, B, T, H, dk, dv, c, scale, N)
+
+
+def test_noalloc_validation(L):
+    """The allocation-free prefill validates as kda_chunk_fwd_z, before it looks up
+    its static scratch array (so every error below comes without a HIP call)."""
+    assert L.kda_chunk_fwd_workspace_bytes(1, 4096, 8, 128, 128, 64) > 0  # these sizes use the scratch
+    assert noalloc(L, it=9) == ERR_DTYPE
+    assert noalloc(L, T=-1) == ERR_SHAPE
+    assert noalloc(L, dk=48) == ERR_UNSUPPORTED
+    assert noalloc(L, gmin=-5.5) == ERR_UNSUPPORTED
+    for name in ("q", "k", "v", "beta", "z", "A", "o"):
+        assert noalloc(L, **{name: None}) == ERR_NULL, name
+    assert noalloc(L, o=P(4)) == ERR_ALIAS
+    assert noalloc(L, q=ctypes.c_void_p(0x10000004)) == ERR_ALIGN
+    assert noalloc(L, B=0) == OK
