@@ -77,6 +77,7 @@ constexpr int kRsrcFlags = 0x00020000;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -140,36 +141,43 @@ __device__ __forceinline__ uint32_t bload32(__amdgpu_buffer_rsrc_t r, int voff, 
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
 
-// Raw inputs of one 16-token tile, held by its gate wavefront from the load to
-// the gate (lane -> channels 2 lane, 2 lane + 1; value column lane).
+// Raw inputs of one 16-token tile, held by its gate wavefront from the load to the
+// gate.  Lane layout of the gate wavefronts: lane l takes tokens 8 (l >> 5) .. +7 of
+// the tile (its half) and key channels 4 (l & 31) .. +3, so a token row of one
+// tensor is one 8-byte load per lane over 32 lanes (two token rows per
+// instruction); value columns 2 (l & 31), +1 of the slice, 4 bytes per token.
 template <bool FROM_Z> struct RawTile {
-  uint32_t k[16], q[16];       // bf16 pairs
-  uint32_t g0[16];             // z pairs (bf16), or chunk-local G of channel 2 lane (fp32)
-  uint32_t g1[FROM_Z ? 1 : 16];  // chunk-local G of channel 2 lane + 1 (fp32)
-  uint32_t gb[2];              // G before the tile (G path)
-  uint32_t v[16];              // value column, bf16 in the low half
-  uint32_t beta;               // beta of token ln of the tile (lanes 0..15)
+  u32x2 k[8], q[8];              // bf16 quads
+  u32x2 z[FROM_Z ? 8 : 1];       // decay logits (bf16 quads)
+  f32x4 g[FROM_Z ? 1 : 8];       // chunk-local G of the four channels
+  f32x4 gb;                      // G before the tile (G path)
+  uint32_t v[8];                 // two value columns, bf16 pair
+  uint32_t beta;                 // beta of tile token l (lanes 0..15)
 };
 
 // Raw inputs of one wavefront's 16-token tile, token offsets clamped to the chunk,
 // in four parts (keys; queries; gate inputs; values and beta) so that the loads
-// of a tile can go out in different phases.
+// of a tile can go out in different phases.  The token offset is part of the
+// per-lane offset (the two halves of the wavefront read different tokens), which
+// the buffer resource's range check covers.
 template <int DVS, bool FROM_Z, int PART, bool SEG>
 __device__ __forceinline__ void load_part(RawTile<FROM_Z>& R, const ChunkArgs& a, int b, int h, int t0, int i,
                                           int ln, int j0) {
   using namespace mf;
-  static_assert(DVS <= 64, "one value column per lane");
+  static_assert(DVS <= 64, "two value columns per lane of a half-wavefront");
   const int T = a.T, H = a.H;
   const int n = min(C, T - t0);
   const int64_t row0 = (static_cast<int64_t>(b) * T + t0) * H + h;
   const int64_t span = static_cast<int64_t>(n - 1) * H + 1;
   const int rowb = H * DK * 2;
-  const int c0 = 2 * ln;
+  const int tb = 16 * i + 8 * (ln >> 5);  // first token of this lane's half of the tile
+  const int cq = ln & 31;
   if constexpr (PART == 0 || PART == 1) {
     const auto r = rsrc(static_cast<const uint16_t*>(PART == 0 ? a.k : a.q) + row0 * DK, span * DK * 2);
 #pragma unroll
-    for (int tt = 0; tt < 16; ++tt) {
-      const uint32_t x = bload32(r, c0 * 2, min(16 * i + tt, n - 1) * rowb);
+    for (int tt = 0; tt < 8; ++tt) {
+      const u32x2 x = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, min(tb + tt, n - 1) * rowb + 8 * cq, 0, 0));
       if constexpr (PART == 0)
         R.k[tt] = x;
       else
@@ -179,29 +187,26 @@ __device__ __forceinline__ void load_part(RawTile<FROM_Z>& R, const ChunkArgs& a
     if constexpr (FROM_Z) {
       const auto rz = rsrc(static_cast<const uint16_t*>(a.z) + row0 * DK, span * DK * 2);
 #pragma unroll
-      for (int tt = 0; tt < 16; ++tt) R.g0[tt] = bload32(rz, c0 * 2, min(16 * i + tt, n - 1) * rowb);
+      for (int tt = 0; tt < 8; ++tt)
+        R.z[tt] = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(rz, min(tb + tt, n - 1) * rowb + 8 * cq, 0, 0));
     } else {
       const auto rg = rsrc(a.G + row0 * DK, span * DK * 4);
 #pragma unroll
-      for (int tt = 0; tt < 16; ++tt) {
-        const u32x2 g = __builtin_bit_cast(
-            u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, c0 * 4, min(16 * i + tt, n - 1) * rowb * 2, 0));
-        R.g0[tt] = g[0];
-        R.g1[tt] = g[1];
-      }
-      const u32x2 gb = __builtin_bit_cast(
-          u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, c0 * 4, min(max(16 * i - 1, 0), n - 1) * rowb * 2, 0));
-      R.gb[0] = gb[0];
-      R.gb[1] = gb[1];
+      for (int tt = 0; tt < 8; ++tt)
+        R.g[tt] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, min(tb + tt, n - 1) * rowb * 2 + 16 * cq, 0, 0));
+      R.gb = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, min(max(16 * i - 1, 0), n - 1) * rowb * 2 + 16 * cq, 0, 0));
     }
   } else {
     const auto rv = rsrc(static_cast<const uint16_t*>(a.v) + row0 * DK + j0, span * DK * 2);
     const auto rb = rsrc(static_cast<const uint16_t*>(a.beta) + row0, span * 2);
-    if (ln < DVS) {
+    if (cq < DVS / 2) {
 #pragma unroll
-      for (int tt = 0; tt < 16; ++tt)
+      for (int tt = 0; tt < 8; ++tt)
         R.v[tt] = (SEG && a.v_zero) ? 0u
-                                    : __builtin_amdgcn_raw_buffer_load_b16(rv, ln * 2, min(16 * i + tt, n - 1) * rowb, 0);
+                                    : __builtin_amdgcn_raw_buffer_load_b32(rv, min(tb + tt, n - 1) * rowb + 4 * cq, 0, 0);
     }
     if (ln < 16) R.beta = __builtin_amdgcn_raw_buffer_load_b16(rb, min(16 * i + ln, n - 1) * H * 2, 0, 0);
   }
@@ -216,32 +221,26 @@ __device__ __forceinline__ void load_tile(RawTile<FROM_Z>& R, const ChunkArgs& a
   load_part<DVS, FROM_Z, 3, SEG>(R, a, b, h, t0, i, ln, j0);
 }
 
-// Per-token sums over the 64 lanes of a wavefront, for the fused prologue's
-// norms.  v[t] is this lane's part of token t's sum (t < 16); the result in
-// lane l is the total of token (l >> 2) & 15.  Each step pairs every lane with
-// one partner, keeps half of the tokens it still carries and adds the
-// partner's part of them: lanes l and l + 32 (swap of the wavefront halves),
-// l and l + 16 (swap of the odd and even 16-lane rows), l and 15 - l within a
-// row, l and 7 - l within an 8-lane half row; the last two steps sum the quad.
-// The partners' lane offsets, {32, 16, 15, 7, 2, 1}, span all 64 lanes once.
-__device__ __forceinline__ float wave_token_sums16(const float (&v)[16], int ln) {
-  float w[8];  // token m + 8 (lane bit 5)
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[m]), __float_as_uint(v[m + 8]), false, false);
-    w[m] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
-  }
-  float x[4];  // token m + 4 (bit 4) + 8 (bit 5)
+// Per-token sums over the 32 lanes of a half-wavefront, for the fused prologue's
+// norms.  v[t] is this lane's part of token t's sum (t < 8, tokens of its half);
+// the result in lane l is the total of token (l >> 2) & 7 of its half.  Each step
+// pairs every lane with one partner of the same half, keeps half of the tokens it
+// still carries and adds the partner's part of them: lanes l and l ^ 16 (swap of
+// the odd and even 16-lane rows), l and 15 - l within a row, l and 7 - l within an
+// 8-lane half row; the last two steps sum the quad.  The partners' lane offsets,
+// {16, 15, 7, 2, 1}, span the 32 lanes of the half once.
+__device__ __forceinline__ float half_token_sums8(const float (&v)[8], int ln) {
+  float w[4];  // token m + 4 (lane bit 4)
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(w[m]), __float_as_uint(w[m + 4]), false, false);
-    x[m] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[m]), __float_as_uint(v[m + 4]), false, false);
+    w[m] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
   }
   const bool b3 = (ln & 8) != 0, b2 = (ln & 4) != 0;
-  float y[2];  // token m + 2 (bit 3) + 4 (bit 4) + 8 (bit 5)
+  float y[2];  // token m + 2 (bit 3) + 4 (bit 4)
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
-    const float keep = b3 ? x[m + 2] : x[m], send = b3 ? x[m] : x[m + 2];
+    const float keep = b3 ? w[m + 2] : w[m], send = b3 ? w[m] : w[m + 2];
     y[m] = keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), 0x140, 0xf, 0xf, false));
   }
   const float keep = b2 ? y[1] : y[0], send = b2 ? y[0] : y[1];
@@ -249,6 +248,12 @@ __device__ __forceinline__ float wave_token_sums16(const float (&v)[16], int ln)
   z += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(z), 0x4E, 0xf, 0xf, false));  // quad [2,3,0,1]
   z += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(z), 0xB1, 0xf, 0xf, false));  // quad [1,0,3,2]
   return z;
+}
+
+// The value of x in lane l ^ 32 (the other half of the wavefront).
+__device__ __forceinline__ float other_half(float x, int ln) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((ln & 32) ? s[0] : s[1]);
 }
 
 // Off-diagonal tile pairs (i, j < i) of the L / P products, per gate wavefront.
@@ -339,7 +344,7 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
     ln = l;
     g4 = l >> 4;   // MFMA lane group
     r16 = l & 15;  // MFMA lane row/column
-    c0 = 2 * l;    // gate layout: channels c0, c0+1
+    c0 = 4 * (l & 31);  // gate layout: channels c0 .. c0+3 (tokens of half l >> 5)
   };
   relane();
   // this workgroup's chunks: segment sg of the sequence (all of it for one segment)
@@ -583,153 +588,196 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
     // The gate wavefronts are the longer side of every phase but A1: there they
     // yield instruction issue to the state-chain wavefront sharing their SIMD
     // (its U and (q Gamma) S products), elsewhere they take it.
+    //
+    // Lane layout: lane l holds tokens 8 gh .. 8 gh + 7 of its tile (gh = l >> 5, the
+    // half) for channels c0 .. c0 + 3; products along the tile's tokens are formed
+    // within each half and joined across the halves (lanes l and l ^ 32).
     __builtin_amdgcn_s_setprio(2);
     const int i = wv - 4;  // this wavefront's 16-token tile
-    float ea0 = 0.f, ea1 = 0.f;
+    float ea[4] = {0.f, 0.f, 0.f, 0.f};
     const float gmin_l2e = a.g_min * kLog2e;
     if constexpr (FROM_Z) {
-      ea0 = __expf(a.A[h * DK + c0]) * kLog2e;
-      ea1 = __expf(a.A[h * DK + c0 + 1]) * kLog2e;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ea[j] = __expf(a.A[h * DK + c0 + j]) * kLog2e;
     }
     RawTile<FROM_Z> R;
-    uint32_t kr[16], qr[16], ks[16];  // A1 -> A2: bf16 pairs of k r, q r, k sf
-    float D0 = 1.f, D1 = 1.f;         // A1 -> A2: decay over the tile
-    uint32_t kh[16];                  // A2 -> 2: (k Gamma_C / Gamma)^T pairs
-    float gc0 = 1.f, gc1 = 1.f;       // A2 -> 2: Gamma_C (written by tile 0's wavefront)
-    float rho = 1.f;                  // A1 -> 2 (prologue): query normaliser of token (ln >> 2) & 15
+    u32x2 kr[8], qr[8], ks[8];  // A1 -> A2: bf16 quads of k r, q r, k sf
+    float Dt[4] = {1.f, 1.f, 1.f, 1.f};  // A1 -> A2: decay over the tile
+    u32x4 kh[4];                         // A2 -> 2: (k Gamma_C / Gamma)^T, 8 tokens per channel
+    float gc[4] = {1.f, 1.f, 1.f, 1.f};  // A2 -> 2: Gamma_C (written by tile 0's wavefront)
+    float rho = 1.f;                     // A1 -> 2 (prologue): query normaliser of token (ln >> 2) & 7 of the half
+    auto q4 = [](u32x2 x, int j) __attribute__((always_inline)) {  // channel j of a bf16 quad
+      return (j & 1) ? bfhi(x[j >> 1]) : bflo(x[j >> 1]);
+    };
+    auto pack4 = [](float x0, float x1, float x2, float x3) __attribute__((always_inline)) {
+      return u32x2{pack2(x0, x1), pack2(x2, x3)};
+    };
 
     // gate of chunk tc: within-tile decay products, tile decays -> sD; q r -> sQR, v^T, beta
     // FULL: every token of the chunk is valid (all chunks but a ragged last one)
     auto gate_a1 = [&](int tc, auto full_c) __attribute__((always_inline)) {
       constexpr bool FULL = decltype(full_c)::value;
       const int n = FULL ? C : min(C, T - tc);
+      const int gh = ln >> 5;
+      const int tb = 16 * i + 8 * gh;  // chunk-local token of this lane's first
       if (ln < 16) {
         const int t = 16 * i + ln;
         const float bl = bf16_to_f32(static_cast<uint16_t>(R.beta));
         sBeta[t] = (FULL || t < n) ? (NORM ? sigmoid_fast(bl) : bl) : 0.f;
       }
-      if (ln < DVS) {  // v^T, value column ln of the slice, tokens of this tile
-        uint32_t w[8];
+      if ((ln & 31) < DVS / 2) {  // v^T: value columns 2 (l & 31), +1 of the slice, this half's tokens
+        uint32_t lo[4], hi[4];
 #pragma unroll
-        for (int tp = 0; tp < 8; ++tp) {
-          const int t = 16 * i + 2 * tp;
-          const uint32_t lo = (FULL || t < n) ? (R.v[2 * tp] & 0xffffu) : 0u;
-          const uint32_t hi = (FULL || t + 1 < n) ? (R.v[2 * tp + 1] & 0xffffu) : 0u;
-          w[tp] = lo | (hi << 16);
+        for (int tp = 0; tp < 4; ++tp) {
+          const int t = tb + 2 * tp;
+          const uint32_t v0 = (FULL || t < n) ? R.v[2 * tp] : 0u;
+          const uint32_t v1 = (FULL || t + 1 < n) ? R.v[2 * tp + 1] : 0u;
+          lo[tp] = (v0 & 0xffffu) | (v1 << 16);
+          hi[tp] = (v0 >> 16) | (v1 & 0xffff0000u);
         }
-        u32x4* dv = reinterpret_cast<u32x4*>(&sVT[ln * TS + 16 * i]);
-        dv[0] = u32x4{w[0], w[1], w[2], w[3]};
-        dv[1] = u32x4{w[4], w[5], w[6], w[7]};
+        const int col = 2 * (ln & 31);
+        *reinterpret_cast<u32x4*>(&sVT[col * TS + tb]) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+        *reinterpret_cast<u32x4*>(&sVT[(col + 1) * TS + tb]) = u32x4{hi[0], hi[1], hi[2], hi[3]};
       }
-      // prologue: 1 / sqrt(|k_t|^2 + eps) of the tile's tokens (uniform values), and the
-      // query normalisers, kept for the state chain
-      float nk[16];
+      // prologue: 1 / sqrt(|k_t|^2 + eps) of this half's tokens, and the query
+      // normalisers, kept for the state chain
+      float nk[8];
 #pragma unroll
-      for (int tt = 0; tt < 16; ++tt) nk[tt] = 1.f;
+      for (int tt = 0; tt < 8; ++tt) nk[tt] = 1.f;
       if constexpr (NORM) {
-        float pk[16], pq[16];
+        float pk[8], pq[8];
+        // sums of squares of this lane's four channels: the quad is bit-cast whole and
+        // split with vector shuffles (no bit-cast of a single vector element)
+        auto sumsq = [](u32x2 x) __attribute__((always_inline)) {
+          const bf16x4 b = __builtin_bit_cast(bf16x4, x);
+          const bf16x2 lo = __builtin_shufflevector(b, b, 0, 1), hi = __builtin_shufflevector(b, b, 2, 3);
+          return __builtin_amdgcn_fdot2_f32_bf16(hi, hi, __builtin_amdgcn_fdot2_f32_bf16(lo, lo, 0.f, false), false);
+        };
 #pragma unroll
-        for (int tt = 0; tt < 16; ++tt) {
-          pk[tt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, R.k[tt]),
-                                                   __builtin_bit_cast(bf16x2, R.k[tt]), 0.f, false);
-          pq[tt] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, R.q[tt]),
-                                                   __builtin_bit_cast(bf16x2, R.q[tt]), 0.f, false);
+        for (int tt = 0; tt < 8; ++tt) {
+          pk[tt] = sumsq(R.k[tt]);
+          pq[tt] = sumsq(R.q[tt]);
         }
-        const float rkl = rsqrt_fast(wave_token_sums16(pk, ln) + kL2Eps);
-        rho = rsqrt_fast(wave_token_sums16(pq, ln) + kL2Eps);
+        const float rkl = rsqrt_fast(half_token_sums8(pk, ln) + kL2Eps);
+        rho = rsqrt_fast(half_token_sums8(pq, ln) + kL2Eps);
 #pragma unroll
-        for (int tt = 0; tt < 16; ++tt) nk[tt] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rkl), 4 * tt));
+        for (int tt = 0; tt < 8; ++tt) {
+          const float n0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rkl), 4 * tt));
+          const float n1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rkl), 32 + 4 * tt));
+          nk[tt] = gh ? n1 : n0;
+        }
       }
+      // r (prefix products up to and including t) and sf (products after t), within
+      // the tile: E / F carry the other half's product into the first / second half
+      float rr[8][4], sfv[8][4];
       if constexpr (FROM_Z) {
-        float al0[16], al1[16];
+        float al[8][4];
 #pragma unroll
-        for (int tt = 0; tt < 16; ++tt) {
-          const bool valid = FULL || 16 * i + tt < n;
-          al0[tt] = valid ? fast_exp2(gate_log2(bflo(R.g0[tt]), ea0, gmin_l2e)) : 1.f;
-          al1[tt] = valid ? fast_exp2(gate_log2(bfhi(R.g0[tt]), ea1, gmin_l2e)) : 1.f;
-        }
-        float p0 = 1.f, p1 = 1.f;  // prefix products r_t
+        for (int tt = 0; tt < 8; ++tt) {
+          const bool valid = FULL || tb + tt < n;
 #pragma unroll
-        for (int tt = 0; tt < 16; ++tt) {
-          const bool valid = FULL || 16 * i + tt < n;
-          p0 *= al0[tt];
-          p1 *= al1[tt];
-          const uint32_t k = valid ? R.k[tt] : 0u, q = valid ? R.q[tt] : 0u;
-          kr[tt] = pack2(bflo(k) * (p0 * nk[tt]), bfhi(k) * (p1 * nk[tt]));
-          qr[tt] = pack2(bflo(q) * p0, bfhi(q) * p1);
+          for (int j = 0; j < 4; ++j)
+            al[tt][j] = valid ? fast_exp2(gate_log2(q4(R.z[tt], j), ea[j], gmin_l2e)) : 1.f;
         }
-        float s0 = 1.f, s1 = 1.f;  // exclusive suffix products sf_t
 #pragma unroll
-        for (int tt = 15; tt >= 0; --tt) {
-          const uint32_t k = (FULL || 16 * i + tt < n) ? R.k[tt] : 0u;
-          ks[tt] = pack2(bflo(k) * (s0 * nk[tt]), bfhi(k) * (s1 * nk[tt]));
-          s0 *= al0[tt];
-          s1 *= al1[tt];
-        }
-        D0 = s0;
-        D1 = s1;
-      } else {
-        // chunk-local sums G (natural log, fp32); log2 within this tile
-        float base0 = 0.f, base1 = 0.f;
-        if (i > 0 && (FULL || 16 * i < n)) {
-          base0 = __uint_as_float(R.gb[0]) * kLog2e;
-          base1 = __uint_as_float(R.gb[1]) * kLog2e;
-        }
-        float last0 = base0, last1 = base1;
+        for (int j = 0; j < 4; ++j) {
+          float P = 1.f;  // this half's product
 #pragma unroll
-        for (int tt = 0; tt < 16; ++tt) {
-          if (FULL || 16 * i + tt < n) {
-            last0 = __uint_as_float(R.g0[tt]) * kLog2e;
-            last1 = __uint_as_float(R.g1[tt]) * kLog2e;
+          for (int tt = 0; tt < 8; ++tt) P *= al[tt][j];
+          const float Po = other_half(P, ln);
+          Dt[j] = gh ? Po * P : P * Po;  // first half's product times the second's, in both halves
+          float p = gh ? Po : 1.f;
+#pragma unroll
+          for (int tt = 0; tt < 8; ++tt) {
+            p *= al[tt][j];
+            rr[tt][j] = p;
+          }
+          float sf = gh ? 1.f : Po;
+#pragma unroll
+          for (int tt = 7; tt >= 0; --tt) {
+            sfv[tt][j] = sf;
+            sf *= al[tt][j];
           }
         }
+      } else {
+        // chunk-local sums G (natural log, fp32); log2 within this tile: r = 2^(G - base),
+        // sf = 2^(last - G), D = 2^(last - base), with base = G before the tile and last = G
+        // at the tile's last valid token
+        const bool any = FULL || 16 * i < n;
+        const bool mine = FULL || tb < n;  // this half holds a valid token
+        const int tl = FULL ? 7 : min(7, max(0, n - 1 - tb));
+        float base[4], mylast[4], last[4];
 #pragma unroll
-        for (int tt = 0; tt < 16; ++tt) {
-          const bool valid = FULL || 16 * i + tt < n;
-          const float G0 = valid ? __uint_as_float(R.g0[tt]) * kLog2e : last0;
-          const float G1 = valid ? __uint_as_float(R.g1[tt]) * kLog2e : last1;
-          const float r0 = fast_exp2(G0 - base0), r1 = fast_exp2(G1 - base1);
-          const uint32_t k = valid ? R.k[tt] : 0u, q = valid ? R.q[tt] : 0u;
-          kr[tt] = pack2(bflo(k) * r0, bfhi(k) * r1);
-          qr[tt] = pack2(bflo(q) * r0, bfhi(q) * r1);
-          ks[tt] = pack2(bflo(k) * fast_exp2(last0 - G0), bfhi(k) * fast_exp2(last1 - G1));
+        for (int j = 0; j < 4; ++j) {
+          base[j] = (i > 0 && any) ? R.gb[j] * kLog2e : 0.f;
+          float g_tl = 0.f;
+#pragma unroll
+          for (int tt = 0; tt < 8; ++tt)
+            if (tt == tl) g_tl = R.g[tt][j] * kLog2e;
+          mylast[j] = mine ? g_tl : base[j];
+          const float other = other_half(mylast[j], ln);
+          // the second half's last valid token is the tile's, when that half has one
+          const bool second_valid = FULL || 16 * i + 8 < n;
+          last[j] = gh ? (second_valid ? mylast[j] : other) : (second_valid ? other : mylast[j]);
+          Dt[j] = fast_exp2(last[j] - base[j]);
         }
-        D0 = fast_exp2(last0 - base0);
-        D1 = fast_exp2(last1 - base1);
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) {
+          const bool valid = FULL || tb + tt < n;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float G = valid ? R.g[tt][j] * kLog2e : last[j];
+            rr[tt][j] = fast_exp2(G - base[j]);
+            sfv[tt][j] = fast_exp2(last[j] - G);
+          }
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        const bool valid = FULL || tb + tt < n;
+        const u32x2 k = valid ? R.k[tt] : u32x2{0u, 0u};
+        const u32x2 q = valid ? R.q[tt] : u32x2{0u, 0u};
+        kr[tt] = pack4(q4(k, 0) * (rr[tt][0] * nk[tt]), q4(k, 1) * (rr[tt][1] * nk[tt]),
+                       q4(k, 2) * (rr[tt][2] * nk[tt]), q4(k, 3) * (rr[tt][3] * nk[tt]));
+        qr[tt] = pack4(q4(q, 0) * rr[tt][0], q4(q, 1) * rr[tt][1], q4(q, 2) * rr[tt][2], q4(q, 3) * rr[tt][3]);
+        ks[tt] = pack4(q4(k, 0) * (sfv[tt][0] * nk[tt]), q4(k, 1) * (sfv[tt][1] * nk[tt]),
+                       q4(k, 2) * (sfv[tt][2] * nk[tt]), q4(k, 3) * (sfv[tt][3] * nk[tt]));
       }
       // k sf of this tile is the anchored-key slot (i + 1, i) as it stands (no tile
       // in between); the scaled slots read it back in the next phase
       if (i < 3) {
 #pragma unroll
-        for (int tt = 0; tt < 16; ++tt) *reinterpret_cast<uint32_t*>(&sKA[(slot(i + 1, i) * 16 + tt) * RS + c0]) = ks[tt];
+        for (int tt = 0; tt < 8; ++tt)
+          *reinterpret_cast<u32x2*>(&sKA[(slot(i + 1, i) * 16 + 8 * gh + tt) * RS + c0]) = ks[tt];
       }
-      sD[i * DK + c0] = D0;
-      sD[i * DK + c0 + 1] = D1;
+      if (gh == 0) *reinterpret_cast<f32x4*>(&sD[i * DK + c0]) = f32x4{Dt[0], Dt[1], Dt[2], Dt[3]};
     };
 
     // k r, anchored keys, eB (sD complete and the k r storage free)
     auto gate_a2 = [&]() __attribute__((always_inline)) {
-      float d0[4], d1[4];
+      const int gh = ln >> 5;
+      f32x4 dd[4];
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        d0[ii] = sD[ii * DK + c0];
-        d1[ii] = sD[ii * DK + c0 + 1];
-      }
-      float eB0 = 1.f, eB1 = 1.f, af0 = 1.f, af1 = 1.f;
+      for (int ii = 0; ii < 4; ++ii) dd[ii] = *reinterpret_cast<const f32x4*>(&sD[ii * DK + c0]);
+      float eB[4] = {1.f, 1.f, 1.f, 1.f}, af[4] = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        if (ii < i) { eB0 *= d0[ii]; eB1 *= d1[ii]; }
-        if (ii > i) { af0 *= d0[ii]; af1 *= d1[ii]; }
-      }
-      sEB[i * DK + c0] = eB0;
-      sEB[i * DK + c0 + 1] = eB1;
+      for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (ii < i) eB[j] *= dd[ii][j];
+          if (ii > i) af[j] *= dd[ii][j];
+        }
+      if (gh == 0) *reinterpret_cast<f32x4*>(&sEB[i * DK + c0]) = f32x4{eB[0], eB[1], eB[2], eB[3]};
       // anchored keys of the diagonal pair, (k_s sf_s) / D_i
       {
-        const float f0 = fast_rcp(D0), f1 = fast_rcp(D1);
-        uint16_t* dst = sKA + slot(i, i) * 16 * RS + c0;
+        float f[4];
 #pragma unroll
-        for (int tt = 0; tt < 16; ++tt)
-          *reinterpret_cast<uint32_t*>(dst + tt * RS) = pack2(bflo(ks[tt]) * f0, bfhi(ks[tt]) * f1);
+        for (int j = 0; j < 4; ++j) f[j] = fast_rcp(Dt[j]);
+        uint16_t* dst = sKA + (slot(i, i) * 16 + 8 * gh) * RS + c0;
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt)
+          *reinterpret_cast<u32x2*>(dst + tt * RS) =
+              pack4(q4(ks[tt], 0) * f[0], q4(ks[tt], 1) * f[1], q4(ks[tt], 2) * f[2], q4(ks[tt], 3) * f[3]);
       }
       // anchored keys two or three tiles apart, k_s e^(B_m - G_s) = (k_s sf_s) prod_{j < ii < m} D_ii,
       // one slot per wavefront of tiles 1..3: (3,1), (2,0), (3,0); k sf of tile j is read
@@ -737,53 +785,53 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
       if (i > 0) {
         const int m = i == 2 ? 2 : 3;
         const int j = i == 1 ? 1 : 0;
-        float fa0 = 1.f, fa1 = 1.f;
+        float fa[4] = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
-          if (ii > j && ii < m) { fa0 *= d0[ii]; fa1 *= d1[ii]; }
-        const uint16_t* src = sKA + slot(j + 1, j) * 16 * RS + c0;
-        uint16_t* dst = sKA + slot(m, j) * 16 * RS + c0;
-        uint32_t w[16];
 #pragma unroll
-        for (int tt = 0; tt < 16; ++tt) w[tt] = *reinterpret_cast<const uint32_t*>(src + tt * RS);
+          for (int c = 0; c < 4; ++c)
+            if (ii > j && ii < m) fa[c] *= dd[ii][c];
+        const uint16_t* src = sKA + (slot(j + 1, j) * 16 + 8 * gh) * RS + c0;
+        uint16_t* dst = sKA + (slot(m, j) * 16 + 8 * gh) * RS + c0;
+        u32x2 w[8];
 #pragma unroll
-        for (int tt = 0; tt < 16; ++tt)
-          *reinterpret_cast<uint32_t*>(dst + tt * RS) = pack2(bflo(w[tt]) * fa0, bfhi(w[tt]) * fa1);
+        for (int tt = 0; tt < 8; ++tt) w[tt] = *reinterpret_cast<const u32x2*>(src + tt * RS);
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt)
+          *reinterpret_cast<u32x2*>(dst + tt * RS) =
+              pack4(q4(w[tt], 0) * fa[0], q4(w[tt], 1) * fa[1], q4(w[tt], 2) * fa[2], q4(w[tt], 3) * fa[3]);
       }
 #pragma unroll
-      for (int tt = 0; tt < 16; ++tt) {
-        *reinterpret_cast<uint32_t*>(&sKR[(16 * i + tt) * RS + c0]) = kr[tt];
+      for (int tt = 0; tt < 8; ++tt) {
+        const int row = 16 * i + 8 * gh + tt;
+        *reinterpret_cast<u32x2*>(&sKR[row * RS + c0]) = kr[tt];
         if constexpr (!STO) {
           // q r (read by the next phase 2) and q Gamma (read by the next A1); the state
           // chain's reads of the current chunk's q Gamma ended with A1
-          *reinterpret_cast<uint32_t*>(&sQR[(16 * i + tt) * RS + c0]) = qr[tt];
-          *reinterpret_cast<uint32_t*>(&sQt[(16 * i + tt) * RS + c0]) =
-              pack2(bflo(qr[tt]) * eB0, bfhi(qr[tt]) * eB1);
+          *reinterpret_cast<u32x2*>(&sQR[row * RS + c0]) = qr[tt];
+          *reinterpret_cast<u32x2*>(&sQt[row * RS + c0]) =
+              pack4(q4(qr[tt], 0) * eB[0], q4(qr[tt], 1) * eB[1], q4(qr[tt], 2) * eB[2], q4(qr[tt], 3) * eB[3]);
         }
       }
+      // (k Gamma_C / Gamma)^T of this half's tokens: channel c0 + j, tokens 8 gh .. + 7
 #pragma unroll
-      for (int tp = 0; tp < 8; ++tp) {
-        const uint32_t a0 = ks[2 * tp], a1 = ks[2 * tp + 1];
-        kh[tp] = pack2(bflo(a0) * af0, bflo(a1) * af0);
-        kh[8 + tp] = pack2(bfhi(a0) * af1, bfhi(a1) * af1);
+      for (int j = 0; j < 4; ++j) {
+        uint32_t w[4];
+#pragma unroll
+        for (int tp = 0; tp < 4; ++tp) w[tp] = pack2(q4(ks[2 * tp], j) * af[j], q4(ks[2 * tp + 1], j) * af[j]);
+        kh[j] = u32x4{w[0], w[1], w[2], w[3]};
       }
-      gc0 = af0 * D0;
-      gc1 = af1 * D1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) gc[j] = af[j] * Dt[j];
     };
 
     // tiles the state chain reads in A2 (written once the previous chunk's A2 is done)
     auto gate_b = [&]() __attribute__((always_inline)) {
-      u32x4* d = reinterpret_cast<u32x4*>(&sKhT[c0 * TS + 16 * i]);
-      d[0] = u32x4{kh[0], kh[1], kh[2], kh[3]};
-      d[1] = u32x4{kh[4], kh[5], kh[6], kh[7]};
-      d = reinterpret_cast<u32x4*>(&sKhT[(c0 + 1) * TS + 16 * i]);
-      d[0] = u32x4{kh[8], kh[9], kh[10], kh[11]};
-      d[1] = u32x4{kh[12], kh[13], kh[14], kh[15]};
-      if (i == 0) {
-        sGC[c0] = gc0;
-        sGC[c0 + 1] = gc1;
-      }
-      if (NORM && (ln & 3) == 0) sRho[16 * i + (ln >> 2)] = rho;
+      const int gh = ln >> 5;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(&sKhT[(c0 + j) * TS + 16 * i + 8 * gh]) = kh[j];
+      if (i == 0 && gh == 0) *reinterpret_cast<f32x4*>(&sGC[c0]) = f32x4{gc[0], gc[1], gc[2], gc[3]};
+      if (NORM && (ln & 3) == 0) sRho[16 * i + 8 * gh + ((ln >> 2) & 7)] = rho;
     };
 
     // ---- prologue: operand tiles of chunk 0
