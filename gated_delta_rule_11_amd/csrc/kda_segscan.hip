@@ -4,70 +4,88 @@
 // the zero state, segment p ends in S~_p; its transition (the map applied to
 // an entry state, the product of the per-token maps (I - beta k k^T) Diag(alpha))
 // is M_p.  The true entry states follow by a prefix scan over segments,
-//   E_0 = S_in,  E_{p+1} = M_p E_p + S~_p,
-// here in fp32, one workgroup per (b, h, 16-column block of the state), the
-// column block of E held in LDS while the segments are walked in order.
+//   E_0 = S_in,  E_{p+1} = M_p E_p + S~_p.
 // Layouts: St [BH, nseg - 1, dk, dv] and M [BH, nseg - 1, dk, dk] (the last
 // segment's are never needed), E [BH, nseg, dk, dv].
+//
+// One workgroup per (b, h, 16-column block of the state), eight wavefronts, one
+// 16-row tile of the block each.  Each step is a 128-deep product on fp32
+// matrix cores (v_mfma_f32_16x16x4_f32): the wavefront's rows of M_p from global
+// memory (fetched during the previous step), the column block of E_p from LDS,
+// where it is kept transposed (column-major) so that each lane reads its 32
+// contiguous k values with 16-byte reads; two LDS copies alternate, so a step
+// has one barrier.  The steps are sequential; the loads of step p + 1 are in
+// flight during step p.
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
 
 namespace kda {
 
 constexpr int kScanCols = 16;
+constexpr int kScanEtStride = 128 + 4;  // floats per transposed column (16-byte aligned rows)
 
-template <int DK>
-__global__ __launch_bounds__(256) void segscan_kernel(const float* __restrict__ S_in, const float* __restrict__ St,
+__global__ __launch_bounds__(512) void segscan_kernel(const float* __restrict__ S_in, const float* __restrict__ St,
                                                        const float* __restrict__ M, float* __restrict__ E, int nseg,
                                                        int dv) {
-  static_assert(DK * kScanCols == 256 * 8, "256 threads x 8 outputs");
+  constexpr int DK = 128;
   const int ncb = dv / kScanCols;
   const int bh = blockIdx.x / ncb;
-  const int cb = blockIdx.x % ncb;
-  const int tid = threadIdx.x;
-  const int r = tid >> 1;          // state row (key channel)
-  const int c8 = (tid & 1) * 8;    // first of this thread's 8 columns in the block
-  __shared__ float Eb[DK][kScanCols];
+  const int c0 = (blockIdx.x % ncb) * kScanCols;
+  const int w = threadIdx.x >> 6;  // row tile: rows 16 w .. 16 w + 15
+  const int l = threadIdx.x & 63;
+  const int lr = l & 15, lg = l >> 4;
+  __shared__ __attribute__((aligned(16))) float ET[2][kScanCols][kScanEtStride];
 
   const int64_t sz = static_cast<int64_t>(DK) * dv;
-  float e[8];
+  // this lane's four outputs of the tile: rows 16 w + 4 lg + v, column c0 + lr
+  const int64_t out0 = static_cast<int64_t>(16 * w + 4 * lg) * dv + c0 + lr;
+  f32x4 e;
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    e[j] = S_in ? S_in[static_cast<int64_t>(bh) * sz + static_cast<int64_t>(r) * dv + cb * kScanCols + c8 + j] : 0.f;
+  for (int v = 0; v < 4; ++v) e[v] = S_in ? S_in[bh * sz + out0 + static_cast<int64_t>(v) * dv] : 0.f;
+
+  // A operands of step p: M_p[16 w + lr][32 lg + kk], kk = 0..31; B: E_p[32 lg + kk][c0 + lr]
+  f32x4 a_nx[8], s_nx;
+  auto fetch = [&](int p) __attribute__((always_inline)) {
+    const int64_t sm = static_cast<int64_t>(bh) * (nseg - 1) + p;
+    const f32x4* mr = reinterpret_cast<const f32x4*>(M + sm * DK * DK + static_cast<int64_t>(16 * w + lr) * DK + 32 * lg);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) a_nx[q] = mr[q];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) s_nx[v] = St[sm * sz + out0 + static_cast<int64_t>(v) * dv];
+  };
+  if (nseg > 1) fetch(0);
+
   for (int p = 0; p < nseg; ++p) {
-    const int64_t seg = static_cast<int64_t>(bh) * nseg + p;        // in E
-    const int64_t sm = static_cast<int64_t>(bh) * (nseg - 1) + p;   // in St and M (p < nseg - 1 below)
+    const int64_t seg = static_cast<int64_t>(bh) * nseg + p;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      E[seg * sz + static_cast<int64_t>(r) * dv + cb * kScanCols + c8 + j] = e[j];
-      Eb[r][c8 + j] = e[j];
-    }
+    for (int v = 0; v < 4; ++v) E[seg * sz + out0 + static_cast<int64_t>(v) * dv] = e[v];
     if (p + 1 == nseg) break;
+    // E_p's column block, transposed, into this step's LDS copy
+    float(*et)[kScanEtStride] = ET[p & 1];
+    *reinterpret_cast<f32x4*>(&et[lr][16 * w + 4 * lg]) = e;
     __syncthreads();
-    const float* Mr = M + sm * DK * DK + static_cast<int64_t>(r) * DK;
-    const float* Sr = St + sm * sz + static_cast<int64_t>(r) * dv + cb * kScanCols + c8;
-    float acc[8];
+    f32x4 a[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = Sr[j];
-    for (int kk = 0; kk < DK; kk += 4) {
-      const f32x4 m4 = *reinterpret_cast<const f32x4*>(Mr + kk);
+    for (int q = 0; q < 8; ++q) a[q] = a_nx[q];
+    f32x4 acc = s_nx;
+    if (p + 2 < nseg) fetch(p + 1);
+    const f32x4* br = reinterpret_cast<const f32x4*>(&et[lr][32 * lg]);
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < 8; ++q) {
+      const f32x4 b = br[q];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] += m4[q] * Eb[kk + q][c8 + j];
+      for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q][u], b[u], acc, 0, 0, 0);
     }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 8; ++j) e[j] = acc[j];
+    e = acc;
   }
 }
 
 hipError_t launch_segscan(const SegScanArgs& a, hipStream_t st) {
   if (a.dk != 128 || a.dv % kScanCols) return hipErrorNotSupported;
   const int64_t nwg = static_cast<int64_t>(a.BH) * (a.dv / kScanCols);
-  if (nwg == 0) return hipSuccess;
-  hipLaunchKernelGGL(segscan_kernel<128>, dim3(static_cast<uint32_t>(nwg)), dim3(256), 0, st, a.S_in, a.St, a.M,
-                     a.E, a.nseg, a.dv);
+  if (nwg == 0 || a.nseg < 1) return hipSuccess;
+  hipLaunchKernelGGL(segscan_kernel, dim3(static_cast<uint32_t>(nwg)), dim3(512), 0, st, a.S_in, a.St, a.M, a.E,
+                     a.nseg, a.dv);
   return hipGetLastError();
 }
 
