@@ -9,7 +9,8 @@
 // owns four consecutive elements of the row (one 8- or 16-byte load and one
 // 16-byte store per token), walks the chunk's tokens in order carrying the four
 // running sums, and issues the loads of eight tokens before it uses them, so that
-// the loads of a thread overlap instead of waiting one token at a time.
+// the loads of a thread overlap instead of waiting one token at a time.  Loads and
+// stores are non-temporal: every byte is touched once, so nothing is kept in cache.
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
 
@@ -18,12 +19,16 @@ namespace kda {
 template <typename Tin> struct quad;
 template <> struct quad<float> {
   typedef f32x4 raw;
-  __device__ __forceinline__ static raw load(const float* p, int64_t i) { return *reinterpret_cast<const f32x4*>(p + i); }
+  __device__ __forceinline__ static raw load(const float* p, int64_t i) {
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + i));
+  }
   __device__ __forceinline__ static float at(const raw& r, int e) { return r[e]; }
 };
 template <> struct quad<bf16_t> {
   typedef uint32_t raw __attribute__((ext_vector_type(2)));
-  __device__ __forceinline__ static raw load(const bf16_t* p, int64_t i) { return *reinterpret_cast<const raw*>(p + i); }
+  __device__ __forceinline__ static raw load(const bf16_t* p, int64_t i) {
+    return __builtin_nontemporal_load(reinterpret_cast<const raw*>(p + i));
+  }
   __device__ __forceinline__ static float at(const raw& r, int e) {
     const uint32_t w = r[e >> 1];
     return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
@@ -60,7 +65,7 @@ __global__ __launch_bounds__(256) void gate_kernel(const Tin* __restrict__ z, co
       run[e] += gate_log2(Q::at(r, e), ea[e], gmin_l2e);
       out[e] = run[e] * (1.0f / kLog2e);
     }
-    *reinterpret_cast<f32x4*>(G + (row0 + t) * HD + f) = out;
+    __builtin_nontemporal_store(out, reinterpret_cast<f32x4*>(G + (row0 + t) * HD + f));
   };
   int t = t0;
   for (; t + kGateAhead <= t1; t += kGateAhead) {
