@@ -498,7 +498,7 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
       lds_barrier();
       relane();
 
-      // ---- A1: U = Ut + (-W) S and the inter-chunk part of O, (q Gamma) S
+      // ---- A1: U = Ut + (-W) S, O = (q Gamma) S + P U (stored)
       s16x4 Sb[8], Ub[4];
       f32x4 O[4];
       if (owns_v) {
@@ -524,12 +524,9 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
           }
           O[i] = acc;
         }
-      }
-      lds_barrier();
-      relane();
-
-      // ---- A2: O += P U (stored), S = Diag(Gamma_C) S + (K Gamma_C / Gamma)^T U
-      if (owns_v) {
+        // the intra-chunk part, O += P U, and the output stores: U of this value tile is
+        // complete here, and P was written in phase 2 (the gate wavefronts are the longer
+        // side of this phase, the state chain of A2)
         if (!STO && !(SEG && a.o_skip)) {  // outputs (passes that only need states skip them)
           const auto ro = rsrc(static_cast<Tout*>(a.o) + row0 * DK + j0, (span - 1) * DK * ES + DVS * ES);
           const s16x4 z4 = {0, 0, 0, 0};
@@ -559,6 +556,12 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
             }
           }
         }
+      }
+      lds_barrier();
+      relane();
+
+      // ---- A2: S = Diag(Gamma_C) S + (K Gamma_C / Gamma)^T U
+      if (owns_v) {
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
           f32x4 acc;
