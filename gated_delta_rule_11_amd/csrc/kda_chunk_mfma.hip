@@ -604,7 +604,9 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
       for (int j = 0; j < 4; ++j) ea[j] = __expf(a.A[h * DK + c0 + j]) * kLog2e;
     }
     RawTile<FROM_Z> R;
-    u32x2 kr[8], qr[8], ks[8];  // A1 -> A2: bf16 quads of k r, q r, k sf
+    u32x2 ks[8];                // A1 -> A2: bf16 quads of k sf
+    float rp[8][4];             // A1 -> A2: within-tile prefix products r (0 past the sequence's end)
+    float nkt[8];               // A1 -> A2 (prologue): key normalisers of this lane's tokens
     float Dt[4] = {1.f, 1.f, 1.f, 1.f};  // A1 -> A2: decay over the tile
     u32x4 kh[4];                         // A2 -> 2: (k Gamma_C / Gamma)^T, 8 tokens per channel
     float gc[4] = {1.f, 1.f, 1.f, 1.f};  // A2 -> 2: Gamma_C (written by tile 0's wavefront)
@@ -735,16 +737,17 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
           }
         }
       }
+      // k sf now (the other tiles' wavefronts read it in A2); k r and q r are formed in
+      // A2, where the gate wavefronts have more room, from the raw keys and queries and r
 #pragma unroll
       for (int tt = 0; tt < 8; ++tt) {
         const bool valid = FULL || tb + tt < n;
         const u32x2 k = valid ? R.k[tt] : u32x2{0u, 0u};
-        const u32x2 q = valid ? R.q[tt] : u32x2{0u, 0u};
-        kr[tt] = pack4(q4(k, 0) * (rr[tt][0] * nk[tt]), q4(k, 1) * (rr[tt][1] * nk[tt]),
-                       q4(k, 2) * (rr[tt][2] * nk[tt]), q4(k, 3) * (rr[tt][3] * nk[tt]));
-        qr[tt] = pack4(q4(q, 0) * rr[tt][0], q4(q, 1) * rr[tt][1], q4(q, 2) * rr[tt][2], q4(q, 3) * rr[tt][3]);
         ks[tt] = pack4(q4(k, 0) * (sfv[tt][0] * nk[tt]), q4(k, 1) * (sfv[tt][1] * nk[tt]),
                        q4(k, 2) * (sfv[tt][2] * nk[tt]), q4(k, 3) * (sfv[tt][3] * nk[tt]));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rp[tt][j] = valid ? rr[tt][j] : 0.f;
+        nkt[tt] = nk[tt];
       }
       // k sf of this tile is the anchored-key slot (i + 1, i) as it stands (no tile
       // in between); the scaled slots read it back in the next phase
@@ -807,13 +810,19 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
 #pragma unroll
       for (int tt = 0; tt < 8; ++tt) {
         const int row = 16 * i + 8 * gh + tt;
-        *reinterpret_cast<u32x2*>(&sKR[row * RS + c0]) = kr[tt];
+        const u32x2 k = R.k[tt];
+        *reinterpret_cast<u32x2*>(&sKR[row * RS + c0]) =
+            pack4(q4(k, 0) * (rp[tt][0] * nkt[tt]), q4(k, 1) * (rp[tt][1] * nkt[tt]),
+                  q4(k, 2) * (rp[tt][2] * nkt[tt]), q4(k, 3) * (rp[tt][3] * nkt[tt]));
         if constexpr (!STO) {
           // q r (read by the next phase 2) and q Gamma (read by the next A1); the state
           // chain's reads of the current chunk's q Gamma ended with A1
-          *reinterpret_cast<u32x2*>(&sQR[row * RS + c0]) = qr[tt];
+          const u32x2 q = R.q[tt];
+          *reinterpret_cast<u32x2*>(&sQR[row * RS + c0]) =
+              pack4(q4(q, 0) * rp[tt][0], q4(q, 1) * rp[tt][1], q4(q, 2) * rp[tt][2], q4(q, 3) * rp[tt][3]);
           *reinterpret_cast<u32x2*>(&sQt[row * RS + c0]) =
-              pack4(q4(qr[tt], 0) * eB[0], q4(qr[tt], 1) * eB[1], q4(qr[tt], 2) * eB[2], q4(qr[tt], 3) * eB[3]);
+              pack4(q4(q, 0) * (rp[tt][0] * eB[0]), q4(q, 1) * (rp[tt][1] * eB[1]), q4(q, 2) * (rp[tt][2] * eB[2]),
+                    q4(q, 3) * (rp[tt][3] * eB[3]));
         }
       }
       // (k Gamma_C / Gamma)^T of this half's tokens: channel c0 + j, tokens 8 gh .. + 7
