@@ -52,7 +52,7 @@ DECODE_BYTES_PER_SEQ_HEAD = 2 * 128 * 128 * 4 + 4 * 128 * 2 + 2 + 128 * 2
 # sources it was taken on are unchanged (sha256 of the listed files), else null.
 MEASURED_TRAFFIC = {
     "prefill": {"files": ["gated_delta_rule_11_amd/csrc/kda_chunk_mfma.hip", "gated_delta_rule_11_amd/csrc/kda_common.hpp"],
-                "sha256": "4aa6f5952e38d9e3", "bytes": 5.467e9},
+                "sha256": "28401a345a862692", "bytes": 5.453e9},
     "decode": {"files": ["gated_delta_rule_11_amd/csrc/kda_decode.hip", "gated_delta_rule_11_amd/csrc/kda_common.hpp"],
                "sha256": "289f3a27b8b3e623", "bytes": 1.0849e9},
 }
@@ -79,12 +79,11 @@ def stats(ms):
             "reps": int(a.size)}
 
 
-def _run(cmd, timeout=20):
-    import subprocess
+def _read(path):
     try:
-        r = subprocess.run(cmd, capture_output=True, text=True, timeout=timeout)
-        return r.stdout if r.returncode == 0 else None
-    except (OSError, subprocess.SubprocessError):
+        with open(path) as fh:
+            return fh.read()
+    except OSError:
         return None
 
 
@@ -104,16 +103,17 @@ def environment(torch):
     p = torch.cuda.get_device_properties(0)
     env = {"gpu": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
            "hbm_GiB": round(p.total_memory / 2 ** 30, 1), "torch": torch.__version__, "hip_runtime": torch.version.hip}
-    try:
-        with open("/opt/rocm/.info/version") as fh:
-            env["rocm"] = fh.read().strip()
-    except OSError:
-        env["rocm"] = None
-    hv = _run(["/opt/rocm/bin/hipcc", "--version"])
-    env["hipcc"] = next((l.strip() for l in (hv or "").splitlines() if "clang version" in l), None)
-    clk = _run(["/opt/rocm/bin/rocm-smi", "--showclocks"])
-    env["clocks"] = [l.split(":", 1)[-1].strip() for l in (clk or "").splitlines()
-                     if "sclk" in l or "mclk" in l or "fclk" in l][:3] or None
+    # files only, no child processes (under a profiler every child would start with the
+    # profiler's library preloaded)
+    env["rocm"] = (_read("/opt/rocm/.info/version") or "").strip() or None
+    clocks = []
+    for dev in sorted(os.listdir("/sys/class/drm")) if os.path.isdir("/sys/class/drm") else []:
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk"):
+            txt = _read(os.path.join("/sys/class/drm", dev, "device", name))
+            if txt:
+                cur = [l.strip() for l in txt.splitlines() if l.strip().endswith("*")]
+                clocks.append(f"{dev} {name[7:]}: {cur[0] if cur else txt.split()[-1]}")
+    env["clocks"] = clocks[:4] or None
     env["library_sources_sha256"] = source_sha256()
     try:
         import json as _json

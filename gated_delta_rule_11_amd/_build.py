@@ -60,9 +60,14 @@ def _write_build_info():
         except (OSError, subprocess.SubprocessError):
             return None
     head = git("rev-parse", "HEAD")
+    try:
+        r = subprocess.run([HIPCC, "--version"], capture_output=True, text=True, timeout=60)
+        hv = next((l.strip() for l in r.stdout.splitlines() if "clang version" in l), None)
+    except (OSError, subprocess.SubprocessError):
+        hv = None
     dirty = git("status", "--porcelain", "--", "gated_delta_rule_11_amd/csrc", "include")
     info = {"commit": head, "sources_modified_since_commit": bool(dirty) if dirty is not None else None,
-            "arch": ARCH, "hipcc": HIPCC}
+            "arch": ARCH, "hipcc": HIPCC, "hipcc_version": hv}
     with open(os.path.join(HERE, "build_info.json"), "w") as fh:
         json.dump(info, fh)
 

@@ -67,16 +67,21 @@ __global__ __launch_bounds__(512) void segscan_kernel(const float* __restrict__ 
     f32x4 a[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) a[q] = a_nx[q];
-    f32x4 acc = s_nx;
+    const f32x4 st = s_nx;
     if (p + 2 < nseg) fetch(p + 1);
     const f32x4* br = reinterpret_cast<const f32x4*>(&et[lr][32 * lg]);
+    // four independent accumulators (k = 32 lg + 4 q + u by u) shorten the dependent
+    // chain of products four times; they are summed at the end, in a fixed order
+    f32x4 acc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const f32x4 b = br[q];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q][u], b[u], acc, 0, 0, 0);
+      for (int u = 0; u < 4; ++u) acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q][u], b[u], acc[u], 0, 0, 0);
     }
-    e = acc;
+    e = st + ((acc[0] + acc[1]) + (acc[2] + acc[3]));
   }
 }
 
