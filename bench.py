@@ -349,6 +349,37 @@ def main():
                 small[cs.name]["one_pass_ms"] = one["median"]
         log(f"small configurations: {small}")
 
+    # ---------------- other supported shapes (reported beside the step) ----------------
+    # Shapes outside the matrix-core kernel's (bf16, d_k = d_v = 128, chunk 64) run the fp32
+    # vector-ALU kernel: bf16 with smaller heads or chunk 16, and fp32 inputs.  B=4, H=32,
+    # T=4096, fused gate; bytes per token-head: q, k, z and v, beta in, o out.
+    other = None
+    if run_pre and not args.no_extras:
+        other = {}
+        for dtype, dk_, dv_, ch_ in (("bf16", 64, 64, 64), ("bf16", 32, 32, 64), ("bf16", 128, 128, 16),
+                                     ("f32", 128, 128, 64)):
+            cs = ki.small_spec(4, 32, 4096, dk_, dv_, ch_, dtype, seed=1500 + dk_ + ch_, s0_std=0.01,
+                               name=f"{dtype}_d{dk_}x{dv_}_chunk{ch_}")
+            cd = ki.prefill_inputs(cs)
+            C = {k: to_dev(cd[k], cs.dtype) for k in ("q", "k", "v", "z", "beta")}
+            C["A"] = to_dev(cd["A"], "f32")
+            S0c = to_dev(cd["S0"], "f32")
+            oc = torch.empty((cs.B, cs.T, cs.H, cs.dv), dtype=torch.float32 if dtype == "f32" else torch.bfloat16,
+                             device=dev)
+            Sc = torch.empty((cs.B, cs.H, cs.dk, cs.dv), dtype=torch.float32, device=dev)
+            wsc = workspace(cs.B, cs.T, cs.H, cs.dk, cs.dv, cs.chunk)
+            st_ = stats(timed(lambda: kda.chunk_fwd_z(C["q"], C["k"], C["v"], C["beta"], C["z"], C["A"], -5.0,
+                                                      cs.chunk, S_in=S0c, o=oc, S_out=Sc, workspace=wsc,
+                                                      stream=stream), 10))
+            es = 2 if dtype == "bf16" else 4
+            nbytes = cs.B * cs.T * cs.H * (es * (3 * cs.dk + 2 * cs.dv) + es) + 2 * cs.B * cs.H * cs.dk * cs.dv * 4
+            other[cs.name] = {"ms": st_["median"], "tokens_per_s": round(cs.B * cs.T / (st_["median"] / 1e3), 1),
+                              "frac_hbm": round(nbytes / (st_["median"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                              "matrix_core_kernel": kda.chunk_uses_mfma(
+                                  torch.bfloat16 if dtype == "bf16" else torch.float32, cs.dk, cs.dv, cs.chunk)}
+            del C, S0c, oc, Sc, wsc
+        log(f"other shapes (B=4, H=32, T=4096): {other}")
+
     # ---------------- standalone gate (reported beside the step, not part of it) ----------------
     # kda_gate on the 32K workload: z in (bf16), chunk-local log-decay sums G out (fp32).  The
     # timed prefill fuses this step; the standalone kernel feeds kda_chunk_fwd.
@@ -573,6 +604,7 @@ def main():
         "long_context": long_ctx,
         "prologue": prologue,
         "small_configs": small,
+        "other_shapes": other,
         "gate": gate,
         "backward": backward,
     }
