@@ -1,246 +1,496 @@
-// kda_chunk_generic.hip -- chunked KDA prefill for every supported shape and
-// dtype, fp32 arithmetic on the vector ALUs.
+// kda_chunk_generic.hip -- chunked KDA prefill for every supported shape outside
+// the bf16 matrix-core kernel's (fp32 inputs, dk or dv below 128, chunk 16).
+// fp32 arithmetic throughout; every product runs on fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32).
 //
-// This is the path for fp32 inputs, for dk or dv below 128 and for chunk 16.
-// It runs the chunkwise regrouping of Eq. 1 on sub-chunks of SC = 16 tokens
-// (the 16-token tile of "Kimi K3 reading notes", section 2) with the state
-// carried between sub-chunks.  A sub-chunk never straddles a chunk of the API
-// (16 divides 16 and 64), so G's chunk-local sums give every decay ratio
-// inside it.
+// The chunkwise regrouping of Eq. 1 ("Kimi K3: the paper and proofs side by
+// side", section 2.1.1; the chunkwise form of "Kimi K3: architecture,
+// derivations and a pinned-source audit", section 4.5) on tiles of 16 tokens
+// (the tile of "Kimi K3 reading notes", section 2), the state carried between
+// tiles.  A tile never straddles an API chunk (16 divides 16 and 64), so G's
+// chunk-local sums give every decay ratio inside it.  Inside a tile with entry
+// state S, per key channel c, Gl_t is the log2-decay summed from the tile start
+// through token t, and a = Gl_7 anchors the tile:
+//   L[t,s] = beta_t sum_c (k_tc 2^(Gl_tc - a_c)) (k_sc 2^(a_c - Gl_sc))    s < t
+//   P[t,s] =        sum_c (q_tc 2^(Gl_tc - a_c)) (k_sc 2^(a_c - Gl_sc))    s <= t
+//   X = (I + L)^-1,  Tm = X Diag(beta)
+//   U = Tm (V - (K * 2^Gl) S)                 (= Tm V - W S with W = Tm (K * 2^Gl))
+//   o = scale ((Q * 2^Gl) S + P U)
+//   S <- Diag(2^Gl_15) S + (K * 2^(Gl_15 - Gl))^T U
+// With g >= g_min >= -5.4 every exponent lies within 63 of zero (the anchor is
+// mid-tile), so no factor over- or underflows; a caller's own G obeys the tile
+// bound the header states.  Tokens past the end of the sequence enter as
+// k = q = v = beta = g = 0, which leaves S and the valid rows unchanged.
 //
-// Algebra (derived from Eq. 1, "Kimi K3: the paper and proofs side by side",
-// section 2.1.1; the regrouping is the chunkwise form that "Kimi K3:
-// architecture, derivations and a pinned-source audit", section 4.5 names).
-// Inside a sub-chunk with entry state S, per key channel c, with Gl_t the
-// log-decay summed from the sub-chunk start through token t:
-//   L[t,s] = beta_t sum_c k_tc k_sc 2^(Gl_tc - Gl_sc)      s < t
-//   Tm     = (I + L)^-1 Diag(beta)                           (forward substitution)
-//   W      = Tm (K * 2^Gl),  Ut = Tm V,  U = Ut - W S
-//   P[t,s] = sum_c q_tc k_sc 2^(Gl_tc - Gl_sc)               s <= t
-//   o      = scale ((Q * 2^Gl) S + P U)
-//   S     <- Diag(2^Gl_last) S + (K * 2^(Gl_last - Gl))^T U
-// Every power of two above has a non-positive exponent: Gl is non-increasing
-// in t, so no overflow is possible for any g.
+// Fused prologue (a.prologue): q and k arrive un-normalised, beta as a logit.
+// The products above are formed from the raw rows and the norms applied to
+// their rows and columns afterwards (L -> Diag(rk) L Diag(rk), P -> Diag(rq) P
+// Diag(rk), and the rows of (K * 2^Gl) S, (Q * 2^Gl) S and U), with
+// r = 1 / sqrt(|x|^2 + 1e-6).
 //
-// Fused prologue (a.prologue): q and k arrive un-normalised and beta as a
-// logit; each sub-chunk's rows are divided by sqrt(|x|^2 + 1e-6) in LDS and
-// beta goes through the sigmoid, before any of the above.
-//
-// One workgroup (256 threads) per (b, h, slice of DVS value columns).  The
-// value columns of the state evolve independently given (k, beta, alpha), so
-// slicing changes no arithmetic.
+// One workgroup of eight wavefronts per (b, h, slice of dvs value columns), in
+// two roles that work one tile apart (step n: the key role forms tile n while
+// the state role consumes tile n - 1), one barrier per step:
+//   key role    wavefront w takes key-channel tiles w, w + 4: gate and decay
+//               sums, the anchored factors, its part of L and P (matrix
+//               cores, each lane holding one token's four channels of a tile),
+//               and q 2^Gl, -k 2^Gl, k 2^(Gl_15 - Gl) into LDS;
+//   state role  wavefront w < dvs / 16 owns value columns 16 w .. 16 w + 15 of
+//               the slice and keeps that dk x 16 block of the state in its
+//               accumulators; it forms (K 2^Gl) S and (Q 2^Gl) S, solves X row
+//               by row (lane t forms row t of X by back substitution, the
+//               rows of L read from LDS as broadcasts) while those products
+//               run, then U, o and the state update.
+// LDS is double-buffered by tile parity, so the key role of tile n + 1 never
+// overwrites what the state role of tile n still reads.  Each role prefetches
+// its next tile's inputs one step ahead.
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
 
 namespace kda {
 
 namespace {
-constexpr int SC = 16;
-constexpr int NT = 256;
+
+constexpr int NT = 512;  // four key-role and four state-role wavefronts
+constexpr int KH_STRIDE = 20;  // floats per transposed key row: 16 tokens + 4 (16-byte rows, no bank conflicts)
+
+template <int DK>
+struct TileLds {
+  static constexpr int NCT = DK / 16;              // key-channel tiles
+  static constexpr int NP = NCT < 4 ? NCT : 4;     // wavefronts holding key tiles
+  float lp[NP][2][16][16];                         // partial L and P (rows t, columns s)
+  f32x4 qg[NCT][64];                               // q 2^Gl, lane (t, group) order
+  f32x4 kg[NCT][64];                               // -k 2^Gl, same order
+  float kh[DK][KH_STRIDE];                         // k 2^(Gl_15 - Gl), channel rows, token columns
+  float el[DK];                                    // 2^Gl_15 per channel
+  float beta[16];
+  float nrm[NP][2][16];                            // prologue: partial |k|^2 and |q|^2 per token
+};
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Four consecutive elements of a row, kept raw while the load is in flight.
+template <typename T> struct Row4;
+template <> struct Row4<float> {
+  typedef f32x4 raw;
+  __device__ __forceinline__ static raw load(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+  __device__ __forceinline__ static f32x4 cvt(raw r) { return r; }
+};
+template <> struct Row4<bf16_t> {
+  typedef u32x2 raw;
+  __device__ __forceinline__ static raw load(const bf16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
+  __device__ __forceinline__ static f32x4 cvt(raw r) {
+    return f32x4{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u), __uint_as_float(r.y << 16),
+                 __uint_as_float(r.y & 0xffff0000u)};
+  }
+};
+template <typename T> struct One;
+template <> struct One<float> {
+  typedef float raw;
+  __device__ __forceinline__ static raw load(const float* p) { return *p; }
+  __device__ __forceinline__ static float cvt(raw r) { return r; }
+};
+template <> struct One<bf16_t> {
+  typedef uint16_t raw;
+  __device__ __forceinline__ static raw load(const bf16_t* p) { return p->bits; }
+  __device__ __forceinline__ static float cvt(raw r) { return bf16_to_f32(r); }
+};
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// inclusive prefix sum over the 16 lanes of a DPP row (lanes 16 r .. 16 r + 15)
+__device__ __forceinline__ float row_prefix16(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, true));  // row_shr:1
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, true));  // row_shr:2
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, true));  // row_shr:4
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, true));  // row_shr:8
+  return x;
+}
+__device__ __forceinline__ float lane_value(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(lane << 2, __float_as_int(x)));
+}
+// Orders a prefetch after the last use of the registers it refills: the value
+// is an operand (so it is computed before this point) and memory is clobbered
+// (so no load moves above it).  Without it the compiler issues the next tile's
+// loads first, into other registers, and copies them back at the end of the
+// step, which waits for the loads there.
+__device__ __forceinline__ void settle(f32x4& x) { asm volatile("" : "+v"(x)::"memory"); }
+__device__ __forceinline__ void settle(float& x) { asm volatile("" : "+v"(x)::"memory"); }
+__device__ __forceinline__ float sel4(int g, float a0, float a1, float a2, float a3) {
+  return g == 0 ? a0 : (g == 1 ? a1 : (g == 2 ? a2 : a3));
+}
+
 }  // namespace
 
-template <int DK, int DVS, typename Tin, typename Tout, bool FROM_Z>
-__global__ __launch_bounds__(NT) void chunk_generic_kernel(const ChunkArgs a) {
-  const int nsl = a.dv / DVS;
+template <int DK, typename Tin, bool FROM_Z>
+__global__ __launch_bounds__(NT) void chunk_tile_kernel(const ChunkArgs a, const int dvs) {
+  using Lds = TileLds<DK>;
+  constexpr int NCT = Lds::NCT, NP = Lds::NP;
+  constexpr int CPW = (NCT + 3) / 4;  // key tiles per key wavefront
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  Lds* lds = reinterpret_cast<Lds*>(smem);                         // two copies, by tile parity
+  float* lsol = reinterpret_cast<float*>(smem + 2 * sizeof(Lds));  // [4][16][16]: each state wavefront's L
+
+  const int nsl = a.dv / dvs;
   const int sl = blockIdx.x % nsl;
   const int bh = blockIdx.x / nsl;
   const int h = bh % a.H;
   const int b = bh / a.H;
-  const int tid = threadIdx.x;
-  const int j0 = sl * DVS;
+  const int w = threadIdx.x >> 6;
+  const int l = threadIdx.x & 63;
+  const int li = l & 15, lg = l >> 4;
+  const bool key_role = w < 4;
+  const int kw = w, sw = w - 4;  // index within the role
+  const bool key_wave = key_role && kw < NP;
+  const bool state_wave = !key_role && sw < dvs / 16;
+  const int jcol = sl * dvs + 16 * sw + li;  // state role: this lane's value column
+  const bool norm = a.prologue;
+  const int ntiles = (a.T + 15) / 16;
 
   const Tin* q = static_cast<const Tin*>(a.q);
   const Tin* k = static_cast<const Tin*>(a.k);
   const Tin* v = static_cast<const Tin*>(a.v);
   const Tin* beta = static_cast<const Tin*>(a.beta);
   const Tin* z = static_cast<const Tin*>(a.z);
-  Tout* o = static_cast<Tout*>(a.o);
-
-  __shared__ float Ks[SC][DK], Qs[SC][DK], Gl[SC][DK], Ws[SC][DK];
-  __shared__ float Vs[SC][DVS], Us[SC][DVS];
-  __shared__ float Lm[SC][SC], Pm[SC][SC], Tm[SC][SC];
-  __shared__ float bs[SC];
-  __shared__ float rn[2][SC];  // prologue: 1 / sqrt(|k|^2 + eps), 1 / sqrt(|q|^2 + eps) per token
-  __shared__ float Ss[DK][DVS];
-  __shared__ float eaL[DK];
-
+  const int64_t HDK = static_cast<int64_t>(a.H) * DK;
   const int64_t HDV = static_cast<int64_t>(a.H) * a.dv;
-  const int64_t state_off = static_cast<int64_t>(bh) * DK * a.dv;
+  const int64_t seq0 = static_cast<int64_t>(b) * a.T;  // first token row of this sequence
   const float gmin_l2e = a.g_min * kLog2e;
 
-  for (int e = tid; e < DK * DVS; e += NT) {
-    const int c = e / DVS, j = e % DVS;
-    Ss[c][j] = a.S_in ? a.S_in[state_off + static_cast<int64_t>(c) * a.dv + j0 + j] : 0.f;
-  }
-  if (FROM_Z)
-    for (int c = tid; c < DK; c += NT) eaL[c] = __expf(a.A[h * DK + c]) * kLog2e;
-  __syncthreads();
-
-  for (int t0 = 0; t0 < a.T; t0 += SC) {
-    const int n = min(SC, a.T - t0);
-    if (a.S_ckpt && t0 % 64 == 0) {  // backward checkpoint: the state entering this 64-token block
-      float* ck = a.S_ckpt + (static_cast<int64_t>(bh) * ((a.T + 63) / 64) + t0 / 64) * DK * a.dv;
-      for (int e = tid; e < DK * DVS; e += NT) ck[(e / DVS) * a.dv + j0 + e % DVS] = Ss[e / DVS][e % DVS];
+  // ---- key role: exp(A) log2 e of this lane's channels, prefetched inputs of its next tile
+  float eal[CPW][4];
+#pragma unroll
+  for (int m = 0; m < CPW; ++m)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int ct = kw + 4 * m;
+      eal[m][r] = (FROM_Z && key_wave && ct < NCT) ? __expf(a.A[h * DK + 16 * ct + 4 * lg + r]) * kLog2e : 0.f;
     }
-    // 1. load the sub-chunk; Gl = log2-decay summed from the sub-chunk start
-    for (int e = tid; e < SC * DK; e += NT) {
-      const int i = e / DK, c = e % DK;
-      float kv = 0.f, qv = 0.f, gl = 0.f;
-      if (i < n) {
-        const int64_t row = (static_cast<int64_t>(b) * a.T + t0 + i) * a.H + h;
-        kv = io<Tin>::load(k, row * DK + c);
-        qv = io<Tin>::load(q, row * DK + c);
+  typename Row4<Tin>::raw rk_[CPW], rq_[CPW], rz_[CPW];
+  f32x4 rg_[CPW], rgp_[CPW];
+  typename One<Tin>::raw rb_;
+  // Loads are unconditional (rows clamped into the sequence, key tiles into range,
+  // the last tile fetched again at the end): a load under a branch would make the
+  // compiler copy its result at the join and wait for it there.
+  auto fetch_key = [&](int t0) __attribute__((always_inline)) {
+    const int n = min(16, a.T - t0);
+    const int64_t row = seq0 + t0 + min(li, n - 1);
+#pragma unroll
+    for (int m = 0; m < CPW; ++m) {
+      const int ct = min(kw + 4 * m, NCT - 1);
+      const int64_t e = (row * a.H + h) * DK + 16 * ct + 4 * lg;
+      rk_[m] = Row4<Tin>::load(k + e);
+      rq_[m] = Row4<Tin>::load(q + e);
+      if (FROM_Z) {
+        rz_[m] = Row4<Tin>::load(z + e);
+      } else {
+        // the sum through the token before the tile (same chunk; row t0 - 1 read at t0 = 0
+        // is the tile's own first row, and unused)
+        rg_[m] = *reinterpret_cast<const f32x4*>(a.G + e);
+        rgp_[m] = *reinterpret_cast<const f32x4*>(a.G + e - static_cast<int64_t>(min(li, n - 1) + (t0 > 0)) * HDK);
+      }
+    }
+    rb_ = One<Tin>::load(beta + row * a.H + h);
+  };
+
+  // ---- state role: rows 16 ct + 4 lg + r of column jcol; prefetched values of its next tile
+  const int64_t soff = static_cast<int64_t>(bh) * DK * a.dv + static_cast<int64_t>(4 * lg) * a.dv + jcol;
+  f32x4 S[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      S[ct][r] = (state_wave && a.S_in) ? a.S_in[soff + static_cast<int64_t>(16 * ct + r) * a.dv] : 0.f;
+  typename One<Tin>::raw rv_[4];
+  auto fetch_v = [&](int t0) __attribute__((always_inline)) {
+    const int n = min(16, a.T - t0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int64_t vr = seq0 + t0 + min(4 * lg + t, n - 1);
+      rv_[t] = One<Tin>::load(v + vr * HDV + static_cast<int64_t>(h) * a.dv + jcol);
+    }
+  };
+  // Barrier n closes step n: the key role forms tile n before it, the state role
+  // consumes tile n - 1 before it.  Each role runs its own loop (so no prefetched
+  // register crosses a branch), ntiles + 1 barriers in every wavefront.
+  const int last_t0 = 16 * (ntiles - 1);
+  if (key_role) {
+    if (ntiles > 0) fetch_key(0);
+    for (int it = 0; it < ntiles; ++it) {
+      Lds& cur = lds[it & 1];
+      const int t0 = 16 * it;
+      const int n = min(16, a.T - t0);
+      const bool valid = li < n;
+      f32x4 kk[CPW], qq[CPW], gl[CPW];
+#pragma unroll
+      for (int m = 0; m < CPW; ++m) {
+        kk[m] = Row4<Tin>::cvt(rk_[m]);
+        qq[m] = Row4<Tin>::cvt(rq_[m]);
         if (FROM_Z) {
-          gl = gate_log2(io<Tin>::load(z, row * DK + c), eaL[c], gmin_l2e);
+          const f32x4 zz = Row4<Tin>::cvt(rz_[m]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float g = gate_log2(zz[r], eal[m][r], gmin_l2e);
+            gl[m][r] = valid ? g : 0.f;
+          }
         } else {
-          gl = a.G[row * DK + c] * kLog2e;
-          if (t0 % a.chunk != 0) {  // subtract the sum through token t0 - 1 (same chunk)
-            const int64_t prev = (static_cast<int64_t>(b) * a.T + t0 - 1) * a.H + h;
-            gl -= a.G[prev * DK + c] * kLog2e;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) gl[m][r] = (rg_[m][r] - (t0 % a.chunk != 0 ? rgp_[m][r] : 0.f)) * kLog2e;
+        }
+      }
+      float bval = One<Tin>::cvt(rb_);
+#pragma unroll
+      for (int m = 0; m < CPW; ++m) {
+        settle(kk[m]);
+        settle(qq[m]);
+        settle(gl[m]);
+      }
+      settle(bval);
+      fetch_key(min(t0 + 16, last_t0));
+      if (norm) bval = sigmoid_fast(bval);
+
+      if (key_wave) {  // anchored factors, partial L and P, operand tiles into LDS
+        f32x4 accL = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+        float ssk = 0.f, ssq = 0.f;
+#pragma unroll
+        for (int m = 0; m < CPW; ++m) {
+          const int ct = kw + 4 * m;
+          if (ct >= NCT) continue;
+          f32x4 kf, kb, qf, qgv, kgv;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float kv = valid ? kk[m][r] : 0.f;
+            const float qv = valid ? qq[m][r] : 0.f;
+            ssk += kv * kv;
+            ssq += qv * qv;
+            const float g = FROM_Z ? row_prefix16(gl[m][r]) : gl[m][r];
+            const float anc = lane_value(g, (l & 48) | 7);
+            const float last = lane_value(g, l | 15);
+            const float f = fast_exp2(g - anc), fi = fast_exp2(anc - g), eg = fast_exp2(g);
+            kf[r] = kv * f;
+            kb[r] = kv * fi;
+            qf[r] = qv * f;
+            qgv[r] = qv * eg;
+            kgv[r] = -(kv * eg);
+            cur.kh[16 * ct + 4 * lg + r][li] = kv * fast_exp2(last - g);
+            if (li == 0) cur.el[16 * ct + 4 * lg + r] = fast_exp2(last);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            accL = mfma4(kf[r], kb[r], accL);
+            accP = mfma4(qf[r], kb[r], accP);
+          }
+          cur.qg[ct][l] = qgv;
+          cur.kg[ct][l] = kgv;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          cur.lp[kw][0][4 * lg + r][li] = accL[r];
+          cur.lp[kw][1][4 * lg + r][li] = accP[r];
+        }
+        if (norm) {
+          ssk += __shfl_xor(ssk, 16);
+          ssk += __shfl_xor(ssk, 32);
+          ssq += __shfl_xor(ssq, 16);
+          ssq += __shfl_xor(ssq, 32);
+          if (lg == 0) {
+            cur.nrm[kw][0][li] = ssk;
+            cur.nrm[kw][1][li] = ssq;
           }
         }
       }
-      Ks[i][c] = kv;
-      Qs[i][c] = qv;
-      Gl[i][c] = gl;
-    }
-    for (int e = tid; e < SC * DVS; e += NT) {
-      const int i = e / DVS, j = e % DVS;
-      Vs[i][j] = i < n ? io<Tin>::load(v, (static_cast<int64_t>(b) * a.T + t0 + i) * HDV + static_cast<int64_t>(h) * a.dv + j0 + j) : 0.f;
-    }
-    if (tid < SC) {
-      const float bl = tid < n ? io<Tin>::load(beta, (static_cast<int64_t>(b) * a.T + t0 + tid) * a.H + h) : 0.f;
-      bs[tid] = tid < n ? (a.prologue ? sigmoid_fast(bl) : bl) : 0.f;
+      if (kw == 0 && lg == 0) cur.beta[li] = valid ? bval : 0.f;
+      __syncthreads();
     }
     __syncthreads();
-    if (a.prologue) {  // normalise the rows of k and q (rows past n are zero and stay zero)
-      if (tid < 2 * SC) {
-        const float* row = tid < SC ? Ks[tid] : Qs[tid - SC];
-        float ss = 0.f;
-        for (int c = 0; c < DK; ++c) ss += row[c] * row[c];
-        rn[tid / SC][tid % SC] = rsqrt_fast(ss + kL2Eps);
+  } else if (state_wave) {
+    if (ntiles > 0) fetch_v(0);
+    __syncthreads();
+    for (int it = 0; it < ntiles; ++it) {
+      const Lds& cur = lds[it & 1];
+      const int t0 = 16 * it;
+      const int n = min(16, a.T - t0);
+      float vin[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        vin[t] = (4 * lg + t < n) ? One<Tin>::cvt(rv_[t]) : 0.f;
+        settle(vin[t]);
       }
-      __syncthreads();
-      for (int e = tid; e < SC * DK; e += NT) {
-        const int i = e / DK, c = e % DK;
-        Ks[i][c] *= rn[0][i];
-        Qs[i][c] *= rn[1][i];
+      fetch_v(min(t0 + 16, last_t0));
+
+      if (a.S_ckpt && t0 % 64 == 0) {  // backward checkpoint: the state entering this 64-token block
+        float* ck = a.S_ckpt + (static_cast<int64_t>(bh) * ((a.T + 63) / 64) + t0 / 64) * DK * a.dv;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ck[(16 * ct + 4 * lg + r) * a.dv + jcol] = S[ct][r];
       }
-      __syncthreads();
-    }
-    if (FROM_Z) {  // per-token g -> running sums within the sub-chunk
-      for (int c = tid; c < DK; c += NT)
-        for (int i = 1; i < n; ++i) Gl[i][c] += Gl[i - 1][c];
-      __syncthreads();
-    }
-    // 2. L (strictly lower, times beta_t) and P (lower incl. diagonal)
-    for (int e = tid; e < SC * SC; e += NT) {
-      const int i = e / SC, s = e % SC;
-      float lk = 0.f, pq = 0.f;
-      if (i < n && s <= i) {
-        for (int c = 0; c < DK; ++c) {
-          const float d = fast_exp2(Gl[i][c] - Gl[s][c]) * Ks[s][c];
-          lk += Ks[i][c] * d;
-          pq += Qs[i][c] * d;
+      // prologue norms: rows 4 lg + r (columns of L, P; rows of the products) and token li
+      f32x4 rk4 = {1.f, 1.f, 1.f, 1.f}, rq4 = {1.f, 1.f, 1.f, 1.f};
+      float rk1 = 1.f, rq1 = 1.f;
+      if (norm) {
+        f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sq = {0.f, 0.f, 0.f, 0.f};
+        float s1k = 0.f, s1q = 0.f;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          sk += *reinterpret_cast<const f32x4*>(&cur.nrm[p][0][4 * lg]);
+          sq += *reinterpret_cast<const f32x4*>(&cur.nrm[p][1][4 * lg]);
+          s1k += cur.nrm[p][0][li];
+          s1q += cur.nrm[p][1][li];
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          rk4[r] = rsqrt_fast(sk[r] + kL2Eps);
+          rq4[r] = rsqrt_fast(sq[r] + kL2Eps);
+        }
+        rk1 = rsqrt_fast(s1k + kL2Eps);
+        rq1 = rsqrt_fast(s1q + kL2Eps);
+      }
+      // (-K 2^Gl) S and (Q 2^Gl) S: lane (t, g) supplies token t's channels 16 ct + 4 g + r
+      f32x4 y = {0.f, 0.f, 0.f, 0.f}, oacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const f32x4 kgv = cur.kg[ct][l];
+        const f32x4 qgv = cur.qg[ct][l];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          y = mfma4(kgv[r], S[ct][r], y);
+          oacc = mfma4(qgv[r], S[ct][r], oacc);
         }
       }
-      Lm[i][s] = (s < i) ? bs[i] * lk : 0.f;
-      Pm[i][s] = pq;
-    }
-    __syncthreads();
-    // 3. Tm = (I + L)^-1 Diag(beta): one column per thread, forward substitution
-    if (tid < SC) {
-      const int j = tid;
-      float x[SC];
+      // L and P, row li, columns 4 lg .. 4 lg + 3, summed over the key tiles in a fixed order
+      f32x4 Lr = {0.f, 0.f, 0.f, 0.f}, Pr = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < SC; ++i) {
-        float acc = (i == j) ? 1.f : 0.f;
-        for (int m = 0; m < i; ++m) acc -= Lm[i][m] * x[m];
-        x[i] = acc;
+      for (int p = 0; p < NP; ++p) {
+        Lr += *reinterpret_cast<const f32x4*>(&cur.lp[p][0][li][4 * lg]);
+        Pr += *reinterpret_cast<const f32x4*>(&cur.lp[p][1][li][4 * lg]);
       }
+      const float bt = cur.beta[li];
+      const f32x4 bs4 = *reinterpret_cast<const f32x4*>(&cur.beta[4 * lg]);
 #pragma unroll
-      for (int i = 0; i < SC; ++i) Tm[i][j] = x[i] * bs[j];
-    }
-    __syncthreads();
-    // 4. W = Tm (K * 2^Gl), Ut = Tm V
-    for (int e = tid; e < SC * DK; e += NT) {
-      const int i = e / DK, c = e % DK;
-      float acc = 0.f;
-      for (int s = 0; s <= i; ++s) acc += Tm[i][s] * Ks[s][c] * fast_exp2(Gl[s][c]);
-      Ws[i][c] = acc;
-    }
-    for (int e = tid; e < SC * DVS; e += NT) {
-      const int i = e / DVS, j = e % DVS;
-      float acc = 0.f;
-      for (int s = 0; s <= i; ++s) acc += Tm[i][s] * Vs[s][j];
-      Us[i][j] = acc;
-    }
-    __syncthreads();
-    // 5. U = Ut - W S
-    for (int e = tid; e < SC * DVS; e += NT) {
-      const int i = e / DVS, j = e % DVS;
-      float acc = Us[i][j];
-      for (int c = 0; c < DK; ++c) acc -= Ws[i][c] * Ss[c][j];
-      Us[i][j] = acc;
-    }
-    __syncthreads();
-    // 6. o = scale ((Q * 2^Gl) S + P U)
-    for (int e = tid; e < SC * DVS; e += NT) {
-      const int i = e / DVS, j = e % DVS;
-      if (i < n && !a.o_skip) {
-        float acc = 0.f;
-        for (int c = 0; c < DK; ++c) acc += Qs[i][c] * fast_exp2(Gl[i][c]) * Ss[c][j];
-        for (int s = 0; s <= i; ++s) acc += Pm[i][s] * Us[s][j];
-        io<Tout>::store(o, (static_cast<int64_t>(b) * a.T + t0 + i) * HDV + static_cast<int64_t>(h) * a.dv + j0 + j,
-                        a.scale * acc);
+      for (int r = 0; r < 4; ++r) {
+        const int s = 4 * lg + r;
+        Lr[r] = s < li ? bt * rk1 * Lr[r] * rk4[r] : 0.f;
+        Pr[r] = s <= li ? rq1 * Pr[r] * rk4[r] : 0.f;
       }
+      // X = (I + L)^-1, row li: x_j = [j == li] - sum_{m > j} x_m L[m][j], m from 15 down.
+      // L goes through this wavefront's own LDS block (the LDS operations of one
+      // wavefront complete in order), whose rows every lane then reads as one broadcast.
+      float* lw = lsol + 256 * sw;
+      *reinterpret_cast<f32x4*>(lw + 16 * li + 4 * lg) = Lr;
+      float x[16], acc[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+#pragma unroll
+      for (int m = 15; m >= 0; --m) {
+        x[m] = li == m ? 1.f : (li < m ? 0.f : -acc[m]);
+#pragma unroll
+        for (int j4 = 0; j4 < m; j4 += 4) {
+          const f32x4 lrow = *reinterpret_cast<const f32x4*>(lw + 16 * m + j4);
+#pragma unroll
+          for (int j = j4; j < j4 + 4 && j < m; ++j) acc[j] = fmaf(x[m], lrow[j - j4], acc[j]);
+        }
+      }
+      f32x4 tm;  // Tm = X Diag(beta), row li, columns 4 lg + r
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tm[r] = sel4(lg, x[r], x[4 + r], x[8 + r], x[12 + r]) * bs4[r];
+      // Y = V - K 2^Gl S (rows 4 lg + r), then U = Tm Y
+      if (norm) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[r] = vin[r] + rk4[r] * y[r];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[r] += vin[r];
+      }
+      f32x4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) u = mfma4(tm[t], y[t], u);
+      // o = scale (Q 2^Gl S + P U), rows 4 lg + r
+      if (!a.o_skip) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) oacc[r] *= rq4[r];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) oacc = mfma4(Pr[t], u[t], oacc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 4 * lg + r;
+          if (t < n) {
+            const int64_t oi = (seq0 + t0 + t) * HDV + static_cast<int64_t>(h) * a.dv + jcol;
+            if (a.out_bf16)
+              io<bf16_t>::store(static_cast<bf16_t*>(a.o), oi, a.scale * oacc[r]);
+            else
+              io<float>::store(static_cast<float*>(a.o), oi, a.scale * oacc[r]);
+          }
+        }
+      }
+      // S <- Diag(2^Gl_15) S + (K 2^(Gl_15 - Gl))^T U
+#pragma unroll
+      for (int r = 0; r < 4; ++r) u[r] *= rk4[r];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const f32x4 el4 = *reinterpret_cast<const f32x4*>(&cur.el[16 * ct + 4 * lg]);
+        const f32x4 khv = *reinterpret_cast<const f32x4*>(&cur.kh[16 * ct + li][4 * lg]);
+        S[ct] *= el4;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) S[ct] = mfma4(khv[t], u[t], S[ct]);
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    // 7. S <- Diag(2^Gl_last) S + (K * 2^(Gl_last - Gl))^T U
-    for (int e = tid; e < DK * DVS; e += NT) {
-      const int c = e / DVS, j = e % DVS;
-      const float gl_last = Gl[n - 1][c];
-      float acc = fast_exp2(gl_last) * Ss[c][j];
-      for (int s = 0; s < n; ++s) acc += Ks[s][c] * fast_exp2(gl_last - Gl[s][c]) * Us[s][j];
-      Ss[c][j] = acc;
-    }
-    __syncthreads();
+  } else {
+    for (int it = 0; it <= ntiles; ++it) __syncthreads();
   }
-  if (a.S_out) {
-    for (int e = tid; e < DK * DVS; e += NT) {
-      const int c = e / DVS, j = e % DVS;
-      a.S_out[state_off + static_cast<int64_t>(c) * a.dv + j0 + j] = Ss[c][j];
-    }
+
+  if (state_wave && a.S_out) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a.S_out[soff + static_cast<int64_t>(16 * ct + r) * a.dv] = S[ct][r];
   }
 }
 
-template <int DK, int DVS, typename Tin, typename Tout>
-static hipError_t launch_cg_t(const ChunkArgs& a, hipStream_t st) {
-  const int64_t nblocks = static_cast<int64_t>(a.B) * a.H * (a.dv / DVS);
-  if (nblocks == 0) return hipSuccess;
-  if (a.from_z)
-    hipLaunchKernelGGL((chunk_generic_kernel<DK, DVS, Tin, Tout, true>), dim3(static_cast<uint32_t>(nblocks)),
-                       dim3(NT), 0, st, a);
-  else
-    hipLaunchKernelGGL((chunk_generic_kernel<DK, DVS, Tin, Tout, false>), dim3(static_cast<uint32_t>(nblocks)),
-                       dim3(NT), 0, st, a);
+namespace {
+
+// Value columns per workgroup: 64 (one 16-column block per wavefront), halved
+// while the grid has fewer workgroups than compute units, down to 16.
+int tile_slice_cols(const ChunkArgs& a) {
+  int dvs = a.dv < 64 ? a.dv : 64;
+  const int64_t bh = static_cast<int64_t>(a.B) * a.H;
+  while (dvs > 16 && bh * (a.dv / dvs) < 256) dvs /= 2;
+  return dvs;
+}
+
+template <int DK, typename Tin, bool FROM_Z>
+hipError_t launch_tile_t(const ChunkArgs& a, hipStream_t st, int dvs) {
+  static std::atomic<uint64_t> lds_set{0};
+  auto kern = chunk_tile_kernel<DK, Tin, FROM_Z>;
+  const int bytes = 2 * static_cast<int>(sizeof(TileLds<DK>)) + 4 * 256 * 4;
+  const hipError_t e = set_lds_limit(reinterpret_cast<const void*>(kern), bytes, lds_set);
+  if (e != hipSuccess) return e;
+  const int64_t nblocks = static_cast<int64_t>(a.B) * a.H * (a.dv / dvs);
+  if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(nblocks)), dim3(NT), bytes, st, a, dvs);
   return hipGetLastError();
 }
 
 template <int DK>
-static hipError_t launch_cg_k(const ChunkArgs& a, hipStream_t st) {
-  // value-column slice: 16 columns (the state slice and the sub-chunk fit LDS)
+hipError_t launch_tile_k(const ChunkArgs& a, hipStream_t st, int dvs) {
   if (a.in_bf16)
-    return a.out_bf16 ? launch_cg_t<DK, 16, bf16_t, bf16_t>(a, st) : launch_cg_t<DK, 16, bf16_t, float>(a, st);
-  return a.out_bf16 ? launch_cg_t<DK, 16, float, bf16_t>(a, st) : launch_cg_t<DK, 16, float, float>(a, st);
+    return a.from_z ? launch_tile_t<DK, bf16_t, true>(a, st, dvs) : launch_tile_t<DK, bf16_t, false>(a, st, dvs);
+  return a.from_z ? launch_tile_t<DK, float, true>(a, st, dvs) : launch_tile_t<DK, float, false>(a, st, dvs);
 }
 
+}  // namespace
+
 hipError_t launch_chunk_generic(const ChunkArgs& a, hipStream_t st) {
+  if (static_cast<int64_t>(a.B) * a.H == 0) return hipSuccess;
+  if (a.dv % 16 || a.dv < 16 || a.dv > 128) return hipErrorInvalidValue;
+  const int dvs = tile_slice_cols(a);
   switch (a.dk) {
-    case 16: return launch_cg_k<16>(a, st);
-    case 32: return launch_cg_k<32>(a, st);
-    case 64: return launch_cg_k<64>(a, st);
-    case 128: return launch_cg_k<128>(a, st);
+    case 16: return launch_tile_k<16>(a, st, dvs);
+    case 32: return launch_tile_k<32>(a, st, dvs);
+    case 64: return launch_tile_k<64>(a, st, dvs);
+    case 128: return launch_tile_k<128>(a, st, dvs);
   }
   return hipErrorInvalidValue;
 }
