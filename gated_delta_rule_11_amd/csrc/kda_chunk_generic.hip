@@ -28,22 +28,26 @@
 // Diag(rk), and the rows of (K * 2^Gl) S, (Q * 2^Gl) S and U), with
 // r = 1 / sqrt(|x|^2 + 1e-6).
 //
-// One workgroup of eight wavefronts per (b, h, slice of dvs value columns), in
-// two roles that work one tile apart (step n: the key role forms tile n while
-// the state role consumes tile n - 1), one barrier per step:
-//   key role    wavefront w takes key-channel tiles w, w + 4: gate and decay
-//               sums, the anchored factors, its part of L and P (matrix
-//               cores, each lane holding one token's four channels of a tile),
-//               and q 2^Gl, -k 2^Gl, k 2^(Gl_15 - Gl) into LDS;
-//   state role  wavefront w < dvs / 16 owns value columns 16 w .. 16 w + 15 of
-//               the slice and keeps that dk x 16 block of the state in its
-//               accumulators; it forms (K 2^Gl) S and (Q 2^Gl) S, solves X row
-//               by row (lane t forms row t of X by back substitution, the
-//               rows of L read from LDS as broadcasts) while those products
-//               run, then U, o and the state update.
-// LDS is double-buffered by tile parity, so the key role of tile n + 1 never
-// overwrites what the state role of tile n still reads.  Each role prefetches
-// its next tile's inputs one step ahead.
+// One workgroup of nine wavefronts per (b, h, slice of DVS value columns), a
+// pipeline of three stages one tile apart with one barrier per step (step n:
+// stage 1 on tile n, stage 2 on tile n - 1, stage 3 on tile n - 2):
+//   1  key wavefronts 0-3; wavefront w takes key-channel tiles w, w + 4: gate
+//      and decay sums, the anchored factors, its part of L and P (matrix cores,
+//      each lane holding one token's four channels of a tile), q 2^Gl,
+//      -k 2^Gl, k 2^(Gl_15 - Gl) and the tile's values into LDS;
+//   2  one wavefront (an idle state slot's, else the ninth): L and P summed over
+//      the parts and masked, X solved row by row (lane t forms row t by back
+//      substitution, the rows of L read from LDS as broadcasts), Tm and P into
+//      LDS;
+//   3  state wavefronts 4 .. 4 + DVS/16 - 1, each owning 16 value columns and
+//      that dk x 16 block of the state in its accumulators: (K 2^Gl) S and
+//      (Q 2^Gl) S, U, o and the state update.
+// LDS holds three copies of the per-tile data, by tile index mod 3.  Only the
+// key wavefronts load from memory (one tile ahead), so the state wavefronts
+// never wait behind their own output stores.  The four SIMDs of a compute unit
+// are the limit: a key wavefront's vector work and a state wavefront's matrix
+// instructions on one SIMD do not overlap much, so work is kept off the busiest
+// SIMDs rather than duplicated.
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
 
@@ -51,19 +55,23 @@ namespace kda {
 
 namespace {
 
-constexpr int NT = 512;  // four key-role and four state-role wavefronts
-constexpr int KH_STRIDE = 20;  // floats per transposed key row: 16 tokens + 4 (16-byte rows, no bank conflicts)
+constexpr int NT = 576;        // four key-role, four state-role wavefronts and one more
+constexpr int KH_STRIDE = 20;  // floats per transposed row: 16 tokens + 4 (16-byte rows, no bank conflicts)
 
-template <int DK>
+template <int DK, int DVS>
 struct TileLds {
   static constexpr int NCT = DK / 16;              // key-channel tiles
   static constexpr int NP = NCT < 4 ? NCT : 4;     // wavefronts holding key tiles
   float lp[NP][2][16][16];                         // partial L and P (rows t, columns s)
   f32x4 qg[NCT][64];                               // q 2^Gl, lane (t, group) order
   f32x4 kg[NCT][64];                               // -k 2^Gl, same order
+  f32x4 tm[64];                                    // Tm, row t, columns 4 group .. 4 group + 3
+  f32x4 pm[64];                                    // P (masked), same order
   float kh[DK][KH_STRIDE];                         // k 2^(Gl_15 - Gl), channel rows, token columns
+  float vt[DVS][KH_STRIDE];                        // values of the slice, column rows, token columns
   float el[DK];                                    // 2^Gl_15 per channel
   float beta[16];
+  float rk[16], rq[16];                            // prologue: 1 / |k|, 1 / |q| per token
   float nrm[NP][2][16];                            // prologue: partial |k|^2 and |q|^2 per token
 };
 
@@ -107,8 +115,13 @@ __device__ __forceinline__ float row_prefix16(float x) {
   x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, true));  // row_shr:8
   return x;
 }
-__device__ __forceinline__ float lane_value(float x, int lane) {
-  return __int_as_float(__builtin_amdgcn_ds_bpermute(lane << 2, __float_as_int(x)));
+// lanes 7 and 15 of each 16-lane row, to the whole row (ds_swizzle bit mode within
+// 32-lane halves: lane' = (lane & 0x10) | 7 and (lane & 0x10) | 15)
+__device__ __forceinline__ float row_lane7(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x10 | (7 << 5)));
+}
+__device__ __forceinline__ float row_lane15(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x10 | (15 << 5)));
 }
 // Orders a prefetch after the last use of the registers it refills: the value
 // is an operand (so it is computed before this point) and memory is clobbered
@@ -123,16 +136,17 @@ __device__ __forceinline__ float sel4(int g, float a0, float a1, float a2, float
 
 }  // namespace
 
-template <int DK, typename Tin, bool FROM_Z>
-__global__ __launch_bounds__(NT) void chunk_tile_kernel(const ChunkArgs a, const int dvs) {
-  using Lds = TileLds<DK>;
+template <int DK, int DVS, typename Tin, bool FROM_Z>
+__global__ __launch_bounds__(NT) void chunk_tile_kernel(const ChunkArgs a) {
+  using Lds = TileLds<DK, DVS>;
   constexpr int NCT = Lds::NCT, NP = Lds::NP;
   constexpr int CPW = (NCT + 3) / 4;  // key tiles per key wavefront
+  constexpr int VPL = DVS / 16;       // values per key-role lane per tile
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  Lds* lds = reinterpret_cast<Lds*>(smem);                         // two copies, by tile parity
-  float* lsol = reinterpret_cast<float*>(smem + 2 * sizeof(Lds));  // [4][16][16]: each state wavefront's L
+  Lds* lds = reinterpret_cast<Lds*>(smem);                         // three copies, by tile index mod 3
+  float* lsol = reinterpret_cast<float*>(smem + 3 * sizeof(Lds));  // [16][16]: stage 2's L
 
-  const int nsl = a.dv / dvs;
+  const int nsl = a.dv / DVS;
   const int sl = blockIdx.x % nsl;
   const int bh = blockIdx.x / nsl;
   const int h = bh % a.H;
@@ -143,10 +157,13 @@ __global__ __launch_bounds__(NT) void chunk_tile_kernel(const ChunkArgs a, const
   const bool key_role = w < 4;
   const int kw = w, sw = w - 4;  // index within the role
   const bool key_wave = key_role && kw < NP;
-  const bool state_wave = !key_role && sw < dvs / 16;
-  const int jcol = sl * dvs + 16 * sw + li;  // state role: this lane's value column
+  const bool state_wave = !key_role && sw < DVS / 16;
+  // stage 2 runs on an idle state slot's SIMD when there is one (wavefront w sits on
+  // SIMD w mod 4), else on a ninth wavefront
+  const int solve_w = DVS < 64 ? 7 : 8;
   const bool norm = a.prologue;
   const int ntiles = (a.T + 15) / 16;
+  const int last_t0 = 16 * (ntiles - 1);
 
   const Tin* q = static_cast<const Tin*>(a.q);
   const Tin* k = static_cast<const Tin*>(a.k);
@@ -158,77 +175,64 @@ __global__ __launch_bounds__(NT) void chunk_tile_kernel(const ChunkArgs a, const
   const int64_t seq0 = static_cast<int64_t>(b) * a.T;  // first token row of this sequence
   const float gmin_l2e = a.g_min * kLog2e;
 
-  // ---- key role: exp(A) log2 e of this lane's channels, prefetched inputs of its next tile
-  float eal[CPW][4];
-#pragma unroll
-  for (int m = 0; m < CPW; ++m)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int ct = kw + 4 * m;
-      eal[m][r] = (FROM_Z && key_wave && ct < NCT) ? __expf(a.A[h * DK + 16 * ct + 4 * lg + r]) * kLog2e : 0.f;
-    }
-  typename Row4<Tin>::raw rk_[CPW], rq_[CPW], rz_[CPW];
-  f32x4 rg_[CPW], rgp_[CPW];
-  typename One<Tin>::raw rb_;
-  // Loads are unconditional (rows clamped into the sequence, key tiles into range,
-  // the last tile fetched again at the end): a load under a branch would make the
-  // compiler copy its result at the join and wait for it there.
-  auto fetch_key = [&](int t0) __attribute__((always_inline)) {
-    const int n = min(16, a.T - t0);
-    const int64_t row = seq0 + t0 + min(li, n - 1);
-#pragma unroll
-    for (int m = 0; m < CPW; ++m) {
-      const int ct = min(kw + 4 * m, NCT - 1);
-      const int64_t e = (row * a.H + h) * DK + 16 * ct + 4 * lg;
-      rk_[m] = Row4<Tin>::load(k + e);
-      rq_[m] = Row4<Tin>::load(q + e);
-      if (FROM_Z) {
-        rz_[m] = Row4<Tin>::load(z + e);
-      } else {
-        // the sum through the token before the tile (same chunk; row t0 - 1 read at t0 = 0
-        // is the tile's own first row, and unused)
-        rg_[m] = *reinterpret_cast<const f32x4*>(a.G + e);
-        rgp_[m] = *reinterpret_cast<const f32x4*>(a.G + e - static_cast<int64_t>(min(li, n - 1) + (t0 > 0)) * HDK);
-      }
-    }
-    rb_ = One<Tin>::load(beta + row * a.H + h);
-  };
-
-  // ---- state role: rows 16 ct + 4 lg + r of column jcol; prefetched values of its next tile
-  const int64_t soff = static_cast<int64_t>(bh) * DK * a.dv + static_cast<int64_t>(4 * lg) * a.dv + jcol;
-  f32x4 S[NCT];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      S[ct][r] = (state_wave && a.S_in) ? a.S_in[soff + static_cast<int64_t>(16 * ct + r) * a.dv] : 0.f;
-  typename One<Tin>::raw rv_[4];
-  auto fetch_v = [&](int t0) __attribute__((always_inline)) {
-    const int n = min(16, a.T - t0);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int64_t vr = seq0 + t0 + min(4 * lg + t, n - 1);
-      rv_[t] = One<Tin>::load(v + vr * HDV + static_cast<int64_t>(h) * a.dv + jcol);
-    }
-  };
-  // Barrier n closes step n: the key role forms tile n before it, the state role
-  // consumes tile n - 1 before it.  Each role runs its own loop (so no prefetched
-  // register crosses a branch), ntiles + 1 barriers in every wavefront.
-  const int last_t0 = 16 * (ntiles - 1);
   if (key_role) {
-    if (ntiles > 0) fetch_key(0);
-    for (int it = 0; it < ntiles; ++it) {
-      Lds& cur = lds[it & 1];
+    // ---- stage 1: key wavefront kw holds key tiles kw and kw + 4 (< NCT by construction)
+    float eal[CPW][4];  // exp(A) log2 e of this lane's channels
+#pragma unroll
+    for (int m = 0; m < CPW; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ct = kw + 4 * m;
+        eal[m][r] = (FROM_Z && key_wave && ct < NCT) ? __expf(a.A[h * DK + 16 * ct + 4 * lg + r]) * kLog2e : 0.f;
+      }
+    // values: lane kw * 64 + l loads VPL consecutive columns of token (kw * 64 + l) / 16
+    const int vq = 64 * kw + l;
+    const int vtok = vq >> 4, vc0 = (vq & 15) * VPL;
+    // Inputs are fetched one tile ahead.  Loads are unconditional (rows clamped into
+    // the sequence, key tiles into range, the last tile fetched again at the end): a
+    // load under a branch would make the compiler copy its result at the join and
+    // wait for it there.
+    struct In {
+      typename Row4<Tin>::raw k[CPW], q[CPW], z[CPW];
+      f32x4 g[CPW], gp[CPW];
+      typename One<Tin>::raw b, v[VPL];
+    };
+    auto fetch = [&](In& R, int t0) __attribute__((always_inline)) {
+      const int n = min(16, a.T - t0);
+      const int64_t row = seq0 + t0 + min(li, n - 1);
+#pragma unroll
+      for (int m = 0; m < CPW; ++m) {
+        const int ct = min(kw + 4 * m, NCT - 1);
+        const int64_t e = (row * a.H + h) * DK + 16 * ct + 4 * lg;
+        R.k[m] = Row4<Tin>::load(k + e);
+        R.q[m] = Row4<Tin>::load(q + e);
+        if (FROM_Z) {
+          R.z[m] = Row4<Tin>::load(z + e);
+        } else {
+          // G through the token before the tile (same chunk; at t0 = 0 the tile's own
+          // first row is read, and unused)
+          R.g[m] = *reinterpret_cast<const f32x4*>(a.G + e);
+          R.gp[m] = *reinterpret_cast<const f32x4*>(a.G + e - static_cast<int64_t>(min(li, n - 1) + (t0 > 0)) * HDK);
+        }
+      }
+      R.b = One<Tin>::load(beta + row * a.H + h);
+      const int64_t vrow = seq0 + t0 + min(vtok, n - 1);
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) R.v[e] = One<Tin>::load(v + vrow * HDV + static_cast<int64_t>(h) * a.dv + sl * DVS + vc0 + e);
+    };
+
+    auto step = [&](In& R, int it) __attribute__((always_inline)) {
+      Lds& cur = lds[it % 3];
       const int t0 = 16 * it;
       const int n = min(16, a.T - t0);
       const bool valid = li < n;
       f32x4 kk[CPW], qq[CPW], gl[CPW];
 #pragma unroll
       for (int m = 0; m < CPW; ++m) {
-        kk[m] = Row4<Tin>::cvt(rk_[m]);
-        qq[m] = Row4<Tin>::cvt(rq_[m]);
+        kk[m] = Row4<Tin>::cvt(R.k[m]);
+        qq[m] = Row4<Tin>::cvt(R.q[m]);
         if (FROM_Z) {
-          const f32x4 zz = Row4<Tin>::cvt(rz_[m]);
+          const f32x4 zz = Row4<Tin>::cvt(R.z[m]);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float g = gate_log2(zz[r], eal[m][r], gmin_l2e);
@@ -236,10 +240,16 @@ __global__ __launch_bounds__(NT) void chunk_tile_kernel(const ChunkArgs a, const
           }
         } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) gl[m][r] = (rg_[m][r] - (t0 % a.chunk != 0 ? rgp_[m][r] : 0.f)) * kLog2e;
+          for (int r = 0; r < 4; ++r) gl[m][r] = (R.g[m][r] - (t0 % a.chunk != 0 ? R.gp[m][r] : 0.f)) * kLog2e;
         }
       }
-      float bval = One<Tin>::cvt(rb_);
+      float bval = One<Tin>::cvt(R.b);
+      float vv[VPL];
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) {
+        vv[e] = vtok < n ? One<Tin>::cvt(R.v[e]) : 0.f;
+        settle(vv[e]);
+      }
 #pragma unroll
       for (int m = 0; m < CPW; ++m) {
         settle(kk[m]);
@@ -247,48 +257,71 @@ __global__ __launch_bounds__(NT) void chunk_tile_kernel(const ChunkArgs a, const
         settle(gl[m]);
       }
       settle(bval);
-      fetch_key(min(t0 + 16, last_t0));
+      fetch(R, min(t0 + 16, last_t0));
       if (norm) bval = sigmoid_fast(bval);
 
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) cur.vt[vc0 + e][vtok] = vv[e];
       if (key_wave) {  // anchored factors, partial L and P, operand tiles into LDS
+        // decay sums and the row broadcasts of the anchor and the tile total first: a
+        // broadcast issued after an LDS write would wait for the write (the LDS counter
+        // is in order)
+        f32x4 g[CPW], anc[CPW], last[CPW];
+#pragma unroll
+        for (int m = 0; m < CPW; ++m)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) g[m][r] = FROM_Z ? row_prefix16(gl[m][r]) : gl[m][r];
+#pragma unroll
+        for (int m = 0; m < CPW; ++m)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            anc[m][r] = row_lane7(g[m][r]);
+            last[m][r] = row_lane15(g[m][r]);
+          }
         f32x4 accL = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
         float ssk = 0.f, ssq = 0.f;
+        f32x4 qgv[CPW], kgv[CPW], khv[CPW], elv[CPW];
 #pragma unroll
         for (int m = 0; m < CPW; ++m) {
-          const int ct = kw + 4 * m;
-          if (ct >= NCT) continue;
-          f32x4 kf, kb, qf, qgv, kgv;
+          f32x4 kf, kb, qf;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float kv = valid ? kk[m][r] : 0.f;
             const float qv = valid ? qq[m][r] : 0.f;
             ssk += kv * kv;
             ssq += qv * qv;
-            const float g = FROM_Z ? row_prefix16(gl[m][r]) : gl[m][r];
-            const float anc = lane_value(g, (l & 48) | 7);
-            const float last = lane_value(g, l | 15);
-            const float f = fast_exp2(g - anc), fi = fast_exp2(anc - g), eg = fast_exp2(g);
+            const float d = g[m][r] - anc[m][r];
+            const float f = fast_exp2(d), fi = fast_exp2(-d), eg = fast_exp2(g[m][r]);
             kf[r] = kv * f;
             kb[r] = kv * fi;
             qf[r] = qv * f;
-            qgv[r] = qv * eg;
-            kgv[r] = -(kv * eg);
-            cur.kh[16 * ct + 4 * lg + r][li] = kv * fast_exp2(last - g);
-            if (li == 0) cur.el[16 * ct + 4 * lg + r] = fast_exp2(last);
+            qgv[m][r] = qv * eg;
+            kgv[m][r] = -(kv * eg);
+            khv[m][r] = kv * fast_exp2(last[m][r] - g[m][r]);
+            elv[m][r] = fast_exp2(last[m][r]);
           }
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             accL = mfma4(kf[r], kb[r], accL);
             accP = mfma4(qf[r], kb[r], accP);
           }
-          cur.qg[ct][l] = qgv;
-          cur.kg[ct][l] = kgv;
+        }
+#pragma unroll
+        for (int m = 0; m < CPW; ++m) {
+          const int ct = kw + 4 * m;
+          cur.qg[ct][l] = qgv[m];
+          cur.kg[ct][l] = kgv[m];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) cur.kh[16 * ct + 4 * lg + r][li] = khv[m][r];
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           cur.lp[kw][0][4 * lg + r][li] = accL[r];
           cur.lp[kw][1][4 * lg + r][li] = accP[r];
         }
+        if (li == 0)
+#pragma unroll
+          for (int m = 0; m < CPW; ++m) *reinterpret_cast<f32x4*>(&cur.el[16 * (kw + 4 * m) + 4 * lg]) = elv[m];
         if (norm) {
           ssk += __shfl_xor(ssk, 16);
           ssk += __shfl_xor(ssk, 32);
@@ -302,69 +335,48 @@ __global__ __launch_bounds__(NT) void chunk_tile_kernel(const ChunkArgs a, const
       }
       if (kw == 0 && lg == 0) cur.beta[li] = valid ? bval : 0.f;
       __syncthreads();
-    }
-    __syncthreads();
-  } else if (state_wave) {
-    if (ntiles > 0) fetch_v(0);
-    __syncthreads();
-    for (int it = 0; it < ntiles; ++it) {
-      const Lds& cur = lds[it & 1];
-      const int t0 = 16 * it;
-      const int n = min(16, a.T - t0);
-      float vin[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        vin[t] = (4 * lg + t < n) ? One<Tin>::cvt(rv_[t]) : 0.f;
-        settle(vin[t]);
-      }
-      fetch_v(min(t0 + 16, last_t0));
+    };
 
-      if (a.S_ckpt && t0 % 64 == 0) {  // backward checkpoint: the state entering this 64-token block
-        float* ck = a.S_ckpt + (static_cast<int64_t>(bh) * ((a.T + 63) / 64) + t0 / 64) * DK * a.dv;
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) ck[(16 * ct + 4 * lg + r) * a.dv + jcol] = S[ct][r];
-      }
-      // prologue norms: rows 4 lg + r (columns of L, P; rows of the products) and token li
-      f32x4 rk4 = {1.f, 1.f, 1.f, 1.f}, rq4 = {1.f, 1.f, 1.f, 1.f};
-      float rk1 = 1.f, rq1 = 1.f;
-      if (norm) {
-        f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sq = {0.f, 0.f, 0.f, 0.f};
-        float s1k = 0.f, s1q = 0.f;
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-          sk += *reinterpret_cast<const f32x4*>(&cur.nrm[p][0][4 * lg]);
-          sq += *reinterpret_cast<const f32x4*>(&cur.nrm[p][1][4 * lg]);
-          s1k += cur.nrm[p][0][li];
-          s1q += cur.nrm[p][1][li];
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          rk4[r] = rsqrt_fast(sk[r] + kL2Eps);
-          rq4[r] = rsqrt_fast(sq[r] + kL2Eps);
-        }
-        rk1 = rsqrt_fast(s1k + kL2Eps);
-        rq1 = rsqrt_fast(s1q + kL2Eps);
-      }
-      // (-K 2^Gl) S and (Q 2^Gl) S: lane (t, g) supplies token t's channels 16 ct + 4 g + r
-      f32x4 y = {0.f, 0.f, 0.f, 0.f}, oacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const f32x4 kgv = cur.kg[ct][l];
-        const f32x4 qgv = cur.qg[ct][l];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          y = mfma4(kgv[r], S[ct][r], y);
-          oacc = mfma4(qgv[r], S[ct][r], oacc);
-        }
-      }
-      // L and P, row li, columns 4 lg .. 4 lg + 3, summed over the key tiles in a fixed order
+    In R;
+    if (ntiles > 0) fetch(R, 0);
+    for (int it = 0; it < ntiles; ++it) step(R, it);
+    __syncthreads();
+    __syncthreads();
+  } else if (w == solve_w) {
+    // ---- stage 2 on tile m at step m + 1: L and P summed over the key parts and
+    // masked, X = (I + L)^-1 row by row, Tm = X Diag(beta); Tm, P and the prologue's
+    // norms into LDS.  This wavefront shares its SIMD with others and would lose most
+    // issue cycles to them (older wavefronts issue first): it runs at the highest
+    // issue priority.
+    __builtin_amdgcn_s_setprio(3);
+    __syncthreads();
+    for (int m = 0; m < ntiles; ++m) {
+      Lds& cur = lds[m % 3];
       f32x4 Lr = {0.f, 0.f, 0.f, 0.f}, Pr = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         Lr += *reinterpret_cast<const f32x4*>(&cur.lp[p][0][li][4 * lg]);
         Pr += *reinterpret_cast<const f32x4*>(&cur.lp[p][1][li][4 * lg]);
+      }
+      f32x4 rk4 = {1.f, 1.f, 1.f, 1.f};
+      float rk1 = 1.f, rq1 = 1.f;
+      if (norm) {
+        f32x4 sk = {0.f, 0.f, 0.f, 0.f};
+        float s1k = 0.f, s1q = 0.f;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          sk += *reinterpret_cast<const f32x4*>(&cur.nrm[p][0][4 * lg]);
+          s1k += cur.nrm[p][0][li];
+          s1q += cur.nrm[p][1][li];
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rk4[r] = rsqrt_fast(sk[r] + kL2Eps);
+        rk1 = rsqrt_fast(s1k + kL2Eps);
+        rq1 = rsqrt_fast(s1q + kL2Eps);
+        if (lg == 0) {
+          cur.rk[li] = rk1;
+          cur.rq[li] = rq1;
+        }
       }
       const float bt = cur.beta[li];
       const f32x4 bs4 = *reinterpret_cast<const f32x4*>(&cur.beta[4 * lg]);
@@ -374,44 +386,97 @@ __global__ __launch_bounds__(NT) void chunk_tile_kernel(const ChunkArgs a, const
         Lr[r] = s < li ? bt * rk1 * Lr[r] * rk4[r] : 0.f;
         Pr[r] = s <= li ? rq1 * Pr[r] * rk4[r] : 0.f;
       }
-      // X = (I + L)^-1, row li: x_j = [j == li] - sum_{m > j} x_m L[m][j], m from 15 down.
-      // L goes through this wavefront's own LDS block (the LDS operations of one
-      // wavefront complete in order), whose rows every lane then reads as one broadcast.
-      float* lw = lsol + 256 * sw;
-      *reinterpret_cast<f32x4*>(lw + 16 * li + 4 * lg) = Lr;
-      float x[16], acc[16];
+      // row li of X: x_j = [j == li] - sum_{m > j} x_m L[m][j], m from 15 down.  With
+      // acc_j started at -[j == li], x_m = -acc_m for every lane (rows above li stay 0).
+      // L goes through LDS (the LDS operations of one wavefront complete in order),
+      // whose rows every lane reads as broadcasts, all before the substitution starts.
+      *reinterpret_cast<f32x4*>(lsol + 16 * li + 4 * lg) = Lr;
+      f32x4 lrow[16][4];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+      for (int mm = 1; mm < 16; ++mm)
 #pragma unroll
-      for (int m = 15; m >= 0; --m) {
-        x[m] = li == m ? 1.f : (li < m ? 0.f : -acc[m]);
+        for (int j4 = 0; j4 < mm; j4 += 4) lrow[mm][j4 / 4] = *reinterpret_cast<const f32x4*>(lsol + 16 * mm + j4);
+      float acc[16];
 #pragma unroll
-        for (int j4 = 0; j4 < m; j4 += 4) {
-          const f32x4 lrow = *reinterpret_cast<const f32x4*>(lw + 16 * m + j4);
+      for (int j = 0; j < 16; ++j) acc[j] = li == j ? -1.f : 0.f;
 #pragma unroll
-          for (int j = j4; j < j4 + 4 && j < m; ++j) acc[j] = fmaf(x[m], lrow[j - j4], acc[j]);
-        }
-      }
+      for (int mm = 15; mm >= 1; --mm)
+#pragma unroll
+        for (int j = 0; j < mm; ++j) acc[j] = fmaf(-acc[mm], lrow[mm][j / 4][j % 4], acc[j]);
       f32x4 tm;  // Tm = X Diag(beta), row li, columns 4 lg + r
 #pragma unroll
-      for (int r = 0; r < 4; ++r) tm[r] = sel4(lg, x[r], x[4 + r], x[8 + r], x[12 + r]) * bs4[r];
-      // Y = V - K 2^Gl S (rows 4 lg + r), then U = Tm Y
-      if (norm) {
+      for (int r = 0; r < 4; ++r) tm[r] = -sel4(lg, acc[r], acc[4 + r], acc[8 + r], acc[12 + r]) * bs4[r];
+      cur.tm[l] = tm;
+      cur.pm[l] = Pr;
+      __syncthreads();
+    }
+    __syncthreads();
+  } else if (state_wave) {
+    // ---- stage 2 (tile it + 1) and stage 3 (tile it) at step it + 2
+    const int jcol = sl * DVS + 16 * sw + li;
+    const int64_t soff = static_cast<int64_t>(bh) * DK * a.dv + static_cast<int64_t>(4 * lg) * a.dv + jcol;
+    f32x4 S[NCT];  // rows 16 ct + 4 lg + r of value column jcol of the state
 #pragma unroll
-        for (int r = 0; r < 4; ++r) y[r] = vin[r] + rk4[r] * y[r];
-      } else {
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) y[r] += vin[r];
+      for (int r = 0; r < 4; ++r) S[ct][r] = a.S_in ? a.S_in[soff + static_cast<int64_t>(16 * ct + r) * a.dv] : 0.f;
+
+    __syncthreads();
+    __syncthreads();
+    for (int it = 0; it < ntiles; ++it) {
+      const Lds& cur = lds[it % 3];
+      const int t0 = 16 * it;
+      const int n = min(16, a.T - t0);
+      if (a.S_ckpt && t0 % 64 == 0) {  // backward checkpoint: the state entering this 64-token block
+        float* ck = a.S_ckpt + (static_cast<int64_t>(bh) * ((a.T + 63) / 64) + t0 / 64) * DK * a.dv;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ck[(16 * ct + 4 * lg + r) * a.dv + jcol] = S[ct][r];
       }
+      // (-K 2^Gl) S and (Q 2^Gl) S: lane (t, g) supplies token t's channels 16 ct + 4 g + r;
+      // two accumulators each (even and odd k steps) halve the dependent chains
+      f32x4 ya[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      f32x4 oa[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const f32x4 kgv = cur.kg[ct][l];
+        const f32x4 qgv = cur.qg[ct][l];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          ya[r & 1] = mfma4(kgv[r], S[ct][r], ya[r & 1]);
+          oa[r & 1] = mfma4(qgv[r], S[ct][r], oa[r & 1]);
+        }
+      }
+      f32x4 y = ya[0] + ya[1], oacc = oa[0] + oa[1];
+      const f32x4 vin = *reinterpret_cast<const f32x4*>(&cur.vt[16 * sw + li][4 * lg]);  // rows 4 lg + r
+      const f32x4 tm = cur.tm[l];
+      const f32x4 pm = cur.pm[l];
+      f32x4 rk4 = {1.f, 1.f, 1.f, 1.f}, rq4 = {1.f, 1.f, 1.f, 1.f};
+      if (norm) {
+        rk4 = *reinterpret_cast<const f32x4*>(&cur.rk[4 * lg]);
+        rq4 = *reinterpret_cast<const f32x4*>(&cur.rq[4 * lg]);
+      }
+      y = vin + rk4 * y;
+      // U = Tm Y (rows 4 lg + r)
       f32x4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int t = 0; t < 4; ++t) u = mfma4(tm[t], y[t], u);
-      // o = scale (Q 2^Gl S + P U), rows 4 lg + r
+      // S <- Diag(2^Gl_15) S + (K 2^(Gl_15 - Gl))^T U
+      const f32x4 uk = u * rk4;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const f32x4 el4 = *reinterpret_cast<const f32x4*>(&cur.el[16 * ct + 4 * lg]);
+        const f32x4 khv = *reinterpret_cast<const f32x4*>(&cur.kh[16 * ct + li][4 * lg]);
+        S[ct] *= el4;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) S[ct] = mfma4(khv[t], uk[t], S[ct]);
+      }
+      // o = scale (Q 2^Gl S + P U)
       if (!a.o_skip) {
+        oacc *= rq4;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) oacc[r] *= rq4[r];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) oacc = mfma4(Pr[t], u[t], oacc);
+        for (int t = 0; t < 4; ++t) oacc = mfma4(pm[t], u[t], oacc);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 4 * lg + r;
@@ -424,35 +489,23 @@ __global__ __launch_bounds__(NT) void chunk_tile_kernel(const ChunkArgs a, const
           }
         }
       }
-      // S <- Diag(2^Gl_15) S + (K 2^(Gl_15 - Gl))^T U
-#pragma unroll
-      for (int r = 0; r < 4; ++r) u[r] *= rk4[r];
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const f32x4 el4 = *reinterpret_cast<const f32x4*>(&cur.el[16 * ct + 4 * lg]);
-        const f32x4 khv = *reinterpret_cast<const f32x4*>(&cur.kh[16 * ct + li][4 * lg]);
-        S[ct] *= el4;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) S[ct] = mfma4(khv[t], u[t], S[ct]);
-      }
       __syncthreads();
     }
+    if (a.S_out) {
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) a.S_out[soff + static_cast<int64_t>(16 * ct + r) * a.dv] = S[ct][r];
+    }
   } else {
-    for (int it = 0; it <= ntiles; ++it) __syncthreads();
-  }
-
-  if (state_wave && a.S_out) {
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) a.S_out[soff + static_cast<int64_t>(16 * ct + r) * a.dv] = S[ct][r];
+    for (int it = 0; it < ntiles + 2; ++it) __syncthreads();
   }
 }
 
 namespace {
 
-// Value columns per workgroup: 64 (one 16-column block per wavefront), halved
-// while the grid has fewer workgroups than compute units, down to 16.
+// Value columns per workgroup: 64 (one 16-column block per state wavefront),
+// halved while the grid has fewer workgroups than compute units, down to 16.
 int tile_slice_cols(const ChunkArgs& a) {
   int dvs = a.dv < 64 ? a.dv : 64;
   const int64_t bh = static_cast<int64_t>(a.B) * a.H;
@@ -460,24 +513,34 @@ int tile_slice_cols(const ChunkArgs& a) {
   return dvs;
 }
 
-template <int DK, typename Tin, bool FROM_Z>
-hipError_t launch_tile_t(const ChunkArgs& a, hipStream_t st, int dvs) {
+template <int DK, int DVS, typename Tin, bool FROM_Z>
+hipError_t launch_tile_t(const ChunkArgs& a, hipStream_t st) {
   static std::atomic<uint64_t> lds_set{0};
-  auto kern = chunk_tile_kernel<DK, Tin, FROM_Z>;
-  const int bytes = 2 * static_cast<int>(sizeof(TileLds<DK>)) + 4 * 256 * 4;
+  auto kern = chunk_tile_kernel<DK, DVS, Tin, FROM_Z>;
+  const int bytes = 3 * static_cast<int>(sizeof(TileLds<DK, DVS>)) + 256 * 4;
   const hipError_t e = set_lds_limit(reinterpret_cast<const void*>(kern), bytes, lds_set);
   if (e != hipSuccess) return e;
-  const int64_t nblocks = static_cast<int64_t>(a.B) * a.H * (a.dv / dvs);
+  const int64_t nblocks = static_cast<int64_t>(a.B) * a.H * (a.dv / DVS);
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(nblocks)), dim3(NT), bytes, st, a, dvs);
+  hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(nblocks)), dim3(NT), bytes, st, a);
   return hipGetLastError();
 }
 
-template <int DK>
-hipError_t launch_tile_k(const ChunkArgs& a, hipStream_t st, int dvs) {
+template <int DK, int DVS>
+hipError_t launch_tile_v(const ChunkArgs& a, hipStream_t st) {
   if (a.in_bf16)
-    return a.from_z ? launch_tile_t<DK, bf16_t, true>(a, st, dvs) : launch_tile_t<DK, bf16_t, false>(a, st, dvs);
-  return a.from_z ? launch_tile_t<DK, float, true>(a, st, dvs) : launch_tile_t<DK, float, false>(a, st, dvs);
+    return a.from_z ? launch_tile_t<DK, DVS, bf16_t, true>(a, st) : launch_tile_t<DK, DVS, bf16_t, false>(a, st);
+  return a.from_z ? launch_tile_t<DK, DVS, float, true>(a, st) : launch_tile_t<DK, DVS, float, false>(a, st);
+}
+
+template <int DK>
+hipError_t launch_tile_k(const ChunkArgs& a, hipStream_t st) {
+  switch (tile_slice_cols(a)) {
+    case 16: return launch_tile_v<DK, 16>(a, st);
+    case 32: return launch_tile_v<DK, 32>(a, st);
+    case 64: return launch_tile_v<DK, 64>(a, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -485,12 +548,11 @@ hipError_t launch_tile_k(const ChunkArgs& a, hipStream_t st, int dvs) {
 hipError_t launch_chunk_generic(const ChunkArgs& a, hipStream_t st) {
   if (static_cast<int64_t>(a.B) * a.H == 0) return hipSuccess;
   if (a.dv % 16 || a.dv < 16 || a.dv > 128) return hipErrorInvalidValue;
-  const int dvs = tile_slice_cols(a);
   switch (a.dk) {
-    case 16: return launch_tile_k<16>(a, st, dvs);
-    case 32: return launch_tile_k<32>(a, st, dvs);
-    case 64: return launch_tile_k<64>(a, st, dvs);
-    case 128: return launch_tile_k<128>(a, st, dvs);
+    case 16: return launch_tile_k<16>(a, st);
+    case 32: return launch_tile_k<32>(a, st);
+    case 64: return launch_tile_k<64>(a, st);
+    case 128: return launch_tile_k<128>(a, st);
   }
   return hipErrorInvalidValue;
 }
