@@ -34,6 +34,7 @@ if ROOT not in sys.path:
 METRIC = "KDA chunked-prefill tokens/sec/GPU (H=32,d=128,T=32K); decode tokens/sec"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP32_MFMA_PEAK_TFLOPS = 157.3  # dense fp32 matrix-core peak of the MI355X
 # Algorithmic work per token-head of the chunked prefill at d = 128, chunk 64:
 # 2 * [3 * d_k * d_v + C * (1.5 d_k + d_v)] flops (W S, Q S, K^T U; L, P, T K;
 # T V and P U), and bytes: q, k, v, z (bf16) + beta (bf16) + o (bf16).
@@ -350,9 +351,11 @@ def main():
         log(f"small configurations: {small}")
 
     # ---------------- other supported shapes (reported beside the step) ----------------
-    # Shapes outside the matrix-core kernel's (bf16, d_k = d_v = 128, chunk 64) run the fp32
-    # vector-ALU kernel: bf16 with smaller heads or chunk 16, and fp32 inputs.  B=4, H=32,
-    # T=4096, fused gate; bytes per token-head: q, k, z and v, beta in, o out.
+    # Shapes outside the bf16 matrix-core kernel's (d_k = d_v = 128, chunk 64) run the fp32
+    # matrix-core tile kernel: bf16 with smaller heads or chunk 16, and fp32 inputs.  B=4,
+    # H=32, T=4096, fused gate; bytes per token-head: q, k, z and v, beta in, o out; fp32
+    # flops per token-head of its products: L and P (16 d_k each), (K 2^Gl) S, (Q 2^Gl) S
+    # and the state update (d_k d_v each), U and P U (16 d_v each), as multiply-adds.
     other = None
     if run_pre and not args.no_extras:
         other = {}
@@ -373,8 +376,11 @@ def main():
                                                       stream=stream), 10))
             es = 2 if dtype == "bf16" else 4
             nbytes = cs.B * cs.T * cs.H * (es * (3 * cs.dk + 2 * cs.dv) + es) + 2 * cs.B * cs.H * cs.dk * cs.dv * 4
+            flops = cs.B * cs.T * cs.H * 2 * (3 * cs.dk * cs.dv + 32 * (cs.dk + cs.dv))
             other[cs.name] = {"ms": st_["median"], "tokens_per_s": round(cs.B * cs.T / (st_["median"] / 1e3), 1),
                               "frac_hbm": round(nbytes / (st_["median"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                              "fp32_tflops": round(flops / (st_["median"] / 1e3) / 1e12, 2),
+                              "frac_fp32_mfma": round(flops / (st_["median"] / 1e3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
                               "matrix_core_kernel": kda.chunk_uses_mfma(
                                   torch.bfloat16 if dtype == "bf16" else torch.float32, cs.dk, cs.dv, cs.chunk)}
             del C, S0c, oc, Sc, wsc
