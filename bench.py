@@ -384,7 +384,23 @@ def main():
                               "matrix_core_kernel": kda.chunk_uses_mfma(
                                   torch.bfloat16 if dtype == "bf16" else torch.float32, cs.dk, cs.dv, cs.chunk)}
             del C, S0c, oc, Sc, wsc
-        log(f"other shapes (B=4, H=32, T=4096): {other}")
+        # few, long sequences of such a shape: B*H = 8, where kda_chunk_fwd_z cuts each
+        # sequence into segments itself; its one-pass time beside it
+        cs = ki.small_spec(1, 8, 16384, 128, 128, 64, "f32", seed=1600, s0_std=0.01, name="f32_d128x128_B1_H8_T16384")
+        cd = ki.prefill_inputs(cs)
+        C = {k: to_dev(cd[k], "f32") for k in ("q", "k", "v", "z", "beta", "A", "S0")}
+        oc = torch.empty((cs.B, cs.T, cs.H, cs.dv), dtype=torch.float32, device=dev)
+        Sc = torch.empty((cs.B, cs.H, cs.dk, cs.dv), dtype=torch.float32, device=dev)
+        wsc = workspace(cs.B, cs.T, cs.H, cs.dk, cs.dv, cs.chunk)
+        st_ = stats(timed(lambda: kda.chunk_fwd_z(C["q"], C["k"], C["v"], C["beta"], C["z"], C["A"], -5.0, 64,
+                                                  S_in=C["S0"], o=oc, S_out=Sc, workspace=wsc, stream=stream), 10))
+        one = stats(timed(lambda: kda.chunk_fwd_z_segmented(C["q"], C["k"], C["v"], C["beta"], C["z"], C["A"], 1,
+                                                            -5.0, 64, S_in=C["S0"], o=oc, S_out=Sc, stream=stream), 10))
+        other[cs.name] = {"ms": st_["median"], "tokens_per_s": round(cs.B * cs.T / (st_["median"] / 1e3), 1),
+                          "one_pass_ms": one["median"],
+                          "workspace_bytes": 0 if wsc is None else int(wsc.numel())}
+        del C, oc, Sc, wsc
+        log(f"other shapes (B=4, H=32, T=4096; and B=1, H=8, T=16384): {other}")
 
     # ---------------- standalone gate (reported beside the step, not part of it) ----------------
     # kda_gate on the 32K workload: z in (bf16), chunk-local log-decay sums G out (fp32).  The

@@ -179,19 +179,21 @@ int64_t seg_ws_floats(int64_t bh, int64_t nseg, int64_t dk, int64_t dv) {
 // cut into segments ("Kimi K3 reading notes", section 7).  The segment-parallel form
 // does about three passes' work (end states, transitions, then outputs), so it pays
 // only once it multiplies the parallelism well beyond that: here when at least
-// kMinSegs segments of at least kMinSegChunks chunks each fit, with the two
-// 64-column slices per (b, h, segment) of the widest launch filling kFillUnits.
+// kMinSegs segments of at least kMinSegTokens tokens each fit, with the 64-column
+// slices per (b, h, segment) of the widest launch (d_v / 64 of them, at least one)
+// filling kFillUnits.  The rule depends on the sizes only, not on the input dtype
+// (both kernels slice d_v = 128 into two 64-column slices at their widest).
 constexpr int64_t kFillUnits = 256;   // compute units of the MI355X
 constexpr int64_t kMinSegs = 4;
-constexpr int64_t kMinSegChunks = 4;
+constexpr int64_t kMinSegTokens = 256;
 int64_t auto_segments(int64_t B, int64_t T, int64_t H, int dk, int dv, int chunk) {
-  kda::ChunkArgs a{};
-  a.dk = dk; a.dv = dv; a.chunk = chunk; a.in_bf16 = true; a.H = int(H);
-  if (!kda::chunk_mfma_supports(a)) return 1;  // the segment passes exist on the matrix-core path only
+  (void)dk;
   const int64_t bh = B * H, nch = (T + chunk - 1) / chunk;
   if (bh <= 0 || nch <= 0) return 1;
-  int64_t segs = kFillUnits / (2 * bh);
-  segs = segs < nch / kMinSegChunks ? segs : nch / kMinSegChunks;
+  const int64_t per = dv >= 64 ? dv / 64 : 1;
+  const int64_t min_chunks = kMinSegTokens / chunk;
+  int64_t segs = kFillUnits / (per * bh);
+  segs = segs < nch / min_chunks ? segs : nch / min_chunks;
   return segs >= kMinSegs ? segs : 1;
 }
 
@@ -258,13 +260,15 @@ kda_status chunk_common(const void* q, const void* k, const void* v, const void*
   a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = o_dtype == KDA_BF16; a.from_z = from_z;
   a.prologue = prologue;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (!kda::chunk_mfma_supports(a)) {
-    if (!auto_form && lay.nseg > 1) return KDA_ERR_UNSUPPORTED;
-    return from_hip(kda::launch_chunk_generic(a, st));
-  }
+  // bf16, d = 128, chunk 64 on the bf16 matrix-core kernel; every other shape on the
+  // fp32 matrix-core tile kernel
+  const bool mfma = kda::chunk_mfma_supports(a);
+  auto launch = [&](const kda::ChunkArgs& c) {
+    return mfma ? kda::launch_chunk_mfma(c, st) : kda::launch_chunk_generic(c, st);
+  };
   // the segment passes take the fused gate without the prologue; the automatic form
   // runs the other variants in one pass
-  if (lay.nseg <= 1 || !from_z || prologue) return from_hip(kda::launch_chunk_mfma(a, st));
+  if (lay.nseg <= 1 || !from_z || prologue) return from_hip(launch(a));
 
   // Segment-parallel form ("Kimi K3 reading notes", section 7): the segments but the
   // last from the zero state (end states St) and from the identity with zero values
@@ -277,15 +281,15 @@ kda_status chunk_common(const void* q, const void* k, const void* v, const void*
   a.seg_chunks = lay.seg_chunks;
   kda::ChunkArgs pa = a;  // pass A: end states from the zero state
   pa.nseg = nseg - 1; pa.S_in = nullptr; pa.S_out = St; pa.S_out_mode = 1; pa.o_skip = true;
-  kda::ChunkArgs pb = pa;  // pass B: transitions (identity entry state, zero values)
-  pb.S_identity = true; pb.v_zero = true; pb.S_out = M;
+  kda::ChunkArgs pb = pa;  // pass B: transitions (identity entry state, zero values, dk columns)
+  pb.S_identity = true; pb.v_zero = true; pb.S_out = M; pb.dv = dk;
   kda::ChunkArgs pc = a;  // pass C: outputs and the final state from the true entry states
   pc.nseg = nseg; pc.S_in = E; pc.S_in_seg = true; pc.S_out_mode = 2;
   const kda::SegScanArgs sa{S_in, St, M, E, int(bh), nseg, dk, dv};
-  hipError_t e = kda::launch_chunk_mfma(pa, st);
-  if (e == hipSuccess) e = kda::launch_chunk_mfma(pb, st);
+  hipError_t e = launch(pa);
+  if (e == hipSuccess) e = launch(pb);
   if (e == hipSuccess) e = kda::launch_segscan(sa, st);
-  if (e == hipSuccess) e = kda::launch_chunk_mfma(pc, st);
+  if (e == hipSuccess) e = launch(pc);
   return from_hip(e);
 }
 

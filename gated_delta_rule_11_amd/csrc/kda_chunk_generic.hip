@@ -146,9 +146,11 @@ __global__ __launch_bounds__(NT) void chunk_tile_kernel(const ChunkArgs a) {
   Lds* lds = reinterpret_cast<Lds*>(smem);                         // three copies, by tile index mod 3
   float* lsol = reinterpret_cast<float*>(smem + 3 * sizeof(Lds));  // [16][16]: stage 2's L
 
+  // workgroup -> ((b*H + h) * nseg + segment, slice)
   const int nsl = a.dv / DVS;
   const int sl = blockIdx.x % nsl;
-  const int bh = blockIdx.x / nsl;
+  const int bhs = blockIdx.x / nsl;
+  const int bh = bhs / a.nseg, sg = bhs % a.nseg;
   const int h = bh % a.H;
   const int b = bh / a.H;
   const int w = threadIdx.x >> 6;
@@ -162,8 +164,12 @@ __global__ __launch_bounds__(NT) void chunk_tile_kernel(const ChunkArgs a) {
   // SIMD w mod 4), else on a ninth wavefront
   const int solve_w = DVS < 64 ? 7 : 8;
   const bool norm = a.prologue;
-  const int ntiles = (a.T + 15) / 16;
-  const int last_t0 = 16 * (ntiles - 1);
+  // this workgroup's tokens: segment sg (chunk-aligned, so tile-aligned), or the whole sequence
+  const int64_t seg_len = a.seg_chunks > 0 ? static_cast<int64_t>(a.seg_chunks) * a.chunk : a.T;
+  const int t_begin = static_cast<int>(min(static_cast<int64_t>(sg) * seg_len, static_cast<int64_t>(a.T)));
+  const int t_end = static_cast<int>(min(t_begin + seg_len, static_cast<int64_t>(a.T)));
+  const int ntiles = (t_end - t_begin + 15) / 16;
+  const int last_t0 = t_begin + 16 * (ntiles - 1);
 
   const Tin* q = static_cast<const Tin*>(a.q);
   const Tin* k = static_cast<const Tin*>(a.k);
@@ -197,8 +203,12 @@ __global__ __launch_bounds__(NT) void chunk_tile_kernel(const ChunkArgs a) {
       f32x4 g[CPW], gp[CPW];
       typename One<Tin>::raw b, v[VPL];
     };
+    // values taken as zero (a transition pass) are not read: the loads then go to q,
+    // in range, and their results are dropped
+    const Tin* vsrc = a.v_zero ? q : v;
+    const int64_t vrow_len = a.v_zero ? static_cast<int64_t>(DK) : a.dv;
     auto fetch = [&](In& R, int t0) __attribute__((always_inline)) {
-      const int n = min(16, a.T - t0);
+      const int n = min(16, t_end - t0);
       const int64_t row = seq0 + t0 + min(li, n - 1);
 #pragma unroll
       for (int m = 0; m < CPW; ++m) {
@@ -218,13 +228,14 @@ __global__ __launch_bounds__(NT) void chunk_tile_kernel(const ChunkArgs a) {
       R.b = One<Tin>::load(beta + row * a.H + h);
       const int64_t vrow = seq0 + t0 + min(vtok, n - 1);
 #pragma unroll
-      for (int e = 0; e < VPL; ++e) R.v[e] = One<Tin>::load(v + vrow * HDV + static_cast<int64_t>(h) * a.dv + sl * DVS + vc0 + e);
+      for (int e = 0; e < VPL; ++e)
+        R.v[e] = One<Tin>::load(vsrc + (vrow * a.H + h) * vrow_len + sl * DVS + vc0 + e);
     };
 
     auto step = [&](In& R, int it) __attribute__((always_inline)) {
       Lds& cur = lds[it % 3];
-      const int t0 = 16 * it;
-      const int n = min(16, a.T - t0);
+      const int t0 = t_begin + 16 * it;
+      const int n = min(16, t_end - t0);
       const bool valid = li < n;
       f32x4 kk[CPW], qq[CPW], gl[CPW];
 #pragma unroll
@@ -247,7 +258,7 @@ __global__ __launch_bounds__(NT) void chunk_tile_kernel(const ChunkArgs a) {
       float vv[VPL];
 #pragma unroll
       for (int e = 0; e < VPL; ++e) {
-        vv[e] = vtok < n ? One<Tin>::cvt(R.v[e]) : 0.f;
+        vv[e] = (vtok < n && !a.v_zero) ? One<Tin>::cvt(R.v[e]) : 0.f;
         settle(vv[e]);
       }
 #pragma unroll
@@ -338,7 +349,7 @@ __global__ __launch_bounds__(NT) void chunk_tile_kernel(const ChunkArgs a) {
     };
 
     In R;
-    if (ntiles > 0) fetch(R, 0);
+    if (ntiles > 0) fetch(R, t_begin);
     for (int it = 0; it < ntiles; ++it) step(R, it);
     __syncthreads();
     __syncthreads();
@@ -414,20 +425,24 @@ __global__ __launch_bounds__(NT) void chunk_tile_kernel(const ChunkArgs a) {
   } else if (state_wave) {
     // ---- stage 2 (tile it + 1) and stage 3 (tile it) at step it + 2
     const int jcol = sl * DVS + 16 * sw + li;
-    const int64_t soff = static_cast<int64_t>(bh) * DK * a.dv + static_cast<int64_t>(4 * lg) * a.dv + jcol;
+    const int64_t soff = static_cast<int64_t>(4 * lg) * a.dv + jcol;  // within one state
+    const int64_t sin_base = static_cast<int64_t>(a.S_in_seg ? bhs : bh) * DK * a.dv;
     f32x4 S[NCT];  // rows 16 ct + 4 lg + r of value column jcol of the state
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) S[ct][r] = a.S_in ? a.S_in[soff + static_cast<int64_t>(16 * ct + r) * a.dv] : 0.f;
+      for (int r = 0; r < 4; ++r)
+        S[ct][r] = a.S_identity ? (16 * ct + 4 * lg + r == jcol ? 1.f : 0.f)
+                   : a.S_in     ? a.S_in[sin_base + soff + static_cast<int64_t>(16 * ct + r) * a.dv]
+                                : 0.f;
 
     __syncthreads();
     __syncthreads();
     for (int it = 0; it < ntiles; ++it) {
       const Lds& cur = lds[it % 3];
-      const int t0 = 16 * it;
-      const int n = min(16, a.T - t0);
-      if (a.S_ckpt && t0 % 64 == 0) {  // backward checkpoint: the state entering this 64-token block
+      const int t0 = t_begin + 16 * it;
+      const int n = min(16, t_end - t0);
+      if (a.S_ckpt && t0 % 64 == 0) {  // backward checkpoint (one segment): the state entering this 64-token block
         float* ck = a.S_ckpt + (static_cast<int64_t>(bh) * ((a.T + 63) / 64) + t0 / 64) * DK * a.dv;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
@@ -491,11 +506,13 @@ __global__ __launch_bounds__(NT) void chunk_tile_kernel(const ChunkArgs a) {
       }
       __syncthreads();
     }
-    if (a.S_out) {
+    // final state: per (b, h); per (b, h, segment); or from the last segment only
+    if (a.S_out && (a.S_out_mode != 2 || sg == a.nseg - 1)) {
+      const int64_t sout_base = static_cast<int64_t>(a.S_out_mode == 1 ? bhs : bh) * DK * a.dv;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) a.S_out[soff + static_cast<int64_t>(16 * ct + r) * a.dv] = S[ct][r];
+        for (int r = 0; r < 4; ++r) a.S_out[sout_base + soff + static_cast<int64_t>(16 * ct + r) * a.dv] = S[ct][r];
     }
   } else {
     for (int it = 0; it < ntiles + 2; ++it) __syncthreads();
@@ -508,8 +525,8 @@ namespace {
 // halved while the grid has fewer workgroups than compute units, down to 16.
 int tile_slice_cols(const ChunkArgs& a) {
   int dvs = a.dv < 64 ? a.dv : 64;
-  const int64_t bh = static_cast<int64_t>(a.B) * a.H;
-  while (dvs > 16 && bh * (a.dv / dvs) < 256) dvs /= 2;
+  const int64_t units = static_cast<int64_t>(a.B) * a.H * a.nseg;  // (b, h, segment)
+  while (dvs > 16 && units * (a.dv / dvs) < 256) dvs /= 2;
   return dvs;
 }
 
@@ -520,7 +537,7 @@ hipError_t launch_tile_t(const ChunkArgs& a, hipStream_t st) {
   const int bytes = 3 * static_cast<int>(sizeof(TileLds<DK, DVS>)) + 256 * 4;
   const hipError_t e = set_lds_limit(reinterpret_cast<const void*>(kern), bytes, lds_set);
   if (e != hipSuccess) return e;
-  const int64_t nblocks = static_cast<int64_t>(a.B) * a.H * (a.dv / DVS);
+  const int64_t nblocks = static_cast<int64_t>(a.B) * a.H * a.nseg * (a.dv / DVS);
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(nblocks)), dim3(NT), bytes, st, a);
   return hipGetLastError();
@@ -546,7 +563,8 @@ hipError_t launch_tile_k(const ChunkArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_chunk_generic(const ChunkArgs& a, hipStream_t st) {
-  if (static_cast<int64_t>(a.B) * a.H == 0) return hipSuccess;
+  if (static_cast<int64_t>(a.B) * a.H * a.nseg == 0) return hipSuccess;
+  if (a.S_identity && a.dv != a.dk) return hipErrorInvalidValue;
   if (a.dv % 16 || a.dv < 16 || a.dv > 128) return hipErrorInvalidValue;
   switch (a.dk) {
     case 16: return launch_tile_k<16>(a, st);

@@ -8,11 +8,11 @@
 // Layouts: St [BH, nseg - 1, dk, dv] and M [BH, nseg - 1, dk, dk] (the last
 // segment's are never needed), E [BH, nseg, dk, dv].
 //
-// One workgroup per (b, h, 16-column block of the state), eight wavefronts, one
-// 16-row tile of the block each.  Each step is a 128-deep product on fp32
+// One workgroup per (b, h, 16-column block of the state), dk / 16 wavefronts,
+// one 16-row tile of the block each.  Each step is a dk-deep product on fp32
 // matrix cores (v_mfma_f32_16x16x4_f32): the wavefront's rows of M_p from global
 // memory (fetched during the previous step), the column block of E_p from LDS,
-// where it is kept transposed (column-major) so that each lane reads its 32
+// where it is kept transposed (column-major) so that each lane reads its dk / 4
 // contiguous k values with 16-byte reads; two LDS copies alternate, so a step
 // has one barrier.  The steps are sequential; the loads of step p + 1 are in
 // flight during step p.
@@ -22,19 +22,20 @@
 namespace kda {
 
 constexpr int kScanCols = 16;
-constexpr int kScanEtStride = 128 + 4;  // floats per transposed column (16-byte aligned rows)
 
-__global__ __launch_bounds__(512) void segscan_kernel(const float* __restrict__ S_in, const float* __restrict__ St,
-                                                       const float* __restrict__ M, float* __restrict__ E, int nseg,
-                                                       int dv) {
-  constexpr int DK = 128;
+template <int DK>
+__global__ __launch_bounds__(DK * 4) void segscan_kernel(const float* __restrict__ S_in, const float* __restrict__ St,
+                                                          const float* __restrict__ M, float* __restrict__ E, int nseg,
+                                                          int dv) {
+  constexpr int ES = DK + 4;  // floats per transposed column (16-byte aligned rows)
+  constexpr int KQ = DK / 16;  // 16-byte groups of k per lane
   const int ncb = dv / kScanCols;
   const int bh = blockIdx.x / ncb;
   const int c0 = (blockIdx.x % ncb) * kScanCols;
   const int w = threadIdx.x >> 6;  // row tile: rows 16 w .. 16 w + 15
   const int l = threadIdx.x & 63;
   const int lr = l & 15, lg = l >> 4;
-  __shared__ __attribute__((aligned(16))) float ET[2][kScanCols][kScanEtStride];
+  __shared__ __attribute__((aligned(16))) float ET[2][kScanCols][ES];
 
   const int64_t sz = static_cast<int64_t>(DK) * dv;
   // this lane's four outputs of the tile: rows 16 w + 4 lg + v, column c0 + lr
@@ -43,13 +44,14 @@ __global__ __launch_bounds__(512) void segscan_kernel(const float* __restrict__ 
 #pragma unroll
   for (int v = 0; v < 4; ++v) e[v] = S_in ? S_in[bh * sz + out0 + static_cast<int64_t>(v) * dv] : 0.f;
 
-  // A operands of step p: M_p[16 w + lr][32 lg + kk], kk = 0..31; B: E_p[32 lg + kk][c0 + lr]
-  f32x4 a_nx[8], s_nx;
+  // A operands of step p: M_p[16 w + lr][(DK / 4) lg + kk], kk < DK / 4; B: E_p[(DK / 4) lg + kk][c0 + lr]
+  f32x4 a_nx[KQ], s_nx;
   auto fetch = [&](int p) __attribute__((always_inline)) {
     const int64_t sm = static_cast<int64_t>(bh) * (nseg - 1) + p;
-    const f32x4* mr = reinterpret_cast<const f32x4*>(M + sm * DK * DK + static_cast<int64_t>(16 * w + lr) * DK + 32 * lg);
+    const f32x4* mr =
+        reinterpret_cast<const f32x4*>(M + sm * DK * DK + static_cast<int64_t>(16 * w + lr) * DK + (DK / 4) * lg);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) a_nx[q] = mr[q];
+    for (int q = 0; q < KQ; ++q) a_nx[q] = mr[q];
 #pragma unroll
     for (int v = 0; v < 4; ++v) s_nx[v] = St[sm * sz + out0 + static_cast<int64_t>(v) * dv];
   };
@@ -61,22 +63,22 @@ __global__ __launch_bounds__(512) void segscan_kernel(const float* __restrict__ 
     for (int v = 0; v < 4; ++v) E[seg * sz + out0 + static_cast<int64_t>(v) * dv] = e[v];
     if (p + 1 == nseg) break;
     // E_p's column block, transposed, into this step's LDS copy
-    float(*et)[kScanEtStride] = ET[p & 1];
+    float(*et)[ES] = ET[p & 1];
     *reinterpret_cast<f32x4*>(&et[lr][16 * w + 4 * lg]) = e;
     __syncthreads();
-    f32x4 a[8];
+    f32x4 a[KQ];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) a[q] = a_nx[q];
+    for (int q = 0; q < KQ; ++q) a[q] = a_nx[q];
     const f32x4 st = s_nx;
     if (p + 2 < nseg) fetch(p + 1);
-    const f32x4* br = reinterpret_cast<const f32x4*>(&et[lr][32 * lg]);
-    // four independent accumulators (k = 32 lg + 4 q + u by u) shorten the dependent
+    const f32x4* br = reinterpret_cast<const f32x4*>(&et[lr][(DK / 4) * lg]);
+    // four independent accumulators (k = (DK / 4) lg + 4 q + u by u) shorten the dependent
     // chain of products four times; they are summed at the end, in a fixed order
     f32x4 acc[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < KQ; ++q) {
       const f32x4 b = br[q];
 #pragma unroll
       for (int u = 0; u < 4; ++u) acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q][u], b[u], acc[u], 0, 0, 0);
@@ -85,13 +87,24 @@ __global__ __launch_bounds__(512) void segscan_kernel(const float* __restrict__ 
   }
 }
 
+template <int DK>
+static hipError_t launch_segscan_k(const SegScanArgs& a, hipStream_t st, int64_t nwg) {
+  hipLaunchKernelGGL(segscan_kernel<DK>, dim3(static_cast<uint32_t>(nwg)), dim3(DK * 4), 0, st, a.S_in, a.St, a.M,
+                     a.E, a.nseg, a.dv);
+  return hipGetLastError();
+}
+
 hipError_t launch_segscan(const SegScanArgs& a, hipStream_t st) {
-  if (a.dk != 128 || a.dv % kScanCols) return hipErrorNotSupported;
+  if (a.dv % kScanCols) return hipErrorNotSupported;
   const int64_t nwg = static_cast<int64_t>(a.BH) * (a.dv / kScanCols);
   if (nwg == 0 || a.nseg < 1) return hipSuccess;
-  hipLaunchKernelGGL(segscan_kernel, dim3(static_cast<uint32_t>(nwg)), dim3(512), 0, st, a.S_in, a.St, a.M, a.E,
-                     a.nseg, a.dv);
-  return hipGetLastError();
+  switch (a.dk) {
+    case 16: return launch_segscan_k<16>(a, st, nwg);
+    case 32: return launch_segscan_k<32>(a, st, nwg);
+    case 64: return launch_segscan_k<64>(a, st, nwg);
+    case 128: return launch_segscan_k<128>(a, st, nwg);
+  }
+  return hipErrorNotSupported;
 }
 
 }  // namespace kda

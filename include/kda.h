@@ -76,9 +76,10 @@ const char* kda_status_string(int status);
  * takes a workspace and the status codes are negative. */
 int kda_version(void);
 
-/* 1 when kda_chunk_fwd / kda_chunk_fwd_z run the MFMA kernel (bf16 matrix
- * products with fp32 accumulation) for these arguments, 0 when they run the
- * fp32 vector-ALU kernel.  Pure query: touches no device. */
+/* 1 when kda_chunk_fwd / kda_chunk_fwd_z run the bf16 matrix-core kernel
+ * (bf16 matrix products with fp32 accumulation) for these arguments, 0 when
+ * they run the fp32 matrix-core tile kernel (fp32 products throughout).  Pure
+ * query: touches no device. */
 int kda_chunk_uses_mfma(kda_dtype in_dtype, int dk, int dv, int chunk);
 
 /*
@@ -109,11 +110,10 @@ kda_status kda_gate(const void* z, kda_dtype z_dtype, const float* A,
  * Pure host computation; negative or zero-sized arguments give 0.
  *
  * The library picks the launch form from the sizes alone: one pass over the
- * sequence when B*H alone fills the GPU, otherwise (few, long sequences on the
- * matrix-core path, fused gate) the segment-parallel form of "Kimi K3 reading
- * notes", section 7, whose per-segment end states, transitions and entry
- * states live in the workspace.  Both forms give the same result within the
- * stated tolerance.
+ * sequence when B*H alone fills the GPU, otherwise (few, long sequences, fused
+ * gate) the segment-parallel form of "Kimi K3 reading notes", section 7, whose
+ * per-segment end states, transitions and entry states live in the workspace.
+ * Both forms give the same result within the stated tolerance.
  */
 size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk);
 
@@ -130,8 +130,8 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int ch
  *
  *   q, k   [B,T,H,dk] in_dtype     v [B,T,H,dv] in_dtype     beta [B,T,H] in_dtype
  *   G      [B,T,H,dk] fp32 chunk-local sums (chunk must match kda_gate's).
- *          On the matrix-core path (kda_chunk_uses_mfma) every channel's
- *          log-decay over any aligned 16-token tile, G at the tile's last
+ *          Every channel's log-decay over any aligned 16-token tile (both
+ *          kernels anchor their decay factors per tile), G at the tile's last
  *          token minus G before its first, must be at least -86.4: the
  *          tile's decay must be a normal fp32 number and its reciprocal
  *          finite.  G from kda_gate with g_min >= -5.4 always is; the
@@ -275,8 +275,8 @@ kda_status kda_chunk_bwd_z(const void* q, const void* k, const void* v, const vo
 /*
  * kda_chunk_fwd_z_segmented -- kda_chunk_fwd_z for few, long sequences.
  *
- * Same inputs, outputs and result as kda_chunk_fwd_z (within the bf16
- * tolerance: the arithmetic is regrouped).  The sequence is cut into
+ * Same inputs, outputs and result as kda_chunk_fwd_z (within the stated
+ * tolerance of the input dtype: the arithmetic is regrouped).  The sequence is cut into
  * `segments` chunk-aligned segments that run in parallel, using the fragment
  * decomposition of "Kimi K3 reading notes", section 7: each segment from the
  * zero state gives its end state S~_p; from the identity with zero values, its
@@ -286,10 +286,8 @@ kda_status kda_chunk_bwd_z(const void* q, const void* k, const void* v, const vo
  * pass, for `segments` times the parallelism: the form for small B*H and long
  * T (a million tokens on 8 heads), where one pass leaves most of the GPU idle.
  *
- * Applies to the MFMA shape (bf16 inputs, dk = dv = 128, chunk 64; see
- * kda_chunk_uses_mfma); other shapes return KDA_ERR_UNSUPPORTED when
- * segments > 1.  segments == 1, or T within one segment's length, runs the
- * plain kda_chunk_fwd_z (no workspace needed).
+ * Applies to every supported shape and dtype.  segments == 1, or T within
+ * one segment's length, runs the plain kda_chunk_fwd_z (no workspace needed).
  *
  * workspace: caller-owned device memory, 16-byte aligned, at least
  * kda_chunk_fwd_z_segmented_workspace_bytes(B, H, dk, dv, segments) bytes

@@ -242,8 +242,11 @@ def test_segmented_validation(L):
     assert chunk_seg(L, wsb=need - 4) == ERR_WORKSPACE
     assert chunk_seg(L, ws=ctypes.c_void_p(0xa0000008)) == ERR_ALIGN
     assert chunk_seg(L, ws=P(6)) == ERR_ALIAS                     # workspace over the output
-    assert chunk_seg(L, it=F32) == ERR_UNSUPPORTED                # segments need the MFMA shape
-    assert chunk_seg(L, dk=64) == ERR_UNSUPPORTED
+    # every shape and dtype takes segments (these get past validation; without a GPU
+    # they stop at their first HIP call)
+    assert chunk_seg(L, it=F32) == ERR_HIP
+    assert chunk_seg(L, dk=64, wsb=L.kda_chunk_fwd_z_segmented_workspace_bytes(1, 2, 64, 128, 4)) == ERR_HIP
+    assert chunk_seg(L, dk=48) == ERR_UNSUPPORTED
     assert chunk_seg(L, B=0) == OK
 
 
@@ -346,7 +349,9 @@ def test_chunk_workspace_query_and_validation(L):
     q = L.kda_chunk_fwd_workspace_bytes
     assert q(4, 32768, 32, 128, 128, 64) == 0       # B*H = 128 fills the GPU in one pass
     assert q(1, 64, 8, 128, 128, 64) == 0           # a single chunk: nothing to split
-    assert q(1, 4096, 32, 64, 64, 64) == 0          # the segment passes are matrix-core only
+    assert q(4, 4096, 64, 64, 64, 64) == 0          # B*H = 256 fills the GPU at d_v = 64
+    assert q(1, 4096, 32, 64, 64, 64) > 0           # B*H = 32 at d_v = 64: eight segments
+    assert q(1, 4096, 8, 128, 128, 16) == q(1, 4096, 8, 128, 128, 64)  # 256-token segments either way
     few = q(1, 4096, 8, 128, 128, 64)               # B*H = 8, 64 chunks: segment-parallel
     assert few > 0 and few % 16 == 0
     assert q(1, 1 << 20, 8, 128, 128, 64) >= few

@@ -139,3 +139,48 @@ def test_prefill_1m_slow_decay_segmented():
     assert_states("segmented vs oracle, S", host64(S[:, h0:h0 + 2]), S_ref, TOL["bf16"], offset=(0, h0))
     del o, S, o1, S1
     torch.cuda.empty_cache()
+
+
+# The fp32 matrix-core tile kernel (every shape but bf16 d = 128 chunk 64) runs the
+# same three passes; the transitions have d_k columns whatever d_v is.  fp32
+# arithmetic throughout, so the fp32 tolerance holds for bf16 inputs too.
+GEN_CASES = [  # B, H, T, dk, dv, chunk, dtype, segments, z_mean, s0_std
+    (1, 2, 1000, 128, 128, 64, "f32", 4, -6.0, 0.5),   # ragged last chunk and segment, slow decay
+    (1, 3, 777, 64, 32, 16, "bf16", 5, -6.0, 0.3),     # d_k > d_v, chunk 16
+    (2, 2, 640, 32, 128, 64, "f32", 3, -4.0, 0.2),     # d_k < d_v
+    (1, 1, 300, 16, 16, 16, "f32", 8, -8.0, 1.0),      # smallest dims, slowest decay, many segments
+    (1, 2, 1024, 128, 128, 16, "bf16", 6, -6.0, 0.0),  # bf16, chunk 16
+]
+
+
+@pytest.mark.parametrize("B,H,T,dk,dv,chunk,dtype,segs,zm,s0", GEN_CASES)
+def test_segmented_tile_kernel_vs_oracle(B, H, T, dk, dv, chunk, dtype, segs, zm, s0):
+    assert not kda.chunk_uses_mfma(torch.bfloat16 if dtype == "bf16" else torch.float32, dk, dv, chunk)
+    spec = ki.small_spec(B, H, T, dk, dv, chunk, dtype, seed=4300 + T + dk + segs, z_mean=zm, s0_std=s0)
+    say(f"case segmented tile kernel B={B} H={H} T={T} dk={dk} dv={dv} chunk={chunk} {dtype} segments={segs}")
+    d = ki.prefill_inputs(spec)
+    dd = dev_inputs(d, dtype)
+    o, S = kda.chunk_fwd_z_segmented(dd["q"], dd["k"], dd["v"], dd["beta"], dd["z"], dd["A"], segs, -5.0, chunk,
+                                     S_in=dd["S0"], o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    f = f64_inputs(d, dtype)
+    o_ref, S_ref = oracle.forward_z(f["q"], f["k"], f["v"], f["beta"], f["z"], f["A"], -5.0, f["S0"])
+    assert_tokens("segmented vs oracle, o", host64(o), o_ref, TOL["f32"], block=16)
+    assert_states("segmented vs oracle, S", host64(S), S_ref, TOL["f32"])
+
+
+def test_tile_kernel_picks_segments_itself():
+    """fp32, d = 128, 8 heads of 4096 tokens: kda_chunk_fwd_z cuts each sequence into
+    16 segments itself (its workspace query says so) and matches the oracle."""
+    B, H, T = 1, 8, 4096
+    assert kda.chunk_fwd_workspace_bytes(B, T, H, 128, 128, 64) > 0
+    spec = ki.small_spec(B, H, T, 128, 128, 64, "f32", seed=4400, z_mean=-6.0, s0_std=0.3)
+    say("case fp32 d=128 B=1 H=8 T=4096 through kda_chunk_fwd_z (automatic segments)")
+    d = ki.prefill_inputs(spec)
+    dd = dev_inputs(d, "f32")
+    o, S = kda.chunk_fwd_z(dd["q"], dd["k"], dd["v"], dd["beta"], dd["z"], dd["A"], -5.0, 64, S_in=dd["S0"])
+    torch.cuda.synchronize()
+    f = f64_inputs(d, "f32")
+    o_ref, S_ref = oracle.forward_z(f["q"], f["k"], f["v"], f["beta"], f["z"], f["A"], -5.0, f["S0"])
+    assert_tokens("automatic segments vs oracle, o", host64(o), o_ref, TOL["f32"])
+    assert_states("automatic segments vs oracle, S", host64(S), S_ref, TOL["f32"])
