@@ -50,17 +50,19 @@ def test_replay_small(dtype, dk, dv):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_replay_equals_decode_steps(dtype):
-    """Replaying every draft gives, bit for bit, what n_draft kda_decode_step calls give."""
-    n_draft, N, H, dk, dv = 5, 4, 2, 128, 128
+@pytest.mark.parametrize("g_min,n_draft", [(-5.0, 5), (-6.0, 19)])
+def test_replay_equals_decode_steps(dtype, g_min, n_draft):
+    """Replaying every draft gives, bit for bit, what n_draft kda_decode_step calls give
+    (19 drafts span three staging groups)."""
+    N, H, dk, dv = 4, 2, 128, 128
     spec, d = _case(n_draft, N, H, dk, dv, dtype, seed=77)
-    say(f"case replay==decode {dtype}")
+    say(f"case replay==decode {dtype} g_min={g_min} n_draft={n_draft}")
     dd = dev_inputs(d, dtype)
     acc = torch.full((N,), n_draft, dtype=torch.int32, device=DEV)
-    o, S = kda.decode_replay(dd["q"], dd["k"], dd["v"], dd["z"], dd["beta"], dd["A"], dd["S0"], acc)
+    o, S = kda.decode_replay(dd["q"], dd["k"], dd["v"], dd["z"], dd["beta"], dd["A"], dd["S0"], acc, g_min=g_min)
     S_dec = dd["S0"].clone()
-    outs = [kda.decode_step(dd["q"][t], dd["k"][t], dd["v"][t], dd["z"][t], dd["beta"][t], dd["A"], S_dec)
-            for t in range(n_draft)]
+    outs = [kda.decode_step(dd["q"][t], dd["k"][t], dd["v"][t], dd["z"][t], dd["beta"][t], dd["A"], S_dec,
+                            g_min=g_min) for t in range(n_draft)]
     torch.cuda.synchronize()
     assert torch.equal(torch.stack(outs), o)
     assert torch.equal(S_dec, S)
@@ -99,3 +101,24 @@ def test_replay_decode_workload_sampled():
     es = rel_l2(host64(S)[sel], S_ref)
     say(f"  sampled rel-L2 o={eo:.3e} S_commit={es:.3e}")
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_replay_three_groups_vs_oracle(dtype):
+    """19 drafts (three staging groups), accepted prefixes inside every group, against
+    the oracle."""
+    n_draft, N, H, dk, dv = 19, 8, 2, 64, 64
+    spec, d = _case(n_draft, N, H, dk, dv, dtype, seed=91)
+    acc = np.array([0, 19, 3, 8, 9, 15, 16, 12], dtype=np.int32)
+    say(f"case replay n_draft={n_draft} {dtype} accepted={acc.tolist()}")
+    f = f64_inputs(d, dtype)
+    o_ref, S_ref = oracle.replay(f["q"], f["k"], f["v"], f["z"], f["beta"], f["A"], f["S0"], acc)
+    dd = dev_inputs(d, dtype)
+    o, S = kda.decode_replay(dd["q"], dd["k"], dd["v"], dd["z"], dd["beta"], dd["A"], dd["S0"],
+                             torch.from_numpy(acc).to(DEV))
+    torch.cuda.synchronize()
+    eo, es = rel_l2(host64(o), o_ref), rel_l2(host64(S), S_ref)
+    say(f"  rel-L2 o={eo:.3e} S_commit={es:.3e}")
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+    for i in range(N):
+        assert rel_l2(host64(S[i]), S_ref[i]) <= TOL[dtype], i
