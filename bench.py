@@ -351,11 +351,12 @@ def main():
         log(f"small configurations: {small}")
 
     # ---------------- other supported shapes (reported beside the step) ----------------
-    # Shapes outside the bf16 matrix-core kernel's (d_k = d_v = 128, chunk 64) run the fp32
-    # matrix-core tile kernel: bf16 with smaller heads or chunk 16, and fp32 inputs.  B=4,
-    # H=32, T=4096, fused gate; bytes per token-head: q, k, z and v, beta in, o out; fp32
-    # flops per token-head of its products: L and P (16 d_k each), (K 2^Gl) S, (Q 2^Gl) S
-    # and the state update (d_k d_v each), U and P U (16 d_v each), as multiply-adds.
+    # Shapes outside the bf16 matrix-core kernel's (d_k = d_v = 128, chunk 64) run the tile
+    # kernel (fp32 products for fp32 inputs, bf16 products for bf16 inputs): bf16 with
+    # smaller heads or chunk 16, and fp32 inputs.  B=4, H=32, T=4096, fused gate; bytes per
+    # token-head: q, k, z and v, beta in, o out; flops per token-head of its products:
+    # L and P (16 d_k each), (K 2^Gl) S, (Q 2^Gl) S and the state update (d_k d_v each),
+    # U and P U (16 d_v each), as multiply-adds, against the peak of the product dtype.
     other = None
     if run_pre and not args.no_extras:
         other = {}
@@ -379,8 +380,10 @@ def main():
             flops = cs.B * cs.T * cs.H * 2 * (3 * cs.dk * cs.dv + 32 * (cs.dk + cs.dv))
             other[cs.name] = {"ms": st_["median"], "tokens_per_s": round(cs.B * cs.T / (st_["median"] / 1e3), 1),
                               "frac_hbm": round(nbytes / (st_["median"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-                              "fp32_tflops": round(flops / (st_["median"] / 1e3) / 1e12, 2),
-                              "frac_fp32_mfma": round(flops / (st_["median"] / 1e3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
+                              "matrix_tflops": round(flops / (st_["median"] / 1e3) / 1e12, 2),
+                              "matrix_dtype": dtype,
+                              "frac_matrix_peak": round(flops / (st_["median"] / 1e3) / 1e12 /
+                                                        (BF16_PEAK_TFLOPS if dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS), 4),
                               "matrix_core_kernel": kda.chunk_uses_mfma(
                                   torch.bfloat16 if dtype == "bf16" else torch.float32, cs.dk, cs.dv, cs.chunk)}
             del C, S0c, oc, Sc, wsc

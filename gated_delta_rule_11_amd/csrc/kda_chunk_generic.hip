@@ -48,6 +48,8 @@
 // are the limit: a key wavefront's vector work and a state wavefront's matrix
 // instructions on one SIMD do not overlap much, so work is kept off the busiest
 // SIMDs rather than duplicated.
+#include <type_traits>
+
 #include "kda_common.hpp"
 #include "kda_launch.hpp"
 
@@ -107,6 +109,37 @@ template <> struct One<bf16_t> {
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// four floats -> four bf16, round to nearest even (two v_cvt_pk_bf16_f32)
+__device__ __forceinline__ s16x4 bf4(f32x4 x) {
+  const u32x2 r = {__builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x[0], x[1]}, bf16x2)),
+                   __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x[2], x[3]}, bf16x2))};
+  return __builtin_bit_cast(s16x4, r);
+}
+// One 16 x 16 x 16 product whose lane (row or column l % 16, group g = l / 16) holds
+// k = 4 g .. 4 g + 3 of both operands, the layout of every product here: four fp32
+// 16x16x4 products (k = 4 g + r in step r), or, for bf16 inputs (BF), one bf16
+// 16x16x16 product of the operands rounded to bf16 (fp32 accumulation).
+template <bool BF>
+__device__ __forceinline__ f32x4 mm16(f32x4 a, f32x4 b, f32x4 c) {
+  if constexpr (BF) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bf4(a), bf4(b), c, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) c = mfma4(a[r], b[r], c);
+    return c;
+  }
+}
+template <bool BF>
+__device__ __forceinline__ f32x4 mm16b(f32x4 a, s16x4 b_bf, f32x4 b, f32x4 c) {  // b already rounded (BF)
+  if constexpr (BF) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bf4(a), b_bf, c, 0, 0, 0);
+  } else {
+    return mm16<false>(a, b, c);
+  }
+}
 // inclusive prefix sum over the 16 lanes of a DPP row (lanes 16 r .. 16 r + 15)
 __device__ __forceinline__ float row_prefix16(float x) {
   x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, true));  // row_shr:1
@@ -139,6 +172,7 @@ __device__ __forceinline__ float sel4(int g, float a0, float a1, float a2, float
 template <int DK, int DVS, typename Tin, bool FROM_Z>
 __global__ __launch_bounds__(NT) void chunk_tile_kernel(const ChunkArgs a) {
   using Lds = TileLds<DK, DVS>;
+  constexpr bool BF = std::is_same<Tin, bf16_t>::value;  // bf16 products for bf16 inputs
   constexpr int NCT = Lds::NCT, NP = Lds::NP;
   constexpr int CPW = (NCT + 3) / 4;  // key tiles per key wavefront
   constexpr int VPL = DVS / 16;       // values per key-role lane per tile
@@ -311,11 +345,8 @@ __global__ __launch_bounds__(NT) void chunk_tile_kernel(const ChunkArgs a) {
             khv[m][r] = kv * fast_exp2(last[m][r] - g[m][r]);
             elv[m][r] = fast_exp2(last[m][r]);
           }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            accL = mfma4(kf[r], kb[r], accL);
-            accP = mfma4(qf[r], kb[r], accP);
-          }
+          accL = mm16<BF>(kf, kb, accL);
+          accP = mm16<BF>(qf, kb, accP);
         }
 #pragma unroll
         for (int m = 0; m < CPW; ++m) {
@@ -457,10 +488,16 @@ __global__ __launch_bounds__(NT) void chunk_tile_kernel(const ChunkArgs a) {
       for (int ct = 0; ct < NCT; ++ct) {
         const f32x4 kgv = cur.kg[ct][l];
         const f32x4 qgv = cur.qg[ct][l];
+        if constexpr (BF) {
+          const s16x4 sb = bf4(S[ct]);
+          ya[ct & 1] = mm16b<true>(kgv, sb, S[ct], ya[ct & 1]);
+          oa[ct & 1] = mm16b<true>(qgv, sb, S[ct], oa[ct & 1]);
+        } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          ya[r & 1] = mfma4(kgv[r], S[ct][r], ya[r & 1]);
-          oa[r & 1] = mfma4(qgv[r], S[ct][r], oa[r & 1]);
+          for (int r = 0; r < 4; ++r) {
+            ya[r & 1] = mfma4(kgv[r], S[ct][r], ya[r & 1]);
+            oa[r & 1] = mfma4(qgv[r], S[ct][r], oa[r & 1]);
+          }
         }
       }
       f32x4 y = ya[0] + ya[1], oacc = oa[0] + oa[1];
@@ -474,24 +511,19 @@ __global__ __launch_bounds__(NT) void chunk_tile_kernel(const ChunkArgs a) {
       }
       y = vin + rk4 * y;
       // U = Tm Y (rows 4 lg + r)
-      f32x4 u = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) u = mfma4(tm[t], y[t], u);
+      const f32x4 u = mm16<BF>(tm, y, f32x4{0.f, 0.f, 0.f, 0.f});
       // S <- Diag(2^Gl_15) S + (K 2^(Gl_15 - Gl))^T U
       const f32x4 uk = u * rk4;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         const f32x4 el4 = *reinterpret_cast<const f32x4*>(&cur.el[16 * ct + 4 * lg]);
         const f32x4 khv = *reinterpret_cast<const f32x4*>(&cur.kh[16 * ct + li][4 * lg]);
-        S[ct] *= el4;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) S[ct] = mfma4(khv[t], uk[t], S[ct]);
+        S[ct] = mm16<BF>(khv, uk, S[ct] * el4);
       }
       // o = scale (Q 2^Gl S + P U)
       if (!a.o_skip) {
         oacc *= rq4;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) oacc = mfma4(pm[t], u[t], oacc);
+        oacc = mm16<BF>(pm, u, oacc);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 4 * lg + r;

@@ -3,9 +3,9 @@ d = 128, chunk 64 kernel) at head counts large enough that the library picks
 its 32- and 64-value-column slices (the smaller tests run 16-column slices):
 B*H >= 64 gives 32-column slices of dv >= 64, B*H >= 128 gives 64-column slices
 of dv = 128.  Ragged T, every entry path (fused gate, precomputed G, fused
-prologue), per-sequence and per-block relative L2 against the fp64 oracle.
-This kernel computes in fp32 throughout, so with fp32 outputs bf16 inputs meet
-the fp32 bar (1e-5) too: a stricter check than the bf16 tolerance."""
+prologue), per-sequence and per-block relative L2 against the fp64 oracle, at
+the tolerance of the input dtype (fp32 inputs: fp32 products throughout; bf16
+inputs: bf16 products with fp32 accumulation)."""
 import pytest
 import torch
 
@@ -46,5 +46,5 @@ def test_wide_grid_vs_oracle(B, H, T, dk, dv, chunk, dtype, path, s0):
     run = oracle.forward_z_prologue if path == "prologue" else oracle.forward_z
     o_ref, S_ref = run(f["q"], f["k"], f["v"], f["beta"], f["z"], f["A"], -5.0, f["S0"])
     assert o.dtype == torch.float32
-    assert_tokens("o", host64(o), o_ref, TOL["f32"], block=16)
-    assert_states("S", host64(S), S_ref, TOL["f32"])
+    assert_tokens("o", host64(o), o_ref, TOL[dtype], block=16)
+    assert_states("S", host64(S), S_ref, TOL[dtype])
