@@ -108,6 +108,26 @@ template <> struct io1<bf16_t> {
 __device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// four floats -> four bf16 (round to nearest even), the A or B operand of one lane
+__device__ __forceinline__ s16x4_t bw_bf4(f32x4 x) {
+  const u32x2_t r = {__builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{x[0], x[1]}, bf16x2_t)),
+                     __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{x[2], x[3]}, bf16x2_t))};
+  return __builtin_bit_cast(s16x4_t, r);
+}
+// 16 x 16 x 16 product, lane group g holding k = 4 g .. 4 g + 3 of both operands
+__device__ __forceinline__ f32x4 mma16bf(f32x4 a, f32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bw_bf4(a), bw_bf4(b), c, 0, 0, 0);
+}
+
+// Four consecutive fp32 values of a 17-float-stride row (not 16-byte aligned).
+__device__ __forceinline__ f32x4 rows4(const float* p) {
+  f32x4 r;
+  r[0] = p[0]; r[1] = p[1]; r[2] = p[2]; r[3] = p[3];
+  return r;
+}
 
 // Workgroup barrier ordering LDS only: the next sub-chunk's inputs stay in flight across it.
 __device__ __forceinline__ void bw_barrier() {
@@ -125,6 +145,9 @@ __device__ __forceinline__ void bw_barrier_global() {
 template <int DK, int DV, int NSP, typename Tin, typename Tdo>
 __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
   using namespace bw;
+  // bf16 inputs: the long contractions (over d_k or d_v) on bf16 matrix cores, operands
+  // rounded to bf16, fp32 accumulation; the 16-deep products over tokens stay fp32
+  constexpr bool BF = std::is_same<Tin, bf16_t>::value;
   constexpr int DVS = DV / NSP;  // value columns of this workgroup's slice
   using Ly = Layout<DK, DVS>;
   constexpr int NKT = DK / 16, NVT = DVS / 16;
@@ -357,10 +380,17 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
         an = *reinterpret_cast<const f32x4*>(ar + 4 * qd + 4);
         bn = *reinterpret_cast<const f32x4*>(br + 4 * qd + 4);
       }
-      acc0 = mma4(av[0], bv[0], acc0);
-      acc1 = mma4(av[1], bv[1], acc1);
-      acc0 = mma4(av[2], bv[2], acc0);
-      acc1 = mma4(av[3], bv[3], acc1);
+      if constexpr (BF) {
+        if (qd & 1)
+          acc1 = mma16bf(av, bv, acc1);
+        else
+          acc0 = mma16bf(av, bv, acc0);
+      } else {
+        acc0 = mma4(av[0], bv[0], acc0);
+        acc1 = mma4(av[1], bv[1], acc1);
+        acc0 = mma4(av[2], bv[2], acc0);
+        acc1 = mma4(av[3], bv[3], acc1);
+      }
       av = an;
       bv = bn;
     }
@@ -445,15 +475,31 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
   auto w_ut = [&](f32x4& Ut) {
     if (own_c) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (BF) {
+        f32x4 bv;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) acc = mma4(sT[r16 * RS + 4 * kb + g4], sKt[(4 * kb + g4) * RK + 16 * ct + r16], acc);
+        for (int e = 0; e < 4; ++e) bv[e] = sKt[(4 * g4 + e) * RK + 16 * ct + r16];
+        acc = mma16bf(rows4(sT + r16 * RS + 4 * g4), bv, acc);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+          acc = mma4(sT[r16 * RS + 4 * kb + g4], sKt[(4 * kb + g4) * RK + 16 * ct + r16], acc);
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) sW[(4 * g4 + e) * RK + 16 * ct + r16] = acc[e];
     }
     Ut = f32x4{0.f, 0.f, 0.f, 0.f};
     if (own_j) {
+      if constexpr (BF) {
+        f32x4 bv;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) Ut = mma4(sT[r16 * RS + 4 * kb + g4], sV[(4 * kb + g4) * RV + 16 * jt + r16], Ut);
+        for (int e = 0; e < 4; ++e) bv[e] = sV[(4 * g4 + e) * RV + 16 * jt + r16];
+        Ut = mma16bf(rows4(sT + r16 * RS + 4 * g4), bv, Ut);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+          Ut = mma4(sT[r16 * RS + 4 * kb + g4], sV[(4 * kb + g4) * RV + 16 * jt + r16], Ut);
+      }
     }
   };
 
@@ -463,10 +509,18 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
     f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c2 = 0; c2 < NKT; ++c2) {
+      if constexpr (BF) {
+        const f32x4 av = *reinterpret_cast<const f32x4*>(Asrc + r16 * RK + 16 * c2 + 4 * g4);
+        if (c2 & 1)
+          acc2 = mma16bf(av, Y[c2], acc2);
+        else
+          acc = mma16bf(av, Y[c2], acc);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; e += 2) {
-        acc = mma4(Asrc[r16 * RK + 16 * c2 + 4 * g4 + e], Y[c2][e], acc);
-        acc2 = mma4(Asrc[r16 * RK + 16 * c2 + 4 * g4 + e + 1], Y[c2][e + 1], acc2);
+        for (int e = 0; e < 4; e += 2) {
+          acc = mma4(Asrc[r16 * RK + 16 * c2 + 4 * g4 + e], Y[c2][e], acc);
+          acc2 = mma4(Asrc[r16 * RK + 16 * c2 + 4 * g4 + e + 1], Y[c2][e + 1], acc2);
+        }
       }
     }
     return acc + acc2;
@@ -476,10 +530,18 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
     f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j2 = 0; j2 < NVT; ++j2) {
+      if constexpr (BF) {
+        const f32x4 av = *reinterpret_cast<const f32x4*>(Asrc + r16 * RV + 16 * j2 + 4 * g4);
+        if (j2 & 1)
+          acc2 = mma16bf(av, Y[j2], acc2);
+        else
+          acc = mma16bf(av, Y[j2], acc);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; e += 2) {
-        acc = mma4(Asrc[r16 * RV + 16 * j2 + 4 * g4 + e], Y[j2][e], acc);
-        acc2 = mma4(Asrc[r16 * RV + 16 * j2 + 4 * g4 + e + 1], Y[j2][e + 1], acc2);
+        for (int e = 0; e < 4; e += 2) {
+          acc = mma4(Asrc[r16 * RV + 16 * j2 + 4 * g4 + e], Y[j2][e], acc);
+          acc2 = mma4(Asrc[r16 * RV + 16 * j2 + 4 * g4 + e + 1], Y[j2][e + 1], acc2);
+        }
       }
     }
     return acc + acc2;
@@ -525,8 +587,15 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
           f32x4 acc;
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc[e] = sGl[16 * c2 + 4 * g4 + e] * Sc[c2][e];
+          if constexpr (BF) {
+            f32x4 av;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc = mma4(-sKh[(4 * g4 + e) * RK + 16 * c2 + r16], negU[e], acc);
+            for (int e = 0; e < 4; ++e) av[e] = -sKh[(4 * g4 + e) * RK + 16 * c2 + r16];
+            acc = mma16bf(av, negU, acc);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc = mma4(-sKh[(4 * g4 + e) * RK + 16 * c2 + r16], negU[e], acc);
+          }
           Sc[c2] = acc;
 #pragma unroll
           for (int e = 0; e < 4; ++e) dst[(16 * c2 + 4 * g4 + e) * DV + j0 + 16 * jt + r16] = acc[e];
@@ -563,8 +632,19 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
         const f32x4 WS = over_c(sW, Sc, f32x4{0.f, 0.f, 0.f, 0.f});
         // dU = P^T dO + Kh dS_next
         f32x4 acc = over_c(sKh, dSc, f32x4{0.f, 0.f, 0.f, 0.f});
+        if constexpr (BF) {
+          f32x4 av, bv;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) acc = mma4(sP[(4 * kb + g4) * RS + r16], sdO[(4 * kb + g4) * RV + 16 * jt + r16], acc);
+          for (int e = 0; e < 4; ++e) {
+            av[e] = sP[(4 * g4 + e) * RS + r16];
+            bv[e] = sdO[(4 * g4 + e) * RV + 16 * jt + r16];
+          }
+          acc = mma16bf(av, bv, acc);
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+            acc = mma4(sP[(4 * kb + g4) * RS + r16], sdO[(4 * kb + g4) * RV + 16 * jt + r16], acc);
+        }
         dUc = acc;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -614,11 +694,23 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
           f32x4 acc, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc[e] = sGl[16 * c2 + 4 * g4 + e] * dSc[c2][e];
+          if constexpr (BF) {
+            f32x4 av, bv, wv4;
 #pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-            acc = mma4(sQt[(4 * kb + g4) * RK + 16 * c2 + r16], sdO[(4 * kb + g4) * RV + 16 * jt + r16], acc);
+            for (int e = 0; e < 4; ++e) {
+              av[e] = sQt[(4 * g4 + e) * RK + 16 * c2 + r16];
+              bv[e] = sdO[(4 * g4 + e) * RV + 16 * jt + r16];
+              wv4[e] = -sW[(4 * g4 + e) * RK + 16 * c2 + r16];
+            }
+            acc = mma16bf(av, bv, acc);
+            acc2 = mma16bf(wv4, dUc, acc2);
+          } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc2 = mma4(-sW[(4 * g4 + e) * RK + 16 * c2 + r16], dUc[e], acc2);
+            for (int kb = 0; kb < 4; ++kb)
+              acc = mma4(sQt[(4 * kb + g4) * RK + 16 * c2 + r16], sdO[(4 * kb + g4) * RV + 16 * jt + r16], acc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc2 = mma4(-sW[(4 * g4 + e) * RK + 16 * c2 + r16], dUc[e], acc2);
+          }
           dSc[c2] = acc + acc2;
         }
       }
@@ -629,10 +721,23 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
           f32x4 acc, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc[e] = gl * dSt[j2][e];
+          if constexpr (BF) {
+            f32x4 a1, b1, a2, b2;
 #pragma unroll
-          for (int kb = 0; kb < 4; ++kb) {
-            acc = mma4(sdO[(4 * kb + g4) * RV + 16 * j2 + r16], sQt[(4 * kb + g4) * RK + 16 * ct + r16], acc);
-            acc2 = mma4(-sdU[(4 * kb + g4) * RV + 16 * j2 + r16], sW[(4 * kb + g4) * RK + 16 * ct + r16], acc2);
+            for (int e = 0; e < 4; ++e) {
+              a1[e] = sdO[(4 * g4 + e) * RV + 16 * j2 + r16];
+              b1[e] = sQt[(4 * g4 + e) * RK + 16 * ct + r16];
+              a2[e] = -sdU[(4 * g4 + e) * RV + 16 * j2 + r16];
+              b2[e] = sW[(4 * g4 + e) * RK + 16 * ct + r16];
+            }
+            acc = mma16bf(a1, b1, acc);
+            acc2 = mma16bf(a2, b2, acc2);
+          } else {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+              acc = mma4(sdO[(4 * kb + g4) * RV + 16 * j2 + r16], sQt[(4 * kb + g4) * RK + 16 * ct + r16], acc);
+              acc2 = mma4(-sdU[(4 * kb + g4) * RV + 16 * j2 + r16], sW[(4 * kb + g4) * RK + 16 * ct + r16], acc2);
+            }
           }
           dSt[j2] = acc + acc2;
         }
@@ -643,8 +748,15 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
       // ---- dV (value-column tiles, stored); dT's second part dW Kt^T; dKt = T^T dW (key-row tiles)
       if (own_j) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (BF) {
+          f32x4 av;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc = mma4(sT[(4 * g4 + e) * RS + r16], dUc[e], acc);
+          for (int e = 0; e < 4; ++e) av[e] = sT[(4 * g4 + e) * RS + r16];
+          acc = mma16bf(av, dUc, acc);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc = mma4(sT[(4 * g4 + e) * RS + r16], dUc[e], acc);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = 4 * g4 + e;
@@ -658,6 +770,8 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
       }
       f32x4 dKt = {0.f, 0.f, 0.f, 0.f}, dKb = {0.f, 0.f, 0.f, 0.f};
       if (own_c) {
+        // fp32 products for every input dtype: the gate's derivative takes differences
+        // of these gradients' terms that cancel
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
           dKt = mma4(sT[(4 * kb + g4) * RS + r16], sdW[(4 * kb + g4) * RK + 16 * ct + r16], dKt);
