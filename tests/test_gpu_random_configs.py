@@ -1,0 +1,110 @@
+"""GPU parity on configurations drawn at random (fixed seeds, so every run checks
+the same cases): head sizes, chunk length, input and output dtypes, batch,
+heads, ragged sequence lengths, gate floor, output scale, initial state and
+entry point (fused gate, precomputed G, fused prologue, an explicit segment
+count) for the chunked prefill, and the same for decode steps.  Each case is
+compared with the fp64 oracle per sequence and per 16-token block, at the
+tolerance of the input dtype.  The hand-picked cases elsewhere cover the edges
+one at a time; these mix them."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_11_amd as kda
+import kda_inputs as ki
+import oracle
+from tests._gpu import TOL, assert_states, assert_tokens, dev_inputs, f64_inputs, host64, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+DIMS = (16, 32, 64, 128)
+LENGTHS = (0, 1, 15, 17, 63, 64, 65, 129, 200, 333, 512)
+PATHS = ("z", "G", "prologue", "segmented")
+
+
+def _prefill_cases(n=24, seed=20261):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dtype = str(rng.choice(["f32", "bf16"]))
+        if i % 6 == 0:  # the matrix-core kernel's shape, regularly
+            dtype, dk, dv, chunk = "bf16", 128, 128, 64
+        else:
+            dk, dv, chunk = int(rng.choice(DIMS)), int(rng.choice(DIMS)), int(rng.choice([16, 64]))
+        path = str(rng.choice(PATHS))
+        T = int(rng.choice(LENGTHS))
+        if path == "segmented" and T == 0:
+            T = 65
+        cases.append(dict(
+            B=int(rng.integers(1, 4)), H=int(rng.integers(1, 7)), T=T, dk=dk, dv=dv, chunk=chunk, dtype=dtype,
+            path=path, segs=int(rng.integers(1, 7)), s0=float(rng.choice([0.0, 0.2])),
+            zm=float(rng.choice([0.0, -3.0, 2.0])), g_min=float(rng.choice([-5.4, -5.0, -2.0, 0.0])),
+            scale=float(rng.choice([1.0, 0.125])), o_bf16=bool(dtype == "bf16" and rng.integers(0, 2)),
+            seed=7000 + i))
+    return cases
+
+
+def _id(c):
+    return (f"{c['path']}-{c['dtype']}-B{c['B']}H{c['H']}T{c['T']}-d{c['dk']}x{c['dv']}-c{c['chunk']}"
+            f"-g{c['g_min']}-s{c['segs']}")
+
+
+@pytest.mark.parametrize("c", _prefill_cases(), ids=_id)
+def test_random_prefill_vs_oracle(c):
+    say(f"case random prefill {c}")
+    spec = ki.small_spec(c["B"], c["H"], c["T"], c["dk"], c["dv"], c["chunk"], c["dtype"], seed=c["seed"],
+                         s0_std=c["s0"], z_mean=c["zm"], raw=(c["path"] == "prologue"))
+    d = ki.prefill_inputs(spec)
+    dd = dev_inputs(d, c["dtype"])
+    o_dtype = torch.bfloat16 if c["o_bf16"] else torch.float32
+    g_min, chunk, scale = c["g_min"], c["chunk"], c["scale"]
+    args = (dd["q"], dd["k"], dd["v"], dd["beta"])
+    if c["path"] == "z":
+        o, S = kda.chunk_fwd_z(*args, dd["z"], dd["A"], g_min, chunk, S_in=dd["S0"], o_dtype=o_dtype, scale=scale)
+    elif c["path"] == "G":
+        G = kda.gate(dd["z"], dd["A"], g_min, chunk)
+        o, S = kda.chunk_fwd(*args, G, chunk, S_in=dd["S0"], o_dtype=o_dtype, scale=scale)
+    elif c["path"] == "prologue":
+        o, S = kda.chunk_fwd_z_prologue(*args, dd["z"], dd["A"], g_min, chunk, S_in=dd["S0"], o_dtype=o_dtype,
+                                        scale=scale)
+    else:
+        o, S = kda.chunk_fwd_z_segmented(*args, dd["z"], dd["A"], c["segs"], g_min, chunk, S_in=dd["S0"],
+                                         o_dtype=o_dtype, scale=scale)
+    torch.cuda.synchronize()
+    assert o.dtype == o_dtype
+    f = f64_inputs(d, c["dtype"])
+    run = oracle.forward_z_prologue if c["path"] == "prologue" else oracle.forward_z
+    o_ref, S_ref = run(f["q"], f["k"], f["v"], f["beta"], f["z"], f["A"], g_min, f["S0"], scale)
+    tol = TOL[c["dtype"]]
+    assert_tokens("o", host64(o), o_ref, tol, block=16)
+    assert_states("S", host64(S), S_ref, tol)
+
+
+def _decode_cases(n=10, seed=20262):
+    rng = np.random.default_rng(seed)
+    return [dict(N=int(rng.integers(1, 9)), H=int(rng.integers(1, 5)), dk=int(rng.choice(DIMS)),
+                 dv=int(rng.choice(DIMS)), dtype=str(rng.choice(["f32", "bf16"])), prologue=bool(rng.integers(0, 2)),
+                 g_min=float(rng.choice([-5.0, -2.0, 0.0])), scale=float(rng.choice([1.0, 0.125])), seed=7100 + i)
+            for i in range(n)]
+
+
+@pytest.mark.parametrize("c", _decode_cases(),
+                         ids=lambda c: f"{c['dtype']}-N{c['N']}H{c['H']}-d{c['dk']}x{c['dv']}-p{int(c['prologue'])}")
+def test_random_decode_vs_oracle(c):
+    say(f"case random decode {c}")
+    spec = ki.DecodeSpec("decode_random", N=c["N"], H=c["H"], dk=c["dk"], dv=c["dv"], steps=5, dtype=c["dtype"],
+                         s_std=0.1, seed=c["seed"], raw=c["prologue"])
+    d = ki.decode_inputs(spec)
+    f = f64_inputs(d, c["dtype"])
+    run = oracle.decode_prologue if c["prologue"] else oracle.decode
+    o_ref, S_ref = run(f["q"], f["k"], f["v"], f["z"], f["beta"], f["A"], f["S0"], c["g_min"], c["scale"])
+    dd = dev_inputs(d, c["dtype"])
+    S = dd["S0"].clone()
+    step = kda.decode_step_prologue if c["prologue"] else kda.decode_step
+    outs = [step(dd["q"][s], dd["k"][s], dd["v"][s], dd["z"][s], dd["beta"][s], dd["A"], S, c["g_min"],
+                 o_dtype=torch.float32, scale=c["scale"]) for s in range(spec.steps)]
+    torch.cuda.synchronize()
+    o = torch.stack(outs)
+    eo, es = rel_l2(host64(o), o_ref), rel_l2(host64(S), S_ref)
+    say(f"  rel-L2 o={eo:.3e} S={es:.3e}")
+    assert eo <= TOL[c["dtype"]] and es <= TOL[c["dtype"]]
