@@ -364,9 +364,12 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
   // ---- 16 x 16 tile: sum over K of A[r][k] B[c][k] (both row-major with stride RSTR).
   // Any assignment of the K channels to the K / 4 products' lane groups gives the same
   // sum; lane group g4 takes channels (K / 4) g4 .. (K / 4) g4 + K / 4 - 1, so each lane
-  // reads its operands as contiguous 16-byte vectors.
-  auto mm_nt = [&](const float* Ap, const float* Bp, auto k_c, int RSTR) {
+  // reads its operands as contiguous 16-byte vectors.  MBF: bf16 operands (bf16 inputs
+  // only); dP and dT take fp32 operands for every input dtype, since dbeta and the gate's
+  // derivative are sums of their elements' products whose terms can cancel.
+  auto mm_nt = [&](const float* Ap, const float* Bp, auto k_c, int RSTR, auto bf_c) {
     constexpr int K = decltype(k_c)::value, KQ = K / 4;
+    constexpr bool MBF = BF && decltype(bf_c)::value;
     static_assert(KQ % 4 == 0, "16-byte operand reads");
     const float* ar = Ap + r16 * RSTR + KQ * g4;
     const float* br = Bp + r16 * RSTR + KQ * g4;
@@ -380,7 +383,7 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
         an = *reinterpret_cast<const f32x4*>(ar + 4 * qd + 4);
         bn = *reinterpret_cast<const f32x4*>(br + 4 * qd + 4);
       }
-      if constexpr (BF) {
+      if constexpr (MBF) {
         if (qd & 1)
           acc1 = mma16bf(av, bv, acc1);
         else
@@ -426,7 +429,7 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
       return;
     }
     if (wv == 0 || (BWD && wv == 1)) {
-      const f32x4 acc = mm_nt(wv == 0 ? sKt : sQt, sKb, std::integral_constant<int, DK>{}, RK);
+      const f32x4 acc = mm_nt(wv == 0 ? sKt : sQt, sKb, std::integral_constant<int, DK>{}, RK, std::true_type{});
       // acc[e] = X[t][s] with t = 4 g4 + e, s = r16
       if (wv == 1) {
 #pragma unroll
@@ -675,7 +678,7 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
         if (g4 == 0) sdGl[16 * ct + r16] = part;
       }
       if (wv == W_DP) {  // dP = lower(dO U^T)
-        const f32x4 acc = mm_nt(sdO, sU, std::integral_constant<int, DVS>{}, RV);
+        const f32x4 acc = mm_nt(sdO, sU, std::integral_constant<int, DVS>{}, RV, std::false_type{});
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = 4 * g4 + e;
@@ -683,7 +686,7 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
         }
       }
       if (wv == W_DT0) {  // dU V^T
-        const f32x4 acc = mm_nt(sdU, sV, std::integral_constant<int, DVS>{}, RV);
+        const f32x4 acc = mm_nt(sdU, sV, std::integral_constant<int, DVS>{}, RV, std::false_type{});
 #pragma unroll
         for (int e = 0; e < 4; ++e) sdT0[(4 * g4 + e) * RS + r16] = acc[e];
       }
@@ -764,7 +767,7 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
         }
       }
       if (wv == W_DT1) {  // dW Kt^T
-        const f32x4 acc = mm_nt(sdW, sKt, std::integral_constant<int, DK>{}, RK);
+        const f32x4 acc = mm_nt(sdW, sKt, std::integral_constant<int, DK>{}, RK, std::false_type{});
 #pragma unroll
         for (int e = 0; e < 4; ++e) sdT1[(4 * g4 + e) * RS + r16] = acc[e];
       }

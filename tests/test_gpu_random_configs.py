@@ -2,9 +2,9 @@
 the same cases): head sizes, chunk length, input and output dtypes, batch,
 heads, ragged sequence lengths, gate floor, output scale, initial state and
 entry point (fused gate, precomputed G, fused prologue, an explicit segment
-count) for the chunked prefill, and the same for decode steps.  Each case is
-compared with the fp64 oracle per sequence and per 16-token block, at the
-tolerance of the input dtype.  The hand-picked cases elsewhere cover the edges
+count) for the chunked prefill, the same for decode steps, and for the
+backward.  Each case is compared with the fp64 oracle (per sequence and per
+16-token block for the prefill outputs), at the tolerance of the input dtype.  The hand-picked cases elsewhere cover the edges
 one at a time; these mix them."""
 import numpy as np
 import pytest
@@ -13,7 +13,8 @@ import torch
 import gated_delta_rule_11_amd as kda
 import kda_inputs as ki
 import oracle
-from tests._gpu import TOL, assert_states, assert_tokens, dev_inputs, f64_inputs, host64, rel_l2, say
+import oracle.backward as OB
+from tests._gpu import TOL, assert_states, assert_tokens, dev, dev_inputs, f64_inputs, host64, rel_l2, say
 
 pytestmark = pytest.mark.gpu
 
@@ -108,3 +109,36 @@ def test_random_decode_vs_oracle(c):
     eo, es = rel_l2(host64(o), o_ref), rel_l2(host64(S), S_ref)
     say(f"  rel-L2 o={eo:.3e} S={es:.3e}")
     assert eo <= TOL[c["dtype"]] and es <= TOL[c["dtype"]]
+
+
+def _backward_cases(n=8, seed=20263):
+    rng = np.random.default_rng(seed)
+    return [dict(B=int(rng.integers(1, 3)), H=int(rng.integers(1, 4)),
+                 T=int(rng.choice([1, 15, 16, 17, 64, 65, 100, 150])), dk=int(rng.choice(DIMS)),
+                 dv=int(rng.choice(DIMS)), dtype=str(rng.choice(["f32", "bf16"])), s0=float(rng.choice([0.0, 0.2])),
+                 zm=float(rng.choice([0.0, -4.0, 2.0])), with_dS=bool(rng.integers(0, 2)),
+                 scale=float(rng.choice([1.0, 0.125])), g_min=float(rng.choice([-5.0, -2.0, 0.0])), seed=7200 + i)
+            for i in range(n)]
+
+
+@pytest.mark.parametrize("c", _backward_cases(),
+                         ids=lambda c: f"{c['dtype']}-B{c['B']}H{c['H']}T{c['T']}-d{c['dk']}x{c['dv']}-g{c['g_min']}")
+def test_random_backward_vs_oracle(c):
+    say(f"case random backward {c}")
+    spec = ki.small_spec(c["B"], c["H"], c["T"], c["dk"], c["dv"], 64, c["dtype"], seed=c["seed"], s0_std=c["s0"],
+                         z_mean=c["zm"])
+    d = ki.prefill_inputs(spec)
+    rng = np.random.default_rng([c["seed"], 1])
+    do = ki.round_storage(rng.standard_normal((spec.B, spec.T, spec.H, spec.dv)), spec.dtype)
+    dS = ki.round_to_f32(rng.standard_normal((spec.B, spec.H, spec.dk, spec.dv)) * 0.1) if c["with_dS"] else None
+    dd = dev_inputs(d, spec.dtype)
+    g = kda.chunk_bwd_z(dd["q"], dd["k"], dd["v"], dd["beta"], dd["z"], dd["A"], dev(do, spec.dtype),
+                        None if dS is None else dev(dS, "f32"), c["g_min"], dd["S0"], c["scale"])
+    torch.cuda.synchronize()
+    f = f64_inputs(d, spec.dtype)
+    ref = OB.backward_z(f["q"], f["k"], f["v"], f["beta"], f["z"], f["A"], ki.to_f64(do, spec.dtype),
+                        None if dS is None else dS.astype(np.float64), c["g_min"], f["S0"], c["scale"])
+    errs = {n: rel_l2(host64(g[n]), ref[n]) for n in ("dq", "dk", "dv", "dbeta", "dz", "dA", "dS_in")}
+    say("  rel-L2 " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    for n, e in errs.items():
+        assert e <= TOL[c["dtype"]], (n, e)
