@@ -1,9 +1,10 @@
 """GPU parity of the backward pass (kda_chunk_bwd_z) against the fp64 oracle's
 reverse-mode derivative (oracle.backward), on the same rounded inputs and the
 same upstream gradients.  Tolerance: relative L2 per gradient, 1e-5 for fp32
-inputs and 1e-2 for bf16 inputs (the bf16 path takes its checkpoints from the
-bf16 matrix-core forward and runs its long products with bf16 operands and fp32
-accumulation; measured up to 5e-3)."""
+inputs (1e-4 for the gate's derivatives dz and dA, whose chunk-form terms cancel:
+see ``bwd_tol``) and 1e-2 for bf16 inputs (the bf16 path takes its checkpoints
+from the bf16 matrix-core forward and runs its long products with bf16 operands
+and fp32 accumulation; measured up to 5e-3)."""
 import numpy as np
 import pytest
 import torch
@@ -11,7 +12,7 @@ import torch
 import gated_delta_rule_11_amd as kda
 import kda_inputs as ki
 import oracle.backward as OB
-from tests._gpu import DEV, TOL, dev, dev_inputs, f64_inputs, host64, rel_l2, say
+from tests._gpu import DEV, TOL, bwd_tol, dev, dev_inputs, f64_inputs, host64, rel_l2, say
 
 pytestmark = pytest.mark.gpu
 
@@ -60,7 +61,7 @@ def test_backward_vs_oracle(B, H, T, dk, dv, dtype, s0, zm, with_dS, scale):
         errs[name] = rel_l2(host64(g[name]), ref[rname])
     say("  rel-L2 " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
     for name, e in errs.items():
-        assert e <= TOL[dtype], (name, e)
+        assert e <= bwd_tol(dtype, name), (name, e)
 
 
 def test_backward_empty_and_deterministic():
@@ -111,7 +112,7 @@ def test_backward_one_slice_many_heads(dtype):
         errs["dS_in"] = rel_l2(host64(g["dS_in"][:, h:h + 1]), ref["dS_in"])
         say(f"  h={h} rel-L2 " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
         for name, e in errs.items():
-            assert e <= TOL[dtype], (h, name, e)
+            assert e <= bwd_tol(dtype, name), (h, name, e)
 
 
 def test_backward_32k_sampled():

@@ -2,7 +2,8 @@
 the same cases): head sizes, chunk length, input and output dtypes, batch,
 heads, ragged sequence lengths, gate floor, output scale, initial state and
 entry point (fused gate, precomputed G, fused prologue, an explicit segment
-count) for the chunked prefill, the same for decode steps, and for the
+count) for the chunked prefill, with many heads for the launch shapes that
+depend on the head count, the same for decode steps, the draft replay and the
 backward.  Each case is compared with the fp64 oracle (per sequence and per
 16-token block for the prefill outputs), at the tolerance of the input dtype.  The hand-picked cases elsewhere cover the edges
 one at a time; these mix them."""
@@ -14,7 +15,7 @@ import gated_delta_rule_11_amd as kda
 import kda_inputs as ki
 import oracle
 import oracle.backward as OB
-from tests._gpu import TOL, assert_states, assert_tokens, dev, dev_inputs, f64_inputs, host64, rel_l2, say
+from tests._gpu import TOL, assert_states, assert_tokens, bwd_tol, dev, dev_inputs, f64_inputs, host64, rel_l2, say
 
 pytestmark = pytest.mark.gpu
 
@@ -23,7 +24,7 @@ LENGTHS = (0, 1, 15, 17, 63, 64, 65, 129, 200, 333, 512)
 PATHS = ("z", "G", "prologue", "segmented")
 
 
-def _prefill_cases(n=24, seed=20261):
+def _prefill_cases(n=48, seed=20261):
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(n):
@@ -50,7 +51,27 @@ def _id(c):
             f"-g{c['g_min']}-s{c['segs']}")
 
 
-@pytest.mark.parametrize("c", _prefill_cases(), ids=_id)
+def _wide_cases(n=8, seed=20264):
+    """Many heads (B*H from 8 to 512): the launch shapes that depend on the head count
+    (value-column slices of the matrix-core and tile kernels, segment counts chosen by
+    the library)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dtype = str(rng.choice(["f32", "bf16"]))
+        if i % 2 == 0:
+            dk = dv = 128
+            chunk = 64
+        else:
+            dk, dv, chunk = int(rng.choice(DIMS)), int(rng.choice(DIMS)), int(rng.choice([16, 64]))
+        cases.append(dict(B=int(rng.choice([1, 2, 4, 8])), H=int(rng.choice([8, 16, 32, 64])),
+                          T=int(rng.choice([17, 64, 100])), dk=dk, dv=dv, chunk=chunk, dtype=dtype,
+                          path=str(rng.choice(["z", "G"])), segs=1, s0=0.2, zm=float(rng.choice([0.0, -3.0])),
+                          g_min=-5.0, scale=1.0, o_bf16=False, seed=7300 + i))
+    return cases
+
+
+@pytest.mark.parametrize("c", _prefill_cases() + _wide_cases(), ids=_id)
 def test_random_prefill_vs_oracle(c):
     say(f"case random prefill {c}")
     spec = ki.small_spec(c["B"], c["H"], c["T"], c["dk"], c["dv"], c["chunk"], c["dtype"], seed=c["seed"],
@@ -81,7 +102,7 @@ def test_random_prefill_vs_oracle(c):
     assert_states("S", host64(S), S_ref, tol)
 
 
-def _decode_cases(n=10, seed=20262):
+def _decode_cases(n=16, seed=20262):
     rng = np.random.default_rng(seed)
     return [dict(N=int(rng.integers(1, 9)), H=int(rng.integers(1, 5)), dk=int(rng.choice(DIMS)),
                  dv=int(rng.choice(DIMS)), dtype=str(rng.choice(["f32", "bf16"])), prologue=bool(rng.integers(0, 2)),
@@ -111,7 +132,7 @@ def test_random_decode_vs_oracle(c):
     assert eo <= TOL[c["dtype"]] and es <= TOL[c["dtype"]]
 
 
-def _backward_cases(n=8, seed=20263):
+def _backward_cases(n=16, seed=20263):
     rng = np.random.default_rng(seed)
     return [dict(B=int(rng.integers(1, 3)), H=int(rng.integers(1, 4)),
                  T=int(rng.choice([1, 15, 16, 17, 64, 65, 100, 150])), dk=int(rng.choice(DIMS)),
@@ -141,4 +162,35 @@ def test_random_backward_vs_oracle(c):
     errs = {n: rel_l2(host64(g[n]), ref[n]) for n in ("dq", "dk", "dv", "dbeta", "dz", "dA", "dS_in")}
     say("  rel-L2 " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
     for n, e in errs.items():
-        assert e <= TOL[c["dtype"]], (n, e)
+        assert e <= bwd_tol(c["dtype"], n), (n, e)
+
+
+def _replay_cases(n=8, seed=20265):
+    rng = np.random.default_rng(seed)
+    return [dict(n_draft=int(rng.integers(1, 20)), N=int(rng.integers(1, 9)), H=int(rng.integers(1, 4)),
+                 dk=int(rng.choice(DIMS)), dv=int(rng.choice(DIMS)), dtype=str(rng.choice(["f32", "bf16"])),
+                 g_min=float(rng.choice([-5.0, -2.0, 0.0])), scale=float(rng.choice([1.0, 0.125])), seed=7400 + i)
+            for i in range(n)]
+
+
+@pytest.mark.parametrize("c", _replay_cases(),
+                         ids=lambda c: f"{c['dtype']}-n{c['n_draft']}-N{c['N']}H{c['H']}-d{c['dk']}x{c['dv']}")
+def test_random_replay_vs_oracle(c):
+    say(f"case random replay {c}")
+    spec = ki.DecodeSpec("replay_random", N=c["N"], H=c["H"], dk=c["dk"], dv=c["dv"], steps=c["n_draft"],
+                         dtype=c["dtype"], s_std=0.1, seed=c["seed"])
+    d = ki.decode_inputs(spec)
+    acc = np.random.default_rng([c["seed"], 2]).integers(0, c["n_draft"] + 1, size=c["N"]).astype(np.int32)
+    f = f64_inputs(d, c["dtype"])
+    o_ref, S_ref = oracle.replay(f["q"], f["k"], f["v"], f["z"], f["beta"], f["A"], f["S0"], acc, c["g_min"],
+                                 c["scale"])
+    dd = dev_inputs(d, c["dtype"])
+    snap = dd["S0"].clone()
+    o, S = kda.decode_replay(dd["q"], dd["k"], dd["v"], dd["z"], dd["beta"], dd["A"], dd["S0"],
+                             torch.from_numpy(acc).to(dd["A"].device), c["g_min"], o_dtype=torch.float32,
+                             scale=c["scale"])
+    torch.cuda.synchronize()
+    assert torch.equal(dd["S0"], snap)  # the snapshot is read only
+    eo, es = rel_l2(host64(o), o_ref), rel_l2(host64(S), S_ref)
+    say(f"  accepted {acc.tolist()} rel-L2 o={eo:.3e} S_commit={es:.3e}")
+    assert eo <= TOL[c["dtype"]] and es <= TOL[c["dtype"]]
