@@ -63,8 +63,7 @@ struct Layout {
   static constexpr int EB = DT + 4 * DK * 4;            // [4][128] fp32 decay before tile i
   static constexpr int GC = EB + 4 * DK * 4;            // [128] fp32 chunk decay
   static constexpr int BT = GC + DK * 4;                // [64] fp32 beta
-  static constexpr int RH = BT + C * 4;                 // [64] fp32 query normalisers (fused prologue)
-  static constexpr int LF = RH + C * 4;                 // [4][16][LFS] fp32 (L_ii)^T, one per chain wavefront
+  static constexpr int LF = BT + C * 4;                 // [4][16][LFS] fp32 (L_ii)^T, one per chain wavefront
   static constexpr int BYTES = LF + 4 * 16 * LFS * 4;
   static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
@@ -277,9 +276,11 @@ __constant__ int8_t kOffPairs8[4][2][2] = {{{1, 0}, {3, 0}}, {{2, 1}, {3, 1}}, {
 // workgroup per segment; identity entry state, zero values, outputs skipped,
 // per-segment states); the plain instantiation compiles all of that out.
 // NORM instantiations fuse the prologue: the gate wavefronts take each token's
-// key norm (a lane reduction) into the factors the raw keys are multiplied by
-// anyway, compute beta = sigmoid(logit), and hand the query normalisers to the
-// state chain, which applies them to the output rows (o is linear in q_t).
+// key and query norms (lane reductions) into the factors the raw keys and queries
+// are multiplied by anyway, and compute beta = sigmoid(logit).  The query is
+// normalised before its decay factor is applied: a raw query scaled by the decay
+// of a saturated tile (down to e^-86.4) could fall below the smallest normal
+// number and lose its precision.
 //
 // STO (state only) instantiations serve the segment passes that write no outputs
 // (end states, transitions, backward checkpoints): no queries are loaded and neither
@@ -308,7 +309,6 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
   float* sEB = reinterpret_cast<float*>(smem + Ly::EB);
   float* sGC = reinterpret_cast<float*>(smem + Ly::GC);
   float* sBeta = reinterpret_cast<float*>(smem + Ly::BT);
-  float* sRho = reinterpret_cast<float*>(smem + Ly::RH);
   float* sLf = reinterpret_cast<float*>(smem + Ly::LF);
 
   // workgroup -> ((b*H + h) * nseg + segment, slice); the slices of one head and
@@ -533,8 +533,6 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             f32x4 acc = O[i];
-            // prologue: query normalisers of this lane's four output rows
-            const f32x4 rho = NORM ? *reinterpret_cast<const f32x4*>(&sRho[16 * i + 4 * g4]) : f32x4{1.f, 1.f, 1.f, 1.f};
             const uint16_t* Pr = &sP[(16 * i + r16) * TS + 4 * g4];
 #pragma unroll
             for (int m = 0; m + 1 <= i; m += 2)
@@ -548,7 +546,7 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
             for (int v = 0; v < 4; ++v) {
               const int t = 16 * i + 4 * g4 + v;
               const int voff = (t * H * DK + 16 * wv + r16) * ES;
-              const float ov = NORM ? (a.scale * rho[v]) * acc[v] : a.scale * acc[v];
+              const float ov = a.scale * acc[v];
               if (ES == 2)
                 __builtin_amdgcn_raw_buffer_store_b16(f2bf(ov), ro, voff, 0, 0);
               else
@@ -610,7 +608,7 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
     float Dt[4] = {1.f, 1.f, 1.f, 1.f};  // A1 -> A2: decay over the tile
     u32x4 kh[4];                         // A2 -> 2: (k Gamma_C / Gamma)^T, 8 tokens per channel
     float gc[4] = {1.f, 1.f, 1.f, 1.f};  // A2 -> 2: Gamma_C (written by tile 0's wavefront)
-    float rho = 1.f;                     // A1 -> 2 (prologue): query normaliser of token (ln >> 2) & 7 of the half
+    float nqt[8];                        // A1 -> A2 (prologue): query normalisers of this lane's tokens
     auto q4 = [](u32x2 x, int j) __attribute__((always_inline)) {  // channel j of a bf16 quad
       return (j & 1) ? bfhi(x[j >> 1]) : bflo(x[j >> 1]);
     };
@@ -644,11 +642,10 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
         *reinterpret_cast<u32x4*>(&sVT[col * TS + tb]) = u32x4{lo[0], lo[1], lo[2], lo[3]};
         *reinterpret_cast<u32x4*>(&sVT[(col + 1) * TS + tb]) = u32x4{hi[0], hi[1], hi[2], hi[3]};
       }
-      // prologue: 1 / sqrt(|k_t|^2 + eps) of this half's tokens, and the query
-      // normalisers, kept for the state chain
-      float nk[8];
+      // prologue: 1 / sqrt(|x_t|^2 + eps) of this half's keys and queries
+      float nk[8], nq[8];
 #pragma unroll
-      for (int tt = 0; tt < 8; ++tt) nk[tt] = 1.f;
+      for (int tt = 0; tt < 8; ++tt) nk[tt] = nq[tt] = 1.f;
       if constexpr (NORM) {
         float pk[8], pq[8];
         // sums of squares of this lane's four channels: the quad is bit-cast whole and
@@ -664,12 +661,15 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
           pq[tt] = sumsq(R.q[tt]);
         }
         const float rkl = rsqrt_fast(half_token_sums8(pk, ln) + kL2Eps);
-        rho = rsqrt_fast(half_token_sums8(pq, ln) + kL2Eps);
+        const float rql = rsqrt_fast(half_token_sums8(pq, ln) + kL2Eps);
 #pragma unroll
         for (int tt = 0; tt < 8; ++tt) {
           const float n0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rkl), 4 * tt));
           const float n1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rkl), 32 + 4 * tt));
           nk[tt] = gh ? n1 : n0;
+          const float m0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rql), 4 * tt));
+          const float m1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rql), 32 + 4 * tt));
+          nq[tt] = gh ? m1 : m0;
         }
       }
       // r (prefix products up to and including t) and sf (products after t), within
@@ -748,6 +748,7 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
 #pragma unroll
         for (int j = 0; j < 4; ++j) rp[tt][j] = valid ? rr[tt][j] : 0.f;
         nkt[tt] = nk[tt];
+        nqt[tt] = nq[tt];
       }
       // k sf of this tile is the anchored-key slot (i + 1, i) as it stands (no tile
       // in between); the scaled slots read it back in the next phase
@@ -817,12 +818,15 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
         if constexpr (!STO) {
           // q r (read by the next phase 2) and q Gamma (read by the next A1); the state
           // chain's reads of the current chunk's q Gamma ended with A1
+          // (prologue: the query's normaliser taken into the same factor)
           const u32x2 q = R.q[tt];
+          const float nq = nqt[tt];
           *reinterpret_cast<u32x2*>(&sQR[row * RS + c0]) =
-              pack4(q4(q, 0) * rp[tt][0], q4(q, 1) * rp[tt][1], q4(q, 2) * rp[tt][2], q4(q, 3) * rp[tt][3]);
+              pack4(q4(q, 0) * (rp[tt][0] * nq), q4(q, 1) * (rp[tt][1] * nq), q4(q, 2) * (rp[tt][2] * nq),
+                    q4(q, 3) * (rp[tt][3] * nq));
           *reinterpret_cast<u32x2*>(&sQt[row * RS + c0]) =
-              pack4(q4(q, 0) * (rp[tt][0] * eB[0]), q4(q, 1) * (rp[tt][1] * eB[1]), q4(q, 2) * (rp[tt][2] * eB[2]),
-                    q4(q, 3) * (rp[tt][3] * eB[3]));
+              pack4(q4(q, 0) * (rp[tt][0] * nq * eB[0]), q4(q, 1) * (rp[tt][1] * nq * eB[1]),
+                    q4(q, 2) * (rp[tt][2] * nq * eB[2]), q4(q, 3) * (rp[tt][3] * nq * eB[3]));
         }
       }
       // (k Gamma_C / Gamma)^T of this half's tokens: channel c0 + j, tokens 8 gh .. + 7
@@ -843,7 +847,6 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
 #pragma unroll
       for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(&sKhT[(c0 + j) * TS + 16 * i + 8 * gh]) = kh[j];
       if (i == 0 && gh == 0) *reinterpret_cast<f32x4*>(&sGC[c0]) = f32x4{gc[0], gc[1], gc[2], gc[3]};
-      if (NORM && (ln & 3) == 0) sRho[16 * i + 8 * gh + ((ln >> 2) & 7)] = rho;
     };
 
     // ---- prologue: operand tiles of chunk 0

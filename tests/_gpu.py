@@ -6,7 +6,15 @@ tensor: at a million tokens one 64-token block is 1/16384 of the output, so a
 block that came out entirely wrong would barely move a whole-tensor relative
 L2.  ``assert_tokens`` therefore checks the relative L2 of every (b, h)
 sequence and of every 64-token block of it, and ``assert_states`` that of
-every (b, h) state, each against the same tolerance."""
+every (b, h) state, each against the same tolerance.
+
+A sequence or block whose outputs are smaller than the tensor's typical
+magnitude is measured against that typical magnitude instead of its own (its
+error norm over the norm it would have at the tensor's RMS per element): an
+output that is a short sum of products can be far smaller than the terms that
+form it (one token's output is beta (q . k) v), and rounding of those terms,
+at the level the dtype allows, is then a large fraction of it.  A wrong block
+still fails: its error is of the order of the typical magnitude."""
 from __future__ import annotations
 
 import sys
@@ -19,6 +27,26 @@ import kda_inputs as ki
 DEV = "cuda:0"
 TOL = {"f32": 1e-5, "bf16": 1e-2}
 BLOCK = 64
+
+
+def grad_errors(g: dict, ref: dict, names) -> dict:
+    """Relative L2 of each gradient against the fp64 reference.  A gradient whose reference
+    is exactly zero (a structural zero: dz and dA with one token and a zero initial state,
+    where the state that the decay acts on is zero) cannot come out exactly zero from
+    rounded arithmetic; it is measured by its largest magnitude over the largest magnitude
+    among the call's non-zero reference gradients."""
+    refs = {n: np.asarray(ref[n], np.float64) for n in names}
+    gots = {n: host64(g[n]) for n in names}
+    scale = max([float(np.abs(r).max()) for r in refs.values() if r.size and np.any(r)] or [0.0])
+    out = {}
+    for n in names:
+        r, x = refs[n], gots[n]
+        if r.size and not np.any(r) and scale > 0.0:
+            assert np.all(np.isfinite(x)), f"non-finite values in {n}"
+            out[n] = float(np.abs(x).max()) / scale
+        else:
+            out[n] = rel_l2(x, r)
+    return out
 
 
 def bwd_tol(dtype: str, name: str) -> float:
@@ -76,8 +104,10 @@ def _ratio(d2: np.ndarray, r2: np.ndarray) -> np.ndarray:
 def token_report(x: np.ndarray, ref: np.ndarray, block: int = BLOCK) -> dict:
     """x, ref [B, T, H, d]: relative L2 over the whole tensor, per (b, h)
     sequence and per (b, h, block of ``block`` tokens; the last block also takes
-    the remainder of T, so it holds ``block`` to 2 ``block`` - 1 tokens); the
-    largest absolute error and where it is."""
+    the remainder of T, so it holds ``block`` to 2 ``block`` - 1 tokens), each of
+    the latter two with its reference energy floored at the tensor's mean energy
+    per element times its element count; the largest absolute error and where
+    it is."""
     x = np.asarray(x, np.float64)
     ref = np.asarray(ref, np.float64)
     assert x.shape == ref.shape and x.ndim == 4, (x.shape, ref.shape)
@@ -93,8 +123,13 @@ def token_report(x: np.ndarray, ref: np.ndarray, block: int = BLOCK) -> dict:
     starts = np.arange(nb) * block
     d2b = np.add.reduceat(d2, starts, axis=1) if T else np.zeros((B, 1, H))  # [B, nb, H]
     r2b = np.add.reduceat(r2, starts, axis=1) if T else np.zeros((B, 1, H))
-    blk = _ratio(d2b, r2b)
-    pair = _ratio(d2b.sum(axis=1), r2b.sum(axis=1))  # [B, H]
+    # the floor: the energy the sequence or block would have at the tensor's mean energy
+    # per element (0 when the whole reference is zero: then only exact zeros pass)
+    e_mean = float(r2.sum()) / max(1, x.size)
+    n_blk = np.diff(np.append(starts, T)) if T else np.zeros(1)  # tokens per block
+    fl_b = e_mean * x.shape[3] * n_blk[None, :, None]
+    blk = _ratio(d2b, np.maximum(r2b, fl_b))
+    pair = _ratio(d2b.sum(axis=1), np.maximum(r2b.sum(axis=1), e_mean * x.shape[3] * T))  # [B, H]
     whole = float(_ratio(np.array(d2b.sum()), np.array(r2b.sum())))
     ab = np.abs(diff)
     iw = np.unravel_index(int(np.argmax(ab)), ab.shape) if ab.size else (0, 0, 0, 0)

@@ -12,7 +12,7 @@ import torch
 import gated_delta_rule_11_amd as kda
 import kda_inputs as ki
 import oracle.backward as OB
-from tests._gpu import DEV, TOL, bwd_tol, dev, dev_inputs, f64_inputs, host64, rel_l2, say
+from tests._gpu import DEV, TOL, bwd_tol, dev, dev_inputs, f64_inputs, grad_errors, host64, rel_l2, say
 
 pytestmark = pytest.mark.gpu
 
@@ -56,9 +56,7 @@ def test_backward_vs_oracle(B, H, T, dk, dv, dtype, s0, zm, with_dS, scale):
     spec = ki.small_spec(B, H, T, dk, dv, 64, dtype, seed=6100 + T + dk + dv, s0_std=s0, z_mean=zm)
     say(f"case backward B={B} H={H} T={T} dk={dk} dv={dv} {dtype} s0={s0} z_mean={zm} dS_out={with_dS}")
     g, ref = _run(spec, with_dS, scale)
-    errs = {}
-    for name, rname in GRADS:
-        errs[name] = rel_l2(host64(g[name]), ref[rname])
+    errs = grad_errors(g, ref, [name for name, _ in GRADS])
     say("  rel-L2 " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
     for name, e in errs.items():
         assert e <= bwd_tol(dtype, name), (name, e)

@@ -15,7 +15,8 @@ import gated_delta_rule_11_amd as kda
 import kda_inputs as ki
 import oracle
 import oracle.backward as OB
-from tests._gpu import TOL, assert_states, assert_tokens, bwd_tol, dev, dev_inputs, f64_inputs, host64, rel_l2, say
+from tests._gpu import (TOL, assert_states, assert_tokens, bwd_tol, dev, dev_inputs, f64_inputs, grad_errors, host64,
+                        rel_l2, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -159,7 +160,7 @@ def test_random_backward_vs_oracle(c):
     f = f64_inputs(d, spec.dtype)
     ref = OB.backward_z(f["q"], f["k"], f["v"], f["beta"], f["z"], f["A"], ki.to_f64(do, spec.dtype),
                         None if dS is None else dS.astype(np.float64), c["g_min"], f["S0"], c["scale"])
-    errs = {n: rel_l2(host64(g[n]), ref[n]) for n in ("dq", "dk", "dv", "dbeta", "dz", "dA", "dS_in")}
+    errs = grad_errors(g, ref, ("dq", "dk", "dv", "dbeta", "dz", "dA", "dS_in"))
     say("  rel-L2 " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
     for n, e in errs.items():
         assert e <= bwd_tol(c["dtype"], n), (n, e)

@@ -67,6 +67,28 @@ def test_state_per_sequence_and_exact_zero():
     assert token_report(nz, z)["block_max"] == np.inf
 
 
+def test_small_sequences_are_measured_against_the_typical_magnitude():
+    """A sequence whose outputs are 100 times smaller than the rest, off by rounding at
+    the rest's magnitude, passes; the same sequence off by more than the tolerance times
+    the typical magnitude, or set to zero, fails."""
+    rng = np.random.default_rng(4)
+    ref = rng.standard_normal((1, 256, 4, 8))
+    ref[0, :, 2] *= 1e-2
+    x = _noisy(ref, 1e-3, rng)  # noise at 1e-3 of the tensor's RMS everywhere
+    r = token_report(x, ref)
+    assert r["pair_max"] < 2e-3 and r["block_max"] < 3e-3  # the small head: 1e-1 of its own norm
+    wrong = x.copy()
+    wrong[0, :, 2] += 3e-2 * np.sqrt(np.mean(ref * ref))
+    with pytest.raises(AssertionError):
+        assert_tokens("small sequence off", wrong, ref, 1e-2)
+    lost = x.copy()
+    lost[0, 64:128, 1] = 0.0  # a block of a typical head lost
+    r = token_report(lost, ref)
+    assert r["block_at"] == (0, 64, 1) and r["block_max"] > 0.5
+    with pytest.raises(AssertionError, match="rel-L2"):
+        assert_tokens("lost", lost, ref, 1e-2)
+
+
 def test_non_finite_output_fails():
     ref = np.ones((1, 64, 1, 4))
     x = ref.copy()
