@@ -50,9 +50,11 @@ bool sizes_ok(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv) {
 
 kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
 
-// g_min accepted by the gate and the chunked prefill: 16 g_min >= -86.4 keeps the
-// decay of any 16-token tile (and so its reciprocal) a normal fp32 number.
-constexpr float kGminFloor = -5.4f;
+// g_min accepted by the gate and the chunked prefill (the pages fix -5): 16 g_min >= -80
+// keeps the decay of any 16-token tile and its reciprocal normal fp32 numbers with room to
+// spare, so that a unit-norm query or key component down to about 1e-3 times that decay is
+// still a normal number (the matrix-core kernel anchors its decay factors at tile starts).
+constexpr float kGminFloor = -5.0f;
 bool gmin_ok(float g) { return isfinite(g) && g <= 0.f && g >= kGminFloor; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }

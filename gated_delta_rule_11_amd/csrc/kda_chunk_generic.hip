@@ -17,7 +17,7 @@
 //   U = Tm (V - (K * 2^Gl) S)                 (= Tm V - W S with W = Tm (K * 2^Gl))
 //   o = scale ((Q * 2^Gl) S + P U)
 //   S <- Diag(2^Gl_15) S + (K * 2^(Gl_15 - Gl))^T U
-// With g >= g_min >= -5.4 every exponent lies within 63 of zero (the anchor is
+// With g >= g_min >= -5 every exponent lies within 58 of zero (the anchor is
 // mid-tile), so no factor over- or underflows; a caller's own G obeys the tile
 // bound the header states.  Tokens past the end of the sequence enter as
 // k = q = v = beta = g = 0, which leaves S and the valid rows unchanged.

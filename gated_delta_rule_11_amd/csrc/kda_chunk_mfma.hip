@@ -279,7 +279,7 @@ __constant__ int8_t kOffPairs8[4][2][2] = {{{1, 0}, {3, 0}}, {{2, 1}, {3, 1}}, {
 // key and query norms (lane reductions) into the factors the raw keys and queries
 // are multiplied by anyway, and compute beta = sigmoid(logit).  The query is
 // normalised before its decay factor is applied: a raw query scaled by the decay
-// of a saturated tile (down to e^-86.4) could fall below the smallest normal
+// of a saturated tile (down to e^-80) could fall below the smallest normal
 // number and lose its precision.
 //
 // STO (state only) instantiations serve the segment passes that write no outputs

@@ -94,7 +94,7 @@ int kda_chunk_uses_mfma(kda_dtype in_dtype, int dk, int dv, int chunk);
  * (-80, 0) the same section states.
  *
  *   z      [B,T,H,dk] in z_dtype (device)     A [H,dk] fp32 (device)
- *   g_min  lower bound of g (the pages fix -5), in [-5.4, 0]: the range the
+ *   g_min  lower bound of g (the pages fix -5), in [-5, 0]: the range the
  *          chunked prefill accepts (KDA_ERR_UNSUPPORTED otherwise)
  *   chunk  1, 16 or 64
  *   G      [B,T,H,dk] fp32 (device, written); must not overlap z or A
@@ -132,10 +132,10 @@ size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int ch
  *   G      [B,T,H,dk] fp32 chunk-local sums (chunk must match kda_gate's).
  *          Every channel's log-decay over any aligned 16-token tile (both
  *          kernels anchor their decay factors per tile), G at the tile's last
- *          token minus G before its first, must be at least -86.4: the
- *          tile's decay must be a normal fp32 number and its reciprocal
- *          finite.  G from kda_gate with g_min >= -5.4 always is; the
- *          bounded gate of the pages (g_min = -5) keeps it above -80.
+ *          token minus G before its first, must be at least -80: the
+ *          tile's decay and its reciprocal must be normal fp32 numbers,
+ *          and so must a query or key component times that decay.  G from
+ *          kda_gate (g_min >= -5, the bounded gate of the pages) always is.
  *   S_in   [B,H,dk,dv] fp32 or NULL (zero state)
  *   o      [B,T,H,dv] in o_dtype (written)
  *   S_out  [B,H,dk,dv] fp32 or NULL (not written); may equal S_in exactly
@@ -160,9 +160,9 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v,
  * decay logits z [B,T,H,dk] (in_dtype), A [H,dk] fp32 and g_min instead of G.
  * Equal to kda_gate followed by kda_chunk_fwd up to rounding; this is the
  * path that avoids the fp32 round trip of G through memory.  g_min must lie
- * in [-5.4, 0] (16 g_min >= -86.4 keeps every 16-token tile's decay a
- * normal fp32 number and its reciprocal finite); other values return
- * KDA_ERR_UNSUPPORTED.
+ * in [-5, 0] (16 g_min >= -80 keeps every 16-token tile's decay, its
+ * reciprocal and a query or key component times that decay normal fp32
+ * numbers); other values return KDA_ERR_UNSUPPORTED.
  * Workspace: as kda_chunk_fwd.
  */
 kda_status kda_chunk_fwd_z(const void* q, const void* k, const void* v,

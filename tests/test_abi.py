@@ -104,8 +104,9 @@ def test_gate_validation(L):
     assert gate(L, chunk=32) == ERR_UNSUPPORTED
     assert gate(L, gmin=1.0) == ERR_UNSUPPORTED
     assert gate(L, gmin=float("nan")) == ERR_UNSUPPORTED
-    assert gate(L, gmin=-5.5) == ERR_UNSUPPORTED     # 16 g_min >= -86.4: tile decays stay normal fp32
-    assert gate(L, gmin=-5.4, z=None) == ERR_NULL    # the floor itself is accepted
+    assert gate(L, gmin=-5.5) == ERR_UNSUPPORTED     # 16 g_min >= -80: tile decays stay normal fp32
+    assert gate(L, gmin=-5.01) == ERR_UNSUPPORTED
+    assert gate(L, gmin=-5.0, z=None) == ERR_NULL    # the floor itself is accepted
     assert gate(L, z=None) == ERR_NULL
     assert gate(L, G=None) == ERR_NULL
     assert gate(L, A=None) == ERR_NULL
@@ -140,7 +141,8 @@ def test_chunk_validation(L):
     assert chunk(L, B=0) == OK
     assert chunk_z(L, gmin=-6.0) == ERR_UNSUPPORTED
     assert chunk_z(L, gmin=-5.5) == ERR_UNSUPPORTED
-    assert chunk_z(L, gmin=-5.4, q=None) == ERR_NULL
+    assert chunk_z(L, gmin=-5.4) == ERR_UNSUPPORTED
+    assert chunk_z(L, gmin=-5.0, q=None) == ERR_NULL
     assert chunk_z(L, gmin=0.5) == ERR_UNSUPPORTED
     assert chunk_z(L, z=None) == ERR_NULL
     assert chunk_z(L, A=None) == ERR_NULL

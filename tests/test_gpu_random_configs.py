@@ -41,7 +41,7 @@ def _prefill_cases(n=48, seed=20261):
         cases.append(dict(
             B=int(rng.integers(1, 4)), H=int(rng.integers(1, 7)), T=T, dk=dk, dv=dv, chunk=chunk, dtype=dtype,
             path=path, segs=int(rng.integers(1, 7)), s0=float(rng.choice([0.0, 0.2])),
-            zm=float(rng.choice([0.0, -3.0, 2.0])), g_min=float(rng.choice([-5.4, -5.0, -2.0, 0.0])),
+            zm=float(rng.choice([0.0, -3.0, 2.0])), g_min=float(rng.choice([-5.0, -4.5, -2.0, 0.0])),
             scale=float(rng.choice([1.0, 0.125])), o_bf16=bool(dtype == "bf16" and rng.integers(0, 2)),
             seed=7000 + i))
     return cases
