@@ -159,11 +159,18 @@ def state_report(x: np.ndarray, ref: np.ndarray) -> dict:
             "max_abs": float(ab.max()) if ab.size else 0.0}
 
 
+# Sequences shorter than one 16-token tile are judged over the whole tensor only: the
+# relative L2 of one token's outputs is that of a single dot product of rounded operands
+# (beta (q . k) v), which has no relative bound at any resolution where q . k cancels.
+MIN_UNIT_TOKENS = 16
+
+
 def assert_tokens(label: str, x: np.ndarray, ref: np.ndarray, tol: float, block: int = BLOCK,
                   offset: tuple = (0, 0)) -> dict:
-    """Relative L2 <= tol over every (b, h) sequence and every ``block``-token
-    block of it (and so over the whole tensor).  ``offset`` = (b0, h0) of x
-    within the full tensor, for the printed coordinates."""
+    """Relative L2 <= tol over the whole tensor and, for sequences of at least
+    MIN_UNIT_TOKENS tokens, over every (b, h) sequence and every ``block``-token
+    block of it.  ``offset`` = (b0, h0) of x within the full tensor, for the
+    printed coordinates."""
     r = token_report(x, ref, block)
     b0, h0 = offset
     pb, ph = r["pair_at"]
@@ -172,8 +179,10 @@ def assert_tokens(label: str, x: np.ndarray, ref: np.ndarray, tol: float, block:
     say(f"  {label}: rel-L2 whole {r['whole']:.3e}; worst (b,h) {r['pair_max']:.3e} at ({pb + b0},{ph + h0}); "
         f"worst of {r['blocks']} {block}-token blocks {r['block_max']:.3e} at (b={bb + b0}, t={bt}, h={bh + h0}); "
         f"max-abs {r['max_abs']:.3e} at (b={mb + b0}, t={mt}, h={mh + h0}, c={mc})")
-    assert r["pair_max"] <= tol, f"{label}: sequence rel-L2 {r['pair_max']:.3e} > {tol}"
-    assert r["block_max"] <= tol, f"{label}: {block}-token block rel-L2 {r['block_max']:.3e} > {tol}"
+    assert r["whole"] <= tol, f"{label}: whole-tensor rel-L2 {r['whole']:.3e} > {tol}"
+    if x.shape[1] >= MIN_UNIT_TOKENS:
+        assert r["pair_max"] <= tol, f"{label}: sequence rel-L2 {r['pair_max']:.3e} > {tol}"
+        assert r["block_max"] <= tol, f"{label}: {block}-token block rel-L2 {r['block_max']:.3e} > {tol}"
     return r
 
 
