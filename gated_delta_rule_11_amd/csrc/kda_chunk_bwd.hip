@@ -1,4 +1,4 @@
-// kda_chunk_bwd.hip -- backward pass of the fused-gate KDA prefill, fp32 MFMA.
+// kda_chunk_bwd.hip -- backward pass of the fused-gate KDA prefill on matrix cores.
 //
 // The forward is Eq. 1 of "Kimi K3: the paper and proofs side by side",
 // section 2.1.1, with the gate of "Kimi K3 reading notes", section 2, in the
@@ -28,9 +28,13 @@
 // The forward left the state entering each block (checkpoints); the workgroup
 // first recomputes the states entering the block's later sub-chunks (into a
 // per-workgroup scratch, L2-resident), then runs the sub-chunks backwards.
-// All products run on v_mfma_f32_16x16x4_f32 (fp32 operands, as the generic
-// forward): lane i supplies A[i % 16][i / 16] and B[i / 16][i % 16] and holds
-// D[4 (i / 16) + v][i % 16].  The state S and the running gradient dS are held
+// fp32 inputs: every product runs on v_mfma_f32_16x16x4_f32 (fp32 operands): lane
+// i supplies A[i % 16][i / 16] and B[i / 16][i % 16] and holds D[4 (i / 16) + v][i % 16].
+// bf16 inputs: the products run on v_mfma_f32_16x16x16_bf16 (bf16 operands, fp32
+// accumulation) with the same lane layout, lane group g holding k = 4 g .. 4 g + 3,
+// except dKt = T^T dW, the dL-free parts of dQt and dKb, dP, dT and the M, dM, Y, dL
+// chain, which stay fp32 for every input dtype: dbeta and dG sum products of these with
+// the inputs whose terms cancel.  The state S and the running gradient dS are held
 // in registers twice: by value-column tile (wavefront w owns columns 16 w..)
 // for the products that contract over key channels, and transposed, by key-row
 // tile, for those that contract over value channels.
@@ -145,8 +149,7 @@ __device__ __forceinline__ void bw_barrier_global() {
 template <int DK, int DV, int NSP, typename Tin, typename Tdo>
 __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
   using namespace bw;
-  // bf16 inputs: the long contractions (over d_k or d_v) on bf16 matrix cores, operands
-  // rounded to bf16, fp32 accumulation; the 16-deep products over tokens stay fp32
+  // bf16 inputs: bf16 operands for the products the file header lists, fp32 accumulation
   constexpr bool BF = std::is_same<Tin, bf16_t>::value;
   constexpr int DVS = DV / NSP;  // value columns of this workgroup's slice
   using Ly = Layout<DK, DVS>;
