@@ -62,6 +62,20 @@ def bwd_tol(dtype: str, name: str) -> float:
     return TOL[dtype]
 
 
+def fwd_tol(dtype: str, path: str, chunk: int) -> float:
+    """Relative-L2 bar of a prefill.  On the precomputed-G path (``kda_gate``, then
+    ``kda_chunk_fwd``) with fp32 inputs and 64-token chunks it is 5e-5: G holds
+    chunk-local sums of the per-token log-decay, up to 64 |g_min| = 320 in magnitude,
+    where consecutive fp32 numbers are 3.05e-5 apart, and every decay factor comes from
+    a difference of two such sums, so the rounding of G alone (no kernel involved) moves
+    the fp64 result by up to 8e-6 per (b, h) state in seeded cases
+    (``tests/test_parity_metric.py``).  With 16-token chunks (|G| <= 80) and on the
+    paths that form decays from per-token factors, the input dtype's bar holds."""
+    if dtype == "f32" and path == "G" and chunk > 16:
+        return 5e-5
+    return TOL[dtype]
+
+
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()

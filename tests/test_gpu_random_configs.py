@@ -5,7 +5,9 @@ entry point (fused gate, precomputed G, fused prologue, an explicit segment
 count) for the chunked prefill, with many heads for the launch shapes that
 depend on the head count, the same for decode steps, the draft replay and the
 backward.  Each case is compared with the fp64 oracle (per sequence and per
-16-token block for the prefill outputs), at the tolerance of the input dtype.  The hand-picked cases elsewhere cover the edges
+16-token block for the prefill outputs), at the tolerance of the input dtype
+(5e-5 on the precomputed-G path with fp32 inputs and 64-token chunks, where the fp32
+rounding of G's chunk-local sums alone moves the result by up to 8e-6).  The hand-picked cases elsewhere cover the edges
 one at a time; these mix them."""
 import numpy as np
 import pytest
@@ -15,8 +17,8 @@ import gated_delta_rule_11_amd as kda
 import kda_inputs as ki
 import oracle
 import oracle.backward as OB
-from tests._gpu import (TOL, assert_states, assert_tokens, bwd_tol, dev, dev_inputs, f64_inputs, grad_errors, host64,
-                        rel_l2, say)
+from tests._gpu import (TOL, assert_states, assert_tokens, bwd_tol, dev, dev_inputs, f64_inputs, fwd_tol, grad_errors,
+                        host64, rel_l2, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -72,7 +74,12 @@ def _wide_cases(n=8, seed=20264):
     return cases
 
 
-@pytest.mark.parametrize("c", _prefill_cases() + _wide_cases(), ids=_id)
+# a precomputed-G case with a whole fast-decaying 64-token chunk (|G| past 200), fp32
+G_ROUNDING_CASE = dict(B=4, H=64, T=64, dk=128, dv=128, chunk=64, dtype="f32", path="G", segs=1, s0=0.2, zm=0.0,
+                       g_min=-5.0, scale=1.0, o_bf16=False, seed=7312)
+
+
+@pytest.mark.parametrize("c", _prefill_cases() + _wide_cases() + [G_ROUNDING_CASE], ids=_id)
 def test_random_prefill_vs_oracle(c):
     say(f"case random prefill {c}")
     spec = ki.small_spec(c["B"], c["H"], c["T"], c["dk"], c["dv"], c["chunk"], c["dtype"], seed=c["seed"],
@@ -98,7 +105,7 @@ def test_random_prefill_vs_oracle(c):
     f = f64_inputs(d, c["dtype"])
     run = oracle.forward_z_prologue if c["path"] == "prologue" else oracle.forward_z
     o_ref, S_ref = run(f["q"], f["k"], f["v"], f["beta"], f["z"], f["A"], g_min, f["S0"], scale)
-    tol = TOL[c["dtype"]]
+    tol = fwd_tol(c["dtype"], c["path"], chunk)
     assert_tokens("o", host64(o), o_ref, tol, block=16)
     assert_states("S", host64(S), S_ref, tol)
 

@@ -95,3 +95,37 @@ def test_non_finite_output_fails():
     x[0, 3, 0, 0] = np.nan
     with pytest.raises(AssertionError, match="non-finite"):
         token_report(x, ref)
+
+
+def test_fp32_rounding_of_G_alone_moves_the_fp64_result():
+    """What the fp32 bar of the precomputed-G path with 64-token chunks (``fwd_tol``: 5e-5)
+    has to admit, measured without any kernel: the fp64 recurrence driven by the per-token
+    decays that G's chunk-local sums imply once rounded to fp32 (summed in fp32, in token
+    order), against the same recurrence on the exact decays.  A whole fast-decaying chunk
+    takes |G| past 200, where fp32 numbers are 1.5e-5 apart.  With 16-token chunks the same
+    rounding is far below the 1e-5 bar."""
+    import kda_inputs as ki
+    import oracle
+    from tests._gpu import f64_inputs, fwd_tol, state_report
+
+    def moved(chunk):
+        spec = ki.small_spec(4, 64, 64, 128, 128, chunk, "f32", seed=7312, s0_std=0.2)
+        f = f64_inputs(ki.prefill_inputs(spec), "f32")
+        g = oracle.gate(f["z"], f["A"], -5.0, 1)
+        g32 = g.astype(np.float32)
+        G32 = np.empty_like(g32)
+        for t in range(spec.T):
+            G32[:, t] = g32[:, t] if t % chunk == 0 else (G32[:, t - 1] + g32[:, t]).astype(np.float32)
+        g_impl = G32.astype(np.float64)
+        g_impl[:, 1:] -= np.where((np.arange(1, spec.T) % chunk == 0)[None, :, None, None], 0.0,
+                                  G32[:, :-1].astype(np.float64))
+        _, S_ref = oracle.recurrence(f["q"], f["k"], f["v"], f["beta"], g, f["S0"])
+        _, S_g32 = oracle.recurrence(f["q"], f["k"], f["v"], f["beta"], g_impl, f["S0"])
+        return state_report(S_g32, S_ref)["pair_max"], float(np.abs(G32).max())
+
+    m64, gmax = moved(64)
+    m16, _ = moved(16)
+    print(f"chunk 64: max |G| {gmax:.1f}, worst (b, h) state moved by {m64:.2e}; chunk 16: {m16:.2e}")
+    assert gmax > 200.0
+    assert 3e-6 < m64 < fwd_tol("f32", "G", 64) / 4  # near the input dtype's 1e-5, well inside 5e-5
+    assert m16 < fwd_tol("f32", "G", 16) / 4
