@@ -322,7 +322,8 @@ def main():
     # ---------------- the two small configurations (reported beside the step) ----------------
     # The tiny fp32 case and the 4K-token bf16 prefill, each one kda_chunk_fwd_z call with
     # its inputs resident (20 timed calls after one warm-up).  The 4K-token prefill has
-    # B*H = 8, so the call runs the segment-parallel form; its one-pass time is given too.
+    # B*H = 8, so the call runs the segment-parallel form; its one-pass time is given too, and
+    # the time of kda_gate followed by kda_chunk_fwd (which also picks that form).
     small = None
     if run_pre and not args.no_extras:
         small = {}
@@ -348,6 +349,15 @@ def main():
                     C["q"], C["k"], C["v"], C["beta"], C["z"], C["A"], 1, -5.0, cs.chunk, S_in=S0c, o=oc, S_out=Sc,
                     stream=stream), 20))
                 small[cs.name]["one_pass_ms"] = one["median"]
+                # the unfused pair, kda_gate then kda_chunk_fwd, which picks the same form
+                Gc = torch.empty((cs.B, cs.T, cs.H, cs.dk), dtype=torch.float32, device=dev)
+
+                def gate_then_fwd():
+                    kda.gate(C["z"], C["A"], -5.0, cs.chunk, out=Gc, stream=stream)
+                    kda.chunk_fwd(C["q"], C["k"], C["v"], C["beta"], Gc, cs.chunk, S_in=S0c, o=oc, S_out=Sc,
+                                  workspace=wsc, stream=stream)
+                small[cs.name]["gate_then_chunk_fwd_ms"] = stats(timed(gate_then_fwd, 20))["median"]
+                del Gc
         log(f"small configurations: {small}")
 
     # ---------------- other supported shapes (reported beside the step) ----------------

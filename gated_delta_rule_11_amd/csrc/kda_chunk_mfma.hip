@@ -951,11 +951,15 @@ static hipError_t launch_mfma_d(const ChunkArgs& a, hipStream_t st, int ns) {
     return a.out_bf16 ? launch_mfma_t<DVS, true, bf16_t, false, true>(a, st, ns)
                       : launch_mfma_t<DVS, true, float, false, true>(a, st, ns);
   }
-  if (seg) {  // segment passes: fused gate only
-    if (!a.from_z) return hipErrorNotSupported;
-    if (a.o_skip) return launch_mfma_t<DVS, true, bf16_t, true, false, true>(a, st, ns);  // no outputs
-    return a.out_bf16 ? launch_mfma_t<DVS, true, bf16_t, true>(a, st, ns)
-                      : launch_mfma_t<DVS, true, float, true>(a, st, ns);
+  if (seg) {  // segment passes, with the fused gate or a precomputed G
+    if (a.from_z) {
+      if (a.o_skip) return launch_mfma_t<DVS, true, bf16_t, true, false, true>(a, st, ns);  // no outputs
+      return a.out_bf16 ? launch_mfma_t<DVS, true, bf16_t, true>(a, st, ns)
+                        : launch_mfma_t<DVS, true, float, true>(a, st, ns);
+    }
+    if (a.o_skip) return launch_mfma_t<DVS, false, bf16_t, true, false, true>(a, st, ns);
+    return a.out_bf16 ? launch_mfma_t<DVS, false, bf16_t, true>(a, st, ns)
+                      : launch_mfma_t<DVS, false, float, true>(a, st, ns);
   }
   if (a.from_z)
     return a.out_bf16 ? launch_mfma_t<DVS, true, bf16_t, false>(a, st, ns)

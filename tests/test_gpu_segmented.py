@@ -1,4 +1,5 @@
-"""GPU parity of the segment-parallel prefill (kda_chunk_fwd_z_segmented)
+"""GPU parity of the segment-parallel prefill (kda_chunk_fwd_z_segmented, and the
+form kda_chunk_fwd_z and kda_chunk_fwd choose themselves for few, long sequences)
 against the fp64 oracle, and against the one-pass GPU prefill on the same
 inputs.  Tolerance: relative L2 1e-2 (bf16 inputs), separately for o and the
 final state; the segmented form regroups the arithmetic, so it is compared to
@@ -13,8 +14,8 @@ import torch
 import gated_delta_rule_11_amd as kda
 import kda_inputs as ki
 import oracle
-from tests._gpu import (DEV, TOL, assert_states, assert_tokens, dev_inputs, f64_inputs, host64, rel_l2, say,
-                        sub_inputs)
+from tests._gpu import (DEV, TOL, assert_states, assert_tokens, dev_inputs, f64_inputs, fwd_tol, host64, rel_l2,
+                        say, sub_inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -183,3 +184,25 @@ def test_tile_kernel_picks_segments_itself():
     o_ref, S_ref = oracle.forward_z(f["q"], f["k"], f["v"], f["beta"], f["z"], f["A"], -5.0, f["S0"])
     assert_tokens("automatic segments vs oracle, o", host64(o), o_ref, TOL["f32"])
     assert_states("automatic segments vs oracle, S", host64(S), S_ref, TOL["f32"])
+
+
+@pytest.mark.parametrize("dtype,dk,dv,chunk", [("bf16", 128, 128, 64), ("f32", 128, 128, 64), ("bf16", 64, 32, 16)])
+def test_precomputed_gate_picks_segments_itself(dtype, dk, dv, chunk):
+    """kda_gate, then kda_chunk_fwd on four sequences of 2085 tokens: kda_chunk_fwd runs
+    the segment-parallel form itself (eight segments; the matrix-core kernel for the first
+    shape, the tile kernel for the others), with slow decay and a given entry state so that
+    the segment boundaries carry state, and matches the oracle per sequence and block."""
+    B, H, T = 1, 4, 2085
+    assert kda.chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk) > 0
+    spec = ki.small_spec(B, H, T, dk, dv, chunk, dtype, seed=4500 + dk + chunk, z_mean=-6.0, s0_std=0.3)
+    say(f"case precomputed gate, automatic segments: B={B} H={H} T={T} dk={dk} dv={dv} chunk={chunk} {dtype}")
+    d = ki.prefill_inputs(spec)
+    dd = dev_inputs(d, dtype)
+    G = kda.gate(dd["z"], dd["A"], -5.0, chunk)
+    o, S = kda.chunk_fwd(dd["q"], dd["k"], dd["v"], dd["beta"], G, chunk, S_in=dd["S0"], o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    f = f64_inputs(d, dtype)
+    o_ref, S_ref = oracle.forward_z(f["q"], f["k"], f["v"], f["beta"], f["z"], f["A"], -5.0, f["S0"])
+    tol = fwd_tol(dtype, "G", chunk)
+    assert_tokens("automatic segments (precomputed G) vs oracle, o", host64(o), o_ref, tol, block=16)
+    assert_states("automatic segments (precomputed G) vs oracle, S", host64(S), S_ref, tol)
