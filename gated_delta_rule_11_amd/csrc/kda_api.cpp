@@ -268,9 +268,7 @@ kda_status chunk_common(const void* q, const void* k, const void* v, const void*
   auto launch = [&](const kda::ChunkArgs& c) {
     return mfma ? kda::launch_chunk_mfma(c, st) : kda::launch_chunk_generic(c, st);
   };
-  // the segment passes take the fused gate or a precomputed G, without the prologue;
-  // the automatic form runs the fused prologue in one pass
-  if (lay.nseg <= 1 || prologue) return from_hip(launch(a));
+  if (lay.nseg <= 1) return from_hip(launch(a));
 
   // Segment-parallel form ("Kimi K3 reading notes", section 7): the segments but the
   // last from the zero state (end states St) and from the identity with zero values

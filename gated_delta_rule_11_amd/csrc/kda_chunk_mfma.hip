@@ -288,7 +288,7 @@ __constant__ int8_t kOffPairs8[4][2][2] = {{{1, 0}, {3, 0}}, {{2, 1}, {3, 1}}, {
 template <int DVS, bool FROM_Z, typename Tout, bool SEG, bool NORM, bool STO>
 __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int ns, int xcd_map) {
   using namespace mf;
-  static_assert(!NORM || (FROM_Z && !SEG), "the fused prologue runs with the fused gate, in one pass");
+  static_assert(!NORM || FROM_Z, "the fused prologue runs with the fused gate");
   static_assert(!STO || SEG, "state-only passes are segment passes");
   using Ly = Layout<DVS>;
   constexpr int NJT = DVS / 16;  // value-column tiles in the slice (chain wavefront w owns tile w)
@@ -656,20 +656,24 @@ __global__ __launch_bounds__(512) void chunk_mfma_kernel(const ChunkArgs a, int 
           return __builtin_amdgcn_fdot2_f32_bf16(hi, hi, __builtin_amdgcn_fdot2_f32_bf16(lo, lo, 0.f, false), false);
         };
 #pragma unroll
-        for (int tt = 0; tt < 8; ++tt) {
-          pk[tt] = sumsq(R.k[tt]);
-          pq[tt] = sumsq(R.q[tt]);
-        }
+        for (int tt = 0; tt < 8; ++tt) pk[tt] = sumsq(R.k[tt]);
         const float rkl = rsqrt_fast(half_token_sums8(pk, ln) + kL2Eps);
-        const float rql = rsqrt_fast(half_token_sums8(pq, ln) + kL2Eps);
 #pragma unroll
         for (int tt = 0; tt < 8; ++tt) {
           const float n0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rkl), 4 * tt));
           const float n1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rkl), 32 + 4 * tt));
           nk[tt] = gh ? n1 : n0;
-          const float m0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rql), 4 * tt));
-          const float m1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rql), 32 + 4 * tt));
-          nq[tt] = gh ? m1 : m0;
+        }
+        if constexpr (!STO) {  // state-only passes load no queries
+#pragma unroll
+          for (int tt = 0; tt < 8; ++tt) pq[tt] = sumsq(R.q[tt]);
+          const float rql = rsqrt_fast(half_token_sums8(pq, ln) + kL2Eps);
+#pragma unroll
+          for (int tt = 0; tt < 8; ++tt) {
+            const float m0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rql), 4 * tt));
+            const float m1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rql), 32 + 4 * tt));
+            nq[tt] = gh ? m1 : m0;
+          }
         }
       }
       // r (prefix products up to and including t) and sf (products after t), within
@@ -946,8 +950,13 @@ template <int DVS>
 static hipError_t launch_mfma_d(const ChunkArgs& a, hipStream_t st, int ns) {
   const bool seg = a.nseg > 1 || a.seg_chunks > 0 || a.S_in_seg || a.S_out_mode != 0 || a.S_identity ||
                    a.v_zero || a.o_skip || a.S_ckpt;
-  if (a.prologue) {  // fused prologue: fused gate, one pass
-    if (!a.from_z || seg) return hipErrorNotSupported;
+  if (a.prologue) {  // fused prologue: fused gate, one pass or segment passes
+    if (!a.from_z) return hipErrorNotSupported;
+    if (seg) {
+      if (a.o_skip) return launch_mfma_t<DVS, true, bf16_t, true, true, true>(a, st, ns);
+      return a.out_bf16 ? launch_mfma_t<DVS, true, bf16_t, true, true>(a, st, ns)
+                        : launch_mfma_t<DVS, true, float, true, true>(a, st, ns);
+    }
     return a.out_bf16 ? launch_mfma_t<DVS, true, bf16_t, false, true>(a, st, ns)
                       : launch_mfma_t<DVS, true, float, false, true>(a, st, ns);
   }

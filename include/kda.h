@@ -110,11 +110,9 @@ kda_status kda_gate(const void* z, kda_dtype z_dtype, const float* A,
  * Pure host computation; negative or zero-sized arguments give 0.
  *
  * The library picks the launch form from the sizes alone: one pass over the
- * sequence when B*H alone fills the GPU, otherwise (few, long sequences;
- * kda_chunk_fwd and kda_chunk_fwd_z) the segment-parallel form of "Kimi K3
- * reading notes", section 7, whose per-segment end states, transitions and
- * entry states live in the workspace.  kda_chunk_fwd_z_prologue runs one pass
- * whatever the sizes (its workspace is sized the same, for one contract).
+ * sequence when B*H alone fills the GPU, otherwise (few, long sequences) the
+ * segment-parallel form of "Kimi K3 reading notes", section 7, whose
+ * per-segment end states, transitions and entry states live in the workspace.
  * Both forms give the same result within the stated tolerance.
  */
 size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk);

@@ -186,23 +186,32 @@ def test_tile_kernel_picks_segments_itself():
     assert_states("automatic segments vs oracle, S", host64(S), S_ref, TOL["f32"])
 
 
+@pytest.mark.parametrize("entry", ["precomputed G", "fused prologue"])
 @pytest.mark.parametrize("dtype,dk,dv,chunk", [("bf16", 128, 128, 64), ("f32", 128, 128, 64), ("bf16", 64, 32, 16)])
-def test_precomputed_gate_picks_segments_itself(dtype, dk, dv, chunk):
-    """kda_gate, then kda_chunk_fwd on four sequences of 2085 tokens: kda_chunk_fwd runs
-    the segment-parallel form itself (eight segments; the matrix-core kernel for the first
-    shape, the tile kernel for the others), with slow decay and a given entry state so that
-    the segment boundaries carry state, and matches the oracle per sequence and block."""
+def test_other_entry_points_pick_segments_themselves(entry, dtype, dk, dv, chunk):
+    """kda_gate then kda_chunk_fwd, and kda_chunk_fwd_z_prologue on raw inputs, on four
+    sequences of 2085 tokens: each runs the segment-parallel form itself (eight segments;
+    the matrix-core kernel for the first shape, the tile kernel for the others), with slow
+    decay and a given entry state so that the segment boundaries carry state, and matches
+    the oracle per sequence and block."""
     B, H, T = 1, 4, 2085
     assert kda.chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk) > 0
-    spec = ki.small_spec(B, H, T, dk, dv, chunk, dtype, seed=4500 + dk + chunk, z_mean=-6.0, s0_std=0.3)
-    say(f"case precomputed gate, automatic segments: B={B} H={H} T={T} dk={dk} dv={dv} chunk={chunk} {dtype}")
+    prologue = entry == "fused prologue"
+    spec = ki.small_spec(B, H, T, dk, dv, chunk, dtype, seed=4500 + dk + chunk + prologue, z_mean=-6.0, s0_std=0.3,
+                         raw=prologue)
+    say(f"case {entry}, automatic segments: B={B} H={H} T={T} dk={dk} dv={dv} chunk={chunk} {dtype}")
     d = ki.prefill_inputs(spec)
     dd = dev_inputs(d, dtype)
-    G = kda.gate(dd["z"], dd["A"], -5.0, chunk)
-    o, S = kda.chunk_fwd(dd["q"], dd["k"], dd["v"], dd["beta"], G, chunk, S_in=dd["S0"], o_dtype=torch.float32)
+    if prologue:
+        o, S = kda.chunk_fwd_z_prologue(dd["q"], dd["k"], dd["v"], dd["beta"], dd["z"], dd["A"], -5.0, chunk,
+                                        S_in=dd["S0"], o_dtype=torch.float32)
+    else:
+        G = kda.gate(dd["z"], dd["A"], -5.0, chunk)
+        o, S = kda.chunk_fwd(dd["q"], dd["k"], dd["v"], dd["beta"], G, chunk, S_in=dd["S0"], o_dtype=torch.float32)
     torch.cuda.synchronize()
     f = f64_inputs(d, dtype)
-    o_ref, S_ref = oracle.forward_z(f["q"], f["k"], f["v"], f["beta"], f["z"], f["A"], -5.0, f["S0"])
-    tol = fwd_tol(dtype, "G", chunk)
-    assert_tokens("automatic segments (precomputed G) vs oracle, o", host64(o), o_ref, tol, block=16)
-    assert_states("automatic segments (precomputed G) vs oracle, S", host64(S), S_ref, tol)
+    run = oracle.forward_z_prologue if prologue else oracle.forward_z
+    o_ref, S_ref = run(f["q"], f["k"], f["v"], f["beta"], f["z"], f["A"], -5.0, f["S0"])
+    tol = fwd_tol(dtype, "prologue" if prologue else "G", chunk)
+    assert_tokens(f"automatic segments ({entry}) vs oracle, o", host64(o), o_ref, tol, block=16)
+    assert_states(f"automatic segments ({entry}) vs oracle, S", host64(S), S_ref, tol)
