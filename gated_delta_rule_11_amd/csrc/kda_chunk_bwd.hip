@@ -58,8 +58,7 @@ struct Layout {
   static constexpr int RS = 17;
   // [16][RK] tiles
   static constexpr int KT = 0, KB = KT + 16 * RK, QT = KB + 16 * RK, KH = QT + 16 * RK, W = KH + 16 * RK,
-                       GG = W + 16 * RK, DQT = GG + 16 * RK, DKT = DQT + 16 * RK, DKB = DKT + 16 * RK,
-                       DKH = DKB + 16 * RK, DW = DKH + 16 * RK;
+                       GG = W + 16 * RK, DKH = GG + 16 * RK, DW = DKH + 16 * RK;
   // [16][RV] tiles
   static constexpr int V = DW + 16 * RK, DO = V + 16 * RV, U = DO + 16 * RV, DU = U + 16 * RV;
   // [16][RS] small matrices
@@ -162,9 +161,6 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
   float* sKh = sm + Ly::KH;
   float* sW = sm + Ly::W;
   float* sG = sm + Ly::GG;
-  float* sdQt = sm + Ly::DQT;
-  float* sdKt = sm + Ly::DKT;
-  float* sdKb = sm + Ly::DKB;
   float* sdKh = sm + Ly::DKH;
   float* sdW = sm + Ly::DW;
   float* sV = sm + Ly::V;
@@ -249,7 +245,7 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
     }
   };
 
-  float dA_acc = 0.f;  // lanes 4c .. 4c + 3: this workgroup's part of dA[h][c]
+  float dA_acc = 0.f;  // key-row-tile lanes (g4, r16): part of dA[h][16 ct + r16]
 
   // ---- sub-chunk inputs.  The raw values of the next sub-chunk in processing order are
   // loaded into registers while the current one is processed, four consecutive channels
@@ -301,8 +297,8 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
   };
 
   // ---- sub-chunk (blk, s) into LDS from the prefetched registers; BWD also takes q and dO.
-  // Three steps: every thread stores its elements and computes the gate; one thread per key
-  // channel sums the log-decay over the tokens; every thread scales its elements.
+  // Two steps: every thread stores its elements and computes the gate; four lanes per key
+  // channel sum the log-decay over the tokens and scale the channel's elements.
   auto load_sub = [&](int blk, int s, int t0, int n, bool BWD) {
     const auto kr = pk, zr = pz, qr = pq, vr = pv;
     const auto orw = po;
@@ -338,29 +334,39 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
     if (tid < SC) sBeta[tid] = tid < n ? io1<Tin>::wide(br) : 0.f;
     bw_barrier();
     relane();
-    if (tid < DK) {  // running log-decay over the sub-chunk
-      float G = 0.f;
+    if (tid < 4 * DK) {
+      // running log-decay over the sub-chunk, four lanes per key channel with four tokens
+      // each: lane r of the quad continues the sum from lane r - 1's last value, in token
+      // order, then every lane scales its own four elements
+      const int c = tid >> 2, qd = tid & 3;
+      float gv[4], Gv[4], G = 0.f;
 #pragma unroll
-      for (int t = 0; t < SC; ++t) {
-        G += sG[t * RK + tid];
-        sG[t * RK + tid] = G;
+      for (int i = 0; i < 4; ++i) gv[i] = sG[(4 * qd + i) * RK + c];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (qd == r) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            G += gv[i];
+            Gv[i] = G;
+          }
+        }
+        G = __shfl(G, (ln & ~3) + r);
       }
-      sGl[tid] = __expf(G);
-    }
-    bw_barrier();
-    relane();
+      const float gl = __expf(G);  // e^(G_last)
+      if (qd == 0) sGl[c] = gl;
 #pragma unroll
-    for (int i = 0; i < (SC * DK + NT - 1) / NT; ++i) {
-      const int e = tid + i * NT, t = e / DK, c = e % DK;
-      if (SC * DK % NT != 0 && e >= SC * DK) break;
-      const int o = t * RK + c;
-      const float G = sG[o], kv = sKt[o];
-      const float Gm = __expf(G), Gi = __expf(-G);
-      const float kb = kv * Gi;
-      sKt[o] = kv * Gm;
-      sKb[o] = kb;
-      sKh[o] = kb * sGl[c];  // k e^(G_last - G)
-      if (BWD) sQt[o] = sQt[o] * Gm;
+      for (int i = 0; i < 4; ++i) {
+        const int o = (4 * qd + i) * RK + c;
+        const float kv = sKt[o];
+        const float Gm = __expf(Gv[i]), Gi = __expf(-Gv[i]);
+        const float kb = kv * Gi;
+        sG[o] = Gv[i];
+        sKt[o] = kv * Gm;
+        sKb[o] = kb;
+        sKh[o] = kb * gl;  // k e^(G_last - G)
+        if (BWD) sQt[o] = sQt[o] * Gm;
+      }
     }
   };
 
@@ -840,68 +846,48 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
       bw_barrier();
       relane();
 
-      // ---- dKt += dAL Kb; dKb += dAL^T Kt (key-row tiles) -> LDS with dQt
+      // ---- dKt += dAL Kb; dKb += dAL^T Kt (key-row tiles); then, from the accumulators,
+      // dq, dk and dG of the wavefront's 16 key channels: lane (g4, r16) holds tokens
+      // 4 g4 .. 4 g4 + 3 of channel c = 16 ct + r16.  dg = reverse cumulative sum of dG over
+      // the sub-chunk (the last token also carries Gam_last's uses), dz = dg g_min sigma
+      // (1 - sigma) e^A and dA += dz z: suffix sums in a lane, then across the lane groups.
       if (own_c) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
           dKt = mma4(sdAL[r16 * RS + 4 * kb + g4], sKb[(4 * kb + g4) * RK + 16 * ct + r16], dKt);
           dKb = mma4(sdAL[(4 * kb + g4) * RS + r16], sKt[(4 * kb + g4) * RK + 16 * ct + r16], dKb);
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int o = (4 * g4 + e) * RK + 16 * ct + r16;
-          sdKt[o] = dKt[e];
-          sdKb[o] = dKb[e];
-          sdQt[o] = dQt[e];
-        }
-      }
-      bw_barrier();
-      relane();
-
-      // ---- every element: dq, dk and dG (over G, no longer needed)
-#pragma unroll
-      for (int i = 0; i < (SC * DK + NT - 1) / NT; ++i) {
-        const int e = tid + i * NT, t = e / DK, c = e % DK;
-        if (SC * DK % NT != 0 && e >= SC * DK) break;
-        const int o = t * RK + c;
-        const float Gm = __expf(sG[o]), Gi = __expf(-sG[o]);
-        const float dqt = sdQt[o], dkt = sdKt[o], dkb = sdKb[o], dkh = sdKh[o];
-        sG[o] = dqt * sQt[o] + dkt * sKt[o] - dkb * sKb[o] - dkh * sKh[o];
-        if (t < n) {
-          const int64_t row = (static_cast<int64_t>(b) * T + t0 + t) * H + h;
-          gq[row * DK + c] = dqt * Gm;
-          gk[row * DK + c] = dkt * Gm + (dkb + dkh * sGl[c]) * Gi;
-        }
-      }
-      bw_barrier();
-      relane();
-      // ---- dg = reverse cumulative sum of dG over the sub-chunk (the last token also carries
-      // Gam_last's uses), then dz = dg g_min sigma (1 - sigma) e^A and dA += dz z.  Four lanes
-      // per key channel, four tokens each: suffix sums in a lane, then across the quad.
-      if (tid < 4 * DK) {
-        const int c = tid >> 2, qd = tid & 3;
+        const int c = 16 * ct + r16;
         float dg[4], tail = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int o = (4 * qd + i) * RK + c;
-          dg[i] = sG[o];
-          tail += sdKh[o] * sKh[o];
+        for (int e = 0; e < 4; ++e) {
+          const int t = 4 * g4 + e;
+          const int o = t * RK + c;
+          const float Gm = __expf(sG[o]), Gi = __expf(-sG[o]);
+          const float dkh = sdKh[o], kh = sKh[o];
+          dg[e] = dQt[e] * sQt[o] + dKt[e] * sKt[o] - dKb[e] * sKb[o] - dkh * kh;
+          tail += dkh * kh;
+          if (t < n) {
+            const int64_t row = (static_cast<int64_t>(b) * T + t0 + t) * H + h;
+            gq[row * DK + c] = dQt[e] * Gm;
+            gk[row * DK + c] = dKt[e] * Gm + (dKb[e] + dkh * sGl[c]) * Gi;
+          }
         }
 #pragma unroll
         for (int i = 2; i >= 0; --i) dg[i] += dg[i + 1];  // suffix sums within the lane's tokens
-        tail += __shfl_xor(tail, 1);
-        tail += __shfl_xor(tail, 2);
-        float later = 0.f;  // the sums of the quad's later lanes (later tokens)
+        tail += __shfl_xor(tail, 16);
+        tail += __shfl_xor(tail, 32);
+        float later = 0.f;  // the sums of the later lane groups (later tokens)
 #pragma unroll
         for (int r = 1; r < 4; ++r) {
-          const float x = __shfl(dg[0], (ln & ~3) + r);
-          later += r > qd ? x : 0.f;
+          const float x = __shfl(dg[0], r16 + 16 * r);
+          later += r > g4 ? x : 0.f;
         }
         const float base = sdGl[c] * sGl[c] + tail + later;
         const float ea = sEA[c];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int t = 4 * qd + i;
+          const int t = 4 * g4 + i;
           if (t < n) {
             const int o = t * RK + c;
             const float sg = sSig[o];
@@ -921,10 +907,10 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) dst[(16 * c2 + 4 * g4 + e) * DV + j0 + 16 * jt + r16] = dSc[c2][e];
   }
-  // dA: the four lanes of each key channel hold parts over their tokens
-  dA_acc += __shfl_xor(dA_acc, 1);
-  dA_acc += __shfl_xor(dA_acc, 2);
-  if (tid < 4 * DK && (tid & 3) == 0) a.dA_part[(static_cast<int64_t>(bh) * NSP + sp) * DK + (tid >> 2)] = dA_acc;
+  // dA: the four lane groups of each key channel hold parts over their tokens
+  dA_acc += __shfl_xor(dA_acc, 16);
+  dA_acc += __shfl_xor(dA_acc, 32);
+  if (own_c && g4 == 0) a.dA_part[(static_cast<int64_t>(bh) * NSP + sp) * DK + 16 * ct + r16] = dA_acc;
 }
 
 // The second value slice's parts of the key-side gradients, added to the first's.
