@@ -410,10 +410,8 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
   };
 
   // ---- wave 0: AL = Kt Kb^T, then M = (I + L)^-1 and T = M Diag(beta); wave 1 (BWD):
-  // P = lower(Qt Kb^T).  The inverse takes one column per lane (lanes 0..15),
-  // right-looking: once x[m] is final, column m of L is applied to the rows below it,
-  // read from an fp32 copy of L^T in LDS at a wave-uniform address (a broadcast).  Only
-  // wave 0 touches the copy and its LDS accesses complete in order: no barrier between.
+  // P = lower(Qt Kb^T).  The inverse is a product of four factors formed by repeated
+  // squaring on fp32 matrix cores (below).
   // cw (recompute): also leave M and AL in the cache slot; cached (backward): take M and
   // AL as prefetched from the slot the recompute filled instead of forming them again.
   f32x4 pre_m = {}, pre_al = {};  // wave 0: lane (g4, r16) holds row 4 g4 + e, column r16
@@ -455,29 +453,45 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
           if (cw) cw[256 + t * 16 + r16] = acc[e];
           lv[e] = r16 < t ? sBeta[t] * acc[e] : 0.f;
         }
-        // L^T[s][t] = L[t][s]: row r16 of the copy, columns 4 g4 .. 4 g4 + 3
-        *reinterpret_cast<f32x4*>(sLt + r16 * Ly::LS + 4 * g4) = lv;
-        float x[SC];
+        // M = (I + L)^-1 = (I + N)(I + N^2)(I + N^4)(I + N^8) with N = -L (strictly lower
+        // triangular, so N^16 = 0), on matrix cores.  Matrices are held in the accumulator
+        // layout (lane (g4, r16): rows 4 g4 .. 4 g4 + 3 of column r16), each product's left
+        // factor as its transpose in that layout; L^T comes through an fp32 copy in LDS
+        // (written and read by this wavefront only, in order).
+        *reinterpret_cast<f32x4*>(sLt + r16 * Ly::LS + 4 * g4) = lv;  // sLt[s][t] = L[t][s]
+        f32x4 nn, nt, id;
 #pragma unroll
-        for (int r = 0; r < SC; ++r) x[r] = (r == ln) ? 1.f : 0.f;
-#pragma unroll
-        for (int m = 0; m < SC - 1; ++m) {
-#pragma unroll
-          for (int q4 = (m + 1) / 4; q4 < 4; ++q4) {
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(sLt + m * Ly::LS + 4 * q4);
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-              if (4 * q4 + u > m) x[4 * q4 + u] -= l4[u] * x[m];
-          }
+        for (int e = 0; e < 4; ++e) {
+          nn[e] = -lv[e];
+          nt[e] = -sLt[(4 * g4 + e) * Ly::LS + r16];
+          id[e] = (4 * g4 + e == r16) ? 1.f : 0.f;
         }
-        if (ln < SC) {
-          const float bs = sBeta[ln];
+        // c + X Y, given X^T and Y in the accumulator layout (k = 4 g4 + v in step v)
+        auto mm16 = [](f32x4 xt, f32x4 y, f32x4 c) {
 #pragma unroll
-          for (int t = 0; t < SC; ++t) {
-            sM[t * RS + ln] = x[t];
-            sT[t * RS + ln] = x[t] * bs;
-            if (cw) cw[t * 16 + ln] = x[t];
+          for (int v = 0; v < 4; ++v) c = mma4(xt[v], y[v], c);
+          return c;
+        };
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        f32x4 pm = id + nn, pt = id + nt;  // I + N and its transpose
+#pragma unroll
+        for (int lev = 0; lev < 3; ++lev) {
+          const f32x4 n2 = mm16(nt, nn, zero);             // N^(2^(lev+1))
+          const f32x4 pn = mm16(pt, n2, pm);               // P (I + that)
+          if (lev < 2) {
+            const f32x4 n2t = mm16(nn, nt, zero);          // its transpose
+            pt = mm16(n2, pt, pt);                         // and P's
+            nt = n2t;
           }
+          nn = n2;
+          pm = pn;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 4 * g4 + e;
+          sM[t * RS + r16] = pm[e];
+          sT[t * RS + r16] = pm[e] * sBeta[r16];
+          if (cw) cw[t * 16 + r16] = pm[e];
         }
       }
     }
