@@ -36,9 +36,9 @@
 //      each lane holding one token's four channels of a tile), q 2^Gl,
 //      -k 2^Gl, k 2^(Gl_15 - Gl) and the tile's values into LDS;
 //   2  one wavefront (an idle state slot's, else the ninth): L and P summed over
-//      the parts and masked, X solved row by row (lane t forms row t by back
-//      substitution, the rows of L read from LDS as broadcasts), Tm and P into
-//      LDS;
+//      the parts and masked, X = (I + L)^-1 (by repeated squaring on fp32 matrix
+//      cores where the solve has its SIMD to itself, else row by row by back
+//      substitution on the vector unit), Tm and P into LDS;
 //   3  state wavefronts 4 .. 4 + DVS/16 - 1, each owning 16 value columns and
 //      that dk x 16 block of the state in its accumulators: (K 2^Gl) S and
 //      (Q 2^Gl) S, U, o and the state update.
@@ -197,6 +197,11 @@ __global__ __launch_bounds__(NT) void chunk_tile_kernel(const ChunkArgs a) {
   // stage 2 runs on an idle state slot's SIMD when there is one (wavefront w sits on
   // SIMD w mod 4), else on a ninth wavefront
   const int solve_w = DVS < 64 ? 7 : 8;
+  // The solve's SIMD is otherwise idle when it runs in state slot 7 and key wavefront 3
+  // has no key tile (d_k <= 48): there X = (I + L)^-1 goes to the matrix cores (a short
+  // dependent chain of products); elsewhere the SIMD's matrix pipe is busy with a key or
+  // state wavefront's products and the back substitution on the vector unit is faster.
+  constexpr bool kMfmaSolve = DVS < 64 && NCT <= 3;
   const bool norm = a.prologue;
   // this workgroup's tokens: segment sg (chunk-aligned, so tile-aligned), or the whole sequence
   const int64_t seg_len = a.seg_chunks > 0 ? static_cast<int64_t>(a.seg_chunks) * a.chunk : a.T;
@@ -386,7 +391,7 @@ __global__ __launch_bounds__(NT) void chunk_tile_kernel(const ChunkArgs a) {
     __syncthreads();
   } else if (w == solve_w) {
     // ---- stage 2 on tile m at step m + 1: L and P summed over the key parts and
-    // masked, X = (I + L)^-1 row by row, Tm = X Diag(beta); Tm, P and the prologue's
+    // masked, X = (I + L)^-1, Tm = X Diag(beta); Tm, P and the prologue's
     // norms into LDS.  This wavefront shares its SIMD with others and would lose most
     // issue cycles to them (older wavefronts issue first): it runs at the highest
     // issue priority.
@@ -428,26 +433,59 @@ __global__ __launch_bounds__(NT) void chunk_tile_kernel(const ChunkArgs a) {
         Lr[r] = s < li ? bt * rk1 * Lr[r] * rk4[r] : 0.f;
         Pr[r] = s <= li ? rq1 * Pr[r] * rk4[r] : 0.f;
       }
-      // row li of X: x_j = [j == li] - sum_{m > j} x_m L[m][j], m from 15 down.  With
-      // acc_j started at -[j == li], x_m = -acc_m for every lane (rows above li stay 0).
-      // L goes through LDS (the LDS operations of one wavefront complete in order),
-      // whose rows every lane reads as broadcasts, all before the substitution starts.
-      *reinterpret_cast<f32x4*>(lsol + 16 * li + 4 * lg) = Lr;
-      f32x4 lrow[16][4];
+      f32x4 tm;  // Tm = X Diag(beta): row li, columns 4 lg + r
+      if constexpr (kMfmaSolve) {
+        // X^T = (I + M)(I + M^2)(I + M^4)(I + M^8) with M = -L^T (strictly upper triangular,
+        // so M^16 = 0): three squarings and three products on fp32 matrix cores, whatever
+        // the input dtype.  Each matrix and its transpose are kept in the products' lane
+        // layout (lane (lg, li): rows 4 lg .. 4 lg + 3 of column li; a product takes its left
+        // factor as that factor's transpose in that layout).  Lr is L^T in it; L itself comes
+        // through LDS (the LDS operations of one wavefront complete in order).
+        *reinterpret_cast<f32x4*>(lsol + 16 * li + 4 * lg) = Lr;  // lsol[t][s] = L[t][s]
+        f32x4 nn, nt, id;
 #pragma unroll
-      for (int mm = 1; mm < 16; ++mm)
+        for (int r = 0; r < 4; ++r) {
+          nn[r] = -Lr[r];
+          nt[r] = -lsol[(4 * lg + r) * 16 + li];
+          id[r] = (4 * lg + r == li) ? 1.f : 0.f;
+        }
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        f32x4 pm = id + nn, pt = id + nt;  // I + M and its transpose
 #pragma unroll
-        for (int j4 = 0; j4 < mm; j4 += 4) lrow[mm][j4 / 4] = *reinterpret_cast<const f32x4*>(lsol + 16 * mm + j4);
-      float acc[16];
+        for (int lev = 0; lev < 3; ++lev) {
+          const f32x4 n2 = mm16<false>(nt, nn, zero);  // M^(2^(lev+1))
+          const f32x4 pn = mm16<false>(pt, n2, pm);    // P (I + that)
+          if (lev < 2) {
+            const f32x4 n2t = mm16<false>(nn, nt, zero);
+            pt = mm16<false>(n2, pt, pt);
+            nt = n2t;
+          }
+          nn = n2;
+          pm = pn;
+        }
 #pragma unroll
-      for (int j = 0; j < 16; ++j) acc[j] = li == j ? -1.f : 0.f;
+        for (int r = 0; r < 4; ++r) tm[r] = pm[r] * bs4[r];
+      } else {
+        // row li of X: x_j = [j == li] - sum_{m > j} x_m L[m][j], m from 15 down.  With
+        // acc_j started at -[j == li], x_m = -acc_m for every lane (rows above li stay 0).
+        // L goes through LDS (the LDS operations of one wavefront complete in order),
+        // whose rows every lane reads as broadcasts, all before the substitution starts.
+        *reinterpret_cast<f32x4*>(lsol + 16 * li + 4 * lg) = Lr;
+        f32x4 lrow[16][4];
 #pragma unroll
-      for (int mm = 15; mm >= 1; --mm)
+        for (int mm = 1; mm < 16; ++mm)
 #pragma unroll
-        for (int j = 0; j < mm; ++j) acc[j] = fmaf(-acc[mm], lrow[mm][j / 4][j % 4], acc[j]);
-      f32x4 tm;  // Tm = X Diag(beta), row li, columns 4 lg + r
+          for (int j4 = 0; j4 < mm; j4 += 4) lrow[mm][j4 / 4] = *reinterpret_cast<const f32x4*>(lsol + 16 * mm + j4);
+        float acc[16];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) tm[r] = -sel4(lg, acc[r], acc[4 + r], acc[8 + r], acc[12 + r]) * bs4[r];
+        for (int j = 0; j < 16; ++j) acc[j] = li == j ? -1.f : 0.f;
+#pragma unroll
+        for (int mm = 15; mm >= 1; --mm)
+#pragma unroll
+          for (int j = 0; j < mm; ++j) acc[j] = fmaf(-acc[mm], lrow[mm][j / 4][j % 4], acc[j]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tm[r] = -sel4(lg, acc[r], acc[4 + r], acc[8 + r], acc[12 + r]) * bs4[r];
+      }
       cur.tm[l] = tm;
       cur.pm[l] = Pr;
       __syncthreads();
