@@ -53,7 +53,7 @@ DECODE_BYTES_PER_SEQ_HEAD = 2 * 128 * 128 * 4 + 4 * 128 * 2 + 2 + 128 * 2
 # sources it was taken on are unchanged (sha256 of the listed files), else null.
 MEASURED_TRAFFIC = {
     "prefill": {"files": ["gated_delta_rule_11_amd/csrc/kda_chunk_mfma.hip", "gated_delta_rule_11_amd/csrc/kda_common.hpp"],
-                "sha256": "ad10804ecce16970", "bytes": 5.453e9},
+                "sha256": "3989b7b130f32519", "bytes": 5.453e9},
     "decode": {"files": ["gated_delta_rule_11_amd/csrc/kda_decode.hip", "gated_delta_rule_11_amd/csrc/kda_common.hpp"],
                "sha256": "289f3a27b8b3e623", "bytes": 1.0849e9},
 }
