@@ -332,9 +332,8 @@ size_t kda_chunk_bwd_z_workspace_bytes(int B, int T, int H, int dk, int dv) {
   const size_t bh = size_t(B) * size_t(H), sz = size_t(dk) * size_t(dv);
   const size_t nblk = (size_t(T) + 63) / 64;
   const size_t nsp = size_t(kda::chunk_bwd_slices(B, H, dv));
-  const size_t parts = nsp == 2 ? bh * size_t(T) * (3 * size_t(dk) + 1) : 0;  // second slice's key-side parts
-  const size_t mcache = bh * nsp * size_t(kda::kBwdMCacheFloats);                 // recompute's M and AL
-  return (bh * (nblk + 3) * sz + bh * nsp * size_t(dk) + mcache + parts) * 4;
+  const size_t mcache = bh * nsp * size_t(kda::kBwdMCacheFloats);  // recompute's M and AL
+  return (bh * (nblk + 3) * sz + bh * nsp * size_t(dk) + mcache) * 4;
 }
 
 kda_status kda_chunk_bwd_z(const void* q, const void* k, const void* v, const void* beta, const void* z,
@@ -377,7 +376,6 @@ kda_status kda_chunk_bwd_z(const void* q, const void* k, const void* v, const vo
   float* dA_part = sub_states + bh * 3 * dk * dv;
   const int nsp = kda::chunk_bwd_slices(B, H, dv);
   float* mcache = dA_part + bh * nsp * dk;
-  float* parts = mcache + bh * nsp * kda::kBwdMCacheFloats;
   // forward pass that only leaves the state entering every 64-token block
   kda::ChunkArgs f{};
   f.q = q; f.k = k; f.v = v; f.beta = beta; f.z = z; f.A = A; f.g_min = g_min; f.S_in = S_in;
@@ -389,12 +387,6 @@ kda_status kda_chunk_bwd_z(const void* q, const void* k, const void* v, const vo
   kda::BwdArgs bwa{q, k, v, beta, z, A, g_min, d_o, dS_out, ckpt, sub_states, dA_part, dq, dk_, dv_, dbeta, dz, dA,
                    dS_in, B, T, H, dk, dv, scale, in_dtype == KDA_BF16, do_dtype == KDA_BF16};
   bwa.mcache = mcache;
-  if (nsp == 2) {
-    bwa.part_q = parts;
-    bwa.part_k = parts + ntok * dk;
-    bwa.part_z = parts + 2 * ntok * dk;
-    bwa.part_beta = parts + 3 * ntok * dk;
-  }
   return from_hip(kda::launch_chunk_bwd(bwa, st));
 }
 

@@ -220,11 +220,20 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
   const Tin* beta = static_cast<const Tin*>(a.beta);
   const Tdo* d_o = static_cast<const Tdo*>(a.d_o);
   const float g_min = a.g_min;
-  // key-side gradients: the whole value range (one slice) or this slice's part of it
-  float* const gq = sp == 0 ? a.grad_q : a.part_q;
-  float* const gk = sp == 0 ? a.grad_k : a.part_k;
-  float* const gz = sp == 0 ? a.grad_z : a.part_z;
-  float* const gbeta = sp == 0 ? a.grad_beta : a.part_beta;
+  // key-side gradients: the whole value range (one slice), or, with two slices, this
+  // slice's part of it, added into the zero-filled outputs (two addends onto zero: the
+  // same sum in either order, so the result does not depend on which slice adds first)
+  float* const gq = a.grad_q;
+  float* const gk = a.grad_k;
+  float* const gz = a.grad_z;
+  float* const gbeta = a.grad_beta;
+  auto put = [](float* p, float x) {
+    if constexpr (NSP == 2) {
+      unsafeAtomicAdd(p, x);
+    } else {
+      *p = x;
+    }
+  };
 
   // state by value-column tile: Sc[ct'][e] = S[16 ct' + 4 g4 + e][j0 + 16 jt + r16]
   // state transposed by key-row tile: St[jt'][e] = S[16 ct + r16][j0 + 16 jt' + 4 g4 + e]
@@ -854,7 +863,7 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
           float db = sY[u * RS + 16];
 #pragma unroll
           for (int t = 0; t < SC; ++t) db += (sdT0[t * RS + u] + sdT1[t * RS + u]) * sM[t * RS + u];
-          if (u < n) gbeta[(static_cast<int64_t>(b) * T + t0 + u) * H + h] = db;
+          if (u < n) put(&gbeta[(static_cast<int64_t>(b) * T + t0 + u) * H + h], db);
         }
       }
       bw_barrier();
@@ -883,8 +892,8 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
           tail += dkh * kh;
           if (t < n) {
             const int64_t row = (static_cast<int64_t>(b) * T + t0 + t) * H + h;
-            gq[row * DK + c] = dQt[e] * Gm;
-            gk[row * DK + c] = dKt[e] * Gm + (dKb[e] + dkh * sGl[c]) * Gi;
+            put(&gq[row * DK + c], dQt[e] * Gm);
+            put(&gk[row * DK + c], dKt[e] * Gm + (dKb[e] + dkh * sGl[c]) * Gi);
           }
         }
 #pragma unroll
@@ -906,7 +915,7 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
             const int o = t * RK + c;
             const float sg = sSig[o];
             const float dx = (base + dg[i]) * g_min * sg * (1.f - sg);
-            gz[((static_cast<int64_t>(b) * T + t0 + t) * H + h) * DK + c] = dx * ea;
+            put(&gz[((static_cast<int64_t>(b) * T + t0 + t) * H + h) * DK + c], dx * ea);
             dA_acc += dx * sXz[o];
           }
         }
@@ -927,16 +936,13 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
   if (own_c && g4 == 0) a.dA_part[(static_cast<int64_t>(bh) * NSP + sp) * DK + 16 * ct + r16] = dA_acc;
 }
 
-// The second value slice's parts of the key-side gradients, added to the first's.
-// Two addends: the sum is the same in either order.
-__global__ void add_parts_kernel(float* __restrict__ out, const float* __restrict__ part, int64_t n) {
+// Zero fill (a kernel rather than a memset, so that the launch sequence can be captured).
+__global__ void zero_kernel(float* __restrict__ out, int64_t n) {
   const int64_t i4 = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
   if (i4 + 4 <= n) {
-    f32x4 o = *reinterpret_cast<f32x4*>(out + i4);
-    const f32x4 p = *reinterpret_cast<const f32x4*>(part + i4);
-    *reinterpret_cast<f32x4*>(out + i4) = o + p;
+    *reinterpret_cast<f32x4*>(out + i4) = f32x4{0.f, 0.f, 0.f, 0.f};
   } else {
-    for (int64_t i = i4; i < n; ++i) out[i] += part[i];
+    for (int64_t i = i4; i < n; ++i) out[i] = 0.f;
   }
 }
 
@@ -959,24 +965,22 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   static std::atomic<uint64_t> lds_set{0};
   hipError_t e = set_lds_limit(reinterpret_cast<const void*>(kern), bytes, lds_set);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(static_cast<int64_t>(a.B) * a.H * NSP)), dim3(bw::NT), bytes,
-                     st, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (NSP == 2) {
+  if (NSP == 2) {  // the two slices add into zero-filled key-side gradients
     const int64_t ntok = static_cast<int64_t>(a.B) * a.T * a.H;
-    const struct { float* out; const float* part; int64_t n; } adds[] = {
-        {a.grad_q, a.part_q, ntok * a.dk}, {a.grad_k, a.part_k, ntok * a.dk}, {a.grad_z, a.part_z, ntok * a.dk},
-        {a.grad_beta, a.part_beta, ntok}};
-    for (const auto& ad : adds) {
-      if (ad.n == 0) continue;
-      const int64_t nthr = (ad.n + 3) / 4;
-      hipLaunchKernelGGL(add_parts_kernel, dim3(static_cast<uint32_t>((nthr + 255) / 256)), dim3(256), 0, st, ad.out,
-                         ad.part, ad.n);
+    const struct { float* out; int64_t n; } fills[] = {
+        {a.grad_q, ntok * a.dk}, {a.grad_k, ntok * a.dk}, {a.grad_z, ntok * a.dk}, {a.grad_beta, ntok}};
+    for (const auto& f : fills) {
+      if (f.n == 0) continue;
+      const int64_t nthr = (f.n + 3) / 4;
+      hipLaunchKernelGGL(zero_kernel, dim3(static_cast<uint32_t>((nthr + 255) / 256)), dim3(256), 0, st, f.out, f.n);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(static_cast<int64_t>(a.B) * a.H * NSP)), dim3(bw::NT), bytes,
+                     st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int n = a.H * a.dk;
   hipLaunchKernelGGL(dA_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, st, a.dA_part, a.grad_A, a.B, a.H, a.dk,
                      NSP);
@@ -993,7 +997,7 @@ static hipError_t launch_bwd_s(const BwdArgs& a, hipStream_t st) {
 template <int DK, int DV>
 static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
   if constexpr (DV >= 64) {
-    if (a.part_q) return launch_bwd_s<DK, DV, 2>(a, st);  // two value slices
+    if (chunk_bwd_slices(a.B, a.H, a.dv) == 2) return launch_bwd_s<DK, DV, 2>(a, st);  // two value slices
   }
   return launch_bwd_s<DK, DV, 1>(a, st);
 }

@@ -126,8 +126,6 @@ struct BwdArgs {
   int B, T, H, dk, dv;
   float scale;
   bool in_bf16, do_bf16;
-  // second value slice's parts of dq, dk, dz, dbeta (nullptr: one slice, see chunk_bwd_slices)
-  float *part_q = nullptr, *part_k = nullptr, *part_z = nullptr, *part_beta = nullptr;
   // [B, H, slices, 3, 2, 16, 16]: M = (I + L)^-1 and AL of the sub-chunks a block's
   // recompute formed, reused by its backward sweep (nullptr: formed again)
   float* mcache = nullptr;

@@ -255,8 +255,11 @@ kda_status kda_decode_step_prologue(const void* q, const void* k, const void* v,
  * paper and proofs side by side", section 2.1.1, Equation 1, and the bounded
  * gate of "Kimi K3 reading notes", section 2), computed chunkwise: a forward
  * pass keeps the state entering every 64-token block in the workspace, then
- * one workgroup per (b, h) walks the blocks backwards in 16-token sub-chunks,
- * in fp32 (matrix cores with fp32 operands).
+ * one workgroup per (b, h), or per (b, h, half of the value columns) when that
+ * leaves compute units idle, walks the blocks backwards in 16-token sub-chunks:
+ * matrix-core products with fp32 accumulation, fp32 operands for fp32 inputs and
+ * bf16 operands on the larger products for bf16 inputs.  Deterministic: two
+ * calls on the same inputs give the same bits.
  *
  * Supported: dk, dv in {16, 32, 64, 128}; in_dtype, do_dtype in {f32, bf16};
  * g_min in [-5, 0] (16 g_min >= -80 keeps every in-sub-chunk decay ratio in

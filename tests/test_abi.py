@@ -281,13 +281,13 @@ def test_prologue_validation(L):
 
 
 def test_backward_validation(L):
-    # checkpoints + scratch, dA parts, the recompute's M and AL (3 sub-chunks x 2 x 16 x 16
-    # per (b, h, slice)), and with two value slices the second's key-side parts
+    # checkpoints + scratch, dA parts and the recompute's M and AL (3 sub-chunks x 2 x 16 x 16)
+    # per (b, h, slice); two value slices add their key-side parts into the outputs themselves
     mc = 3 * 2 * 16 * 16
     need = L.kda_chunk_bwd_z_workspace_bytes(2, 100, 3, 64, 32)
     assert need == (2 * 3 * (2 + 3) * 64 * 32 + 2 * 3 * 64 + 2 * 3 * mc) * 4      # one value slice at dv = 32
     two = L.kda_chunk_bwd_z_workspace_bytes(2, 100, 3, 64, 64)
-    assert two == (2 * 3 * (2 + 3) * 64 * 64 + 2 * 3 * 2 * 64 + 2 * 3 * 2 * mc + 2 * 3 * 100 * (3 * 64 + 1)) * 4
+    assert two == (2 * 3 * (2 + 3) * 64 * 64 + 2 * 3 * 2 * 64 + 2 * 3 * 2 * mc) * 4
 
     def bwd(**kw):
         a = dict(q=P(0), k=P(1), v=P(2), beta=P(3), z=P(4), A=P(5), S_in=None, do=P(6), dS_out=None, dq=P(7),
