@@ -63,8 +63,8 @@ struct Layout {
   static constexpr int V = DW + 16 * RK, DO = V + 16 * RV, U = DO + 16 * RV, DU = U + 16 * RV;
   // [16][RS] small matrices
   static constexpr int AL = DU + 16 * RV, L = AL + 16 * RS, P = L + 16 * RS, M = P + 16 * RS, TT = M + 16 * RS,
-                       DP = TT + 16 * RS, DT0 = DP + 16 * RS, DT1 = DT0 + 16 * RS, DM = DT1 + 16 * RS,
-                       Y = DM + 16 * RS, DAL = Y + 16 * RS;
+                       DP = TT + 16 * RS, DT0 = DP + 16 * RS, DT1 = DT0 + 16 * RS,
+                       Y = DT1 + 16 * RS, DAL = Y + 16 * RS;
   // vectors
   static constexpr int BETA = DAL + 16 * RS, GL = BETA + 16, DGL = GL + DK, EA = DGL + DK;
   // [16][RK]: sigma(e^A z) and e^A z of the sub-chunk, kept for the gate's derivative
@@ -174,7 +174,6 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
   float* sdP = sm + Ly::DP;
   float* sdT0 = sm + Ly::DT0;
   float* sdT1 = sm + Ly::DT1;
-  float* sdM = sm + Ly::DM;
   float* sY = sm + Ly::Y;
   float* sdAL = sm + Ly::DAL;
   float* sBeta = sm + Ly::BETA;
@@ -819,21 +818,28 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
       relane();
 
       // ---- wave 0: dM = dT Diag(beta), Y = M^T dM, dL = -strict_lower(Y M^T), dAL = Diag(beta) dL,
-      // dbeta; one wavefront end to end (its own LDS writes are read back in order)
+      // dbeta; one wavefront end to end, the 16 x 16 matrices in registers in the accumulator
+      // layout (lane (g4, r16): rows 4 g4 .. 4 g4 + 3 of column r16; a product takes its left
+      // factor as that factor's transpose in that layout): Y^T = dM^T M, then Y M^T.
       if (wv == 0) {
+        f32x4 dt, dm, ma, mt;
+        const float bu = sBeta[r16];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = 4 * g4 + e;
-          sdM[t * RS + r16] = (sdT0[t * RS + r16] + sdT1[t * RS + r16]) * sBeta[r16];
+          dt[e] = sdT0[t * RS + r16] + sdT1[t * RS + r16];
+          dm[e] = dt[e] * bu;
+          ma[e] = sM[t * RS + r16];  // M
+          mt[e] = sM[r16 * RS + t];  // M^T
         }
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        auto mm16 = [](f32x4 xt, f32x4 y, f32x4 c) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) acc = mma4(sM[(4 * kb + g4) * RS + r16], sdM[(4 * kb + g4) * RS + r16], acc);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sY[(4 * g4 + e) * RS + r16] = acc[e];
-        acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) acc = mma4(sY[r16 * RS + 4 * kb + g4], sM[r16 * RS + 4 * kb + g4], acc);
+          for (int v = 0; v < 4; ++v) c = mma4(xt[v], y[v], c);
+          return c;
+        };
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 yt = mm16(dm, ma, zero);   // Y^T = dM^T M
+        const f32x4 acc = mm16(yt, mt, zero);  // Y M^T
         float dlv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -841,8 +847,12 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
           dlv[e] = r16 < t ? -acc[e] : 0.f;
           sdAL[t * RS + r16] = dlv[e] * sBeta[t];
         }
-        // dbeta_u = sum_t dT[t][u] M[t][u] + sum_s dL[u][s] AL[u][s]: the second sum is a row
-        // sum of the lanes' products, reduced over the 16 lanes of each row group
+        // dbeta_u = sum_t dT[t][u] M[t][u] + sum_s dL[u][s] AL[u][s]: the first is a column sum
+        // of the lanes' products, reduced over the four lane groups; the second a row sum,
+        // reduced over the 16 lanes of each row group
+        float cs = dt[0] * ma[0] + dt[1] * ma[1] + dt[2] * ma[2] + dt[3] * ma[3];
+        cs += __shfl_xor(cs, 16);
+        cs += __shfl_xor(cs, 32);  // column r16's sum, in every lane group
         float rs[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -860,9 +870,7 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
         }
         if (ln < SC) {
           const int u = ln;
-          float db = sY[u * RS + 16];
-#pragma unroll
-          for (int t = 0; t < SC; ++t) db += (sdT0[t * RS + u] + sdT1[t * RS + u]) * sM[t * RS + u];
+          const float db = cs + sY[u * RS + 16];
           if (u < n) put(&gbeta[(static_cast<int64_t>(b) * T + t0 + u) * H + h], db);
         }
       }
