@@ -24,10 +24,14 @@
 // With g >= -5 per token, Gam and 1/Gam stay within [e^-80, e^80] (fp32 normal
 // range), so the products above are plain matrix products.
 //
-// One workgroup (8 wavefronts) per (b, h) walks the 64-token blocks in reverse.
-// The forward left the state entering each block (checkpoints); the workgroup
-// first recomputes the states entering the block's later sub-chunks (into a
-// per-workgroup scratch, L2-resident), then runs the sub-chunks backwards.
+// One workgroup (8 wavefronts) per (b, h), or per (b, h, half of the value columns)
+// when B*H alone would leave compute units idle, walks the 64-token blocks in
+// reverse.  The forward left the state entering each block (checkpoints); the
+// workgroup first recomputes the states entering the block's later sub-chunks (into
+// a per-workgroup scratch, L2-resident), then runs the sub-chunks backwards.  With
+// two slices, each adds its part of the key-side gradients into zero-filled outputs.
+// M = (I + L)^-1 is a product of four factors formed by repeated squaring, on fp32
+// matrix cores for every input dtype.
 // fp32 inputs: every product runs on v_mfma_f32_16x16x4_f32 (fp32 operands): lane
 // i supplies A[i % 16][i / 16] and B[i / 16][i % 16] and holds D[4 (i / 16) + v][i % 16].
 // bf16 inputs: the products run on v_mfma_f32_16x16x16_bf16 (bf16 operands, fp32
