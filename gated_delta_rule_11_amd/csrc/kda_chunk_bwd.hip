@@ -68,7 +68,7 @@ struct Layout {
   // [16][RS] small matrices
   static constexpr int AL = DU + 16 * RV, L = AL + 16 * RS, P = L + 16 * RS, M = P + 16 * RS, TT = M + 16 * RS,
                        DP = TT + 16 * RS, DT0 = DP + 16 * RS, DT1 = DT0 + 16 * RS,
-                       Y = DT1 + 16 * RS, DAL = Y + 16 * RS;
+                       DAL = DT1 + 16 * RS;
   // vectors
   static constexpr int BETA = DAL + 16 * RS, GL = BETA + 16, DGL = GL + DK, EA = DGL + DK;
   // [16][RK]: sigma(e^A z) and e^A z of the sub-chunk, kept for the gate's derivative
@@ -178,7 +178,6 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
   float* sdP = sm + Ly::DP;
   float* sdT0 = sm + Ly::DT0;
   float* sdT1 = sm + Ly::DT1;
-  float* sY = sm + Ly::Y;
   float* sdAL = sm + Ly::DAL;
   float* sBeta = sm + Ly::BETA;
   float* sGl = sm + Ly::GL;
@@ -824,17 +823,19 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
       // ---- wave 0: dM = dT Diag(beta), Y = M^T dM, dL = -strict_lower(Y M^T), dAL = Diag(beta) dL,
       // dbeta; one wavefront end to end, the 16 x 16 matrices in registers in the accumulator
       // layout (lane (g4, r16): rows 4 g4 .. 4 g4 + 3 of column r16; a product takes its left
-      // factor as that factor's transpose in that layout): Y^T = dM^T M, then Y M^T.
+      // factor as that factor's transpose in that layout): Y^T = dM^T M, then Y M^T, and its
+      // transpose M Y^T for dbeta's row sums.
       if (wv == 0) {
-        f32x4 dt, dm, ma, mt;
+        f32x4 dt, dm, ma, mt, alt;
         const float bu = sBeta[r16];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = 4 * g4 + e;
           dt[e] = sdT0[t * RS + r16] + sdT1[t * RS + r16];
           dm[e] = dt[e] * bu;
-          ma[e] = sM[t * RS + r16];  // M
-          mt[e] = sM[r16 * RS + t];  // M^T
+          ma[e] = sM[t * RS + r16];    // M
+          mt[e] = sM[r16 * RS + t];    // M^T
+          alt[e] = sAL[r16 * RS + t];  // AL^T
         }
         auto mm16 = [](f32x4 xt, f32x4 y, f32x4 c) {
 #pragma unroll
@@ -842,40 +843,28 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
           return c;
         };
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 yt = mm16(dm, ma, zero);   // Y^T = dM^T M
-        const f32x4 acc = mm16(yt, mt, zero);  // Y M^T
-        float dlv[4];
+        const f32x4 yt = mm16(dm, ma, zero);    // Y^T = dM^T M
+        const f32x4 acc = mm16(yt, mt, zero);   // Y M^T
+        const f32x4 acct = mm16(mt, yt, zero);  // M Y^T = (Y M^T)^T
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = 4 * g4 + e;
-          dlv[e] = r16 < t ? -acc[e] : 0.f;
-          sdAL[t * RS + r16] = dlv[e] * sBeta[t];
+          sdAL[t * RS + r16] = (r16 < t ? -acc[e] : 0.f) * sBeta[t];
         }
-        // dbeta_u = sum_t dT[t][u] M[t][u] + sum_s dL[u][s] AL[u][s]: the first is a column sum
-        // of the lanes' products, reduced over the four lane groups; the second a row sum,
-        // reduced over the 16 lanes of each row group
+        // dbeta_u = sum_t dT[t][u] M[t][u] + sum_s dL[u][s] AL[u][s]: column u's sums of
+        // dT o M and of (dL o AL)^T (lane (g4, r16) holds dL[r16][4 g4 + e] in acct), each
+        // over the lane's four rows and then over the four lane groups
         float cs = dt[0] * ma[0] + dt[1] * ma[1] + dt[2] * ma[2] + dt[3] * ma[3];
+        float rs = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rs += (4 * g4 + e < r16 ? -acct[e] : 0.f) * alt[e];
         cs += __shfl_xor(cs, 16);
-        cs += __shfl_xor(cs, 32);  // column r16's sum, in every lane group
-        float rs[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 4 * g4 + e;
-          float x = dlv[e] * sAL[t * RS + r16];
-          x += __shfl_xor(x, 1);
-          x += __shfl_xor(x, 2);
-          x += __shfl_xor(x, 4);
-          x += __shfl_xor(x, 8);
-          rs[e] = x;  // row t's sum, in every lane of the row group
-        }
-        if (r16 == 0) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sY[(4 * g4 + e) * RS + 16] = rs[e];  // spare column 16 of Y
-        }
+        rs += __shfl_xor(rs, 16);
+        cs += __shfl_xor(cs, 32);
+        rs += __shfl_xor(rs, 32);
         if (ln < SC) {
-          const int u = ln;
-          const float db = cs + sY[u * RS + 16];
-          if (u < n) put(&gbeta[(static_cast<int64_t>(b) * T + t0 + u) * H + h], db);
+          const int u = ln;  // = r16: lane group 0
+          if (u < n) put(&gbeta[(static_cast<int64_t>(b) * T + t0 + u) * H + h], cs + rs);
         }
       }
       bw_barrier();
