@@ -68,7 +68,7 @@ struct Layout {
   // [16][RS] small matrices
   static constexpr int AL = DU + 16 * RV, L = AL + 16 * RS, P = L + 16 * RS, M = P + 16 * RS, TT = M + 16 * RS,
                        DP = TT + 16 * RS, DT0 = DP + 16 * RS, DT1 = DT0 + 16 * RS,
-                       DAL = DT1 + 16 * RS;
+                       DT2 = DT1 + 16 * RS, DAL = DT2 + 16 * RS;
   // vectors
   static constexpr int BETA = DAL + 16 * RS, GL = BETA + 16, DGL = GL + DK, EA = DGL + DK;
   // [16][RK]: sigma(e^A z) and e^A z of the sub-chunk, kept for the gate's derivative
@@ -178,6 +178,7 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
   float* sdP = sm + Ly::DP;
   float* sdT0 = sm + Ly::DT0;
   float* sdT1 = sm + Ly::DT1;
+  float* sdT2 = sm + Ly::DT2;
   float* sdAL = sm + Ly::DAL;
   float* sBeta = sm + Ly::BETA;
   float* sGl = sm + Ly::GL;
@@ -209,7 +210,10 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
   const bool own_c = wv < NKT;  // key-row tile ct = wv (state transposed)
   const int jt = wv, ct = wv;
   // wavefronts with no value tile of their own take the 16 x 16 products
-  constexpr int W_DP = NW - 1, W_DT0 = NW - 2, W_DT1 = NW - 3;
+  constexpr int W_DP = NW - 1, W_DT0 = NW - 2, W_DT1 = NW - 3, W_DT2 = NW - 4;
+  // dW Kt^T over the key channels in two halves, on two wavefronts of different SIMDs
+  // (from d_k = 32 on: each half's lane-group quarter stays a multiple of four channels)
+  constexpr bool kSplitDT1 = DK >= 32;
   const int nblk = (T + CK - 1) / CK;
   const int64_t SZ = static_cast<int64_t>(DK) * DV;
   const float* ckpt = a.ckpt + static_cast<int64_t>(bh) * nblk * SZ;
@@ -800,7 +804,15 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
           if (t < n) a.grad_v[((static_cast<int64_t>(b) * T + t0 + t) * H + h) * DV + j0 + 16 * jt + r16] = acc[e];
         }
       }
-      if (wv == W_DT1) {  // dW Kt^T
+      if constexpr (kSplitDT1) {  // dW Kt^T, channels 0 .. DK/2 - 1 and DK/2 .. DK - 1
+        if (wv == W_DT1 || wv == W_DT2) {
+          const int k0 = wv == W_DT1 ? 0 : DK / 2;
+          const f32x4 acc = mm_nt(sdW + k0, sKt + k0, std::integral_constant<int, DK / 2>{}, RK, std::false_type{});
+          float* dst = wv == W_DT1 ? sdT1 : sdT2;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dst[(4 * g4 + e) * RS + r16] = acc[e];
+        }
+      } else if (wv == W_DT1) {  // dW Kt^T
         const f32x4 acc = mm_nt(sdW, sKt, std::integral_constant<int, DK>{}, RK, std::false_type{});
 #pragma unroll
         for (int e = 0; e < 4; ++e) sdT1[(4 * g4 + e) * RS + r16] = acc[e];
@@ -832,6 +844,7 @@ __global__ __launch_bounds__(bw::NT) void chunk_bwd_kernel(const BwdArgs a) {
         for (int e = 0; e < 4; ++e) {
           const int t = 4 * g4 + e;
           dt[e] = sdT0[t * RS + r16] + sdT1[t * RS + r16];
+          if constexpr (kSplitDT1) dt[e] += sdT2[t * RS + r16];
           dm[e] = dt[e] * bu;
           ma[e] = sM[t * RS + r16];    // M
           mt[e] = sM[r16 * RS + t];    // M^T
